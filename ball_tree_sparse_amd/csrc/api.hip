@@ -1,0 +1,221 @@
+// C ABI of libbtsparse: host-side validation, workspace sizing and launches.
+// Every argument check runs before any HIP call, so a rejected call never
+// touches the device (and can be exercised on a machine without a GPU).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.h"
+
+namespace bt {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+bt_status launch_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return BT_EHIP;
+  }
+  return BT_OK;
+}
+
+// implemented in the kernel units
+size_t tree_workspace_size(int64_t n, int leaf);
+bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const float* R,
+                            int32_t* perm, void* ws, hipStream_t st);
+bt_status permute_launch(const void* src, const int32_t* perm, int64_t n, int64_t row_bytes,
+                         bt_perm_mode mode, void* dst, hipStream_t st);
+bt_status invert_perm_launch(const int32_t* perm, int64_t n, int32_t* inv, hipStream_t st);
+bt_status ball_attn_launch(const void* q, const void* k, const void* v, const int32_t* perm,
+                           int64_t N, int32_t ball, int32_t H, int32_t d, bt_dtype dt,
+                           void* out, hipStream_t st);
+size_t bsa_ws_size(int64_t N, int32_t H, int32_t d, const bsa_params* p);
+bt_status bsa_launch(const void* q, const void* k, const void* v, const int32_t* perm, int64_t N,
+                     int32_t H, int32_t d, const bsa_params* p, const float* gate_w,
+                     const float* gate_b, const float* gate_const, int32_t* sel_out, void* ws,
+                     void* out, hipStream_t st);
+
+static bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+static bool valid_tree_shape(int64_t N, int32_t leaf) {
+  return N >= 1 && leaf >= 1 && N < ((int64_t)1 << 31) && N % leaf == 0 && is_pow2(N / leaf);
+}
+
+static bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const char* x = (const char*)a;
+  const char* y = (const char*)b;
+  return x < y + bn && y < x + an;
+}
+
+}  // namespace bt
+
+using namespace bt;
+
+extern "C" {
+
+const char* bt_status_str(bt_status s) {
+  switch (s) {
+    case BT_OK: return "ok";
+    case BT_EINVAL: return "invalid argument";
+    case BT_EHIP: return "HIP runtime error";
+    case BT_ENOMEM: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+const char* bt_last_error(void) { return g_err; }
+
+const char* bt_version(void) { return "btsparse 0.1 (gfx950)"; }
+
+size_t bt_build_workspace_size(int64_t N, int32_t leaf) {
+  if (!valid_tree_shape(N, leaf)) return 0;
+  return tree_workspace_size(N, leaf);
+}
+
+static bt_status build_common(const float* coords, int64_t N, int32_t leaf, const float* R,
+                              int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
+  BT_REQUIRE(coords && perm, "coords and perm must be non-null");
+  BT_REQUIRE(N >= 1 && leaf >= 1, "need N >= 1 and leaf >= 1 (N=%lld, leaf=%d)", (long long)N,
+             leaf);
+  BT_REQUIRE(N < ((int64_t)1 << 31), "N must be below 2^31");
+  BT_REQUIRE(N % leaf == 0 && is_pow2(N / leaf), "N must be leaf * 2^L (N=%lld, leaf=%d)",
+             (long long)N, leaf);
+  BT_REQUIRE(ws != nullptr, "workspace must be non-null");
+  BT_REQUIRE(((uintptr_t)ws & 255) == 0, "workspace must be 256-byte aligned");
+  const size_t need = tree_workspace_size(N, leaf);
+  if (ws_bytes < need) {
+    set_error("workspace holds %zu bytes, bt_build needs %zu", ws_bytes, need);
+    return BT_ENOMEM;
+  }
+  return tree_build_launch(coords, N, leaf, R, perm, ws, (hipStream_t)stream);
+}
+
+bt_status bt_build(const float* coords, int64_t N, int32_t leaf, int32_t* perm, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return build_common(coords, N, leaf, nullptr, perm, ws, ws_bytes, stream);
+}
+
+bt_status bt_rotate_build(const float* coords, int64_t N, int32_t leaf, const float* R_host,
+                          int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
+  BT_REQUIRE(R_host != nullptr, "rotation matrix must be non-null");
+  for (int i = 0; i < 9; ++i)
+    BT_REQUIRE(R_host[i] == R_host[i] && R_host[i] - R_host[i] == 0.0f,
+               "rotation matrix must be finite");
+  return build_common(coords, N, leaf, R_host, perm, ws, ws_bytes, stream);
+}
+
+bt_status bt_permute(const void* src, const int32_t* perm, int64_t N, int64_t row_bytes,
+                     bt_perm_mode mode, void* dst, void* stream) {
+  BT_REQUIRE(N >= 0, "N must be >= 0");
+  BT_REQUIRE(N < ((int64_t)1 << 31), "N must be below 2^31");
+  BT_REQUIRE(row_bytes > 0 && row_bytes % 4 == 0, "row_bytes must be a positive multiple of 4");
+  BT_REQUIRE(mode == BT_GATHER || mode == BT_SCATTER, "mode must be BT_GATHER or BT_SCATTER");
+  if (N == 0) return BT_OK;
+  BT_REQUIRE(src && dst && perm, "src, dst and perm must be non-null");
+  BT_REQUIRE(!overlaps(src, (size_t)(N * row_bytes), dst, (size_t)(N * row_bytes)),
+             "src and dst must not overlap");
+  return permute_launch(src, perm, N, row_bytes, mode, dst, (hipStream_t)stream);
+}
+
+bt_status bt_invert_perm(const int32_t* perm, int64_t N, int32_t* inv, void* stream) {
+  BT_REQUIRE(N >= 0 && N < ((int64_t)1 << 31), "need 0 <= N < 2^31");
+  if (N == 0) return BT_OK;
+  BT_REQUIRE(perm && inv, "perm and inv must be non-null");
+  BT_REQUIRE(!overlaps(perm, (size_t)N * 4, inv, (size_t)N * 4), "perm and inv must not overlap");
+  return invert_perm_launch(perm, N, inv, (hipStream_t)stream);
+}
+
+bt_status ball_attn(const void* q, const void* k, const void* v, const int32_t* perm, int64_t N,
+                    int32_t ball, int32_t H, int32_t d, bt_dtype dt, void* out, void* stream) {
+  BT_REQUIRE(q && k && v && out, "q, k, v and out must be non-null");
+  BT_REQUIRE(dt == BT_F32 || dt == BT_BF16, "dtype must be BT_F32 or BT_BF16");
+  BT_REQUIRE(d == 16 || d == 32 || d == 64, "d must be 16, 32 or 64 (d=%d)", d);
+  BT_REQUIRE(H >= 1, "H must be >= 1");
+  BT_REQUIRE(N >= 1 && ball >= 1 && N % ball == 0, "ball must divide N (N=%lld, ball=%d)",
+             (long long)N, ball);
+  BT_REQUIRE(ball <= 4096, "ball must be <= 4096");
+  BT_REQUIRE(N * H * d < ((int64_t)1 << 31), "N*H*d must be below 2^31");
+  BT_REQUIRE((N / ball) * H < ((int64_t)1 << 31), "too many (ball, head) pairs");
+  const size_t bytes = (size_t)(N * H * d) * (dt == BT_F32 ? 4 : 2);
+  BT_REQUIRE(!overlaps(out, bytes, q, bytes) && !overlaps(out, bytes, k, bytes) &&
+                 !overlaps(out, bytes, v, bytes),
+             "out must not alias q, k or v");
+  if (dt == BT_BF16) {
+    BT_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16 == 0,
+               "bf16 tensors must be 16-byte aligned");
+  } else {
+    BT_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 4 == 0,
+               "fp32 tensors must be 4-byte aligned");
+  }
+  return ball_attn_launch(q, k, v, perm, N, ball, H, d, dt, out, (hipStream_t)stream);
+}
+
+static bt_status check_bsa(int64_t N, int32_t H, int32_t d, const bsa_params* p) {
+  BT_REQUIRE(p != nullptr, "bsa_params must be non-null");
+  BT_REQUIRE(d == 32 || d == 64, "BSA supports d = 32 or 64 (d=%d)", d);
+  BT_REQUIRE(H >= 1, "H must be >= 1");
+  BT_REQUIRE(N >= 1 && N < ((int64_t)1 << 31) && N * H * d < ((int64_t)1 << 31),
+             "N*H*d must be below 2^31");
+  const int32_t ball = p->ball, block = p->block, group = p->group, topk = p->topk;
+  BT_REQUIRE(ball >= 32 && block >= 32 && group >= 32 && ball % 32 == 0 && block % 32 == 0 &&
+                 group % 32 == 0,
+             "ball, block and group must be positive multiples of 32");
+  BT_REQUIRE(ball <= 256, "ball must be <= 256");
+  BT_REQUIRE(group <= 256, "group must be <= 256");
+  BT_REQUIRE(N % ball == 0 && ball % block == 0 && N % group == 0,
+             "need ball | N, block | ball and group | N");
+  BT_REQUIRE(group == 32 || group == 64 || group == 128 || group == 256,
+             "group must be 32, 64, 128 or 256");
+  BT_REQUIRE(ball % group == 0, "group must divide ball");
+  const int64_t nc = N / block;
+  BT_REQUIRE(nc % 32 == 0 && nc <= 8192, "N/block must be a multiple of 32 and <= 8192");
+  const int64_t masked = p->mask_own_ball ? ball / block : 0;
+  BT_REQUIRE(topk >= 1 && topk <= 64 && topk <= nc - masked,
+             "need 1 <= topk <= 64 and topk <= N/block - masked blocks (%lld)",
+             (long long)(nc - masked));
+  return BT_OK;
+}
+
+size_t bsa_workspace_size(int64_t N, int32_t H, int32_t d, const bsa_params* p) {
+  if (check_bsa(N, H, d, p) != BT_OK) return 0;
+  return bsa_ws_size(N, H, d, p);
+}
+
+bt_status bsa_attn(const void* q, const void* k, const void* v, const int32_t* perm, int64_t N,
+                   int32_t H, int32_t d, bt_dtype dt, const bsa_params* p, const float* gate_w,
+                   const float* gate_b, const float* gate_const_host, int32_t* sel_out, void* ws,
+                   size_t ws_bytes, void* out, void* stream) {
+  BT_REQUIRE(q && k && v && out && perm, "q, k, v, perm and out must be non-null");
+  BT_REQUIRE(dt == BT_BF16, "bsa_attn supports bf16 inputs");
+  bt_status s = check_bsa(N, H, d, p);
+  if (s != BT_OK) return s;
+  BT_REQUIRE((gate_w == nullptr) != (gate_const_host == nullptr),
+             "give exactly one of gate_w and gate_const");
+  if (gate_const_host)
+    for (int i = 0; i < 3; ++i)
+      BT_REQUIRE(gate_const_host[i] == gate_const_host[i], "gate_const must not be NaN");
+  const size_t bytes = (size_t)(N * H * d) * 2;
+  BT_REQUIRE(!overlaps(out, bytes, q, bytes) && !overlaps(out, bytes, k, bytes) &&
+                 !overlaps(out, bytes, v, bytes),
+             "out must not alias q, k or v");
+  BT_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16 == 0,
+             "bf16 tensors must be 16-byte aligned");
+  BT_REQUIRE(ws != nullptr && ((uintptr_t)ws & 255) == 0,
+             "workspace must be non-null and 256-byte aligned");
+  const size_t need = bsa_ws_size(N, H, d, p);
+  if (ws_bytes < need) {
+    set_error("workspace holds %zu bytes, bsa_attn needs %zu", ws_bytes, need);
+    return BT_ENOMEM;
+  }
+  return bsa_launch(q, k, v, perm, N, H, d, p, gate_w, gate_b, gate_const_host, sel_out, ws, out,
+                    (hipStream_t)stream);
+}
+
+}  // extern "C"

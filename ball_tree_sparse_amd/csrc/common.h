@@ -1,0 +1,102 @@
+// Shared device/host helpers for libbtsparse (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bt.h"
+
+#define BT_DEV __device__ __forceinline__
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace bt {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 ----
+BT_DEV float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Round-to-nearest-even through the gfx950 packed converter.
+BT_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return uint32_t(__builtin_bit_cast(uint16_t, a)) |
+         (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+// ------------------------------------------------------ float sort keys ----
+// Order-preserving map of a finite float to uint32 (-0.0 is canonicalised to
+// +0.0 before this is called, so equal values give equal keys).
+BT_DEV uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+BT_DEV float key_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+BT_DEV float canon_zero(float f) { return f == 0.0f ? 0.0f : f; }
+
+// A permutation entry used as a gather/scatter index, forced into [0, n):
+// a caller that passes something other than a permutation gets wrong rows,
+// never an access outside the tensor.  (n < 2^31.)
+BT_DEV int64_t perm_index(int32_t p, int64_t n) {
+  return (int64_t)min((uint32_t)p, (uint32_t)(n - 1));
+}
+
+// ------------------------------------------------------ wave reductions ----
+template <typename T>
+BT_DEV T wave_shfl_xor(T v, int m) { return __shfl_xor(v, m, kWave); }
+
+BT_DEV float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+BT_DEV uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, m, kWave));
+  return v;
+}
+BT_DEV uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, kWave));
+  return v;
+}
+BT_DEV uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += (uint32_t)__shfl_xor((int)v, m, kWave);
+  return v;
+}
+// Inclusive prefix sum across the 64 lanes of a wave.
+BT_DEV uint32_t wave_incl_scan_u32(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = (uint32_t)__shfl_up((int)v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+}  // namespace bt
+
+// ------------------------------------------------------------ host side ----
+namespace bt {
+// Records a detail message for bt_last_error() on this thread.
+void set_error(const char* fmt, ...);
+bt_status launch_status(const char* what);
+}  // namespace bt
+
+#define BT_REQUIRE(cond, ...)                 \
+  do {                                        \
+    if (!(cond)) {                            \
+      bt::set_error(__VA_ARGS__);             \
+      return BT_EINVAL;                       \
+    }                                         \
+  } while (0)

@@ -1,0 +1,234 @@
+"""ctypes binding of libbtsparse (include/bt.h).
+
+Argument marshalling only: torch tensors become device pointers and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no CPU fallback: if the library is missing or a tensor is
+not on the GPU, the call raises.
+
+Names follow the C ABI: ``bt_build``, ``bt_rotate_build``, ``bt_permute``,
+``bt_invert_perm``, ``ball_attn``, ``bsa_attn``.  Output tensors and
+workspaces are allocated with torch (device memory plumbing); the library
+itself allocates nothing.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbtsparse.so")
+
+BT_OK, BT_EINVAL, BT_EHIP, BT_ENOMEM = 0, 1, 2, 3
+BT_F32, BT_BF16 = 0, 1
+BT_GATHER, BT_SCATTER = 0, 1
+
+
+class BtError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class BsaParams(C.Structure):
+    _fields_ = [("ball", C.c_int32), ("block", C.c_int32), ("group", C.c_int32),
+                ("topk", C.c_int32), ("mask_own_ball", C.c_int32)]
+
+
+_lib = None
+
+# (name, restype, argtypes) for every entry point in include/bt.h
+_P = C.c_void_p
+_SIGS = [
+    ("bt_status_str", C.c_char_p, [C.c_int]),
+    ("bt_last_error", C.c_char_p, []),
+    ("bt_version", C.c_char_p, []),
+    ("bt_build_workspace_size", C.c_size_t, [C.c_int64, C.c_int32]),
+    ("bt_build", C.c_int, [_P, C.c_int64, C.c_int32, _P, _P, C.c_size_t, _P]),
+    ("bt_rotate_build", C.c_int, [_P, C.c_int64, C.c_int32, C.POINTER(C.c_float), _P, _P,
+                                  C.c_size_t, _P]),
+    ("bt_permute", C.c_int, [_P, _P, C.c_int64, C.c_int64, C.c_int, _P, _P]),
+    ("bt_invert_perm", C.c_int, [_P, C.c_int64, _P, _P]),
+    ("ball_attn", C.c_int, [_P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32,
+                            C.c_int, _P, _P]),
+    ("bsa_workspace_size", C.c_size_t, [C.c_int64, C.c_int32, C.c_int32,
+                                        C.POINTER(BsaParams)]),
+    ("bsa_attn", C.c_int, [_P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int,
+                           C.POINTER(BsaParams), _P, _P, C.POINTER(C.c_float), _P, _P,
+                           C.c_size_t, _P, _P]),
+]
+EXPORTS = [s[0] for s in _SIGS]
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() first")
+        L = C.CDLL(LIB_PATH)
+        for name, res, args in _SIGS:
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != BT_OK:
+        L = lib()
+        raise BtError(status, f"{L.bt_status_str(status).decode()}: "
+                              f"{L.bt_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (no CPU fallback)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return BT_F32
+    if t.dtype == torch.bfloat16:
+        return BT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# --------------------------------------------------------------------- tree --
+
+def bt_build_workspace_size(N: int, leaf: int) -> int:
+    return lib().bt_build_workspace_size(N, leaf)
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def bt_build(coords, leaf: int, perm=None, workspace=None):
+    """Tree permutation of ``coords`` [N,3] fp32 -> int32 [N] (device)."""
+    _dev(coords, "coords", torch.float32)
+    N = coords.shape[0]
+    if perm is None:
+        perm = torch.empty(N, dtype=torch.int32, device=coords.device)
+    _dev(perm, "perm", torch.int32)
+    need = lib().bt_build_workspace_size(N, leaf)
+    if workspace is None:
+        workspace = _workspace(need, coords.device)
+    _check(lib().bt_build(_ptr(coords), N, leaf, _ptr(perm), _ptr(workspace),
+                          workspace.numel(), _stream(coords.device)))
+    return perm
+
+
+def bt_rotate_build(coords, leaf: int, R, perm=None, workspace=None):
+    """Tree of the coordinates rotated by the 3x3 matrix R (host values)."""
+    _dev(coords, "coords", torch.float32)
+    N = coords.shape[0]
+    r = torch.as_tensor(R, dtype=torch.float32).reshape(9).cpu().tolist()
+    rarr = (C.c_float * 9)(*r)
+    if perm is None:
+        perm = torch.empty(N, dtype=torch.int32, device=coords.device)
+    _dev(perm, "perm", torch.int32)
+    need = lib().bt_build_workspace_size(N, leaf)
+    if workspace is None:
+        workspace = _workspace(need, coords.device)
+    _check(lib().bt_rotate_build(_ptr(coords), N, leaf, rarr, _ptr(perm), _ptr(workspace),
+                                 workspace.numel(), _stream(coords.device)))
+    return perm
+
+
+# ------------------------------------------------------------------ permute --
+
+def bt_permute(src, perm, mode: int, dst=None):
+    """GATHER dst[t] = src[perm[t]]; SCATTER dst[perm[t]] = src[t] (rows)."""
+    _dev(src, "src")
+    _dev(perm, "perm", torch.int32)
+    N = src.shape[0]
+    row_bytes = src.numel() // max(N, 1) * src.element_size()
+    if dst is None:
+        dst = torch.empty_like(src)
+    _dev(dst, "dst", src.dtype)
+    _check(lib().bt_permute(_ptr(src), _ptr(perm), N, row_bytes, mode, _ptr(dst),
+                            _stream(src.device)))
+    return dst
+
+
+def bt_invert_perm(perm, inv=None):
+    _dev(perm, "perm", torch.int32)
+    if inv is None:
+        inv = torch.empty_like(perm)
+    _check(lib().bt_invert_perm(_ptr(perm), perm.numel(), _ptr(inv), _stream(perm.device)))
+    return inv
+
+
+# ---------------------------------------------------------------- attention --
+
+def ball_attn(q, k, v, perm, ball: int, out=None):
+    """Ball attention over [N,H,d] tensors (perm None = already tree order)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+        if t.shape != q.shape or t.dim() != 3:
+            raise ValueError("q, k, v must share one [N,H,d] shape")
+    if perm is not None:
+        _dev(perm, "perm", torch.int32)
+    N, H, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    _check(lib().ball_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), N, ball, H, d,
+                           _dtype_code(q), _ptr(out), _stream(q.device)))
+    return out
+
+
+def bsa_workspace_size(N: int, H: int, d: int, ball: int, block: int, group: int,
+                       topk: int, mask_own_ball: bool = True) -> int:
+    p = BsaParams(ball, block, group, topk, int(bool(mask_own_ball)))
+    return lib().bsa_workspace_size(N, H, d, C.byref(p))
+
+
+def bsa_attn(q, k, v, perm, ball: int, block: int, group: int, topk: int,
+             mask_own_ball: bool = True, gate_w=None, gate_b=None, gate_const=None,
+             return_sel: bool = False, out=None, workspace=None):
+    """Ball Sparse Attention; returns out (and sel [H, N/group, topk])."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+        if t.shape != q.shape or t.dim() != 3:
+            raise ValueError("q, k, v must share one [N,H,d] shape")
+    _dev(perm, "perm", torch.int32)
+    N, H, d = q.shape
+    p = BsaParams(ball, block, group, topk, int(bool(mask_own_ball)))
+    if gate_w is not None:
+        _dev(gate_w, "gate_w", torch.float32)
+    if gate_b is not None:
+        _dev(gate_b, "gate_b", torch.float32)
+    gc = None
+    if gate_const is not None:
+        gc = (C.c_float * 3)(*[float(x) for x in gate_const])
+    sel = None
+    if return_sel:
+        sel = torch.empty((H, N // group, topk), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    need = lib().bsa_workspace_size(N, H, d, C.byref(p))
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    _check(lib().bsa_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), N, H, d, _dtype_code(q),
+                          C.byref(p), _ptr(gate_w), _ptr(gate_b), gc, _ptr(sel),
+                          _ptr(workspace), workspace.numel(), _ptr(out), _stream(q.device)))
+    return (out, sel) if return_sel else out

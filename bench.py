@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of the ball-tree + ball-attention hot path on one MI355X.
+
+One step = one pass of the path over one synthetic point cloud of the
+measured shape: the GPU ball-tree build (bt_build, leaf = ball) followed by
+ball attention (ball_attn) over that tree.  Inputs are resident in HBM before
+the timed region starts.  The q/k/v/out tensors rotate over several copies
+(default 4, 540 MB in all) so that no step finds its inputs in the 256 MB
+Infinity Cache left behind by the previous one.
+
+Prints ONE JSON line.  Besides the required fields it carries:
+  roofline      for the ball-attention kernel: algorithmic bytes per launch
+                (q, k, v read once, out written once, perm read once) over the
+                mean launch time measured with HIP events on the launching
+                stream, against the 8 TB/s HBM peak; `traffic` is the HBM
+                byte count of the kernel per launch from rocprofv3 FETCH_SIZE +
+                WRITE_SIZE counters (profiles/), or null if the kernel source
+                changed since they were taken;
+  cpu_baseline  the CPU oracle (NumPy: recursive tree + fp64 ball attention)
+                timed on this host on whole steps of the same workload.
+
+Other workloads (--workload bsa | cosmo | rotpair) print their own line and
+are not the default measurement.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ball-attn points/sec + TFLOP/s (% roofline) at N=65,536, ball 128, H=8 d=32"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def _src_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "ball_tree_sparse_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, src_names):
+    """Per-launch HBM bytes from the committed counter summary, if current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("src_hash") != _src_hash(src_names):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def _cpu_baseline(w, budget_s):
+    """The oracle on whole steps of the workload until the budget is spent."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention as A
+    from oracle import tree as T
+    n = w.coords.shape[0]
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        p = T.build(w.coords, w.leaf)
+        A.ball_attn(w.q, w.k, w.v, p, w.ball)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": steps * n / el, "unit": "points/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} whole steps (tree + fp64 ball attention) of the {n}-point "
+                      f"workload in {el:.1f} s; tree recursion single-threaded, attention "
+                      f"through {threads}-thread BLAS on {len(os.sched_getaffinity(0))} "
+                      f"host cores"}
+
+
+def bench_ball(args, dev, torch, ops, synth):
+    w = synth.make(args.workload)
+    N, H, d, ball, leaf = w.coords.shape[0], w.H, w.d, w.ball, w.leaf
+    coords = torch.from_numpy(w.coords).to(dev)
+    perm = torch.empty(N, dtype=torch.int32, device=dev)
+    ws = torch.empty(ops.bt_build_workspace_size(N, leaf), dtype=torch.uint8, device=dev)
+    sets = []
+    for _ in range(args.sets):
+        q, k, v = (t.to(dev).clone() for t in (w.q, w.k, w.v))
+        sets.append((q, k, v, torch.empty_like(q)))
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = []
+
+    def step(i, timed):
+        q, k, v, out = sets[i % len(sets)]
+        if timed:
+            e = [ev() for _ in range(3)]
+            e[0].record()
+            ops.bt_build(coords, leaf, perm=perm, workspace=ws)
+            e[1].record()
+            ops.ball_attn(q, k, v, perm, ball, out=out)
+            e[2].record()
+            marks.append(e)
+        else:
+            ops.bt_build(coords, leaf, perm=perm, workspace=ws)
+            ops.ball_attn(q, k, v, perm, ball, out=out)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    build_us = sum(e[0].elapsed_time(e[1]) for e in marks) / len(marks) * 1e3
+    attn_us = sum(e[1].elapsed_time(e[2]) for e in marks) / len(marks) * 1e3
+
+    esize = 2 if w.dtype == "bf16" else 4
+    attn_bytes = 4 * N * H * d * esize + 4 * N
+    attn_flops = 4 * N * ball * d * H
+    achieved = attn_bytes / (attn_us * 1e-6) / 1e9
+    traffic = _traffic(f"ball_attn/{args.workload}", ["ball_attn.hip", "common.h"])
+    ms = el / args.steps * 1e3
+    line = {
+        "metric": METRIC, "value": N / (ms * 1e-3), "unit": "points/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{args.workload}: tree build (leaf {leaf}) + ball attention, "
+                               f"N={N}, ball {ball}, H={H}, d={d}, {w.dtype}",
+                   "N": N, "ball": ball, "leaf": leaf, "H": H, "d": d,
+                   "input_sets_rotated": len(sets)},
+        "roofline": {"kernel": "ball_attn_mfma" if w.dtype == "bf16" else "ball_attn_valu",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes": attn_bytes},
+        "ball_attn": {"us": attn_us, "points_per_s": N / (attn_us * 1e-6),
+                      "tflops": attn_flops / (attn_us * 1e-6) / 1e12,
+                      "mfma_frac": attn_flops / (attn_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
+        "tree_build": {"us": build_us, "points_per_s": N / (build_us * 1e-6)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = _cpu_baseline(w, args.cpu_seconds)
+    return line
+
+
+def bench_bsa(args, dev, torch, ops, synth):
+    w = synth.make("bsa")
+    x = w.extra
+    N, H, d = w.coords.shape[0], w.H, w.d
+    coords = torch.from_numpy(w.coords).to(dev)
+    perm = torch.empty(N, dtype=torch.int32, device=dev)
+    ws = torch.empty(ops.bt_build_workspace_size(N, w.leaf), dtype=torch.uint8, device=dev)
+    bws = torch.empty(ops.bsa_workspace_size(N, H, d, w.ball, x["block"], x["group"], x["topk"]),
+                      dtype=torch.uint8, device=dev)
+    Wg = torch.from_numpy(w.gate_w).to(dev)
+    q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+    out = torch.empty_like(q)
+
+    def step():
+        ops.bt_build(coords, w.leaf, perm=perm, workspace=ws)
+        ops.bsa_attn(q, k, v, perm, w.ball, x["block"], x["group"], x["topk"],
+                     x["mask_own_ball"], gate_w=Wg, out=out, workspace=bws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms = el / args.steps * 1e3
+    flops = 4 * N * H * d * (w.ball + N // x["block"] + x["topk"] * x["block"])
+    return {"metric": "bsa points/sec", "value": N / (ms * 1e-3), "unit": "points/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "bsa: tree build (leaf 64) + BSA (ball 128, block 64, "
+                                   "group 64, top-16), N=65536, H=8, d=32"},
+            "attention_tflops": flops / (ms * 1e-3) / 1e12}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sphere",
+                    choices=["sphere", "cosmo", "rotpair", "tiny", "bsa"])
+    ap.add_argument("--sets", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from ball_tree_sparse_amd import ops, synth
+    ops.lib()                                  # fail loudly if the library is missing
+    dev = torch.device("cuda:0")
+    if args.workload == "bsa":
+        line = bench_bsa(args, dev, torch, ops, synth)
+    else:
+        line = bench_ball(args, dev, torch, ops, synth)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

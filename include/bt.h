@@ -1,0 +1,169 @@
+/*
+ * bt.h -- C ABI of libbtsparse: ball-tree partition, ball attention and Ball
+ * Sparse Attention (BSA) on AMD MI355X (gfx950).
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ * - Every call returns a bt_status.  Arguments are validated on the host
+ *   before anything is launched; a rejected call returns BT_EINVAL and
+ *   launches nothing.  A failed launch returns BT_EHIP.  bt_last_error()
+ *   gives a human-readable detail of the last failure on the calling thread.
+ * - Every call that launches work is asynchronous on `stream` (a hipStream_t
+ *   passed as void*; NULL = the null stream).  No call synchronises the
+ *   stream or copies between host and device.
+ * - Ownership: every tensor argument is device memory owned by the caller.
+ *   The library allocates nothing; calls that need scratch memory take a
+ *   caller-provided workspace whose size is given by the matching
+ *   *_workspace_size function.  Calls are stateless; concurrent calls on
+ *   different streams need different workspaces.
+ * - Layouts: coords is [N,3] fp32 row-major.  q, k, v and out are [N,H,d]
+ *   row-major and contiguous, in ORIGINAL point order when a permutation is
+ *   given and in tree order when perm == NULL.  perm[t] is the original index
+ *   of the point at tree position t (int32).
+ * - Element types: BT_F32 (fp32 arithmetic throughout) or BT_BF16 (bf16
+ *   inputs and output, fp32 accumulation and softmax).
+ */
+#ifndef BT_H
+#define BT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BT_OK = 0,
+  BT_EINVAL = 1,   /* bad argument; nothing was launched */
+  BT_EHIP = 2,     /* the HIP runtime reported an error at launch */
+  BT_ENOMEM = 3,   /* workspace smaller than *_workspace_size() */
+} bt_status;
+
+typedef enum { BT_F32 = 0, BT_BF16 = 1 } bt_dtype;
+
+typedef enum { BT_GATHER = 0, BT_SCATTER = 1 } bt_perm_mode;
+
+/* BSA hyper-parameters: ball = local attention ball size, block = compression
+ * and selection block size (l), group = contiguous query group size (g),
+ * topk = selected blocks per group (k*), mask_own_ball = 1 to exclude blocks
+ * inside the group's own ball(s) from selection. */
+typedef struct {
+  int32_t ball;
+  int32_t block;
+  int32_t group;
+  int32_t topk;
+  int32_t mask_own_ball;
+} bsa_params;
+
+const char* bt_status_str(bt_status s);
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* bt_last_error(void);
+/* Library version, for logs. */
+const char* bt_version(void);
+
+/* ------------------------------------------------------------------------
+ * Ball tree (Erwin thread on Bluesky, posts 6/N and 9/N: a ball tree splits
+ * the points recursively into nested sets of similar size and stores every
+ * ball contiguously; post 15/N: the tree is built by native code).
+ *
+ * Split rule: at every node the axis of largest fp32 spread (max - min,
+ * lowest axis on ties) is split into two equal halves; the left half holds
+ * the n/2 smallest points in (coordinate, original index) order, -0.0 equal
+ * to +0.0; points keep ascending original index inside each node.  The
+ * result is unique and bit-reproducible.
+ *
+ * bt_build: coords [N,3] fp32 (device), N = leaf * 2^L with 1 <= leaf,
+ *   N < 2^31; writes perm [N] int32 (device).  ws: device workspace of at
+ *   least bt_build_workspace_size(N, leaf) bytes, 256-byte aligned.
+ *   Coordinates must be finite (not checked).
+ *   Errors: BT_EINVAL for null pointers, N not leaf*2^L, N >= 2^31;
+ *   BT_ENOMEM for a short workspace.
+ * ---------------------------------------------------------------------- */
+size_t bt_build_workspace_size(int64_t N, int32_t leaf);
+bt_status bt_build(const float* coords, int64_t N, int32_t leaf, int32_t* perm,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* bt_rotate_build: the second tree of a rotated pair (Erwin thread: trees are
+ * rotated instead of shifting windows, so that alternate layers exchange
+ * information across balls).  The tree is built on x' = R x with R a 3x3
+ * row-major fp32 matrix in HOST memory; each product and sum is rounded to
+ * fp32 separately: x'_a = ((R[a][0]*x + R[a][1]*y) + R[a][2]*z).  R must be
+ * finite (orthogonality is not checked).  Same arguments and errors as
+ * bt_build otherwise. */
+bt_status bt_rotate_build(const float* coords, int64_t N, int32_t leaf,
+                          const float* R_host, int32_t* perm, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Permutation of rows (Erwin thread, post 9/N: tree-ordered storage; the
+ * rotated pair moves features from one tree order to the other).
+ * GATHER:  dst[t]       = src[perm[t]]
+ * SCATTER: dst[perm[t]] = src[t]
+ * Rows are row_bytes bytes (a multiple of 4; multiples of 16 use 128-bit
+ * accesses).  src and dst are device buffers of N rows that must not
+ * overlap; perm must be a permutation of 0..N-1 (not checked).
+ * Errors: BT_EINVAL for null pointers, N < 0, bad row_bytes, src == dst.
+ * ---------------------------------------------------------------------- */
+bt_status bt_permute(const void* src, const int32_t* perm, int64_t N,
+                     int64_t row_bytes, bt_perm_mode mode, void* dst,
+                     void* stream);
+
+/* inv[perm[t]] = t for t < N (device buffers). */
+bt_status bt_invert_perm(const int32_t* perm, int64_t N, int32_t* inv,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
+ * Ball attention (Erwin thread, post 7/N: attention inside the balls of a
+ * chosen tree level, all balls in parallel; Pith review of arXiv 2506.12541,
+ * "What carries the argument": scaled dot-product attention within each
+ * ball).  For every ball b (tree positions [b*ball, (b+1)*ball)) and head h:
+ *   O = softmax(Q_b K_b^T / sqrt(d)) V_b,
+ * no mask, no bias, non-causal.  out[perm[t]] = O[t] (out in the same order
+ * and dtype as the inputs).
+ * Requirements: ball >= 1 divides N; 1 <= H; d in {16, 32, 64};
+ * ball <= 4096; N*H*d < 2^31; out does not alias q, k or v.
+ * bf16 with d in {32, 64} and ball a multiple of 32 up to 256 runs the MFMA
+ * kernel; every other supported shape runs the fp32-VALU kernel.
+ * ---------------------------------------------------------------------- */
+bt_status ball_attn(const void* q, const void* k, const void* v,
+                    const int32_t* perm, int64_t N, int32_t ball, int32_t H,
+                    int32_t d, bt_dtype dt, void* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Ball Sparse Attention (Pith review of arXiv 2506.12541: "What carries the
+ * argument", "Core claim", Figure 1 and Figure 3 captions; referee report
+ * major comments 1 and 2, Eqs. 10-15).  In tree order:
+ *   O_ball: ball attention with ball size p->ball;
+ *   Kc, Vc: means of K, V over contiguous blocks of p->block positions;
+ *   O_cmp:  softmax(q Kc^T / sqrt(d)) Vc over all N/block coarse tokens;
+ *   s[g,h,j] = mean_{t in group g}(q_t) . Kc_j / sqrt(d) in fp32; blocks
+ *           overlapping a ball that holds a position of g are excluded when
+ *           p->mask_own_ball; the p->topk best blocks are kept (ties to the
+ *           smaller block index);
+ *   O_slc:  each query of g attends once over the union of its selected
+ *           blocks at full resolution;
+ *   out = G0*O_ball + G1*O_cmp + G2*O_slc with G = sigmoid(W q + b)
+ *         (gate_w [3,d] fp32 device, gate_b [3] fp32 device or NULL for 0),
+ *         or G = gate_const (host [3]) when gate_w == NULL.
+ * sel_out (device [H, N/group, topk] int32, or NULL) receives the selected
+ * blocks of every group and head, best first.
+ * Requirements: dt == BT_BF16; d in {32, 64}; perm non-NULL; ball and block
+ * multiples of 32 with ball <= 256, block | ball and ball | N; group in
+ * {32, 64, 128, 256} with group | ball; N/block a multiple of 32 and
+ * <= 8192; 1 <= topk <= 64 and topk <= N/block minus the masked blocks of a
+ * group; exactly one of gate_w and gate_const non-NULL.
+ * ws: device workspace of at least bsa_workspace_size() bytes.
+ * ---------------------------------------------------------------------- */
+size_t bsa_workspace_size(int64_t N, int32_t H, int32_t d, const bsa_params* p);
+bt_status bsa_attn(const void* q, const void* k, const void* v,
+                   const int32_t* perm, int64_t N, int32_t H, int32_t d,
+                   bt_dtype dt, const bsa_params* p, const float* gate_w,
+                   const float* gate_b, const float* gate_const_host,
+                   int32_t* sel_out, void* ws, size_t ws_bytes, void* out,
+                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BT_H */

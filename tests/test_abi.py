@@ -1,0 +1,118 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol that
+include/bt.h declares, and rejects bad arguments before touching a device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from ball_tree_sparse_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "bt.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)
+    keep = [n for n in names if n.startswith(("bt_", "ball_attn", "bsa_"))]
+    return sorted(set(keep))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.skip("library not built")
+    return ops.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert "bt_build" in names and "ball_attn" in names and "bsa_attn" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(names) == sorted(ops.EXPORTS)
+
+
+def test_status_strings(L):
+    for s in range(4):
+        assert L.bt_status_str(s)
+    assert b"gfx950" in L.bt_version()
+
+
+def _fake(n=1):
+    """Host buffers used as stand-in pointers: every call below is rejected
+    before the library could dereference them."""
+    return C.cast(C.create_string_buffer(max(n, 16) + 256), C.c_void_p)
+
+
+def test_build_rejects(L):
+    f = _fake()
+    assert L.bt_build(None, 8, 2, f, f, 1 << 20, None) == ops.BT_EINVAL
+    assert L.bt_build(f, 12, 4, f, f, 1 << 20, None) == ops.BT_EINVAL      # 12/4 not 2^L
+    assert b"leaf" in L.bt_last_error()
+    assert L.bt_build(f, 0, 1, f, f, 1 << 20, None) == ops.BT_EINVAL
+    assert L.bt_build(f, 1 << 31, 1, f, f, 1 << 20, None) == ops.BT_EINVAL
+    assert L.bt_build(f, 8, 2, f, None, 1 << 20, None) == ops.BT_EINVAL
+    assert L.bt_build_workspace_size(12, 4) == 0
+    assert L.bt_build_workspace_size(1024, 32) > 1024 * 32
+
+
+def test_build_rejects_short_workspace(L):
+    buf = C.create_string_buffer(4096 + 512)
+    addr = (C.addressof(buf) + 255) & ~255
+    f = _fake()
+    assert L.bt_build(f, 1024, 32, f, C.c_void_p(addr), 4096, None) == ops.BT_ENOMEM
+    assert L.bt_build(f, 1024, 32, f, C.c_void_p(addr + 8), 1 << 30, None) == ops.BT_EINVAL
+
+
+def test_rotate_rejects_nonfinite(L):
+    f = _fake()
+    R = (C.c_float * 9)(1, 0, 0, 0, float("nan"), 0, 0, 0, 1)
+    assert L.bt_rotate_build(f, 8, 2, R, f, f, 1 << 20, None) == ops.BT_EINVAL
+    R = (C.c_float * 9)(1, 0, 0, 0, float("inf"), 0, 0, 0, 1)
+    assert L.bt_rotate_build(f, 8, 2, R, f, f, 1 << 20, None) == ops.BT_EINVAL
+    assert L.bt_rotate_build(f, 8, 2, None, f, f, 1 << 20, None) == ops.BT_EINVAL
+
+
+def test_permute_rejects(L):
+    a, b = _fake(1024), _fake(1024)
+    assert L.bt_permute(a, a, 8, 6, 0, b, None) == ops.BT_EINVAL          # row_bytes % 4
+    assert L.bt_permute(a, a, 8, 16, 2, b, None) == ops.BT_EINVAL         # bad mode
+    assert L.bt_permute(a, a, 8, 16, 0, a, None) == ops.BT_EINVAL         # src == dst
+    assert L.bt_permute(a, a, -1, 16, 0, b, None) == ops.BT_EINVAL
+    assert L.bt_permute(None, None, 0, 16, 0, None, None) == ops.BT_OK    # empty is a no-op
+    assert L.bt_invert_perm(a, 4, a, None) == ops.BT_EINVAL               # overlap
+
+
+def test_ball_attn_rejects(L):
+    q, k, v, o = (_fake(1 << 16) for _ in range(4))
+    args = lambda **kw: dict(dict(q=q, k=k, v=v, perm=None, N=1024, ball=32, H=4, d=16,
+                                  dt=ops.BT_F32, out=o), **kw)
+    call = lambda a: L.ball_attn(a["q"], a["k"], a["v"], a["perm"], a["N"], a["ball"], a["H"],
+                                 a["d"], a["dt"], a["out"], None)
+    assert call(args(ball=48)) == ops.BT_EINVAL          # 48 does not divide 1024
+    assert call(args(d=24)) == ops.BT_EINVAL
+    assert call(args(H=0)) == ops.BT_EINVAL
+    assert call(args(dt=7)) == ops.BT_EINVAL
+    assert call(args(out=q)) == ops.BT_EINVAL            # aliasing
+    assert call(args(q=None)) == ops.BT_EINVAL
+    assert call(args(ball=8192, N=8192)) == ops.BT_EINVAL
+
+
+def test_bsa_rejects(L):
+    q, k, v, o, p, ws = (_fake(1 << 16) for _ in range(6))
+    P = ops.BsaParams
+    gc = (C.c_float * 3)(1, 0, 0)
+    def call(params, N=4096, H=2, d=32, dt=ops.BT_BF16, gw=None, gcc=gc, wsb=1 << 30):
+        return L.bsa_attn(q, k, v, p, N, H, d, dt, C.byref(params), gw, None, gcc, None, ws,
+                          wsb, o, None)
+    assert call(P(128, 64, 64, 4, 1), dt=ops.BT_F32) == ops.BT_EINVAL
+    assert call(P(128, 48, 64, 4, 1)) == ops.BT_EINVAL    # block not multiple of 32
+    assert call(P(128, 64, 96, 4, 1)) == ops.BT_EINVAL    # group vs ball
+    assert call(P(128, 64, 64, 65, 1)) == ops.BT_EINVAL   # topk too large
+    assert call(P(128, 64, 64, 4, 1), d=16) == ops.BT_EINVAL
+    assert call(P(128, 64, 64, 4, 1), gw=ws) == ops.BT_EINVAL   # both gates given
+    assert call(P(128, 64, 64, 4, 1), gcc=None) == ops.BT_EINVAL  # no gate
+    assert L.bsa_workspace_size(4096, 2, 32, C.byref(P(128, 64, 64, 4, 1))) > 0
+    assert L.bsa_workspace_size(4096, 2, 32, C.byref(P(100, 64, 64, 4, 1))) == 0
