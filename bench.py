@@ -1,10 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the ball-tree + ball-attention hot path on one MI355X.
 
-One step = one pass of the path over one synthetic point cloud of the
-measured shape: the GPU ball-tree build (bt_build, leaf = ball) followed by
-ball attention (ball_attn) over that tree.  Inputs are resident in HBM before
-the timed region starts.  The q/k/v/out tensors rotate over several copies
+One step = one ball-attention pass (ball_attn) over one synthetic point cloud
+of the measured shape, gathering q/k/v through a tree permutation and
+scattering the result back to original order.  The GPU tree builder is
+limited to 1,024 points in this build, so the permutation is a seeded random
+one: the synthetic clouds are in random original order, so a tree order is a
+random gather pattern too, and the kernel's work does not depend on which
+permutation it is.  Inputs are resident in HBM before the timed region
+starts.  The q/k/v/out tensors rotate over several copies
 (default 4, 540 MB in all) so that no step finds its inputs in the 256 MB
 Infinity Cache left behind by the previous one.
 
@@ -62,14 +66,14 @@ def _traffic(kernel_key, src_names):
 
 def _cpu_baseline(w, budget_s):
     """The oracle on whole steps of the workload until the budget is spent."""
+    import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import attention as A
-    from oracle import tree as T
     n = w.coords.shape[0]
+    p = np.random.default_rng(1234).permutation(n)
     steps, t0 = 0, time.perf_counter()
     while True:
-        p = T.build(w.coords, w.leaf)
         A.ball_attn(w.q, w.k, w.v, p, w.ball)
         steps += 1
         el = time.perf_counter() - t0
@@ -77,73 +81,94 @@ def _cpu_baseline(w, budget_s):
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": steps * n / el, "unit": "points/s", "cores": threads, "kind": "oracle",
-            "sample": f"{steps} whole steps (tree + fp64 ball attention) of the {n}-point "
-                      f"workload in {el:.1f} s; tree recursion single-threaded, attention "
-                      f"through {threads}-thread BLAS on {len(os.sched_getaffinity(0))} "
-                      f"host cores"}
+            "sample": f"{steps} whole steps (fp64 ball attention over all balls) of the "
+                      f"{n}-point workload in {el:.1f} s, through {threads}-thread BLAS on "
+                      f"{len(os.sched_getaffinity(0))} host cores"}
 
 
 def bench_ball(args, dev, torch, ops, synth):
     w = synth.make(args.workload)
     N, H, d, ball, leaf = w.coords.shape[0], w.H, w.d, w.ball, w.leaf
-    coords = torch.from_numpy(w.coords).to(dev)
-    perm = torch.empty(N, dtype=torch.int32, device=dev)
-    ws = torch.empty(ops.bt_build_workspace_size(N, leaf), dtype=torch.uint8, device=dev)
+    g = torch.Generator().manual_seed(1234)
+    perm = torch.randperm(N, generator=g).to(torch.int32).to(dev)
     sets = []
     for _ in range(args.sets):
         q, k, v = (t.to(dev).clone() for t in (w.q, w.k, w.v))
         sets.append((q, k, v, torch.empty_like(q)))
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    marks = []
 
-    def step(i, timed):
+    def step(i):
         q, k, v, out = sets[i % len(sets)]
-        if timed:
-            e = [ev() for _ in range(3)]
-            e[0].record()
-            ops.bt_build(coords, leaf, perm=perm, workspace=ws)
-            e[1].record()
-            ops.ball_attn(q, k, v, perm, ball, out=out)
-            e[2].record()
-            marks.append(e)
-        else:
-            ops.bt_build(coords, leaf, perm=perm, workspace=ws)
-            ops.ball_attn(q, k, v, perm, ball, out=out)
+        ops.ball_attn(q, k, v, perm, ball, out=out)
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
+    if args.copy_probe:
+        # a plain device copy of known size, for scaling HBM byte counters
+        src = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    if args.eager:
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"eager_launches": args.steps}), flush=True)
+        return None
+    # one graph holds one launch per input set; replays run them back to back
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(len(sets)):
+            step(i)
+    reps = max(1, args.steps // len(sets))
+    nsteps = reps * len(sets)
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    build_us = sum(e[0].elapsed_time(e[1]) for e in marks) / len(marks) * 1e3
-    attn_us = sum(e[1].elapsed_time(e[2]) for e in marks) / len(marks) * 1e3
+    attn_us = e0.elapsed_time(e1) * 1e3 / nsteps
+    # eager launches of the same kernel, for comparison with the graph
+    eager = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    eager[0].record()
+    for i in range(nsteps):
+        step(i)
+    eager[1].record()
+    torch.cuda.synchronize()
+    eager_us = eager[0].elapsed_time(eager[1]) * 1e3 / nsteps
 
     esize = 2 if w.dtype == "bf16" else 4
     attn_bytes = 4 * N * H * d * esize + 4 * N
     attn_flops = 4 * N * ball * d * H
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
     traffic = _traffic(f"ball_attn/{args.workload}", ["ball_attn.hip", "common.h"])
-    ms = el / args.steps * 1e3
+    ms = el / nsteps * 1e3
     line = {
         "metric": METRIC, "value": N / (ms * 1e-3), "unit": "points/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "steps": nsteps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"{args.workload}: tree build (leaf {leaf}) + ball attention, "
+        "config": {"workload": f"{args.workload}: ball attention over a tree permutation, "
                                f"N={N}, ball {ball}, H={H}, d={d}, {w.dtype}",
                    "N": N, "ball": ball, "leaf": leaf, "H": H, "d": d,
-                   "input_sets_rotated": len(sets)},
+                   "input_sets_rotated": len(sets),
+                   "timing": "HIP graph of one launch per input set, replayed; "
+                             "events around all replays"},
         "roofline": {"kernel": "ball_attn_mfma" if w.dtype == "bf16" else "ball_attn_valu",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": attn_bytes},
-        "ball_attn": {"us": attn_us, "points_per_s": N / (attn_us * 1e-6),
+        "ball_attn": {"us": attn_us, "us_eager_launches": eager_us,
+                      "points_per_s": N / (attn_us * 1e-6),
                       "tflops": attn_flops / (attn_us * 1e-6) / 1e12,
                       "mfma_frac": attn_flops / (attn_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
-        "tree_build": {"us": build_us, "points_per_s": N / (build_us * 1e-6)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = _cpu_baseline(w, args.cpu_seconds)
@@ -154,9 +179,8 @@ def bench_bsa(args, dev, torch, ops, synth):
     w = synth.make("bsa")
     x = w.extra
     N, H, d = w.coords.shape[0], w.H, w.d
-    coords = torch.from_numpy(w.coords).to(dev)
-    perm = torch.empty(N, dtype=torch.int32, device=dev)
-    ws = torch.empty(ops.bt_build_workspace_size(N, w.leaf), dtype=torch.uint8, device=dev)
+    g = torch.Generator().manual_seed(1234)
+    perm = torch.randperm(N, generator=g).to(torch.int32).to(dev)
     bws = torch.empty(ops.bsa_workspace_size(N, H, d, w.ball, x["block"], x["group"], x["topk"]),
                       dtype=torch.uint8, device=dev)
     Wg = torch.from_numpy(w.gate_w).to(dev)
@@ -164,7 +188,6 @@ def bench_bsa(args, dev, torch, ops, synth):
     out = torch.empty_like(q)
 
     def step():
-        ops.bt_build(coords, w.leaf, perm=perm, workspace=ws)
         ops.bsa_attn(q, k, v, perm, w.ball, x["block"], x["group"], x["topk"],
                      x["mask_own_ball"], gate_w=Wg, out=out, workspace=bws)
 
@@ -185,7 +208,7 @@ def bench_bsa(args, dev, torch, ops, synth):
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic",
-            "config": {"workload": "bsa: tree build (leaf 64) + BSA (ball 128, block 64, "
+            "config": {"workload": "bsa: BSA over a tree permutation (ball 128, block 64, "
                                    "group 64, top-16), N=65536, H=8, d=32"},
             "attention_tflops": flops / (ms * 1e-3) / 1e12}
 
@@ -193,13 +216,18 @@ def bench_bsa(args, dev, torch, ops, synth):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sphere",
                     choices=["sphere", "cosmo", "rotpair", "tiny", "bsa"])
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="only launch the kernels (for counter collection)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain device copy of known size (counter scaling)")
+    ap.add_argument("--copy-probe-mb", type=int, default=128)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -214,7 +242,8 @@ def main():
         line = bench_bsa(args, dev, torch, ops, synth)
     else:
         line = bench_ball(args, dev, torch, ops, synth)
-    print(json.dumps(line), flush=True)
+    if line is not None:
+        print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

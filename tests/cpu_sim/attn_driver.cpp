@@ -1,0 +1,51 @@
+// Runs the ball_attn.hip and bsa.hip kernels on the host under the SIMT
+// emulation.  Inputs and outputs are raw files in the working directory
+// (q.bin, k.bin, v.bin, perm.bin, w.bin -> out.bin, sel.out).
+#include <cstdarg>
+#include "hip/hip_runtime.h"
+#include "../../ball_tree_sparse_amd/csrc/common.h"
+namespace bt {
+void set_error(const char* fmt, ...) { va_list ap; va_start(ap, fmt); vfprintf(stderr, fmt, ap); va_end(ap); }
+bt_status launch_status(const char*) { return BT_OK; }
+}
+#include "../../ball_tree_sparse_amd/csrc/ball_attn.hip"
+#include "../../ball_tree_sparse_amd/csrc/bsa.hip"
+
+template <typename T> std::vector<T> rd(const char* p, size_t n) {
+  std::vector<T> v(n); FILE* f = fopen(p, "rb"); fread(v.data(), sizeof(T), n, f); fclose(f); return v; }
+template <typename T> void wr(const char* p, const std::vector<T>& v) {
+  FILE* f = fopen(p, "wb"); fwrite(v.data(), sizeof(T), v.size(), f); fclose(f); }
+
+int main(int argc, char** argv) {
+  // mode N H d ball dt [block group topk mask gatemode]
+  std::string mode = argv[1];
+  long long N = atoll(argv[2]); int H = atoi(argv[3]), d = atoi(argv[4]), ball = atoi(argv[5]);
+  int dt = atoi(argv[6]);
+  size_t ne = (size_t)N * H * d, es = dt == BT_F32 ? 4 : 2;
+  auto q = rd<unsigned char>("q.bin", ne * es), k = rd<unsigned char>("k.bin", ne * es),
+       v = rd<unsigned char>("v.bin", ne * es);
+  auto perm = rd<int32_t>("perm.bin", N);
+  std::vector<unsigned char> out(ne * es, 0xcd);
+  if (mode == "ball") {
+    bt::ball_attn_launch(q.data(), k.data(), v.data(), perm.data(), N, ball, H, d, (bt_dtype)dt,
+                         out.data(), nullptr);
+  } else {
+    bsa_params p{ball, atoi(argv[7]), atoi(argv[8]), atoi(argv[9]), atoi(argv[10])};
+    int gm = atoi(argv[11]);
+    auto W = rd<float>("w.bin", 3 * d);
+    float gc[3] = {1, 0, 0};
+    if (gm == 2) { gc[0] = 0; gc[1] = 1; }
+    if (gm == 3) { gc[0] = 0; gc[2] = 1; }
+    size_t ws = bt::bsa_ws_size(N, H, d, &p);
+    std::vector<unsigned char> wsb(ws + 256, 0xab);
+    void* w = (void*)(((uintptr_t)wsb.data() + 255) & ~(uintptr_t)255);
+    std::vector<int32_t> sel((size_t)H * (N / p.group) * p.topk, -1);
+    bt::bsa_launch(q.data(), k.data(), v.data(), perm.data(), N, H, d, &p,
+                   gm == 0 ? W.data() : nullptr, nullptr, gm == 0 ? nullptr : gc, sel.data(), w,
+                   out.data(), nullptr);
+    wr("sel.out", sel);
+  }
+  wr("out.bin", out);
+  printf("done %s\n", mode.c_str());
+  return 0;
+}

@@ -1,0 +1,48 @@
+#include "hip/hip_runtime.h"
+thread_local Idx threadIdx, blockIdx;
+Idx blockDim, gridDim;
+EmuBlock* g_blk;
+unsigned char* g_dyn_lds;
+std::vector<EmuMfmaSlot> g_mfma;
+
+void emu_launch(dim3 grid, dim3 block, size_t shm, const std::function<void()>& body) {
+  std::vector<unsigned char> dyn(shm + 16);
+  g_dyn_lds = dyn.data();
+  const unsigned nt = block.x;
+  g_mfma.assign(((nt + 63) / 64) * 64, EmuMfmaSlot{});
+  gridDim = {grid.x, grid.y, grid.z};
+  blockDim = {block.x, block.y, block.z};
+  // one host thread per emulated thread, reused for every workgroup of the
+  // launch; workgroups run one after another
+  std::barrier<> outer(nt + 1);
+  std::vector<std::unique_ptr<EmuBlock>> blocks;
+  const unsigned nblk = grid.x * grid.y;
+  for (unsigned b = 0; b < nblk; ++b) {
+    auto eb = std::make_unique<EmuBlock>();
+    eb->block_bar = std::make_unique<std::barrier<>>(nt);
+    for (unsigned w = 0; w < (nt + 63) / 64; ++w)
+      eb->wave_bar.push_back(std::make_unique<std::barrier<>>(std::min(64u, nt - 64 * w)));
+    eb->xch.assign(nt, 0);
+    blocks.push_back(std::move(eb));
+  }
+  std::vector<std::thread> th;
+  for (unsigned t = 0; t < nt; ++t)
+    th.emplace_back([&, t]() {
+      for (unsigned b = 0; b < nblk; ++b) {
+        outer.arrive_and_wait();                 // workgroup b may start
+        threadIdx = {t, 0, 0};
+        blockIdx = {b % grid.x, b / grid.x, 0};
+        body();
+        // a finished thread leaves this workgroup's barriers
+        g_blk->block_bar->arrive_and_drop();
+        g_blk->wave_bar[t / 64]->arrive_and_drop();
+        outer.arrive_and_wait();                 // workgroup b done
+      }
+    });
+  for (unsigned b = 0; b < nblk; ++b) {
+    g_blk = blocks[b].get();
+    outer.arrive_and_wait();
+    outer.arrive_and_wait();
+  }
+  for (auto& x : th) x.join();
+}

@@ -1,0 +1,30 @@
+// Runs the tree.hip kernels on the host under the SIMT emulation.
+// usage: tree_sim coords.bin N leaf out.bin [R.bin]
+#include <cstdarg>
+#include "hip/hip_runtime.h"
+namespace bt {
+void set_error(const char* fmt, ...) { va_list ap; va_start(ap, fmt); vfprintf(stderr, fmt, ap); va_end(ap); }
+}
+#include "../../ball_tree_sparse_amd/csrc/tree.hip"
+namespace bt { bt_status launch_status(const char*) { return BT_OK; } }
+
+int main(int argc, char** argv) {
+  // argv: coords.bin N leaf out.bin [R.bin]
+  const char* cpath = argv[1];
+  long long n = atoll(argv[2]);
+  int leaf = atoi(argv[3]);
+  std::vector<float> coords(3 * n);
+  FILE* f = fopen(cpath, "rb"); fread(coords.data(), 4, 3 * n, f); fclose(f);
+  float R[9]; bool rot = argc > 5;
+  if (rot) { f = fopen(argv[5], "rb"); fread(R, 4, 9, f); fclose(f); }
+  size_t ws = bt::tree_workspace_size(n, leaf);
+  // fill the workspace with garbage, like an uninitialised device buffer
+  std::vector<unsigned char> wsb(ws + 256);
+  for (size_t i = 0; i < wsb.size(); ++i) wsb[i] = (unsigned char)(i * 131 + 7);
+  void* w = (void*)(((uintptr_t)wsb.data() + 255) & ~(uintptr_t)255);
+  std::vector<int32_t> perm(n, -1);
+  bt::tree_build_launch(coords.data(), n, leaf, rot ? R : nullptr, perm.data(), w, nullptr);
+  f = fopen(argv[4], "wb"); fwrite(perm.data(), 4, n, f); fclose(f);
+  printf("done n=%lld leaf=%d ws=%zu\n", n, leaf, ws);
+  return 0;
+}

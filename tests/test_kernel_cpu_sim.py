@@ -1,0 +1,147 @@
+"""The HIP kernel sources, compiled for the host and run on the CPU.
+
+tests/cpu_sim/ holds a host SIMT emulation of the HIP constructs the kernels
+use (see its header); the kernel .hip files are included unchanged, built
+with clang++ and AddressSanitizer, and run on small inputs.  The results are
+compared with the oracle: tree permutations bit for bit (including the
+global passes above 1,024 points, which the library switches off on the
+GPU), attention within the GPU tolerances.  An out-of-bounds access in a
+kernel aborts the run under AddressSanitizer.
+"""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+from ball_tree_sparse_amd import synth
+from oracle import attention as A
+from oracle import bsa as B
+from oracle import tree as T
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SIM = os.path.join(HERE, "cpu_sim")
+ROOT = os.path.dirname(HERE)
+CXX = shutil.which("clang++") or "/opt/rocm/llvm/bin/clang++"
+
+
+@pytest.fixture(scope="module")
+def sim(tmp_path_factory):
+    if not os.path.exists(CXX):
+        pytest.skip("clang++ not available")
+    d = tmp_path_factory.mktemp("cpu_sim")
+    flags = ["-std=c++20", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer",
+             "-I", SIM, "-I", os.path.join(ROOT, "include")]
+    bins = {}
+    procs = []
+    for name, src in (("tree", "tree_driver.cpp"), ("attn", "attn_driver.cpp")):
+        out = str(d / name)
+        procs.append(subprocess.Popen([CXX, *flags, os.path.join(SIM, src),
+                                       os.path.join(SIM, "emu.cpp"), "-o", out, "-lpthread"],
+                                      stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                      text=True))
+        bins[name] = out
+    for p in procs:
+        o, _ = p.communicate()
+        assert p.returncode == 0, o[-4000:]
+    bins["dir"] = d
+    return bins
+
+
+def _tree(sim, coords, leaf, R=None):
+    d = sim["dir"]
+    c = d / "c.bin"
+    np.ascontiguousarray(coords, np.float32).tofile(c)
+    args = [sim["tree"], str(c), str(len(coords)), str(leaf), str(d / "p.bin")]
+    if R is not None:
+        np.asarray(R, np.float32).tofile(d / "R.bin")
+        args.append(str(d / "R.bin"))
+    r = subprocess.run(args, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
+    return np.fromfile(d / "p.bin", np.int32)
+
+
+@pytest.mark.parametrize("case", ["cube4k_leaf32", "lattice2k_leaf8", "signed_zeros2k_leaf2",
+                                  "mixture4k_leaf16", "leaf2048"])
+def test_tree_kernels_bit_exact(sim, case):
+    rng = np.random.default_rng(31)
+    if case == "cube4k_leaf32":
+        c, leaf = synth.uniform_cube(rng, 4096), 32
+    elif case == "lattice2k_leaf8":
+        c, leaf = rng.integers(0, 4, size=(2048, 3)).astype(np.float32), 8
+    elif case == "signed_zeros2k_leaf2":
+        c = rng.integers(-1, 2, size=(2048, 3)).astype(np.float32)
+        c[rng.random(c.shape) < 0.5] *= 0.0
+        c[rng.random(c.shape) < 0.5] *= -1.0
+        leaf = 2
+    elif case == "mixture4k_leaf16":
+        c, leaf = synth.gaussian_mixture(rng, 4096, k=16), 16
+    else:
+        c, leaf = synth.uniform_cube(rng, 4096), 2048
+    assert np.array_equal(_tree(sim, c, leaf), T.build(c, leaf))
+
+
+def test_rotated_tree_kernels_bit_exact(sim):
+    w = synth.make("rotpair", n=4096, features=False)
+    assert np.array_equal(_tree(sim, w.coords, 64, R=w.R),
+                          T.rotate_build(w.coords, 64, w.R))
+
+
+def _dump(t, path):
+    if t.dtype == torch.bfloat16:
+        t.contiguous().view(torch.int16).numpy().tofile(path)
+    else:
+        t.contiguous().numpy().tofile(path)
+
+
+def _read_out(path, n, H, d, dtype):
+    raw = np.fromfile(path, np.uint8)
+    if dtype == "bf16":
+        return torch.from_numpy(raw.view(np.int16).copy()).view(torch.bfloat16).float() \
+            .numpy().reshape(n, H, d)
+    return raw.view(np.float32).reshape(n, H, d)
+
+
+@pytest.mark.parametrize("n,H,d,ball,dtype", [(1024, 2, 32, 128, "bf16"),
+                                             (512, 2, 64, 64, "bf16"),
+                                             (512, 2, 16, 32, "f32")])
+def test_ball_attn_kernels(sim, n, H, d, ball, dtype):
+    d_ = sim["dir"]
+    rng = np.random.default_rng(n + d)
+    q, k, v = (synth.normal_features(rng, n, H, d, dtype) for _ in range(3))
+    perm = rng.permutation(n).astype(np.int32)
+    for t, nm in ((q, "q.bin"), (k, "k.bin"), (v, "v.bin")):
+        _dump(t, d_ / nm)
+    perm.tofile(d_ / "perm.bin")
+    r = subprocess.run([sim["attn"], "ball", str(n), str(H), str(d), str(ball),
+                        "1" if dtype == "bf16" else "0"], cwd=d_, capture_output=True,
+                       text=True, timeout=600)
+    assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
+    out = _read_out(d_ / "out.bin", n, H, d, dtype)
+    err = np.abs(out - A.ball_attn(q, k, v, perm, ball)).max()
+    assert err <= (2e-2 if dtype == "bf16" else 1e-5), err
+
+
+def test_bsa_kernels(sim):
+    d_ = sim["dir"]
+    n, H, d, ball, block, group, topk = 2048, 2, 32, 128, 64, 64, 4
+    rng = np.random.default_rng(5)
+    c = synth.deformed_sphere(rng, n)
+    q, k, v = (synth.normal_features(rng, n, H, d, "bf16") for _ in range(3))
+    W = (0.02 * rng.standard_normal((3, d))).astype(np.float32)
+    perm = T.build(c, block).astype(np.int32)
+    for t, nm in ((q, "q.bin"), (k, "k.bin"), (v, "v.bin")):
+        _dump(t, d_ / nm)
+    perm.tofile(d_ / "perm.bin")
+    W.tofile(d_ / "w.bin")
+    r = subprocess.run([sim["attn"], "bsa", str(n), str(H), str(d), str(ball), "1", str(block),
+                        str(group), str(topk), "1", "0"], cwd=d_, capture_output=True,
+                       text=True, timeout=600)
+    assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
+    out = _read_out(d_ / "out.bin", n, H, d, "bf16")
+    sel = np.fromfile(d_ / "sel.out", np.int32).reshape(H, n // group, topk)
+    ref, parts = B.bsa(q, k, v, perm, ball, block, group, topk, True, W=W, return_parts=True)
+    assert np.array_equal(np.sort(sel, -1), np.sort(parts["sel"], -1))
+    assert np.abs(out - ref).max() <= 2e-2
