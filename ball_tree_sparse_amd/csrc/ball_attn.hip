@@ -134,136 +134,286 @@ __global__ __launch_bounds__(kValuThreads) void ball_attn_valu(
 // each group of 16 keys.
 BT_DEV int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-BT_DEV uint16_t u16_of(const u32x4& r, int e) {
-  const uint32_t w = r[e >> 1];
-  return (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+// Halves e of two 16-byte pieces as one word: (lo[e], hi[e]).
+BT_DEV uint32_t pair_u16(const u32x4& lo, const u32x4& hi, int e) {
+  // byte selectors of v_perm_b32: result bytes 0,1 from lo, 2,3 from hi
+  return __builtin_amdgcn_perm(hi[e >> 1], lo[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
 }
 
-template <int D, int BALL>
-__global__ __launch_bounds__(BALL / 32 * 64) void ball_attn_mfma(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ perm,
-    int32_t H, int32_t nballs, int32_t xcd_map, uint16_t* __restrict__ out) {
-  const int64_t N = (int64_t)nballs * BALL;
-  constexpr int NW = BALL / 32;      // waves = 32-query strips
-  constexpr int NT = NW * 64;
-  constexpr int KB = BALL / 32;      // 32-key blocks
-  constexpr int DS = D / 16;         // K steps of S^T
-  constexpr int DB = D / 32;         // 32-row blocks of O^T
-  constexpr int VTS = BALL + 8;      // V^T row stride in bf16 (16 B pad)
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * VTS];
-  __shared__ int32_t sperm[BALL];
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-  // Workgroups are dispatched round-robin over the 8 XCDs; with xcd_map the
-  // 8*k-th..8*k+7-th launches of one XCD take the heads of the same balls, so
-  // the two 64-byte halves of a 128-byte line meet in one L2.
-  int pair = blockIdx.x;
-  if (xcd_map) {
-    const int total = nballs * H;
-    pair = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  }
-  const int b = pair / H;
-  const int h = pair - b * H;
+// Sum of the eight bf16 values of an MFMA operand, added to acc.
+BT_DEV float sum_bf16x8(bf16x8 x, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, acc, false);
+}
+
+// An item is one ball and HPW adjacent heads (HPW = 2 when H is even): the
+// rows of two heads are one 128-byte line, and random 128-byte gathers run
+// about a quarter faster than 64-byte ones.  The workgroup has one wave per
+// 32-query strip; each wave computes the item's heads in turn.  K (row-major,
+// padded) and V^T of the heads sit in LDS.
+//
+// Softmax: the probabilities are rounded to bf16 once, for the P V product,
+// and the normaliser is the sum of those rounded values, so the output is a
+// weighted mean of V rows whose weights sum to one up to fp32 rounding.
+//
+// With PIPE the kernel is persistent and software-pipelined: a workgroup
+// walks items j = blockIdx.x, blockIdx.x + gridDim.x, ...; while item j is
+// computed, the Q/K/V pieces of the next item are in flight into registers
+// and the permutation entries of the one after are in flight too.  Without
+// PIPE a workgroup runs one item.
+template <int D, int BALL, int HPW>
+struct AttnGeom {
+  static constexpr int NW = BALL / 32;      // waves = 32-query strips
+  static constexpr int NT = NW * 64;
+  static constexpr int KB = BALL / 32;      // 32-key blocks
+  static constexpr int DS = D / 16;         // K steps of S^T
+  static constexpr int DB = D / 32;         // 32-row blocks of O^T
+  static constexpr int VTS = BALL + 8;      // V^T row stride (bf16), 16-byte pad
+  static constexpr int KS = D + 8;          // K row stride (bf16), 16-byte pad
+  static constexpr int KPI = D / 16;        // keys per staging piece
+  static constexpr int CPR = HPW * D / 8;   // 16-byte chunks per row of an item
+  static constexpr int IPT = HPW;           // staging pieces per thread
+  static_assert((BALL / KPI) * CPR == NT * IPT, "staging pieces tile the threads");
+};
+
+template <int D, int BALL, int HPW, bool PERM, bool PIPE>
+__global__ __launch_bounds__(BALL / 32 * 64)
+BT_WAVES_PER_EU((BALL >= 256 ? 2 : (PIPE ? 3 : 4)), 8)
+void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                    const uint16_t* __restrict__ v, const int32_t* __restrict__ perm,
+                    int32_t H, int32_t nballs, int32_t xcd_map, uint16_t* __restrict__ out) {
+  using Gm = AttnGeom<D, BALL, HPW>;
+  constexpr int NT = Gm::NT, KB = Gm::KB, DS = Gm::DS, DB = Gm::DB, VTS = Gm::VTS;
+  constexpr int KS = Gm::KS, KPI = Gm::KPI, CPR = Gm::CPR, IPT = Gm::IPT;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[HPW][BALL * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[HPW][D * VTS];
+
+  const int64_t N = (int64_t)nballs * BALL;
+  const int hgroups = H / HPW;
+  const int total = nballs * hgroups;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hf = lane >> 5, c = lane & 31;
   const int64_t rs = (int64_t)H * D;
-  const int64_t hoff = (int64_t)h * D;
 
-  for (int i = tid; i < BALL; i += NT)
-    sperm[i] = perm ? (int32_t)perm_index(perm[b * BALL + i], N) : b * BALL + i;
-  __syncthreads();
+  // Workgroups are dispatched round-robin over the 8 XCDs, and item j runs
+  // on XCD j % 8 (the grid is a multiple of 8).  With xcd_map, the items an
+  // XCD runs at the same time are consecutive (ball, head group) pairs, so
+  // the lines of one point row are fetched at about the same time.
+  auto pair_of = [&](int j) -> int { return xcd_map ? (j & 7) * (total >> 3) + (j >> 3) : j; };
 
-  // ---- stage V^T: 4 keys x 8 d per item, written as 8-byte runs ----------
-  for (int it = tid; it < (BALL / 4) * (D / 8); it += NT) {
-    const int kq = it / (D / 8), dc = it - kq * (D / 8);
-    u32x4 r[4];
+  // Permutation entries of an item for this thread, as loaded: they are
+  // clamped only where row addresses are formed, so that no wait for them is
+  // placed ahead of the rows of the item in flight before them.
+  struct Rows { int32_t q; int32_t kv[IPT][KPI]; int32_t h0; };
+  auto load_rows = [&](int j) -> Rows {
+    Rows r;
+    const int pair = pair_of(j);
+    const int b = pair / hgroups;
+    r.h0 = (pair - b * hgroups) * HPW;
+    const int64_t base = (int64_t)b * BALL;
+    if constexpr (PERM) r.q = perm[base + w * 32 + c];
+    else r.q = (int32_t)(base + w * 32 + c);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      r[u] = *(const u32x4*)(v + (int64_t)sperm[kq * 4 + u] * rs + hoff + dc * 8);
-    const int key0 = kq * 4;
-    const int pos0 = (key0 & ~15) + swap23(key0 & 15);
+    for (int ii = 0; ii < IPT; ++ii) {
+      const int kq = (tid + ii * NT) / CPR;
+      if constexpr (PERM) {
+        if constexpr (KPI == 2) {
+          const int2 pp = *(const int2*)(perm + base + kq * 2);
+          r.kv[ii][0] = pp.x;
+          r.kv[ii][1] = pp.y;
+        } else {
+          const int4 pp = *(const int4*)(perm + base + kq * 4);
+          r.kv[ii][0] = pp.x;
+          r.kv[ii][1] = pp.y;
+          r.kv[ii][2] = pp.z;
+          r.kv[ii][3] = pp.w;
+        }
+      } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      u32x2 pk;
-      pk[0] = uint32_t(u16_of(r[0], e)) | (uint32_t(u16_of(r[1], e)) << 16);
-      pk[1] = uint32_t(u16_of(r[2], e)) | (uint32_t(u16_of(r[3], e)) << 16);
-      *(u32x2*)&vt[(dc * 8 + e) * VTS + pos0] = pk;
-    }
-  }
-
-  // ---- S^T = K Q^T for this wave's 32 queries ----------------------------
-  const int qrow = w * 32 + c;
-  const int64_t pq = sperm[qrow];
-  bf16x8 qf[DS];
-#pragma unroll
-  for (int s = 0; s < DS; ++s) qf[s] = *(const bf16x8*)(q + pq * rs + hoff + s * 16 + hf * 8);
-
-  f32x16 sacc[KB];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const int64_t pk = sperm[kb * 32 + c];
-    bf16x8 kf[DS];
-#pragma unroll
-    for (int s = 0; s < DS; ++s) kf[s] = *(const bf16x8*)(k + pk * rs + hoff + s * 16 + hf * 8);
-    f32x16 a = {};
-#pragma unroll
-    for (int s = 0; s < DS; ++s) a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], a, 0, 0, 0);
-    sacc[kb] = a;
-  }
-
-  // ---- softmax over the keys of query column c (fp32) --------------------
-  const float c2 = 1.4426950408889634f / sqrtf((float)D);   // log2(e)/sqrt(d)
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float moff = -mx * c2;
-  float sum = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], c2, moff));
-      sacc[kb][e] = p;
-      sum += p;
-    }
-  sum += __shfl_xor(sum, 32, 64);
-
-  __syncthreads();   // V^T staged
-
-  // ---- O^T = V^T P^T ------------------------------------------------------
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8 pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sacc[kb][s2 * 8 + e];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 vf = *(const bf16x8*)&vt[(db * 32 + c) * VTS + (kb * 2 + s2) * 16 + hf * 8];
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
+        for (int u = 0; u < KPI; ++u) r.kv[ii][u] = (int32_t)(base + kq * KPI + u);
       }
     }
-  }
+    return r;
+  };
+  auto row_of = [&](int32_t p) -> int64_t { return PERM ? perm_index(p, N) : (int64_t)p; };
 
-  // ---- normalise and store: lane owns dd = db*32 + 8*g + 4*hf + 0..3 -----
-  const float inv = 1.0f / sum;
-  uint16_t* orow = out + pq * rs + hoff;
+  bf16x8 qn[HPW][DS];                // next item: Q fragments (B operand of S^T)
+  u32x4 kn[IPT][KPI], vn[IPT][KPI];  // next item: this thread's K and V pieces
+  auto load_data = [&](const Rows& r) {
+    const uint16_t* qrow = q + row_of(r.q) * rs + (int64_t)r.h0 * D + hf * 8;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+    for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x2 pk;
-      pk[0] = pack_bf16x2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
-      pk[1] = pack_bf16x2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
-      *(u32x2*)(orow + db * 32 + g * 8 + hf * 4) = pk;
+      for (int s = 0; s < DS; ++s) qn[hh][s] = *(const bf16x8*)(qrow + hh * D + s * 16);
+#pragma unroll
+    for (int ii = 0; ii < IPT; ++ii) {
+      const int ch = (tid + ii * NT) % CPR;        // 16-byte chunk of the item row
+      const int64_t off = (int64_t)r.h0 * D + ch * 8;
+#pragma unroll
+      for (int u = 0; u < KPI; ++u) {
+        const int64_t row = row_of(r.kv[ii][u]) * rs + off;
+        kn[ii][u] = *(const u32x4*)(k + row);
+        vn[ii][u] = *(const u32x4*)(v + row);
+      }
     }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int ii = 0; ii < IPT; ++ii) {
+      const int it = tid + ii * NT;
+      const int kq = it / CPR, ch = it - kq * CPR;
+      const int hh = ch / (D / 8), dc = ch - hh * (D / 8);
+      const int key0 = kq * KPI;
+#pragma unroll
+      for (int u = 0; u < KPI; ++u) *(u32x4*)&ks[hh][(key0 + u) * KS + dc * 8] = kn[ii][u];
+      const int pos0 = (key0 & ~15) + swap23(key0 & 15);   // keeps bits 0,1
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (KPI == 2) {
+          *(uint32_t*)&vt[hh][(dc * 8 + e) * VTS + pos0] = pair_u16(vn[ii][0], vn[ii][1], e);
+        } else {
+          u32x2 pk2;
+          pk2[0] = pair_u16(vn[ii][0], vn[ii][1], e);
+          pk2[1] = pair_u16(vn[ii][2], vn[ii][3], e);
+          *(u32x2*)&vt[hh][(dc * 8 + e) * VTS + pos0] = pk2;
+        }
+      }
+    }
+  };
+
+  const float c2 = 1.4426950408889634f / sqrtf((float)D);   // log2(e)/sqrt(d)
+  bf16x8 qc[HPW][DS];
+  // attention of the staged item for its HPW heads and this wave's queries
+  auto attend = [&](const Rows& rc) {
+    uint16_t* orow0 = out + row_of(rc.q) * rs + (int64_t)rc.h0 * D;
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      // ---- S^T = K Q^T ----------------------------------------------------
+      f32x16 sacc[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        f32x16 a = {};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          const bf16x8 kf = *(const bf16x8*)&ks[hh][(kb * 32 + c) * KS + s * 16 + hf * 8];
+          a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qc[hh][s], a, 0, 0, 0);
+        }
+        sacc[kb] = a;
+      }
+      // ---- softmax over the keys of query column c ------------------------
+      // Four independent chains for the maximum and the sum.
+      float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
+      float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float moff = -mx * c2;
+      bf16x8 pf[KB][2];                // P^T operands, rounded once
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pf[kb][s2][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][s2 * 8 + e], c2, moff));
+          s4[(kb * 2 + s2) & 3] = sum_bf16x8(pf[kb][s2], s4[(kb * 2 + s2) & 3]);
+        }
+      float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      sum += __shfl_xor(sum, 32, 64);
+      // ---- O^T = V^T P^T ----------------------------------------------------
+      f32x16 oacc[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 vf =
+                *(const bf16x8*)&vt[hh][(db * 32 + c) * VTS + (kb * 2 + s2) * 16 + hf * 8];
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][s2], oacc[db], 0, 0, 0);
+          }
+      // ---- normalise, regroup across the lane halves, store 16-byte runs ---
+      // Lane (c, hf) holds d = db*32 + 8*g + 4*hf + 0..3 for g = 0..3.  After
+      // one exchange with lane c^32, the hf = 0 lane holds d 0-7 and 16-23
+      // and the hf = 1 lane holds d 8-15 and 24-31 of each 32-column block.
+      const float inv = __builtin_amdgcn_rcpf(sum);
+      uint16_t* orow = orow0 + hh * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        u32x2 pg[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          pg[g][0] = pack_bf16x2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
+          pg[g][1] = pack_bf16x2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
+        }
+        const u32x2 sa = hf ? pg[0] : pg[1], sb = hf ? pg[2] : pg[3];
+        u32x2 ra, rb;
+        ra[0] = (uint32_t)__shfl_xor((int)sa[0], 32, 64);
+        ra[1] = (uint32_t)__shfl_xor((int)sa[1], 32, 64);
+        rb[0] = (uint32_t)__shfl_xor((int)sb[0], 32, 64);
+        rb[1] = (uint32_t)__shfl_xor((int)sb[1], 32, 64);
+        u32x4 c0, c1;
+        if (hf == 0) {
+          c0 = u32x4{pg[0][0], pg[0][1], ra[0], ra[1]};
+          c1 = u32x4{pg[2][0], pg[2][1], rb[0], rb[1]};
+        } else {
+          c0 = u32x4{ra[0], ra[1], pg[1][0], pg[1][1]};
+          c1 = u32x4{rb[0], rb[1], pg[3][0], pg[3][1]};
+        }
+        *(u32x4*)(orow + db * 32 + hf * 8) = c0;
+        *(u32x4*)(orow + db * 32 + 16 + hf * 8) = c1;
+      }
+    }
+  };
+
+  const int G = gridDim.x;
+  int j = blockIdx.x;
+  if (j >= total) return;                    // uniform over the workgroup
+  Rows rc = load_rows(j);
+  load_data(rc);
+  stage();
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qc[hh][s] = qn[hh][s];
+  if constexpr (!PIPE) {                     // one item per workgroup
+    __syncthreads();
+    attend(rc);
+    return;
+  }
+  int jn = j + G;
+  Rows rn = rc;
+  if (jn < total) rn = load_rows(jn);
+
+  for (;;) {
+    const bool has_next = jn < total;
+    if (has_next) load_data(rn);             // rows of the next item
+    const int jnn = jn + G;
+    Rows rnn = rn;
+    if (jnn < total) rnn = load_rows(jnn);   // permutation of the one after
+    __syncthreads();                         // the current item is staged
+    attend(rc);
+    if (!has_next) break;
+    __syncthreads();                         // everyone is done with LDS
+    stage();                                 // waits for the next item's rows
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+      for (int s = 0; s < DS; ++s) qc[hh][s] = qn[hh][s];
+    rc = rn;
+    rn = rnn;
+    jn = jnn;
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -292,29 +442,74 @@ static bt_status launch_valu(const void* q, const void* k, const void* v, const 
   return launch_status("ball_attn_valu");
 }
 
-template <int D>
-static bt_status launch_mfma_d(const void* q, const void* k, const void* v, const int32_t* perm,
-                               int64_t N, int32_t ball, int32_t H, void* out, hipStream_t st) {
-  const int nb = (int)(N / ball);
-  const int total = nb * H;
+// Workgroups of the MFMA kernel: at most kGridPerCu per CU (a multiple of 8
+// for the XCD map), or one per item when there are fewer items.  With more
+// items than that the pipelined form runs.  At 65,536 points, ball 128 and 8
+// heads (2,048 head-pair items), 6 per CU measured best among 3, 6 and 8.
+constexpr int kGridPerCu = 6;
+
+static int attn_grid(int total) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  int g = cus * kGridPerCu;
+  g -= g % 8;
+  if (g < 8) g = 8;
+  return total < g ? total : g;
+}
+
+template <int D, int BB, int HPW>
+static bt_status launch_mfma(const void* q, const void* k, const void* v, const int32_t* perm,
+                             int64_t N, int32_t H, void* out, hipStream_t st) {
+  const int nb = (int)(N / BB);
+  const int total = nb * (H / HPW);
   const int xmap = (total % 8 == 0) ? 1 : 0;
-  dim3 grid(total);
-#define BT_MF(BB)                                                                           \
-  case BB:                                                                                  \
-    hipLaunchKernelGGL((ball_attn_mfma<D, BB>), grid, dim3(BB / 32 * 64), 0, st,           \
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, perm, H, \
-                       nb, xmap, (uint16_t*)out);                                           \
-    break;
-  switch (ball) {
-    BT_MF(32)
-    BT_MF(64)
-    BT_MF(128)
-    BT_MF(256)
-    default:
-      return BT_EINVAL;
+  const int g = attn_grid(total);
+  const bool pipe = g < total;
+  dim3 grid(g), block(BB / 32 * 64);
+#define BT_MF(PERM, PIPE)                                                                    \
+  hipLaunchKernelGGL((ball_attn_mfma<D, BB, HPW, PERM, PIPE>), grid, block, 0, st,          \
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, perm, H, nb, \
+                     xmap, (uint16_t*)out)
+  if (perm) {
+    if (pipe) BT_MF(true, true);
+    else BT_MF(true, false);
+  } else {
+    if (pipe) BT_MF(false, true);
+    else BT_MF(false, false);
   }
 #undef BT_MF
   return launch_status("ball_attn_mfma");
+}
+
+// Head pairs for balls up to 128 points when H is even; single heads
+// otherwise (a 256-point ball already holds 32 score registers per lane, and
+// a second head's staging registers would spill).
+template <int D>
+static bt_status launch_mfma_d(const void* q, const void* k, const void* v, const int32_t* perm,
+                               int64_t N, int32_t ball, int32_t H, void* out, hipStream_t st) {
+  const bool pair = H % 2 == 0;
+  switch (ball) {
+    case 32:
+      return pair ? launch_mfma<D, 32, 2>(q, k, v, perm, N, H, out, st)
+                  : launch_mfma<D, 32, 1>(q, k, v, perm, N, H, out, st);
+    case 64:
+      return pair ? launch_mfma<D, 64, 2>(q, k, v, perm, N, H, out, st)
+                  : launch_mfma<D, 64, 1>(q, k, v, perm, N, H, out, st);
+    case 128:
+      return pair ? launch_mfma<D, 128, 2>(q, k, v, perm, N, H, out, st)
+                  : launch_mfma<D, 128, 1>(q, k, v, perm, N, H, out, st);
+    case 256:
+      return launch_mfma<D, 256, 1>(q, k, v, perm, N, H, out, st);
+    default:
+      return BT_EINVAL;
+  }
 }
 
 bool ball_attn_uses_mfma(bt_dtype dt, int32_t ball, int32_t d) {

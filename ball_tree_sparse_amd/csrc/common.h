@@ -8,6 +8,11 @@
 
 #define BT_DEV __device__ __forceinline__
 
+// Occupancy request (waves per SIMD) for a kernel.
+#ifndef BT_WAVES_PER_EU
+#define BT_WAVES_PER_EU(lo, hi) __attribute__((amdgpu_waves_per_eu(lo, hi)))
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

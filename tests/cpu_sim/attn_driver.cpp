@@ -26,9 +26,9 @@ int main(int argc, char** argv) {
        v = rd<unsigned char>("v.bin", ne * es);
   auto perm = rd<int32_t>("perm.bin", N);
   std::vector<unsigned char> out(ne * es, 0xcd);
-  if (mode == "ball") {
-    bt::ball_attn_launch(q.data(), k.data(), v.data(), perm.data(), N, ball, H, d, (bt_dtype)dt,
-                         out.data(), nullptr);
+  if (mode == "ball" || mode == "ball_noperm") {
+    bt::ball_attn_launch(q.data(), k.data(), v.data(), mode == "ball" ? perm.data() : nullptr, N,
+                         ball, H, d, (bt_dtype)dt, out.data(), nullptr);
   } else {
     bsa_params p{ball, atoi(argv[7]), atoi(argv[8]), atoi(argv[9]), atoi(argv[10])};
     int gm = atoi(argv[11]);

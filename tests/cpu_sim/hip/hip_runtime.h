@@ -27,6 +27,7 @@
 #define __host__
 #define __forceinline__ inline
 #define __launch_bounds__(x)
+#define BT_WAVES_PER_EU(lo, hi)
 #define __shared__ static
 #define __restrict__
 
@@ -34,11 +35,18 @@ typedef int hipError_t;
 #define hipSuccess 0
 typedef void* hipStream_t;
 inline hipError_t hipGetLastError() { return 0; }
+// A small device: launch-size heuristics then give grids of few workgroups,
+// so persistent kernels walk several items each.
+#define hipDeviceAttributeMultiprocessorCount 0
+inline hipError_t hipGetDevice(int* d) { *d = 0; return 0; }
+inline hipError_t hipDeviceGetAttribute(int* v, int, int) { *v = 2; return 0; }
 inline const char* hipGetErrorString(hipError_t) { return "ok"; }
 
 struct dim3 { unsigned x, y, z; dim3(unsigned a = 1, unsigned b = 1, unsigned c = 1) : x(a), y(b), z(c) {} };
 struct float4 { float x, y, z, w; };
 struct uint2 { unsigned x, y; };
+struct int2 { int x, y; };
+struct int4 { int x, y, z, w; };
 inline float4 make_float4(float a, float b, float c, float d) { return {a, b, c, d}; }
 inline uint2 make_uint2(unsigned a, unsigned b) { return {a, b}; }
 
@@ -116,7 +124,20 @@ inline unsigned atomicMax(unsigned* p, unsigned v) {
 
 // ---- math --------------------------------------------------------------
 inline float __builtin_amdgcn_exp2f(float x) { return exp2f(x); }
+inline float __builtin_amdgcn_rcpf(float x) { return 1.0f / x; }
 inline float __expf(float x) { return expf(x); }
+// v_perm_b32 for selector bytes 0-7: byte i of the result is byte sel_i of
+// the 8-byte value {b (bytes 0-3), a (bytes 4-7)}.
+inline unsigned __builtin_amdgcn_perm(unsigned a, unsigned b, unsigned sel) {
+  const unsigned long long ab = ((unsigned long long)a << 32) | b;
+  unsigned r = 0;
+  for (int i = 0; i < 4; ++i) r |= (unsigned)((ab >> (8 * ((sel >> (8 * i)) & 7))) & 0xff) << (8 * i);
+  return r; }
+// v_dot2_f32_bf16: c + a0*b0 + a1*b1 (bf16 products are exact in fp32)
+template <class V>
+inline float __builtin_amdgcn_fdot2_f32_bf16(V a, V b, float c, bool) {
+  return (float)((double)c + (double)(float)a[0] * (double)(float)b[0] +
+                 (double)(float)a[1] * (double)(float)b[1]); }
 
 // ---- dynamic LDS -----------------------------------------------------------
 extern unsigned char* g_dyn_lds;
