@@ -100,7 +100,7 @@ def bench_ball(args, dev, torch, ops, synth):
         q, k, v, out = sets[i % len(sets)]
         ops.ball_attn(q, k, v, perm, ball, out=out)
 
-    for i in range(args.warmup):
+    for i in range(len(sets)):                 # load the kernel, touch every set
         step(i)
     torch.cuda.synchronize()
     if args.copy_probe:
@@ -116,33 +116,39 @@ def bench_ball(args, dev, torch, ops, synth):
         torch.cuda.synchronize()
         print(json.dumps({"eager_launches": args.steps}), flush=True)
         return None
-    # one graph holds one launch per input set; replays run them back to back
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(len(sets)):
-            step(i)
-    reps = max(1, args.steps // len(sets))
-    nsteps = reps * len(sets)
-    for _ in range(2):
-        graph.replay()
+    # warmup: back-to-back launches until the clocks have settled
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
+    # timed region: back-to-back launches on the current stream, HIP events
+    # recorded on that stream around them
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nsteps = args.steps
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(reps):
-        graph.replay()
+    for i in range(nsteps):
+        step(i)
     e1.record()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     attn_us = e0.elapsed_time(e1) * 1e3 / nsteps
-    # eager launches of the same kernel, for comparison with the graph
-    eager = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    eager[0].record()
-    for i in range(nsteps):
-        step(i)
-    eager[1].record()
+    # the same launches replayed from a HIP graph (one launch per input set),
+    # for comparison: replays add a gap between kernels
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(len(sets)):
+            step(i)
+    reps = max(1, nsteps // len(sets))
+    for _ in range(reps):
+        graph.replay()
     torch.cuda.synchronize()
-    eager_us = eager[0].elapsed_time(eager[1]) * 1e3 / nsteps
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(reps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_us = g0.elapsed_time(g1) * 1e3 / (reps * len(sets))
 
     esize = 2 if w.dtype == "bf16" else 4
     attn_bytes = 4 * N * H * d * esize + 4 * N
@@ -159,13 +165,13 @@ def bench_ball(args, dev, torch, ops, synth):
                                f"N={N}, ball {ball}, H={H}, d={d}, {w.dtype}",
                    "N": N, "ball": ball, "leaf": leaf, "H": H, "d": d,
                    "input_sets_rotated": len(sets),
-                   "timing": "HIP graph of one launch per input set, replayed; "
-                             "events around all replays"},
+                   "timing": "back-to-back launches on one stream; HIP events on that "
+                             "stream around the timed launches"},
         "roofline": {"kernel": "ball_attn_mfma" if w.dtype == "bf16" else "ball_attn_valu",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": attn_bytes},
-        "ball_attn": {"us": attn_us, "us_eager_launches": eager_us,
+        "ball_attn": {"us": attn_us, "us_graph_replay": graph_us,
                       "points_per_s": N / (attn_us * 1e-6),
                       "tflops": attn_flops / (attn_us * 1e-6) / 1e12,
                       "mfma_frac": attn_flops / (attn_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
@@ -191,21 +197,22 @@ def bench_bsa(args, dev, torch, ops, synth):
         ops.bsa_attn(q, k, v, perm, w.ball, x["block"], x["group"], x["topk"],
                      x["mask_own_ball"], gate_w=Wg, out=out, workspace=bws)
 
-    for _ in range(args.warmup):
+    warm, steps = min(args.warmup, 300), min(args.steps, 500)   # ~0.65 ms per step
+    for _ in range(warm):
         step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     e1.record()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    ms = el / args.steps * 1e3
+    ms = el / steps * 1e3
     flops = 4 * N * H * d * (w.ball + N // x["block"] + x["topk"] * x["block"])
     return {"metric": "bsa points/sec", "value": N / (ms * 1e-3), "unit": "points/s",
-            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": ms,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic",
             "config": {"workload": "bsa: BSA over a tree permutation (ball 128, block 64, "
@@ -216,8 +223,8 @@ def bench_bsa(args, dev, torch, ops, synth):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=8000)
     ap.add_argument("--workload", default="sphere",
                     choices=["sphere", "cosmo", "rotpair", "tiny", "bsa"])
     ap.add_argument("--sets", type=int, default=4)

@@ -40,6 +40,10 @@ def _run(q, k, v, perm, ball, dev):
     (2048, 2, 64, 256, "bf16"),
     (1024, 4, 16, 32, "bf16"),     # d=16 bf16 -> VALU kernel
     (960, 2, 32, 48, "bf16"),      # ball not a multiple of 32 -> VALU kernel
+    (98432, 4, 32, 128, "bf16"),   # 1,538 head-pair items: persistent pipelined form,
+                                   # two workgroups walk a second item, no XCD remap
+    (98304, 6, 32, 128, "bf16"),   # 2,304 items, pipelined, XCD remap, 3 pairs per ball
+    (16384, 8, 32, 256, "bf16"),   # ball 256: single-head items
 ])
 def test_parity_random_perm(n, H, d, ball, dtype):
     dev = gpu()
