@@ -445,8 +445,9 @@ static bt_status launch_valu(const void* q, const void* k, const void* v, const 
 // Workgroups of the MFMA kernel: at most kGridPerCu per CU (a multiple of 8
 // for the XCD map), or one per item when there are fewer items.  With more
 // items than that the pipelined form runs.  At 65,536 points, ball 128 and 8
-// heads (2,048 head-pair items), 6 per CU measured best among 3, 6 and 8.
-constexpr int kGridPerCu = 6;
+// heads (2,048 head-pair items; about 3 workgroups fit per CU at once), 5
+// per CU measured best among 3 to 8 in steps of a half.
+constexpr int kGridPerCu = 5;
 
 static int attn_grid(int total) {
   static int cus = 0;

@@ -2,27 +2,31 @@
 // argument", "Core claim", Figure 1 and Figure 3 captions; referee report,
 // major comments 1 and 2 on Eqs. 10-15).  Everything runs in tree order:
 //
-//   pool    K, V -> block means Kc (fp32 and bf16), Vc (bf16) over blocks of
-//           l tree positions, plus head-major tree-ordered copies Kt, Vt so
-//           that every later read of a ball or a selected block is one
-//           contiguous run; Q -> fp32 group means qbar (the pooled query).
+//   pool    K, V -> head-major tree-ordered copies (K row-major [h][t][d];
+//           V transposed in 32-key blocks [h][t/32][d][32], the operand
+//           layout of the P V product), block means of K in fp32 ([h][d][j],
+//           for the scores) and bf16 ([h][j][d]) and of V in bf16 (transposed
+//           like V) over blocks of l tree positions; Q -> fp32 group means
+//           qbar (the pooled query).
 //   select  s[g, j] = qbar_g . Kc_j / sqrt(d) in fp32; blocks inside the
 //           group's own ball are excluded; top-k per (group, head) by
 //           repeated wave arg-max (ties to the smaller block index).
 //   fused   one workgroup per (group, head), one wave per 32 queries: the
 //           ball, compression and selection branches run one after another
-//           as online-softmax attention over 128-key chunks (S^T = K Q^T and
-//           O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, V^T staged in LDS),
-//           and are merged with G = sigmoid(W q + b) before one scatter of
-//           the bf16 result to original order.
+//           as online-softmax attention over 64-key chunks (S^T = K Q^T and
+//           O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, both operands read
+//           straight from the pooled layouts, so waves never wait on each
+//           other), and are merged with G = sigmoid(W q + b) before one
+//           scatter of the bf16 result to original order.
 #include "common.h"
 
 namespace bt {
 
-constexpr int kChunk = 128;            // keys per online-softmax step
+constexpr int kChunk = 64;             // keys per online-softmax step
+constexpr int kSelRegs = 16;           // scores per lane held in registers by select
 
 struct BsaLayout {
-  size_t kt, vt, kc32, kcb, vcb, qbar, sel, total;
+  size_t kt, vt, kc32, kcb, vcb, qbar, sel, total;   // vt, vcb: transposed blocks
 };
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -47,18 +51,92 @@ size_t bsa_ws_size(int64_t N, int32_t H, int32_t d, const bsa_params* p) {
 }
 
 // ------------------------------------------------------------------ pool ----
-// Grid (blocks of `len` tree positions, column slices).  A column is 8
-// consecutive bf16 of one head.  Thread (col, rg) sums rows rg, rg+RG, ...;
-// the RG partial sums are then added in a fixed order, so the result is
-// deterministic.  With COPY the rows are also written to the head-major
-// tree-ordered copy dst[h][t][:].
-template <bool COPY, bool F32OUT, bool BF16OUT>
-__global__ __launch_bounds__(256) void bsa_pool(const uint16_t* __restrict__ src,
-                                                const int32_t* __restrict__ perm, int32_t H,
-                                                int32_t d, int32_t len, int64_t N,
-                                                uint16_t* __restrict__ copy,
-                                                float* __restrict__ mean32,
-                                                uint16_t* __restrict__ meanb) {
+// Position of key r (0..31) inside a transposed 32-key block.  The P V
+// product feeds a lane's 8 keys of P^T in the order that the S^T tile gives
+// them (key = 8*(e/4) + 4*hf + e%4 within 16), which is the natural order
+// with bits 2 and 3 of the key index swapped; the mapping is its own inverse.
+BT_DEV int tpos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Grid (block j of `len` tree positions, head group of HP heads), 256
+// threads.  Rows of K and V are gathered through perm (HP*D*2 bytes each, a
+// whole 128-byte line for two heads at d = 32) into LDS; K is written back
+// row-major to kt[h][t][:], V transposed to vt[h][t/32][:][tpos(t%32)]; the
+// block means are summed from LDS in a fixed order (deterministic).
+template <int D, int HP>
+__global__ __launch_bounds__(256) void bsa_pool_kv(const uint16_t* __restrict__ k,
+                                                   const uint16_t* __restrict__ v,
+                                                   const int32_t* __restrict__ perm, int32_t H,
+                                                   int32_t len, int64_t N,
+                                                   uint16_t* __restrict__ kt,
+                                                   uint16_t* __restrict__ vtt,
+                                                   float* __restrict__ kc32,
+                                                   uint16_t* __restrict__ kcb,
+                                                   uint16_t* __restrict__ vct) {
+  HIP_DYNAMIC_SHARED(uint16_t, lds)
+  constexpr int CPR = HP * D / 8;                 // 16-byte chunks per gathered row
+  uint16_t* kl = lds;                             // [len][HP*D]
+  uint16_t* vl = lds + (size_t)len * HP * D;      // [len][HP*D]
+  const int tid = threadIdx.x;
+  const int64_t j = blockIdx.x;
+  const int h0 = blockIdx.y * HP;
+  const int64_t nc = N / len;
+  const int64_t rs = (int64_t)H * D;
+  for (int it = tid; it < len * CPR; it += 256) {
+    const int r = it / CPR, ch = it - r * CPR;
+    const int64_t t = j * len + r;
+    const int64_t pt = perm_index(perm[t], N);
+    const int64_t off = pt * rs + (int64_t)h0 * D + ch * 8;
+    const u32x4 xk = *(const u32x4*)(k + off);
+    const u32x4 xv = *(const u32x4*)(v + off);
+    const int hh = ch / (D / 8), dc = ch - hh * (D / 8);
+    *(u32x4*)(kt + ((int64_t)(h0 + hh) * N + t) * D + dc * 8) = xk;
+    *(u32x4*)(kl + r * (HP * D) + ch * 8) = xk;
+    *(u32x4*)(vl + r * (HP * D) + ch * 8) = xv;
+  }
+  __syncthreads();
+  // V transposed: 16-byte runs of 8 positions of one (head, 32-key block, d)
+  const int nkb = len / 32;
+  for (int it = tid; it < HP * nkb * D * 4; it += 256) {
+    const int q8 = it & 3;
+    const int dd = (it >> 2) % D;
+    const int kb = (it >> 2) / D % nkb;
+    const int hh = (it >> 2) / D / nkb;
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r0 = kb * 32 + tpos(q8 * 8 + 2 * e), r1 = kb * 32 + tpos(q8 * 8 + 2 * e + 1);
+      o[e] = uint32_t(vl[r0 * (HP * D) + hh * D + dd]) |
+             (uint32_t(vl[r1 * (HP * D) + hh * D + dd]) << 16);
+    }
+    const int64_t blk = (j * len) / 32 + kb;
+    *(u32x4*)(vtt + (((int64_t)(h0 + hh) * (N / 32) + blk) * D + dd) * 32 + q8 * 8) = o;
+  }
+  // block means of K (fp32 and bf16) and V (bf16, transposed layout)
+  for (int it = tid; it < 2 * HP * D; it += 256) {
+    const int isv = it / (HP * D), hd = it - isv * (HP * D);
+    const int hh = hd / D, dd = hd - hh * D;
+    const uint16_t* col = (isv ? vl : kl) + hd;
+    float sum = 0.f;
+    for (int r = 0; r < len; ++r) sum += bf16_to_f32(col[r * (HP * D)]);
+    const float m = sum * (1.0f / (float)len);
+    const int h = h0 + hh;
+    if (!isv) {
+      kc32[((int64_t)h * D + dd) * nc + j] = m;
+      kcb[((int64_t)h * nc + j) * D + dd] = (uint16_t)(pack_bf16x2(m, 0.f) & 0xffffu);
+    } else {
+      vct[(((int64_t)h * (nc / 32) + j / 32) * D + dd) * 32 + tpos((int)(j % 32))] =
+          (uint16_t)(pack_bf16x2(m, 0.f) & 0xffffu);
+    }
+  }
+}
+
+// Grid (groups, column slices): fp32 means of Q over groups of `len` tree
+// positions.  A column is 8 consecutive bf16 of one head; thread (col, rg)
+// sums rows rg, rg+RG, ...; the RG partial sums are added in a fixed order.
+__global__ __launch_bounds__(256) void bsa_pool_q(const uint16_t* __restrict__ src,
+                                                  const int32_t* __restrict__ perm, int32_t H,
+                                                  int32_t d, int32_t len, int64_t N,
+                                                  float* __restrict__ mean32) {
   __shared__ float part[256][9];
   const int cols = H * d / 8;
   const int slice = cols < 64 ? cols : 64;
@@ -79,7 +157,6 @@ __global__ __launch_bounds__(256) void bsa_pool(const uint16_t* __restrict__ src
         acc[2 * e] += bf16_to_f32((uint16_t)(x[e] & 0xffffu));
         acc[2 * e + 1] += bf16_to_f32((uint16_t)(x[e] >> 16));
       }
-      if (COPY) *(u32x4*)(copy + ((int64_t)h * N + t) * d + dd) = x;
     }
   }
 #pragma unroll
@@ -94,21 +171,42 @@ __global__ __launch_bounds__(256) void bsa_pool(const uint16_t* __restrict__ src
       for (int e = 0; e < 8; ++e) s[e] += part[g * slice + colw][e];
     const float inv = 1.0f / (float)len;
     const int64_t nb = N / len;
-    if (F32OUT) {
-      float* m32 = mean32 + ((int64_t)h * nb + j) * d + dd;
+    float* m32 = mean32 + ((int64_t)h * nb + j) * d + dd;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m32[e] = s[e] * inv;
-    }
-    if (BF16OUT) {
-      u32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(s[2 * e] * inv, s[2 * e + 1] * inv);
-      *(u32x4*)(meanb + ((int64_t)h * nb + j) * d + dd) = o;
-    }
+    for (int e = 0; e < 8; ++e) m32[e] = s[e] * inv;
   }
 }
 
 // ---------------------------------------------------------------- select ----
+// One step of a wave arg-max over (v, i): take the partner's pair if its
+// value is larger, or equal with a smaller index.  DPP moves with the lane's
+// own value as the fallback, so lanes without a partner keep their pair.
+#define BT_ARGMAX_DPP(CTRL, ROWS)                                                          \
+  {                                                                                        \
+    const float ov = __int_as_float(                                                       \
+        __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xf, \
+                                    false));                                               \
+    const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROWS, 0xf, false);              \
+    const bool take = (ov > v) | ((ov == v) & (oi < i));                                   \
+    v = take ? ov : v;                                                                     \
+    i = take ? oi : i;                                                                     \
+  }
+
+// Wave arg-max: the largest v, ties to the smallest i, returned to every
+// lane.  row_shr 1, 2, 4, 8 leave each row's result in its lane 15; the two
+// row broadcasts gather the four rows into lane 63.
+BT_DEV void wave_argmax(float& v, int& i) {
+  BT_ARGMAX_DPP(0x111, 0xf)    // row_shr:1
+  BT_ARGMAX_DPP(0x112, 0xf)    // row_shr:2
+  BT_ARGMAX_DPP(0x114, 0xf)    // row_shr:4
+  BT_ARGMAX_DPP(0x118, 0xf)    // row_shr:8
+  BT_ARGMAX_DPP(0x142, 0xa)    // row_bcast:15 into rows 1 and 3
+  BT_ARGMAX_DPP(0x143, 0xc)    // row_bcast:31 into rows 2 and 3
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+#undef BT_ARGMAX_DPP
+
 // Workgroup = (head, tile of TG groups).  Scores of the tile live in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void bsa_select(const float* __restrict__ qbar,
@@ -129,11 +227,11 @@ __global__ __launch_bounds__(256) void bsa_select(const float* __restrict__ qbar
     qs[i] = qbar[((int64_t)h * ngroups + g0) * d + i];
   __syncthreads();
   const float scale = 1.0f / sqrtf((float)d);
-  const float* kh = kc32 + (int64_t)h * nc * d;
+  const float* kh = kc32 + (int64_t)h * D * nc;   // [d][nc]: lanes read consecutive blocks
   for (int jb = tid; jb < nc; jb += 256) {
     float kr[D];
 #pragma unroll
-    for (int e = 0; e < D; ++e) kr[e] = kh[(int64_t)jb * D + e];
+    for (int e = 0; e < D; ++e) kr[e] = kh[(int64_t)e * nc + jb];
     for (int g = 0; g < ng; ++g) {
       float s = 0.f;
 #pragma unroll
@@ -152,134 +250,145 @@ __global__ __launch_bounds__(256) void bsa_select(const float* __restrict__ qbar
       for (int64_t jb = lo / block + lane; jb < hi / block; jb += 64) s[jb] = -INFINITY;
     }
     __builtin_amdgcn_wave_barrier();
-    for (int it = 0; it < topk; ++it) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int jb = lane; jb < nc; jb += 64) {
-        const float v = s[jb];
-        if (v > bv) { bv = v; bi = jb; }          // ascending jb: first max kept
-      }
+    if (nc <= 64 * kSelRegs) {
+      // scores of block jb = lane + 64*i held in registers
+      float r[kSelRegs];
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ov = __shfl_xor(bv, m, 64);
-        const int oi = __shfl_xor(bi, m, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      for (int i = 0; i < kSelRegs; ++i) {
+        const int jb = lane + 64 * i;
+        r[i] = jb < nc ? s[jb] : -INFINITY;
       }
-      if (lane == 0) {
-        sel[((int64_t)h * ngroups + gg) * topk + it] = bi;
-        if (bi < nc) s[bi] = -INFINITY;
+      for (int it = 0; it < topk; ++it) {
+        float v = -INFINITY;
+        int i = 0x7fffffff;
+#pragma unroll
+        for (int u = 0; u < kSelRegs; ++u)
+          if (r[u] > v) { v = r[u]; i = lane + 64 * u; }   // ascending index: first max kept
+        wave_argmax(v, i);
+        if (lane == 0) sel[((int64_t)h * ngroups + gg) * topk + it] = i;
+        if ((i & 63) == lane) {
+#pragma unroll
+          for (int u = 0; u < kSelRegs; ++u)
+            if (u == (i >> 6)) r[u] = -INFINITY;
+        }
       }
-      __builtin_amdgcn_wave_barrier();
+    } else {
+      for (int it = 0; it < topk; ++it) {
+        float v = -INFINITY;
+        int i = 0x7fffffff;
+        for (int jb = lane; jb < nc; jb += 64) {
+          const float x = s[jb];
+          if (x > v) { v = x; i = jb; }          // ascending jb: first max kept
+        }
+        wave_argmax(v, i);
+        if (lane == 0) {
+          sel[((int64_t)h * ngroups + gg) * topk + it] = i;
+          if (i < nc) s[i] = -INFINITY;
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
     }
   }
 }
 
 // ----------------------------------------------------------------- fused ----
-BT_DEV int swap23b(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+typedef __bf16 bsa_bf16x2 __attribute__((ext_vector_type(2)));
 
-BT_DEV uint16_t u16_at(const u32x4& r, int e) {
-  const uint32_t x = r[e >> 1];
-  return (uint16_t)((e & 1) ? (x >> 16) : (x & 0xffffu));
+// Sum of the eight bf16 values of an MFMA operand, added to acc.
+BT_DEV float bsa_sum8(bf16x8 x, float acc) {
+  const bsa_bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, acc, false);
 }
 
-// Running state of one branch for the lane's query column.
+// Running state of one branch for the lane's query column.  The softmax
+// weights are rounded once to bf16 for the P V product and the normaliser
+// sums those rounded weights (four chains, lane-local until the merge).
 template <int DB>
 struct Branch {
   f32x16 o[DB];
   float m;      // running max in log2-scaled units
-  float l;      // lane-local partial sum of exp2
+  float l[4];   // partial sums of the rounded weights
 };
 
-template <int D, int NWV>
-struct FusedCtx {
-  static constexpr int DS = D / 16;
-  static constexpr int DB = D / 32;
-  static constexpr int VTS = kChunk + 8;
-};
-
-// One online-softmax step over a chunk of nkb*32 keys whose rows are
-// rowbase(kb) + c for 32-key block kb (rows of a head-major [rows][D] array).
-template <int D, int NT, typename RowFn>
+// One online-softmax step over NKB 32-key blocks.  Block kb's keys are rows
+// row0(kb) .. row0(kb)+31 of the head's row-major K (kh) and of its
+// transposed V blocks (vh: [rows/32][D][32]); row0(kb) is a multiple of 32.
+// Every K and V fragment of the chunk is requested before the first MFMA.
+template <int D, int NKB, typename RowFn>
 BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
-                         RowFn rowbase, int nkb, const bf16x8* qf, float c2, Branch<D / 32>& br,
-                         uint16_t* vt) {
-  constexpr int DS = D / 16, DB = D / 32, VTS = kChunk + 8;
-  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, c = lane & 31;
-  // stage V^T of the chunk (4 keys x 8 d per item)
-  for (int it = tid; it < nkb * 8 * (D / 8); it += NT) {
-    const int kq = it / (D / 8), dc = it - kq * (D / 8);
-    const int key0 = kq * 4;
-    const int64_t row0 = rowbase(key0 >> 5) + (key0 & 31);
-    u32x4 r[4];
+                         RowFn row0, const bf16x8* qf, float c2, Branch<D / 32>& br) {
+  constexpr int DS = D / 16, DB = D / 32;
+  const int lane = threadIdx.x & 63, hf = lane >> 5, c = lane & 31;
+  bf16x8 kf[NKB][DS], vf[NKB][2][DB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) r[u] = *(const u32x4*)(vh + (row0 + u) * D + dc * 8);
-    const int pos0 = (key0 & ~15) + swap23b(key0 & 15);
+  for (int kb = 0; kb < NKB; ++kb) {
+    const int64_t r0 = row0(kb);
+    const uint16_t* krow = kh + (r0 + c) * D + hf * 8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      u32x2 pk;
-      pk[0] = uint32_t(u16_at(r[0], e)) | (uint32_t(u16_at(r[1], e)) << 16);
-      pk[1] = uint32_t(u16_at(r[2], e)) | (uint32_t(u16_at(r[3], e)) << 16);
-      *(u32x2*)&vt[(dc * 8 + e) * VTS + pos0] = pk;
-    }
+    for (int s = 0; s < DS; ++s) kf[kb][s] = *(const bf16x8*)(krow + s * 16);
+    const uint16_t* vblk = vh + r0 * D + c * 32 + hf * 8;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        vf[kb][s2][db] = *(const bf16x8*)(vblk + db * 32 * 32 + s2 * 16);
   }
-  // S^T blocks
-  f32x16 sacc[kChunk / 32];
+  f32x16 sacc[NKB];
 #pragma unroll
-  for (int kb = 0; kb < kChunk / 32; ++kb) {
-    if (kb < nkb) {
-      const int64_t row = rowbase(kb) + c;
-      f32x16 a = {};
+  for (int kb = 0; kb < NKB; ++kb) {
+    f32x16 a = {};
 #pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const bf16x8 kf = *(const bf16x8*)(kh + row * D + s * 16 + hf * 8);
-        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], a, 0, 0, 0);
-      }
-      sacc[kb] = a;
-    }
+    for (int s = 0; s < DS; ++s)
+      a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][s], qf[s], a, 0, 0, 0);
+    sacc[kb] = a;
   }
-  float cm = -INFINITY;
+  // chunk maximum of the raw scores (scaling by c2 > 0 keeps the order)
+  float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-  for (int kb = 0; kb < kChunk / 32; ++kb)
-    if (kb < nkb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) cm = fmaxf(cm, sacc[kb][e] * c2);
+    for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
+  float cm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * c2;
   cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
   const float mn = fmaxf(br.m, cm);
   const float alpha = __builtin_amdgcn_exp2f(br.m - mn);     // 0 on the first chunk
-  br.l *= alpha;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) br.l[i] *= alpha;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) br.o[db][e] *= alpha;
   br.m = mn;
 #pragma unroll
-  for (int kb = 0; kb < kChunk / 32; ++kb)
-    if (kb < nkb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], c2, -mn));
-        sacc[kb][e] = p;
-        br.l += p;
-      }
-  __syncthreads();                                        // V^T staged
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8 pf;
 #pragma unroll
-  for (int kb = 0; kb < kChunk / 32; ++kb) {
-    if (kb < nkb) {
+      for (int e = 0; e < 8; ++e)
+        pf[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][s2 * 8 + e], c2, -mn));
+      br.l[(kb * 2 + s2) & 3] = bsa_sum8(pf, br.l[(kb * 2 + s2) & 3]);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sacc[kb][s2 * 8 + e];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 vf =
-              *(const bf16x8*)&vt[(db * 32 + c) * VTS + (kb * 2 + s2) * 16 + hf * 8];
-          br.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, br.o[db], 0, 0, 0);
-        }
-      }
+      for (int db = 0; db < DB; ++db)
+        br.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][s2][db], pf, br.o[db], 0, 0, 0);
     }
-  }
-  __syncthreads();                                        // V^T free again
+}
+
+// Online softmax over keys [0, len) of a branch in kChunk-key chunks (len is
+// a multiple of 32); row0(key) gives the row of the 32-key block at key.
+template <int D, typename RowFn>
+BT_DEV void attend_range(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
+                         RowFn row0, int len, const bf16x8* qf, float c2, Branch<D / 32>& br) {
+  constexpr int KB = kChunk / 32;
+  int k0 = 0;
+  for (; k0 + kChunk <= len; k0 += kChunk)
+    attend_chunk<D, KB>(kh, vh, [&](int kb) -> int64_t { return row0(k0 + kb * 32); }, qf, c2,
+                        br);
+  for (; k0 < len; k0 += 32)                 // a tail of 32-key blocks
+    attend_chunk<D, 1>(kh, vh, [&](int kb) -> int64_t { return row0(k0); }, qf, c2, br);
 }
 
 template <int D>
@@ -287,13 +396,15 @@ BT_DEV void branch_init(Branch<D / 32>& br) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) br.o[db] = f32x16{};
   br.m = -INFINITY;
-  br.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) br.l[i] = 0.f;
 }
 
 template <int D>
 BT_DEV void branch_merge(const Branch<D / 32>& br, float gate, f32x16* acc) {
-  const float l = br.l + __shfl_xor(br.l, 32, 64);
-  const float f = gate / l;
+  float l = (br.l[0] + br.l[1]) + (br.l[2] + br.l[3]);
+  l += __shfl_xor(l, 32, 64);
+  const float f = gate * __builtin_amdgcn_rcpf(l);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -301,17 +412,15 @@ BT_DEV void branch_merge(const Branch<D / 32>& br, float gate, f32x16* acc) {
 }
 
 template <int D, int NWV>
-__global__ __launch_bounds__(NWV * 64) void bsa_fused(
+__global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(3, 8) void bsa_fused(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ perm,
-    const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt_g,
-    const uint16_t* __restrict__ kcb, const uint16_t* __restrict__ vcb,
+    const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vtt,
+    const uint16_t* __restrict__ kcb, const uint16_t* __restrict__ vct,
     const int32_t* __restrict__ sel, const float* __restrict__ gate_w,
     const float* __restrict__ gate_b, float gc0, float gc1, float gc2, int32_t H, int64_t N,
     int32_t nc, int32_t ngroups, int32_t ball, int32_t block, int32_t topk, int32_t xcd_map,
     uint16_t* __restrict__ out) {
-  constexpr int NT = NWV * 64;
-  constexpr int DS = D / 16, DB = D / 32, VTS = kChunk + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t vts[D * VTS];
+  constexpr int DS = D / 16, DB = D / 32;
   __shared__ int32_t ssel[64];
   const int total = ngroups * H;
   int pair = blockIdx.x;
@@ -357,7 +466,7 @@ __global__ __launch_bounds__(NWV * 64) void bsa_fused(
 
   const float c2 = 1.4426950408889634f / sqrtf((float)D);
   const uint16_t* kh = kt + (int64_t)h * N * D;
-  const uint16_t* vh = vt_g + (int64_t)h * N * D;
+  const uint16_t* vh = vtt + (int64_t)h * N * D;
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
@@ -367,38 +476,25 @@ __global__ __launch_bounds__(NWV * 64) void bsa_fused(
   {
     branch_init<D>(br);
     const int64_t b0 = ((int64_t)g * group / ball) * ball;
-    for (int k0 = 0; k0 < ball; k0 += kChunk) {
-      const int nkb = min(kChunk, ball - k0) / 32;
-      attend_chunk<D, NT>(kh, vh, [&](int kb) -> int64_t { return b0 + k0 + kb * 32; }, nkb,
-                          qf, c2, br, vts);
-    }
+    attend_range<D>(kh, vh, [&](int key) -> int64_t { return b0 + key; }, ball, qf, c2, br);
     branch_merge<D>(br, G0, acc);
   }
   // ---- compression branch: every coarse token ---------------------------
   {
     branch_init<D>(br);
     const uint16_t* kch = kcb + (int64_t)h * nc * D;
-    const uint16_t* vch = vcb + (int64_t)h * nc * D;
-    for (int k0 = 0; k0 < nc; k0 += kChunk) {
-      const int nkb = min(kChunk, nc - k0) / 32;
-      attend_chunk<D, NT>(kch, vch, [&](int kb) -> int64_t { return (int64_t)k0 + kb * 32; },
-                          nkb, qf, c2, br, vts);
-    }
+    const uint16_t* vch = vct + (int64_t)h * nc * D;
+    attend_range<D>(kch, vch, [&](int key) -> int64_t { return key; }, nc, qf, c2, br);
     branch_merge<D>(br, G1, acc);
   }
   // ---- selection branch: the union of the selected blocks ---------------
   {
     branch_init<D>(br);
-    const int nsel = topk * block;
-    for (int k0 = 0; k0 < nsel; k0 += kChunk) {
-      const int nkb = min(kChunk, nsel - k0) / 32;
-      attend_chunk<D, NT>(kh, vh,
-                          [&](int kb) -> int64_t {
-                            const int idx = k0 + kb * 32;
-                            return (int64_t)ssel[idx / block] * block + (idx % block);
-                          },
-                          nkb, qf, c2, br, vts);
-    }
+    attend_range<D>(kh, vh,
+                    [&](int key) -> int64_t {
+                      return (int64_t)ssel[key / block] * block + (key % block);
+                    },
+                    topk * block, qf, c2, br);
     branch_merge<D>(br, G2, acc);
   }
 
@@ -459,15 +555,22 @@ bt_status bsa_launch(const void* q, const void* k, const void* v, const int32_t*
   const int slice = cols < 64 ? cols : 64;
   const dim3 pblk(256);
 
-  // K: tree-ordered copy, fp32 and bf16 block means; V: copy and bf16 means;
-  // Q: fp32 group means (the pooled queries that score the blocks)
-  const dim3 gk(nc, (cols + slice - 1) / slice), gq(ngroups, (cols + slice - 1) / slice);
-  hipLaunchKernelGGL((bsa_pool<true, true, true>), gk, pblk, 0, st, (const uint16_t*)k, perm, H,
-                     d, p->block, N, kt, kc32, kcb);
-  hipLaunchKernelGGL((bsa_pool<true, false, true>), gk, pblk, 0, st, (const uint16_t*)v, perm, H,
-                     d, p->block, N, vt, (float*)nullptr, vcb);
-  hipLaunchKernelGGL((bsa_pool<false, true, false>), gq, pblk, 0, st, (const uint16_t*)q, perm,
-                     H, d, p->group, N, (uint16_t*)nullptr, qbar, (uint16_t*)nullptr);
+  // K, V: tree-ordered copies (V transposed) and block means; Q: fp32 group
+  // means (the pooled queries that score the blocks)
+  const int hp = (H % 2 == 0 && d == 32) ? 2 : 1;
+  const size_t pool_lds = (size_t)2 * p->block * hp * d * sizeof(uint16_t);
+  const dim3 gk(nc, H / hp), gq(ngroups, (cols + slice - 1) / slice);
+  if (d == 32 && hp == 2)
+    hipLaunchKernelGGL((bsa_pool_kv<32, 2>), gk, pblk, pool_lds, st, (const uint16_t*)k,
+                       (const uint16_t*)v, perm, H, p->block, N, kt, vt, kc32, kcb, vcb);
+  else if (d == 32)
+    hipLaunchKernelGGL((bsa_pool_kv<32, 1>), gk, pblk, pool_lds, st, (const uint16_t*)k,
+                       (const uint16_t*)v, perm, H, p->block, N, kt, vt, kc32, kcb, vcb);
+  else
+    hipLaunchKernelGGL((bsa_pool_kv<64, 1>), gk, pblk, pool_lds, st, (const uint16_t*)k,
+                       (const uint16_t*)v, perm, H, p->block, N, kt, vt, kc32, kcb, vcb);
+  hipLaunchKernelGGL(bsa_pool_q, gq, pblk, 0, st, (const uint16_t*)q, perm, H, d, p->group, N,
+                     qbar);
   bt_status s = launch_status("bsa_pool");
   if (s != BT_OK) return s;
 

@@ -91,6 +91,27 @@ template <typename T> inline T __shfl_xor(T v, int m, int w = 64) { return emu_s
 template <typename T> inline T __shfl(T v, int src, int w = 64) { return emu_shfl_from(v, src); }
 template <typename T> inline T __shfl_up(T v, unsigned d, int w = 64) {
   int l = emu_tid() & 63; int s = l >= (int)d ? l - (int)d : l; return emu_shfl_from(v, s); }
+// DPP move with the old value kept where the source lane is invalid or the
+// row is masked off (bound_ctrl off, all banks).  Controls: row_shr:1-15,
+// row_bcast:15, row_bcast:31.
+inline int __builtin_amdgcn_update_dpp(int old, int src, int ctrl, int row_mask, int bank_mask,
+                                       bool bound_ctrl) {
+  const int t = emu_tid(), base = t & ~63, l = t & 63, row = l >> 4, x = l & 15;
+  g_blk->xch[t] = (uint32_t)src;
+  emu_wave_sync();
+  int from = -1;
+  if (ctrl >= 0x111 && ctrl <= 0x11f) { const int k = ctrl - 0x110; if (x >= k) from = l - k; }
+  else if (ctrl == 0x142) { if (row >= 1) from = 16 * row - 1; }
+  else if (ctrl == 0x143) { if (row >= 2) from = 31; }
+  else { fprintf(stderr, "emulator: DPP control %#x not modelled\n", ctrl); abort(); }
+  int r = old;
+  if (from >= 0 && ((row_mask >> row) & 1) && ((bank_mask >> (x >> 2)) & 1))
+    r = (int)(uint32_t)g_blk->xch[base + from];
+  emu_wave_sync();
+  (void)bound_ctrl;
+  return r;
+}
+inline int __builtin_amdgcn_readlane(int v, int lane) { return emu_shfl_from(v, lane); }
 inline unsigned long long __ballot(int p) {
   const int t = emu_tid(), base = t & ~63;
   g_blk->xch[t] = p ? 1 : 0;
