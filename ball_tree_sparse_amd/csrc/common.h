@@ -27,11 +27,12 @@ constexpr int kWave = 64;
 // ---------------------------------------------------------------- bf16 ----
 BT_DEV float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// Round-to-nearest-even through the gfx950 packed converter.
+// Round-to-nearest-even through the gfx950 packed converter (one
+// v_cvt_pk_bf16_f32 for the pair).
+typedef __bf16 bf16x2_pk __attribute__((ext_vector_type(2)));
 BT_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return uint32_t(__builtin_bit_cast(uint16_t, a)) |
-         (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+  const bf16x2_pk v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ------------------------------------------------------ float sort keys ----
