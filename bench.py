@@ -20,8 +20,13 @@ Prints ONE JSON line.  Besides the required fields it carries:
                 byte count of the kernel per launch from rocprofv3 FETCH_SIZE +
                 WRITE_SIZE counters (profiles/), or null if the kernel source
                 changed since they were taken;
-  cpu_baseline  the CPU oracle (NumPy: recursive tree + fp64 ball attention)
-                timed on this host on whole steps of the same workload.
+  cpu_baseline  the CPU oracle (NumPy fp64 ball attention) timed on this
+                host on whole steps of the same workload;
+  rows          the other rows of the path timed in the same run on their
+                own workloads: permute gather/scatter of 512-byte rows at the
+                rotated-pair size, the BSA step, and tree build + fp32 ball
+                attention at 1,024 points (the largest tree the GPU builder
+                takes in this build).
 
 Other workloads (--workload bsa | cosmo | rotpair) print their own line and
 are not the default measurement.
@@ -176,9 +181,89 @@ def bench_ball(args, dev, torch, ops, synth):
                       "tflops": attn_flops / (attn_us * 1e-6) / 1e12,
                       "mfma_frac": attn_flops / (attn_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
     }
+    if not args.no_side_rows:
+        line["rows"] = side_rows(dev, torch, ops, synth)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = _cpu_baseline(w, args.cpu_seconds)
     return line
+
+
+def _event_us(torch, fn, reps, warm=3):
+    """Mean time per call of fn() over reps back-to-back calls (HIP events
+    on the current stream, the stream the library launches on)."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def side_rows(dev, torch, ops, synth):
+    """The other rows of the path, timed in the same run on their own
+    workloads: permute (gather and scatter of 512-byte rows at the rotated-
+    pair size), the BSA step, and tree build + fp32 ball attention at the
+    size the GPU tree builder takes (1,024 points)."""
+    rows = {}
+    # permute: N = 262,144 rows of H*d bf16 = 512 bytes; three source and
+    # destination pairs (805 MB) rotate so that no call finds its rows in the
+    # 256 MB Infinity Cache
+    n, row = 262144, 8 * 32
+    gen = torch.Generator(device=dev).manual_seed(4)
+    srcs = [torch.randint(-32768, 32767, (n, row), dtype=torch.int16, device=dev, generator=gen)
+            for _ in range(3)]
+    dsts = [torch.empty_like(srcs[0]) for _ in range(3)]
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(4)).to(torch.int32).to(dev)
+    nbytes = 2 * n * row * 2 + 4 * n
+    for name, mode in (("gather", ops.BT_GATHER), ("scatter", ops.BT_SCATTER)):
+        it = [0]
+
+        def call():
+            i = it[0] % 3
+            it[0] += 1
+            ops.bt_permute(srcs[i], perm, mode, dst=dsts[i])
+        us = _event_us(torch, call, 60, warm=6)
+        rows["a5_permute_" + name] = {"workload": "N=262144 rows of 512 B (rotated-pair size)",
+                                      "us": us, "GBps": nbytes / us / 1e3,
+                                      "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS}
+    del srcs, dsts
+    # BSA step
+    w = synth.make("bsa")
+    x = w.extra
+    N, H, d = w.coords.shape[0], w.H, w.d
+    p = torch.randperm(N, generator=torch.Generator().manual_seed(1234)).to(torch.int32).to(dev)
+    bws = torch.empty(ops.bsa_workspace_size(N, H, d, w.ball, x["block"], x["group"], x["topk"]),
+                      dtype=torch.uint8, device=dev)
+    Wg = torch.from_numpy(w.gate_w).to(dev)
+    q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+    out = torch.empty_like(q)
+    us = _event_us(torch, lambda: ops.bsa_attn(q, k, v, p, w.ball, x["block"], x["group"],
+                                               x["topk"], x["mask_own_ball"], gate_w=Wg,
+                                               out=out, workspace=bws), 100, warm=20)
+    flops = 4 * N * H * d * (w.ball + N // x["block"] + x["topk"] * x["block"])
+    rows["a7_a11_bsa"] = {"workload": "N=65536 deformed sphere, ball 128, block 64, group 64, "
+                                      "top-16, H=8, d=32 bf16",
+                          "us_per_step": us, "points_per_s": N / (us * 1e-6),
+                          "tflops": flops / (us * 1e-6) / 1e12,
+                          "mfma_frac": flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
+    del q, k, v, out, bws
+    # tree build + fp32 ball attention at 1,024 points
+    w = synth.make("tiny")
+    c = torch.from_numpy(w.coords).to(dev)
+    q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+    tws = torch.empty(max(256, ops.bt_build_workspace_size(c.shape[0], w.leaf)), dtype=torch.uint8,
+                      device=dev)
+    pt = torch.empty(c.shape[0], dtype=torch.int32, device=dev)
+    ot = torch.empty_like(q)
+    us_b = _event_us(torch, lambda: ops.bt_build(c, w.leaf, perm=pt, workspace=tws), 200)
+    us_a = _event_us(torch, lambda: ops.ball_attn(q, k, v, pt, w.ball, out=ot), 200)
+    rows["a1_a4_a6_tiny"] = {"workload": "N=1024 uniform cube, leaf = ball 32, H=4, d=16 fp32",
+                             "build_us": us_b, "ball_attn_us": us_a}
+    return rows
 
 
 def bench_bsa(args, dev, torch, ops, synth):
@@ -229,6 +314,8 @@ def main():
                     choices=["sphere", "cosmo", "rotpair", "tiny", "bsa"])
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side-rows", action="store_true",
+                    help="skip the permute, BSA and tiny tree measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true",
                     help="only launch the kernels (for counter collection)")
