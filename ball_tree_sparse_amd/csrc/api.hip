@@ -144,13 +144,14 @@ bt_status bt_invert_perm(const int32_t* perm, int64_t N, int32_t* inv, void* str
 
 bt_status ball_attn(const void* q, const void* k, const void* v, const int32_t* perm, int64_t N,
                     int32_t ball, int32_t H, int32_t d, bt_dtype dt, void* out, void* stream) {
-  BT_REQUIRE(q && k && v && out, "q, k, v and out must be non-null");
   BT_REQUIRE(dt == BT_F32 || dt == BT_BF16, "dtype must be BT_F32 or BT_BF16");
   BT_REQUIRE(d == 16 || d == 32 || d == 64, "d must be 16, 32 or 64 (d=%d)", d);
   BT_REQUIRE(H >= 1, "H must be >= 1");
-  BT_REQUIRE(N >= 1 && ball >= 1 && N % ball == 0, "ball must divide N (N=%lld, ball=%d)",
+  BT_REQUIRE(N >= 0 && ball >= 1 && N % ball == 0, "ball must divide N (N=%lld, ball=%d)",
              (long long)N, ball);
   BT_REQUIRE(ball <= 4096, "ball must be <= 4096");
+  if (N == 0) return BT_OK;                 // no points: nothing to do
+  BT_REQUIRE(q && k && v && out, "q, k, v and out must be non-null");
   BT_REQUIRE(N * H * d < ((int64_t)1 << 31), "N*H*d must be below 2^31");
   BT_REQUIRE((N / ball) * H < ((int64_t)1 << 31), "too many (ball, head) pairs");
   const size_t bytes = (size_t)(N * H * d) * (dt == BT_F32 ? 4 : 2);

@@ -13,6 +13,7 @@ itself allocates nothing.
 from __future__ import annotations
 
 import ctypes as C
+import math
 import os
 
 import torch
@@ -160,7 +161,7 @@ def bt_permute(src, perm, mode: int, dst=None):
     _dev(src, "src")
     _dev(perm, "perm", torch.int32)
     N = src.shape[0]
-    row_bytes = src.numel() // max(N, 1) * src.element_size()
+    row_bytes = math.prod(src.shape[1:]) * src.element_size()
     if dst is None:
         dst = torch.empty_like(src)
     _dev(dst, "dst", src.dtype)

@@ -124,7 +124,9 @@ bt_status bt_invert_perm(const int32_t* perm, int64_t N, int32_t* inv,
  * no mask, no bias, non-causal.  out[perm[t]] = O[t] (out in the same order
  * and dtype as the inputs).
  * Requirements: ball >= 1 divides N; 1 <= H; d in {16, 32, 64};
- * ball <= 4096; N*H*d < 2^31; out does not alias q, k or v.
+ * ball <= 4096; N*H*d < 2^31; out does not alias q, k or v.  N = 0 is a
+ * no-op (pointers are not used).  Errors: BT_EINVAL for a violated
+ * requirement or a null pointer with N > 0; BT_EHIP if the launch fails.
  * bf16 with d in {32, 64} and ball a multiple of 32 up to 256 runs the MFMA
  * kernel; every other supported shape runs the fp32-VALU kernel.
  * ---------------------------------------------------------------------- */

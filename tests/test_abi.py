@@ -98,6 +98,9 @@ def test_ball_attn_rejects(L):
     assert call(args(out=q)) == ops.BT_EINVAL            # aliasing
     assert call(args(q=None)) == ops.BT_EINVAL
     assert call(args(ball=8192, N=8192)) == ops.BT_EINVAL
+    # no points: a no-op that touches no pointer; shape checks still apply
+    assert call(args(N=0, q=None, k=None, v=None, out=None)) == ops.BT_OK
+    assert call(args(N=0, d=24, q=None, k=None, v=None, out=None)) == ops.BT_EINVAL
 
 
 def test_bsa_rejects(L):

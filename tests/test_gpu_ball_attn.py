@@ -73,6 +73,28 @@ def test_full_attention_when_ball_is_n():
     assert max_abs(got, A.full_attn(q, k, v)) <= 1e-5
 
 
+def test_largest_ball_is_full_attention():
+    """ball = 4,096 (the largest accepted; fp32 VALU kernel) equals full attention."""
+    dev = gpu()
+    q, k, v = _feats(4096, 1, 16, "f32", seed=6)
+    say("ball_attn ball=4096")
+    got = _run(q, k, v, np.random.default_rng(1).permutation(4096), 4096, dev)
+    assert max_abs(got, A.full_attn(q, k, v)) <= 1e-5
+
+
+def test_empty_input_is_a_noop():
+    dev = gpu()
+    say("ball_attn / permute with N = 0")
+    for dt in (torch.bfloat16, torch.float32):
+        q = torch.empty((0, 4, 32), dtype=dt, device=dev)
+        out = ops.ball_attn(q, q.clone(), q.clone(), None, 32)
+        assert out.shape == (0, 4, 32)
+    src = torch.empty((0, 64), dtype=torch.int32, device=dev)
+    p = torch.empty((0,), dtype=torch.int32, device=dev)
+    assert ops.bt_permute(src, p, ops.BT_GATHER).shape == (0, 64)
+    torch.cuda.synchronize()
+
+
 def test_ball_one_returns_v():
     dev = gpu()
     q, k, v = _feats(256, 2, 16, "f32", seed=5)
