@@ -29,10 +29,12 @@
 //                 two children.
 //   Workgroups never wait on each other inside a launch: every hand-over is
 //   a launch boundary.
-//   finish      one wave per node of <= 1024 points: the node is loaded into
-//               LDS and every remaining level is split there (8-bit radix
+//   finish      every node of <= 1024 points is loaded into LDS and every
+//               remaining level is split there by single waves (8-bit radix
 //               select with an LDS histogram, ballot-scan partition), then
-//               perm[t] = idx.
+//               perm[t] = idx.  With few nodes a 16-wave workgroup owns a
+//               node and its waves split that level's segments in parallel;
+//               otherwise each wave owns a node.
 #include "common.h"
 
 namespace bt {
@@ -474,6 +476,29 @@ __global__ __launch_bounds__(kFinishWaves * 64) void tree_finish(const float4* _
   for (int i = lane; i < nf; i += 64) perm[base + i] = __float_as_int(R[i].w);
 }
 
+// One workgroup of kFinishBlockWaves waves per node of <= kFinish points:
+// the segments of a level are independent, so the waves take them in turn
+// (wave w splits segments w, w + waves, ...), with a workgroup barrier
+// between levels.  Used when there are few nodes (a small tree has one).
+constexpr int kFinishBlockWaves = 16;
+
+__global__ __launch_bounds__(kFinishBlockWaves * 64) void tree_finish_block(
+    const float4* __restrict__ rec, int nf, int leaf, int32_t* __restrict__ perm) {
+  __shared__ float4 srec[kFinish];
+  __shared__ uint32_t shist[kFinishBlockWaves][256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t base = (int64_t)blockIdx.x * nf;
+  for (int i = tid; i < nf; i += kFinishBlockWaves * 64) srec[i] = rec[base + i];
+  __syncthreads();
+  for (int m = nf; m > leaf; m >>= 1) {
+    const int nseg = nf / m;
+    for (int sgi = w; sgi < nseg; sgi += kFinishBlockWaves)
+      wave_split(srec + sgi * m, m, shist[w], lane);
+    __syncthreads();
+  }
+  for (int i = tid; i < nf; i += kFinishBlockWaves * 64) perm[base + i] = __float_as_int(srec[i].w);
+}
+
 __global__ __launch_bounds__(kThreads) void tree_write_perm(const float4* __restrict__ rec,
                                                             int64_t n, int32_t* __restrict__ perm) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -594,6 +619,11 @@ bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const floa
     return launch_status("tree_write_perm");
   }
   const int nnodes = (int)(n / p.nf);
+  if (nnodes <= 256) {                       // few nodes: a workgroup per node
+    hipLaunchKernelGGL(tree_finish_block, dim3(nnodes), dim3(kFinishBlockWaves * 64), 0, st,
+                       fin, (int)p.nf, leaf, perm);
+    return launch_status("tree_finish_block");
+  }
   hipLaunchKernelGGL(tree_finish, dim3((nnodes + kFinishWaves - 1) / kFinishWaves),
                      dim3(kFinishWaves * 64), 0, st, fin, (int)p.nf, leaf, nnodes, perm);
   return launch_status("tree_finish");
