@@ -30,6 +30,18 @@ g = group size, k* = selected blocks):
    by all heads; out = G0 * O_ball + G1 * O_cmp + G2 * O_slc.  ``gate_const``
    replaces G by a constant triple so that the (1, 0, 0) reduction can be
    tested exactly.
+
+Group (query) compression (``query_compression=True``): queries are pooled
+before the compression and selection branches ("Core claim": an optional
+coarsening step pools queries before selection and compression; the
+compression branch then runs over Q_cmp, K_cmp, V_cmp of length ceil(N/l),
+referee report major comment 1 on Eq. 15; the runtime it saves is quoted
+under "If this is right").  Reading taken here: the mean query of each block
+of l tree positions attends to all coarse tokens and every token of the
+block takes that result; the mean query of each group (the one that scores
+the blocks) attends once over the union of the group's selected blocks and
+every query of the group takes that result.  The ball branch and the gates
+stay per token.
 """
 from __future__ import annotations
 
@@ -108,6 +120,28 @@ def compression_attn(qt, kc, vc, chunk: int = 4096) -> np.ndarray:
     return out
 
 
+def pooled_compression_attn(qt, kc, vc, block: int) -> np.ndarray:
+    """Group compression: the mean query of each block of l tree positions
+    attends to all coarse tokens; every token of the block takes the result."""
+    qc = pool_blocks(qt, block)                          # [N/l, H, d]
+    return np.repeat(compression_attn(qc, kc, vc), block, axis=0)
+
+
+def pooled_selection_attn(qt, kt, vt, sel, block, group) -> np.ndarray:
+    """Group compression: the mean query of each group attends once over the
+    union of the group's selected blocks; every query of the group takes it."""
+    n, H, d = qt.shape
+    qbar = qt.reshape(n // group, group, H, d).mean(axis=1)   # [G,H,d]
+    out = np.empty_like(qt)
+    r = np.arange(block)
+    for h in range(H):
+        for g_ in range(n // group):
+            keys = (sel[h, g_][:, None] * block + r[None, :]).reshape(-1)
+            o = sdpa(qbar[g_, h][None, :], kt[keys, h], vt[keys, h])[0]
+            out[g_ * group:(g_ + 1) * group, h] = o
+    return out
+
+
 def gates(qt: np.ndarray, W, b) -> np.ndarray:
     """sigmoid(W q + b) for every token and head: [N,H,3]."""
     W = np.asarray(W, dtype=np.float64).reshape(3, -1)
@@ -118,12 +152,13 @@ def gates(qt: np.ndarray, W, b) -> np.ndarray:
 
 def bsa(q, k, v, perm, ball: int, block: int, group: int, topk: int,
         mask_own_ball: bool = True, W=None, b=None, gate_const=None,
-        sel_override=None, return_parts: bool = False):
+        sel_override=None, return_parts: bool = False, query_compression: bool = False):
     """Three-branch BSA output in original order ([N,H,d], fp64).
 
     ``sel_override`` ([H, N/g, k*]) replaces the oracle's own top-k choice, so
     that a row whose selection is a numerical near-tie can be recomputed with
-    another valid set.
+    another valid set.  ``query_compression`` pools the queries of the
+    compression and selection branches (module docstring).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     n, H, d = q.shape
@@ -136,12 +171,18 @@ def bsa(q, k, v, perm, ball: int, block: int, group: int, topk: int,
 
     o_ball = ball_attn(qt, kt, vt, None, ball)
     kc, vc = pool_blocks(kt, block), pool_blocks(vt, block)
-    o_cmp = compression_attn(qt, kc, vc)
+    if query_compression:
+        o_cmp = pooled_compression_attn(qt, kc, vc, block)
+    else:
+        o_cmp = compression_attn(qt, kc, vc)
     if sel_override is None:
         sel, scores = select(qt, kc, ball, block, group, topk, mask_own_ball)
     else:
         sel, scores = np.asarray(sel_override), group_scores(qt, kc, group)
-    o_slc = selection_attn(qt, kt, vt, sel, block, group)
+    if query_compression:
+        o_slc = pooled_selection_attn(qt, kt, vt, sel, block, group)
+    else:
+        o_slc = selection_attn(qt, kt, vt, sel, block, group)
     if gate_const is not None:
         G = np.broadcast_to(np.asarray(gate_const, dtype=np.float64), (n, H, 3))
     else:
@@ -156,5 +197,5 @@ def bsa(q, k, v, perm, ball: int, block: int, group: int, topk: int,
 
 
 __all__ = ["bsa", "select", "own_ball_blocks", "pool_blocks", "group_scores",
-           "topk_blocks", "selection_attn", "compression_attn", "gates",
-           "softmax_rows"]
+           "topk_blocks", "selection_attn", "compression_attn", "pooled_compression_attn",
+           "pooled_selection_attn", "gates", "softmax_rows"]

@@ -174,3 +174,69 @@ def test_mutation_unmasked_is_caught(data):
         own = set(B.own_ball_blocks(g, GRP, BALL, BLK))
         hit += bool(set(parts["sel"][0, g].tolist()) & own)
     assert hit > 0        # without the mask the own ball is usually selected
+
+
+# ---- group (query) compression ------------------------------------------
+
+def _tree_const_queries(q, perm, span, seed):
+    """q whose tree-ordered rows are constant over each run of `span`."""
+    n, H, d = q.shape
+    runs = np.random.default_rng(seed).standard_normal((n // span, H, d))
+    qt = np.repeat(runs, span, axis=0)
+    out = np.empty_like(qt)
+    out[perm] = qt
+    return out
+
+
+def test_query_compression_equals_bsa_for_constant_queries(data):
+    """With every block and group holding one query, pooling changes nothing."""
+    _, k, v, perm = data
+    q = _tree_const_queries(data[0], perm, max(BLK, GRP), seed=5)
+    W = 0.3 * np.random.default_rng(6).standard_normal((3, D))
+    a = B.bsa(q, k, v, perm, BALL, BLK, GRP, TOPK, True, W=W, query_compression=True)
+    b = B.bsa(q, k, v, perm, BALL, BLK, GRP, TOPK, True, W=W)
+    assert np.allclose(a, b, atol=1e-12, rtol=0)
+
+
+def test_query_compression_pools_compression_by_block(data):
+    """Queries constant over blocks of l but not over groups: the compression
+    part equals the per-token one, the selection part does not; pooling the
+    compression queries over the group instead is caught."""
+    _, k, v, perm = data
+    assert GRP > BLK
+    q = _tree_const_queries(data[0], perm, BLK, seed=7)
+    gc = (0.0, 1.0, 0.0)
+    _, pq = B.bsa(q, k, v, perm, BALL, BLK, GRP, TOPK, True, gate_const=gc,
+                  query_compression=True, return_parts=True)
+    _, ps = B.bsa(q, k, v, perm, BALL, BLK, GRP, TOPK, True, gate_const=gc, return_parts=True)
+    assert np.allclose(pq["o_cmp"], ps["o_cmp"], atol=1e-12, rtol=0)
+    assert not np.allclose(pq["o_slc"], ps["o_slc"], atol=1e-6)
+    qt = np.asarray(q)[perm]
+    wrong = np.repeat(B.compression_attn(B.pool_blocks(qt, GRP), pq["kc"], pq["vc"]), GRP, axis=0)
+    assert not np.allclose(wrong, ps["o_cmp"], atol=1e-6)
+
+
+def test_query_compression_selection_is_group_mean_query(data):
+    """Each group's selection output is the attention of its mean query over
+    the selected keys (written out with the library SDPA), shared by the group."""
+    q, k, v, perm = data
+    _, p = B.bsa(q, k, v, perm, BALL, BLK, GRP, TOPK, True, gate_const=(0, 0, 1),
+                 query_compression=True, return_parts=True)
+    qt, kt, vt = q[perm], k[perm], v[perm]
+    for h in range(H):
+        for g_ in (0, N // GRP - 1):
+            rows = slice(g_ * GRP, (g_ + 1) * GRP)
+            keys = (p["sel"][h, g_][:, None] * BLK + np.arange(BLK)[None, :]).reshape(-1)
+            qb = qt[rows, h].mean(axis=0)
+            t = lambda x: torch.from_numpy(np.ascontiguousarray(x))
+            want = torch.nn.functional.scaled_dot_product_attention(
+                t(qb[None, None, :]), t(kt[keys, h][None]), t(vt[keys, h][None])).numpy()[0, 0]
+            assert np.allclose(p["o_slc"][rows, h], want[None, :], atol=1e-12, rtol=0)
+
+
+def test_query_compression_single_block_is_global_mean(data):
+    """ball = block = N: one coarse token, so compression gives every token the
+    mean of V (closed form)."""
+    q, k, v, perm = data
+    out = B.bsa(q, k, v, perm, N, N, GRP, 1, False, gate_const=(0, 1, 0), query_compression=True)
+    assert np.allclose(out, np.broadcast_to(v.mean(axis=0), v.shape), atol=1e-12, rtol=0)
