@@ -187,6 +187,8 @@ static bt_status check_bsa(int64_t N, int32_t H, int32_t d, const bsa_params* p)
   BT_REQUIRE(ball % group == 0, "group must divide ball");
   const int64_t nc = N / block;
   BT_REQUIRE(nc % 32 == 0 && nc <= 8192, "N/block must be a multiple of 32 and <= 8192");
+  BT_REQUIRE(p->query_compression == 0 || p->query_compression == 1,
+             "query_compression must be 0 or 1");
   const int64_t masked = p->mask_own_ball ? ball / block : 0;
   BT_REQUIRE(topk >= 1 && topk <= 64 && topk <= nc - masked,
              "need 1 <= topk <= 64 and topk <= N/block - masked blocks (%lld)",

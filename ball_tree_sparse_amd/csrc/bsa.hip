@@ -26,7 +26,9 @@ constexpr int kChunk = 64;             // keys per online-softmax step
 constexpr int kSelRegs = 16;           // scores per lane held in registers by select
 
 struct BsaLayout {
-  size_t kt, vt, kc32, kcb, vcb, qbar, sel, total;   // vt, vcb: transposed blocks
+  size_t kt, vt, kc32, kcb, vcb, qbar, sel;   // vt, vcb: transposed blocks
+  size_t qc, ocmp, oslc;                      // group compression only
+  size_t total;
 };
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -42,6 +44,11 @@ static BsaLayout bsa_layout(int64_t N, int32_t H, int32_t d, const bsa_params* p
   L.vcb = o; o = a256(o + nc * H * d * 2);
   L.qbar = o; o = a256(o + G * H * d * 4);
   L.sel = o; o = a256(o + G * H * (size_t)p->topk * 4);
+  if (p->query_compression) {
+    L.qc = o; o = a256(o + nc * H * d * 4);
+    L.ocmp = o; o = a256(o + nc * H * d * 4);
+    L.oslc = o; o = a256(o + G * H * d * 4);
+  }
   L.total = o;
   return L;
 }
@@ -411,7 +418,178 @@ BT_DEV void branch_merge(const Branch<D / 32>& br, float gate, f32x16* acc) {
     for (int e = 0; e < 16; ++e) acc[db][e] = fmaf(br.o[db][e], f, acc[db][e]);
 }
 
-template <int D, int NWV>
+// ------------------------------------------------------ group compression ----
+// Pooled (fp32) query rows -> the B operand of S^T = K Q^T, rounded to bf16.
+template <int D>
+BT_DEV void pooled_query_frags(const float* __restrict__ row, bf16x8* qf) {
+  const int hf = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const float4 a = *(const float4*)(row + s * 16 + hf * 8);
+    const float4 b = *(const float4*)(row + s * 16 + hf * 8 + 4);
+    qf[s] = bf16x8{(__bf16)a.x, (__bf16)a.y, (__bf16)a.z, (__bf16)a.w,
+                   (__bf16)b.x, (__bf16)b.y, (__bf16)b.z, (__bf16)b.w};
+  }
+}
+
+// O / l of a finished branch for the lane's query column, written as fp32
+// where `write` holds (every lane takes part in the exchange): lane (c, hf)
+// holds d = db*32 + 8*g + 4*hf + 0..3.
+template <int D>
+BT_DEV void store_branch(const Branch<D / 32>& br, bool write, float* __restrict__ row) {
+  const int hf = (threadIdx.x & 63) >> 5;
+  float l = (br.l[0] + br.l[1]) + (br.l[2] + br.l[3]);
+  l += __shfl_xor(l, 32, 64);
+  const float f = __builtin_amdgcn_rcpf(l);
+  if (!write) return;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(float4*)(row + db * 32 + g * 8 + hf * 4) =
+          make_float4(br.o[db][g * 4] * f, br.o[db][g * 4 + 1] * f, br.o[db][g * 4 + 2] * f,
+                      br.o[db][g * 4 + 3] * f);
+}
+
+// Compression branch of group compression: one wave per 32 block-mean
+// queries of a head, all attending to every coarse token.  Grid (nc/32, H).
+template <int D>
+__global__ __launch_bounds__(64) void bsa_qc_cmp(const float* __restrict__ qc,
+                                                 const uint16_t* __restrict__ kcb,
+                                                 const uint16_t* __restrict__ vct, int32_t nc,
+                                                 float* __restrict__ ocmp) {
+  const int h = blockIdx.y, c = threadIdx.x & 31;
+  const int64_t j = (int64_t)blockIdx.x * 32 + c;          // this lane's coarse query
+  bf16x8 qf[D / 16];
+  pooled_query_frags<D>(qc + ((int64_t)h * nc + j) * D, qf);
+  const float c2 = 1.4426950408889634f / sqrtf((float)D);
+  Branch<D / 32> br;
+  branch_init<D>(br);
+  attend_range<D>(kcb + (int64_t)h * nc * D, vct + (int64_t)h * nc * D,
+                  [&](int key) -> int64_t { return key; }, nc, qf, c2, br);
+  store_branch<D>(br, true, ocmp + ((int64_t)h * nc + j) * D);
+}
+
+// Selection branch of group compression: one wave per (group, head) and a
+// single query -- the group's mean query (fp32) -- over the union of the
+// group's selected blocks, on the vector units (one query would fill 1/32
+// of an MFMA tile).  Keys go in chunks of 1,024 with an online softmax: lane
+// l scores keys l, l+64, ... of the chunk; the weights go to LDS in the
+// position order of the transposed V blocks; then lane (dd, half) adds
+// p * V[., dd] over half of every 32-key block.  Grid (ngroups, H).
+constexpr int kQcsChunk = 1024;
+
+template <int D>
+__global__ __launch_bounds__(64) void bsa_qc_slc(const float* __restrict__ qbar,
+                                                 const uint16_t* __restrict__ kt,
+                                                 const uint16_t* __restrict__ vtt,
+                                                 const int32_t* __restrict__ sel, int64_t N,
+                                                 int32_t nc, int32_t ngroups, int32_t block,
+                                                 int32_t topk, float* __restrict__ oslc) {
+  __shared__ int32_t ssel[64];
+  __shared__ __attribute__((aligned(16))) float ps[kQcsChunk];
+  const int g = blockIdx.x, h = blockIdx.y, lane = threadIdx.x & 63;
+  const int dd = lane & 31, half = lane >> 5;
+  if (lane < topk)   // block indices are forced into range like perm entries
+    ssel[lane] = (int32_t)perm_index(sel[((int64_t)h * ngroups + g) * topk + lane], nc);
+  float qv[D];
+  const float* qrow = qbar + ((int64_t)h * ngroups + g) * D;
+#pragma unroll
+  for (int e = 0; e < D; e += 4) {
+    const float4 x = *(const float4*)(qrow + e);
+    qv[e] = x.x; qv[e + 1] = x.y; qv[e + 2] = x.z; qv[e + 3] = x.w;
+  }
+  __syncthreads();   // ssel
+  const float c2 = 1.4426950408889634f / sqrtf((float)D);
+  const uint16_t* kh = kt + (int64_t)h * N * D;
+  const uint16_t* vh = vtt + (int64_t)h * N * D;
+  auto row_of = [&](int key) -> int64_t {
+    return (int64_t)ssel[key / block] * block + (key % block);
+  };
+  const int nsel = topk * block;
+  float m = -INFINITY, l = 0.f;
+  float o[D / 32] = {};
+  for (int k0 = 0; k0 < nsel; k0 += kQcsChunk) {
+    const int nk = min(kQcsChunk, nsel - k0);          // a multiple of 32
+    // ---- scores of this lane's keys
+    float sc[kQcsChunk / 64];
+    float cm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kQcsChunk / 64; ++i) {
+      const int kl = i * 64 + lane;
+      sc[i] = -INFINITY;
+      if (kl < nk) {
+        const uint16_t* kr = kh + row_of(k0 + kl) * D;
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < D; e += 8) {
+          const u32x4 x = *(const u32x4*)(kr + e);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            s = fmaf(qv[e + 2 * u], bf16_to_f32((uint16_t)(x[u] & 0xffffu)), s);
+            s = fmaf(qv[e + 2 * u + 1], bf16_to_f32((uint16_t)(x[u] >> 16)), s);
+          }
+        }
+        sc[i] = s * c2;
+        cm = fmaxf(cm, sc[i]);
+      }
+    }
+    cm = wave_max(cm);
+    const float mn = fmaxf(m, cm);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);          // 0 on the first chunk
+    m = mn;
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < kQcsChunk / 64; ++i) {
+      const int kl = i * 64 + lane;
+      if (kl < nk) {
+        const float p = __builtin_amdgcn_exp2f(sc[i] - mn);
+        ls += p;
+        ps[(kl & ~31) + tpos(kl & 31)] = p;                  // V^T position order
+      }
+    }
+    l = l * alpha + ls;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    __builtin_amdgcn_wave_barrier();                          // one wave: LDS in order
+    // ---- o[dd] += sum over half of every 32-key block of p * V[., dd]
+    for (int kb = 0; kb < nk / 32; ++kb) {
+      const int64_t tb = row_of(k0 + kb * 32) / 32;           // transposed V block
+      const float* pp = ps + kb * 32 + half * 16;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint16_t* vr = vh + (tb * D + db * 32 + dd) * 32 + half * 16;
+        const u32x4 v0 = *(const u32x4*)vr, v1 = *(const u32x4*)(vr + 8);
+        const float4 p0 = *(const float4*)pp, p1 = *(const float4*)(pp + 4);
+        const float4 p2 = *(const float4*)(pp + 8), p3 = *(const float4*)(pp + 12);
+        const float pv[16] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w,
+                              p2.x, p2.y, p2.z, p2.w, p3.x, p3.y, p3.z, p3.w};
+        float acc = o[db];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          acc = fmaf(pv[2 * u], bf16_to_f32((uint16_t)(v0[u] & 0xffffu)), acc);
+          acc = fmaf(pv[2 * u + 1], bf16_to_f32((uint16_t)(v0[u] >> 16)), acc);
+          acc = fmaf(pv[8 + 2 * u], bf16_to_f32((uint16_t)(v1[u] & 0xffffu)), acc);
+          acc = fmaf(pv[8 + 2 * u + 1], bf16_to_f32((uint16_t)(v1[u] >> 16)), acc);
+        }
+        o[db] = acc;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();                          // ps reused by the next chunk
+  }
+  l = wave_sum_f32(l);
+  const float inv = __builtin_amdgcn_rcpf(l);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const float tot = o[db] + __shfl_xor(o[db], 32, 64);     // the two halves
+    if (half == 0) oslc[((int64_t)h * ngroups + g) * D + db * 32 + dd] = tot * inv;
+  }
+}
+
+// QC (group compression): only the ball branch runs here; the compression
+// and selection results of the token's block and group come from ocmp and
+// oslc (fp32, computed by bsa_qc_cmp / bsa_qc_slc).
+template <int D, int NWV, bool QC>
 __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(3, 8) void bsa_fused(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ perm,
     const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vtt,
@@ -419,6 +597,7 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(3, 8) void bsa_fused(
     const int32_t* __restrict__ sel, const float* __restrict__ gate_w,
     const float* __restrict__ gate_b, float gc0, float gc1, float gc2, int32_t H, int64_t N,
     int32_t nc, int32_t ngroups, int32_t ball, int32_t block, int32_t topk, int32_t xcd_map,
+    const float* __restrict__ ocmp, const float* __restrict__ oslc,
     uint16_t* __restrict__ out) {
   constexpr int DS = D / 16, DB = D / 32;
   __shared__ int32_t ssel[64];
@@ -479,23 +658,41 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(3, 8) void bsa_fused(
     attend_range<D>(kh, vh, [&](int key) -> int64_t { return b0 + key; }, ball, qf, c2, br);
     branch_merge<D>(br, G0, acc);
   }
-  // ---- compression branch: every coarse token ---------------------------
-  {
-    branch_init<D>(br);
-    const uint16_t* kch = kcb + (int64_t)h * nc * D;
-    const uint16_t* vch = vct + (int64_t)h * nc * D;
-    attend_range<D>(kch, vch, [&](int key) -> int64_t { return key; }, nc, qf, c2, br);
-    branch_merge<D>(br, G1, acc);
-  }
-  // ---- selection branch: the union of the selected blocks ---------------
-  {
-    branch_init<D>(br);
-    attend_range<D>(kh, vh,
-                    [&](int key) -> int64_t {
-                      return (int64_t)ssel[key / block] * block + (key % block);
-                    },
-                    topk * block, qf, c2, br);
-    branch_merge<D>(br, G2, acc);
+  if constexpr (QC) {
+    // ---- group compression: the token's block and group results --------
+    const int64_t t = t0 + c;
+    const float* rc = ocmp + ((int64_t)h * nc + t / block) * D;
+    const float* rsl = oslc + ((int64_t)h * ngroups + g) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const float4 a = *(const float4*)(rc + db * 32 + gq * 8 + hf * 4);
+        const float4 b = *(const float4*)(rsl + db * 32 + gq * 8 + hf * 4);
+        acc[db][gq * 4 + 0] = fmaf(G2, b.x, fmaf(G1, a.x, acc[db][gq * 4 + 0]));
+        acc[db][gq * 4 + 1] = fmaf(G2, b.y, fmaf(G1, a.y, acc[db][gq * 4 + 1]));
+        acc[db][gq * 4 + 2] = fmaf(G2, b.z, fmaf(G1, a.z, acc[db][gq * 4 + 2]));
+        acc[db][gq * 4 + 3] = fmaf(G2, b.w, fmaf(G1, a.w, acc[db][gq * 4 + 3]));
+      }
+  } else {
+    // ---- compression branch: every coarse token ---------------------------
+    {
+      branch_init<D>(br);
+      const uint16_t* kch = kcb + (int64_t)h * nc * D;
+      const uint16_t* vch = vct + (int64_t)h * nc * D;
+      attend_range<D>(kch, vch, [&](int key) -> int64_t { return key; }, nc, qf, c2, br);
+      branch_merge<D>(br, G1, acc);
+    }
+    // ---- selection branch: the union of the selected blocks ---------------
+    {
+      branch_init<D>(br);
+      attend_range<D>(kh, vh,
+                      [&](int key) -> int64_t {
+                        return (int64_t)ssel[key / block] * block + (key % block);
+                      },
+                      topk * block, qf, c2, br);
+      branch_merge<D>(br, G2, acc);
+    }
   }
 
   // ---- store: lane owns d = db*32 + 8*gq + 4*hf + 0..3 of query c -------
@@ -512,19 +709,19 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(3, 8) void bsa_fused(
 }
 
 // ------------------------------------------------------------------ host ----
-template <int D>
+template <int D, bool QC>
 static void launch_fused(int nwv, dim3 grid, hipStream_t st, const uint16_t* q,
                          const int32_t* perm, const uint16_t* kt, const uint16_t* vt,
                          const uint16_t* kcb, const uint16_t* vcb, const int32_t* sel,
                          const float* gw, const float* gb, const float* gc, int32_t H, int64_t N,
                          int32_t nc, int32_t ngroups, int32_t ball, int32_t block, int32_t topk,
-                         int32_t xmap, uint16_t* out) {
+                         int32_t xmap, const float* ocmp, const float* oslc, uint16_t* out) {
   const float g0 = gc ? gc[0] : 0.f, g1 = gc ? gc[1] : 0.f, g2 = gc ? gc[2] : 0.f;
 #define BT_FUSED(NW)                                                                          \
   case NW:                                                                                    \
-    hipLaunchKernelGGL((bsa_fused<D, NW>), grid, dim3(NW * 64), 0, st, q, perm, kt, vt, kcb, \
-                       vcb, sel, gw, gb, g0, g1, g2, H, N, nc, ngroups, ball, block, topk,   \
-                       xmap, out);                                                            \
+    hipLaunchKernelGGL((bsa_fused<D, NW, QC>), grid, dim3(NW * 64), 0, st, q, perm, kt, vt,  \
+                       kcb, vcb, sel, gw, gb, g0, g1, g2, H, N, nc, ngroups, ball, block,     \
+                       topk, xmap, ocmp, oslc, out);                                          \
     break;
   switch (nwv) {
     BT_FUSED(1)
@@ -588,17 +785,45 @@ bt_status bsa_launch(const void* q, const void* k, const void* v, const int32_t*
   s = launch_status("bsa_select");
   if (s != BT_OK) return s;
 
+  // group compression: block-mean queries over all coarse tokens, group-mean
+  // queries over their selected blocks
+  const bool qcm = p->query_compression != 0;
+  float* ocmp = qcm ? (float*)(b + L.ocmp) : nullptr;
+  float* oslc = qcm ? (float*)(b + L.oslc) : nullptr;
+  if (qcm) {
+    float* qc = (float*)(b + L.qc);
+    const dim3 gqc(nc, (cols + slice - 1) / slice);
+    hipLaunchKernelGGL(bsa_pool_q, gqc, pblk, 0, st, (const uint16_t*)q, perm, H, d, p->block, N,
+                       qc);
+    const dim3 gcm(nc / 32, H), gsl(ngroups, H);
+    if (d == 32) {
+      hipLaunchKernelGGL(bsa_qc_cmp<32>, gcm, dim3(64), 0, st, qc, kcb, vcb, nc, ocmp);
+      hipLaunchKernelGGL(bsa_qc_slc<32>, gsl, dim3(64), 0, st, qbar, kt, vt, sel, N, nc, ngroups,
+                         p->block, p->topk, oslc);
+    } else {
+      hipLaunchKernelGGL(bsa_qc_cmp<64>, gcm, dim3(64), 0, st, qc, kcb, vcb, nc, ocmp);
+      hipLaunchKernelGGL(bsa_qc_slc<64>, gsl, dim3(64), 0, st, qbar, kt, vt, sel, N, nc, ngroups,
+                         p->block, p->topk, oslc);
+    }
+    s = launch_status("bsa_qc");
+    if (s != BT_OK) return s;
+  }
+
   const int nwv = p->group / 32;
   const int total = ngroups * H;
   const int xmap = (total % 8 == 0) ? 1 : 0;
-  if (d == 32)
-    launch_fused<32>(nwv, dim3(total), st, (const uint16_t*)q, perm, kt, vt, kcb, vcb, sel, gate_w,
-                     gate_b, gate_const, H, N, nc, ngroups, p->ball, p->block, p->topk, xmap,
-                     (uint16_t*)out);
-  else
-    launch_fused<64>(nwv, dim3(total), st, (const uint16_t*)q, perm, kt, vt, kcb, vcb, sel, gate_w,
-                     gate_b, gate_const, H, N, nc, ngroups, p->ball, p->block, p->topk, xmap,
-                     (uint16_t*)out);
+#define BT_FUSED_CALL(DD, QCM)                                                                \
+  launch_fused<DD, QCM>(nwv, dim3(total), st, (const uint16_t*)q, perm, kt, vt, kcb, vcb, sel, \
+                        gate_w, gate_b, gate_const, H, N, nc, ngroups, p->ball, p->block,     \
+                        p->topk, xmap, ocmp, oslc, (uint16_t*)out)
+  if (d == 32) {
+    if (qcm) BT_FUSED_CALL(32, true);
+    else BT_FUSED_CALL(32, false);
+  } else {
+    if (qcm) BT_FUSED_CALL(64, true);
+    else BT_FUSED_CALL(64, false);
+  }
+#undef BT_FUSED_CALL
   return launch_status("bsa_fused");
 }
 

@@ -74,6 +74,11 @@ BT_DEV uint32_t wave_max_u32(uint32_t v) {
   for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, kWave));
   return v;
 }
+BT_DEV float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
 BT_DEV uint32_t wave_sum_u32(uint32_t v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += (uint32_t)__shfl_xor((int)v, m, kWave);

@@ -34,7 +34,8 @@ class BtError(RuntimeError):
 
 class BsaParams(C.Structure):
     _fields_ = [("ball", C.c_int32), ("block", C.c_int32), ("group", C.c_int32),
-                ("topk", C.c_int32), ("mask_own_ball", C.c_int32)]
+                ("topk", C.c_int32), ("mask_own_ball", C.c_int32),
+                ("query_compression", C.c_int32)]
 
 
 _lib = None
@@ -198,22 +199,27 @@ def ball_attn(q, k, v, perm, ball: int, out=None):
 
 
 def bsa_workspace_size(N: int, H: int, d: int, ball: int, block: int, group: int,
-                       topk: int, mask_own_ball: bool = True) -> int:
-    p = BsaParams(ball, block, group, topk, int(bool(mask_own_ball)))
+                       topk: int, mask_own_ball: bool = True,
+                       query_compression: bool = False) -> int:
+    p = BsaParams(ball, block, group, topk, int(bool(mask_own_ball)),
+                  int(bool(query_compression)))
     return lib().bsa_workspace_size(N, H, d, C.byref(p))
 
 
 def bsa_attn(q, k, v, perm, ball: int, block: int, group: int, topk: int,
              mask_own_ball: bool = True, gate_w=None, gate_b=None, gate_const=None,
-             return_sel: bool = False, out=None, workspace=None):
-    """Ball Sparse Attention; returns out (and sel [H, N/group, topk])."""
+             return_sel: bool = False, out=None, workspace=None,
+             query_compression: bool = False):
+    """Ball Sparse Attention; returns out (and sel [H, N/group, topk]).
+    ``query_compression`` selects BSA with group compression."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         _dev(t, name, q.dtype)
         if t.shape != q.shape or t.dim() != 3:
             raise ValueError("q, k, v must share one [N,H,d] shape")
     _dev(perm, "perm", torch.int32)
     N, H, d = q.shape
-    p = BsaParams(ball, block, group, topk, int(bool(mask_own_ball)))
+    p = BsaParams(ball, block, group, topk, int(bool(mask_own_ball)),
+                  int(bool(query_compression)))
     if gate_w is not None:
         _dev(gate_w, "gate_w", torch.float32)
     if gate_b is not None:

@@ -24,9 +24,9 @@ Prints ONE JSON line.  Besides the required fields it carries:
                 host on whole steps of the same workload;
   rows          the other rows of the path timed in the same run on their
                 own workloads: permute gather/scatter of 512-byte rows at the
-                rotated-pair size, the BSA step, and tree build + fp32 ball
-                attention at 1,024 points (the largest tree the GPU builder
-                takes in this build).
+                rotated-pair size, the BSA step (also with group compression),
+                and tree build + fp32 ball attention at 1,024 points (the
+                largest tree the GPU builder takes in this build).
 
 Other workloads (--workload bsa | cosmo | rotpair) print their own line and
 are not the default measurement.
@@ -250,7 +250,21 @@ def side_rows(dev, torch, ops, synth):
                           "us_per_step": us, "points_per_s": N / (us * 1e-6),
                           "tflops": flops / (us * 1e-6) / 1e12,
                           "mfma_frac": flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
-    del q, k, v, out, bws
+    # the same with group (query) compression
+    bws2 = torch.empty(ops.bsa_workspace_size(N, H, d, w.ball, x["block"], x["group"], x["topk"],
+                                              query_compression=True),
+                       dtype=torch.uint8, device=dev)
+    us2 = _event_us(torch, lambda: ops.bsa_attn(q, k, v, p, w.ball, x["block"], x["group"],
+                                                x["topk"], x["mask_own_ball"], gate_w=Wg,
+                                                out=out, workspace=bws2, query_compression=True),
+                    100, warm=20)
+    flops2 = 4 * H * d * (N * w.ball + (N // x["block"]) ** 2 +
+                          (N // x["group"]) * x["topk"] * x["block"])
+    rows["f1_bsa_group_compression"] = {
+        "workload": "as a7_a11_bsa, queries pooled before compression and selection",
+        "us_per_step": us2, "points_per_s": N / (us2 * 1e-6),
+        "tflops": flops2 / (us2 * 1e-6) / 1e12, "speedup_vs_bsa": us / us2}
+    del q, k, v, out, bws, bws2
     # tree build + fp32 ball attention at 1,024 points
     w = synth.make("tiny")
     c = torch.from_numpy(w.coords).to(dev)

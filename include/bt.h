@@ -47,13 +47,16 @@ typedef enum { BT_GATHER = 0, BT_SCATTER = 1 } bt_perm_mode;
 /* BSA hyper-parameters: ball = local attention ball size, block = compression
  * and selection block size (l), group = contiguous query group size (g),
  * topk = selected blocks per group (k*), mask_own_ball = 1 to exclude blocks
- * inside the group's own ball(s) from selection. */
+ * inside the group's own ball(s) from selection, query_compression = 1 for
+ * BSA with group compression (queries pooled before the compression and
+ * selection branches; see bsa_attn). */
 typedef struct {
   int32_t ball;
   int32_t block;
   int32_t group;
   int32_t topk;
   int32_t mask_own_ball;
+  int32_t query_compression;
 } bsa_params;
 
 const char* bt_status_str(bt_status s);
@@ -147,6 +150,13 @@ bt_status ball_attn(const void* q, const void* k, const void* v,
  *           smaller block index);
  *   O_slc:  each query of g attends once over the union of its selected
  *           blocks at full resolution;
+ *   with p->query_compression (group compression: the pages' optional
+ *   coarsening step that pools queries before selection and compression,
+ *   "Core claim"; Eq. 15 over Q_cmp): O_cmp of a token is the attention of
+ *   its block's mean query over all coarse tokens, and O_slc of a token is
+ *   the attention of its group's mean query over the group's selected
+ *   blocks (the block-mean queries are rounded to bf16 for the MFMA; the
+ *   group-mean query's selection attention runs in fp32);
  *   out = G0*O_ball + G1*O_cmp + G2*O_slc with G = sigmoid(W q + b)
  *         (gate_w [3,d] fp32 device, gate_b [3] fp32 device or NULL for 0),
  *         or G = gate_const (host [3]) when gate_w == NULL.
@@ -156,7 +166,8 @@ bt_status ball_attn(const void* q, const void* k, const void* v,
  * multiples of 32 with ball <= 256, block | ball and ball | N; group in
  * {32, 64, 128, 256} with group | ball; N/block a multiple of 32 and
  * <= 8192; 1 <= topk <= 64 and topk <= N/block minus the masked blocks of a
- * group; exactly one of gate_w and gate_const non-NULL.
+ * group; exactly one of gate_w and gate_const non-NULL; query_compression 0
+ * or 1.
  * ws: device workspace of at least bsa_workspace_size() bytes.
  * ---------------------------------------------------------------------- */
 size_t bsa_workspace_size(int64_t N, int32_t H, int32_t d, const bsa_params* p);

@@ -30,20 +30,24 @@ int main(int argc, char** argv) {
     bt::ball_attn_launch(q.data(), k.data(), v.data(), mode == "ball" ? perm.data() : nullptr, N,
                          ball, H, d, (bt_dtype)dt, out.data(), nullptr);
   } else {
-    bsa_params p{ball, atoi(argv[7]), atoi(argv[8]), atoi(argv[9]), atoi(argv[10])};
+    bsa_params p{ball, atoi(argv[7]), atoi(argv[8]), atoi(argv[9]), atoi(argv[10]),
+                 argc > 12 ? atoi(argv[12]) : 0};
     int gm = atoi(argv[11]);
     auto W = rd<float>("w.bin", 3 * d);
     float gc[3] = {1, 0, 0};
     if (gm == 2) { gc[0] = 0; gc[1] = 1; }
     if (gm == 3) { gc[0] = 0; gc[2] = 1; }
     size_t ws = bt::bsa_ws_size(N, H, d, &p);
-    std::vector<unsigned char> wsb(ws + 256, 0xab);
-    void* w = (void*)(((uintptr_t)wsb.data() + 255) & ~(uintptr_t)255);
+    // exactly ws bytes (a multiple of 256), filled with garbage
+    void* w = nullptr;
+    if (posix_memalign(&w, 256, ws) != 0) return 2;
+    memset(w, 0xab, ws);
     std::vector<int32_t> sel((size_t)H * (N / p.group) * p.topk, -1);
     bt::bsa_launch(q.data(), k.data(), v.data(), perm.data(), N, H, d, &p,
                    gm == 0 ? W.data() : nullptr, nullptr, gm == 0 ? nullptr : gc, sel.data(), w,
                    out.data(), nullptr);
     wr("sel.out", sel);
+    free(w);
   }
   wr("out.bin", out);
   printf("done %s\n", mode.c_str());

@@ -18,12 +18,15 @@ int main(int argc, char** argv) {
   float R[9]; bool rot = argc > 5;
   if (rot) { f = fopen(argv[5], "rb"); fread(R, 4, 9, f); fclose(f); }
   size_t ws = bt::tree_workspace_size(n, leaf);
-  // fill the workspace with garbage, like an uninitialised device buffer
-  std::vector<unsigned char> wsb(ws + 256);
-  for (size_t i = 0; i < wsb.size(); ++i) wsb[i] = (unsigned char)(i * 131 + 7);
-  void* w = (void*)(((uintptr_t)wsb.data() + 255) & ~(uintptr_t)255);
+  // exactly ws bytes, 256-byte aligned (ws is a multiple of 256), so that an
+  // access one byte past the workspace is caught; filled with garbage, like an
+  // uninitialised device buffer
+  void* w = nullptr;
+  if (posix_memalign(&w, 256, ws) != 0) return 2;
+  for (size_t i = 0; i < ws; ++i) ((unsigned char*)w)[i] = (unsigned char)(i * 131 + 7);
   std::vector<int32_t> perm(n, -1);
   bt::tree_build_launch(coords.data(), n, leaf, rot ? R : nullptr, perm.data(), w, nullptr);
+  free(w);
   f = fopen(argv[4], "wb"); fwrite(perm.data(), 4, n, f); fclose(f);
   printf("done n=%lld leaf=%d ws=%zu\n", n, leaf, ws);
   return 0;

@@ -52,13 +52,13 @@ def _check_sel(sel_gpu, parts, topk, tau_rel=1e-4):
     return use, ambiguous
 
 
-def _run(q, k, v, perm, W, ball, block, group, topk, mask, gate_const=None):
+def _run(q, k, v, perm, W, ball, block, group, topk, mask, gate_const=None, qc=False):
     dev = gpu()
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     pd = torch.from_numpy(np.asarray(perm, np.int32)).to(dev)
     Wd = None if gate_const is not None else torch.from_numpy(W).to(dev)
     out, sel = ops.bsa_attn(qd, kd, vd, pd, ball, block, group, topk, mask, gate_w=Wd,
-                            gate_const=gate_const, return_sel=True)
+                            gate_const=gate_const, return_sel=True, query_compression=qc)
     torch.cuda.synchronize()
     return out.cpu(), sel.cpu().numpy()
 
@@ -140,3 +140,42 @@ def test_deterministic():
     a, sa = _run(q, k, v, perm, W, 128, 64, 64, 8, True)
     b, sb = _run(q, k, v, perm, W, 128, 64, 64, 8, True)
     assert torch.equal(a, b) and np.array_equal(sa, sb)
+
+
+# ---- group (query) compression --------------------------------------------
+
+@pytest.mark.parametrize("n,H,d,ball,block,group,topk,mask,gates", [
+    (4096, 2, 32, 128, 64, 64, 4, True, None),
+    (4096, 2, 32, 128, 64, 64, 4, True, (0, 1, 0)),   # compression only
+    (4096, 2, 32, 128, 64, 64, 4, True, (0, 0, 1)),   # selection only
+    (8192, 2, 32, 128, 32, 64, 6, True, None),        # block != group
+    (4096, 3, 64, 256, 128, 128, 3, False, None),
+])
+def test_parity_query_compression(n, H, d, ball, block, group, topk, mask, gates):
+    _, q, k, v, W, perm = _setup(n, H, d, seed=n + H + d + topk + 1, leaf=block)
+    say("bsa_attn group compression", n, H, d, ball, block, group, topk, mask, gates)
+    out, sel = _run(q, k, v, perm, W, ball, block, group, topk, mask, gates, qc=True)
+    kw = dict(W=None if gates else W, gate_const=gates, query_compression=True)
+    ref, parts = B.bsa(q, k, v, perm, ball, block, group, topk, mask, return_parts=True, **kw)
+    use, amb = _check_sel(sel, parts, topk)
+    if amb:
+        ref = B.bsa(q, k, v, perm, ball, block, group, topk, mask, sel_override=use, **kw)
+    assert max_abs(out, ref) <= TOL
+
+
+def test_query_compression_full_size():
+    """The 65,536-point BSA workload with group compression."""
+    w = synth.make("bsa")
+    perm = T.build(w.coords, w.leaf)
+    x = w.extra
+    say("bsa group compression full size")
+    out, sel = _run(w.q, w.k, w.v, perm, w.gate_w, w.ball, x["block"], x["group"], x["topk"],
+                    bool(x["mask_own_ball"]), qc=True)
+    kw = dict(W=w.gate_w, query_compression=True)
+    ref, parts = B.bsa(w.q, w.k, w.v, perm, w.ball, x["block"], x["group"], x["topk"], True,
+                       return_parts=True, **kw)
+    use, amb = _check_sel(sel, parts, x["topk"])
+    if amb:
+        ref = B.bsa(w.q, w.k, w.v, perm, w.ball, x["block"], x["group"], x["topk"], True,
+                    sel_override=use, **kw)
+    assert max_abs(out, ref) <= TOL

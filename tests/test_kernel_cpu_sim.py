@@ -142,7 +142,9 @@ def test_ball_attn_kernel_tree_order_input(sim):
     assert np.abs(out - A.ball_attn(q, k, v, None, ball)).max() <= 2e-2
 
 
-def test_bsa_kernels(sim):
+@pytest.mark.parametrize("qc", [0, 1])
+def test_bsa_kernels(sim, qc):
+    """BSA, and BSA with group compression (qc = 1)."""
     d_ = sim["dir"]
     n, H, d, ball, block, group, topk = 2048, 2, 32, 128, 64, 64, 4
     rng = np.random.default_rng(5)
@@ -155,11 +157,12 @@ def test_bsa_kernels(sim):
     perm.tofile(d_ / "perm.bin")
     W.tofile(d_ / "w.bin")
     r = subprocess.run([sim["attn"], "bsa", str(n), str(H), str(d), str(ball), "1", str(block),
-                        str(group), str(topk), "1", "0"], cwd=d_, capture_output=True,
+                        str(group), str(topk), "1", "0", str(qc)], cwd=d_, capture_output=True,
                        text=True, timeout=600)
     assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
     out = _read_out(d_ / "out.bin", n, H, d, "bf16")
     sel = np.fromfile(d_ / "sel.out", np.int32).reshape(H, n // group, topk)
-    ref, parts = B.bsa(q, k, v, perm, ball, block, group, topk, True, W=W, return_parts=True)
+    ref, parts = B.bsa(q, k, v, perm, ball, block, group, topk, True, W=W, return_parts=True,
+                       query_compression=bool(qc))
     assert np.array_equal(np.sort(sel, -1), np.sort(parts["sel"], -1))
     assert np.abs(out - ref).max() <= 2e-2
