@@ -37,6 +37,10 @@ bt_status ball_attn_launch(const void* q, const void* k, const void* v, const in
                            int64_t N, int32_t ball, int32_t H, int32_t d, bt_dtype dt,
                            void* out, hipStream_t st);
 size_t bsa_ws_size(int64_t N, int32_t H, int32_t d, const bsa_params* p);
+bt_status coarsen_launch(const void* x, const int32_t* perm, int64_t N, int32_t ppr, int32_t s,
+                         bt_dtype dt, void* out, hipStream_t st);
+bt_status refine_launch(const void* xc, const int32_t* perm, int64_t N, int32_t ppr, int32_t s,
+                        void* out, hipStream_t st);
 bt_status bsa_launch(const void* q, const void* k, const void* v, const int32_t* perm, int64_t N,
                      int32_t H, int32_t d, const bsa_params* p, const float* gate_w,
                      const float* gate_b, const float* gate_const, int32_t* sel_out, void* ws,
@@ -140,6 +144,46 @@ bt_status bt_invert_perm(const int32_t* perm, int64_t N, int32_t* inv, void* str
   BT_REQUIRE(perm && inv, "perm and inv must be non-null");
   BT_REQUIRE(!overlaps(perm, (size_t)N * 4, inv, (size_t)N * 4), "perm and inv must not overlap");
   return invert_perm_launch(perm, N, inv, (hipStream_t)stream);
+}
+
+// Shared checks of bt_coarsen / bt_refine; sets *ppr to the 16-byte pieces
+// per row.
+static bt_status check_pool(int64_t N, int32_t H, int32_t d, int32_t s, bt_dtype dt,
+                            int32_t* ppr) {
+  BT_REQUIRE(dt == BT_F32 || dt == BT_BF16, "dtype must be BT_F32 or BT_BF16");
+  BT_REQUIRE(H >= 1 && d >= 1, "need H >= 1 and d >= 1");
+  BT_REQUIRE(s >= 1 && N >= 0 && N % s == 0, "s must divide N (N=%lld, s=%d)", (long long)N, s);
+  BT_REQUIRE(N * H * d < ((int64_t)1 << 31), "N*H*d must be below 2^31");
+  const int64_t row = (int64_t)H * d * (dt == BT_F32 ? 4 : 2);
+  BT_REQUIRE(row % 16 == 0, "a row (H*d elements) must be a multiple of 16 bytes");
+  *ppr = (int32_t)(row / 16);
+  return BT_OK;
+}
+
+bt_status bt_coarsen(const void* x, const int32_t* perm, int64_t N, int32_t H, int32_t d,
+                     int32_t s, bt_dtype dt, void* out, void* stream) {
+  int32_t ppr = 0;
+  const bt_status st = check_pool(N, H, d, s, dt, &ppr);
+  if (st != BT_OK) return st;
+  if (N == 0) return BT_OK;
+  BT_REQUIRE(x && out, "x and out must be non-null");
+  BT_REQUIRE((((uintptr_t)x | (uintptr_t)out) & 15) == 0, "x and out must be 16-byte aligned");
+  BT_REQUIRE(!overlaps(x, (size_t)N * ppr * 16, out, (size_t)(N / s) * ppr * 16),
+             "out must not overlap x");
+  return coarsen_launch(x, perm, N, ppr, s, dt, out, (hipStream_t)stream);
+}
+
+bt_status bt_refine(const void* xc, const int32_t* perm, int64_t N, int32_t H, int32_t d,
+                    int32_t s, bt_dtype dt, void* out, void* stream) {
+  int32_t ppr = 0;
+  const bt_status st = check_pool(N, H, d, s, dt, &ppr);
+  if (st != BT_OK) return st;
+  if (N == 0) return BT_OK;
+  BT_REQUIRE(xc && out, "xc and out must be non-null");
+  BT_REQUIRE((((uintptr_t)xc | (uintptr_t)out) & 15) == 0, "xc and out must be 16-byte aligned");
+  BT_REQUIRE(!overlaps(xc, (size_t)(N / s) * ppr * 16, out, (size_t)N * ppr * 16),
+             "out must not overlap xc");
+  return refine_launch(xc, perm, N, ppr, s, out, (hipStream_t)stream);
 }
 
 bt_status ball_attn(const void* q, const void* k, const void* v, const int32_t* perm, int64_t N,

@@ -59,6 +59,10 @@ _SIGS = [
     ("bsa_attn", C.c_int, [_P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int,
                            C.POINTER(BsaParams), _P, _P, C.POINTER(C.c_float), _P, _P,
                            C.c_size_t, _P, _P]),
+    ("bt_coarsen", C.c_int, [_P, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int, _P,
+                             _P]),
+    ("bt_refine", C.c_int, [_P, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int, _P,
+                            _P]),
 ]
 EXPORTS = [s[0] for s in _SIGS]
 
@@ -177,6 +181,42 @@ def bt_invert_perm(perm, inv=None):
         inv = torch.empty_like(perm)
     _check(lib().bt_invert_perm(_ptr(perm), perm.numel(), _ptr(inv), _stream(perm.device)))
     return inv
+
+
+# ------------------------------------------------------ coarsen / refine --
+
+def bt_coarsen(x, perm, s: int, out=None):
+    """[N,H,d] -> coarse level [N/s,H,d] in tree order (perm None: x is
+    already in tree order)."""
+    _dev(x, "x")
+    if x.dim() != 3:
+        raise ValueError("x must be [N,H,d]")
+    if perm is not None:
+        _dev(perm, "perm", torch.int32)
+    N, H, d = x.shape
+    if out is None:
+        out = torch.empty((N // s if s > 0 else 0, H, d), dtype=x.dtype, device=x.device)
+    _dev(out, "out", x.dtype)
+    _check(lib().bt_coarsen(_ptr(x), _ptr(perm), N, H, d, s, _dtype_code(x), _ptr(out),
+                            _stream(x.device)))
+    return out
+
+
+def bt_refine(xc, perm, s: int, out=None):
+    """Coarse level [N/s,H,d] -> [N,H,d]: every child takes its parent's row
+    (original order when perm is given)."""
+    _dev(xc, "xc")
+    if xc.dim() != 3:
+        raise ValueError("xc must be [N/s,H,d]")
+    if perm is not None:
+        _dev(perm, "perm", torch.int32)
+    Nc, H, d = xc.shape
+    if out is None:
+        out = torch.empty((Nc * s, H, d), dtype=xc.dtype, device=xc.device)
+    _dev(out, "out", xc.dtype)
+    _check(lib().bt_refine(_ptr(xc), _ptr(perm), Nc * s, H, d, s, _dtype_code(xc), _ptr(out),
+                           _stream(xc.device)))
+    return out
 
 
 # ---------------------------------------------------------------- attention --

@@ -231,6 +231,31 @@ def side_rows(dev, torch, ops, synth):
                                       "us": us, "GBps": nbytes / us / 1e3,
                                       "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS}
     del srcs, dsts
+    # coarsen / refine by 8 (Erwin's U-Net levels) at the sphere size: three
+    # input sets rotate so that every call reads HBM
+    n, H, d, s = 65536, 8, 32, 8
+    xs = [torch.randint(-32768, 32767, (n, H, d), dtype=torch.int16, device=dev,
+                        generator=gen).view(torch.bfloat16) for _ in range(3)]
+    xs = [x.masked_fill(~torch.isfinite(x), 0) for x in xs]
+    pc = torch.randperm(n, generator=torch.Generator().manual_seed(5)).to(torch.int32).to(dev)
+    cs = [torch.empty((n // s, H, d), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    fs = [torch.empty_like(xs[0]) for _ in range(3)]
+    row = H * d * 2
+    for name, fn, nbytes in (
+            ("coarsen", lambda i: ops.bt_coarsen(xs[i % 3], pc, s, out=cs[i % 3]),
+             n * row + n // s * row + 4 * n),
+            ("refine", lambda i: ops.bt_refine(cs[i % 3], pc, s, out=fs[i % 3]),
+             n // s * row + n * row + 4 * n)):
+        it = [0]
+
+        def call(fn=fn):
+            fn(it[0])
+            it[0] += 1
+        us = _event_us(torch, call, 60, warm=6)
+        rows["f2_" + name] = {"workload": "N=65536, H=8, d=32 bf16, s=8, perm",
+                              "us": us, "GBps": nbytes / us / 1e3,
+                              "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS}
+    del xs, cs, fs
     # BSA step
     w = synth.make("bsa")
     x = w.extra

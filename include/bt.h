@@ -119,6 +119,27 @@ bt_status bt_invert_perm(const int32_t* perm, int64_t N, int32_t* inv,
                          void* stream);
 
 /* ------------------------------------------------------------------------
+ * Coarsening and refinement (Erwin thread, post 8/N: the ball tree is
+ * coarsened and then refined while the attention ball size stays fixed;
+ * post 9/N: every level is contiguous, so these are means over consecutive
+ * tree positions).  Features are [N,H,d] rows of dtype dt; row(t) = perm[t]
+ * when perm != NULL (features in original order), else t (tree order).
+ *   bt_coarsen: out[j] = mean_{r < s} x[row(j*s + r)] for j < N/s; out is the
+ *               coarse level [N/s,H,d] in tree order (fp32 sums in a fixed
+ *               order, rounded once to dt).
+ *   bt_refine:  out[row(t)] = xc[t / s] for t < N (xc: [N/s,H,d]).
+ * Requirements: s >= 1 divides N; H, d >= 1; a row (H*d elements) a multiple
+ * of 16 bytes; N*H*d < 2^31; device buffers, 16-byte aligned, out not
+ * overlapping the input.  N = 0 is a no-op.  Errors: BT_EINVAL for a
+ * violated requirement or a null pointer with N > 0; BT_EHIP if a launch
+ * fails.  Asynchronous on stream; nothing is allocated.
+ * ---------------------------------------------------------------------- */
+bt_status bt_coarsen(const void* x, const int32_t* perm, int64_t N, int32_t H,
+                     int32_t d, int32_t s, bt_dtype dt, void* out, void* stream);
+bt_status bt_refine(const void* xc, const int32_t* perm, int64_t N, int32_t H,
+                    int32_t d, int32_t s, bt_dtype dt, void* out, void* stream);
+
+/* ------------------------------------------------------------------------
  * Ball attention (Erwin thread, post 7/N: attention inside the balls of a
  * chosen tree level, all balls in parallel; Pith review of arXiv 2506.12541,
  * "What carries the argument": scaled dot-product attention within each

@@ -119,3 +119,15 @@ def test_bsa_rejects(L):
     assert call(P(128, 64, 64, 4, 1), gcc=None) == ops.BT_EINVAL  # no gate
     assert L.bsa_workspace_size(4096, 2, 32, C.byref(P(128, 64, 64, 4, 1))) > 0
     assert L.bsa_workspace_size(4096, 2, 32, C.byref(P(100, 64, 64, 4, 1))) == 0
+
+
+def test_coarsen_refine_reject(L):
+    x, o = _fake(1 << 16), _fake(1 << 16)
+    for f in (L.bt_coarsen, L.bt_refine):
+        assert f(x, None, 1024, 4, 32, 3, ops.BT_BF16, o, None) == ops.BT_EINVAL   # 3 does not divide
+        assert f(x, None, 1024, 1, 2, 2, ops.BT_F32, o, None) == ops.BT_EINVAL     # 8-byte rows
+        assert f(x, None, 1024, 4, 32, 0, ops.BT_BF16, o, None) == ops.BT_EINVAL
+        assert f(x, None, 1024, 4, 32, 2, 7, o, None) == ops.BT_EINVAL
+        assert f(None, None, 1024, 4, 32, 2, ops.BT_BF16, o, None) == ops.BT_EINVAL
+        assert f(x, None, 1024, 4, 32, 2, ops.BT_BF16, x, None) == ops.BT_EINVAL   # overlap
+        assert f(None, None, 0, 4, 32, 2, ops.BT_BF16, None, None) == ops.BT_OK    # empty
