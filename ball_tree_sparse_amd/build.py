@@ -14,7 +14,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbtsparse.so")
-SOURCES = ["api.hip", "ball_attn.hip", "permute.hip", "tree.hip", "bsa.hip", "pool.hip"]
+SOURCES = ["api.hip", "ball_attn.hip", "ball_attn_bwd.hip", "permute.hip", "tree.hip", "bsa.hip",
+           "pool.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -37,6 +37,10 @@ bt_status ball_attn_launch(const void* q, const void* k, const void* v, const in
                            int64_t N, int32_t ball, int32_t H, int32_t d, bt_dtype dt,
                            void* out, hipStream_t st);
 size_t bsa_ws_size(int64_t N, int32_t H, int32_t d, const bsa_params* p);
+bt_status ball_attn_bwd_launch(const void* q, const void* k, const void* v, const void* dout,
+                               const int32_t* perm, int64_t N, int32_t ball, int32_t H,
+                               int32_t d, bt_dtype dt, void* dq, void* dk, void* dv,
+                               hipStream_t st);
 bt_status coarsen_launch(const void* x, const int32_t* perm, int64_t N, int32_t ppr, int32_t s,
                          bt_dtype dt, void* out, hipStream_t st);
 bt_status refine_launch(const void* xc, const int32_t* perm, int64_t N, int32_t ppr, int32_t s,
@@ -210,6 +214,32 @@ bt_status ball_attn(const void* q, const void* k, const void* v, const int32_t* 
                "fp32 tensors must be 4-byte aligned");
   }
   return ball_attn_launch(q, k, v, perm, N, ball, H, d, dt, out, (hipStream_t)stream);
+}
+
+bt_status ball_attn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                        const int32_t* perm, int64_t N, int32_t ball, int32_t H, int32_t d,
+                        bt_dtype dt, void* dq, void* dk, void* dv, void* stream) {
+  BT_REQUIRE(dt == BT_F32 || dt == BT_BF16, "dtype must be BT_F32 or BT_BF16");
+  BT_REQUIRE(d == 16 || d == 32 || d == 64, "d must be 16, 32 or 64 (d=%d)", d);
+  BT_REQUIRE(H >= 1, "H must be >= 1");
+  BT_REQUIRE(N >= 0 && ball >= 1 && N % ball == 0, "ball must divide N (N=%lld, ball=%d)",
+             (long long)N, ball);
+  BT_REQUIRE(ball <= 1024, "ball_attn_bwd takes ball <= 1024 (ball=%d)", ball);
+  if (N == 0) return BT_OK;
+  BT_REQUIRE(q && k && v && dout && dq && dk && dv, "tensors must be non-null");
+  BT_REQUIRE(N * H * d < ((int64_t)1 << 31), "N*H*d must be below 2^31");
+  BT_REQUIRE((N / ball) * H < ((int64_t)1 << 31), "too many (ball, head) pairs");
+  const size_t bytes = (size_t)(N * H * d) * (dt == BT_F32 ? 4 : 2);
+  const void* ins[4] = {q, k, v, dout};
+  void* outs[3] = {dq, dk, dv};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 4; ++i)
+      BT_REQUIRE(!overlaps(outs[o], bytes, ins[i], bytes), "gradients must not alias the inputs");
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      BT_REQUIRE(!overlaps(outs[o], bytes, outs[o2], bytes), "dq, dk and dv must not overlap");
+  }
+  return ball_attn_bwd_launch(q, k, v, dout, perm, N, ball, H, d, dt, dq, dk, dv,
+                              (hipStream_t)stream);
 }
 
 static bt_status check_bsa(int64_t N, int32_t H, int32_t d, const bsa_params* p) {

@@ -63,6 +63,8 @@ _SIGS = [
                              _P]),
     ("bt_refine", C.c_int, [_P, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int, _P,
                             _P]),
+    ("ball_attn_bwd", C.c_int, [_P, _P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32,
+                                C.c_int32, C.c_int, _P, _P, _P, _P]),
 ]
 EXPORTS = [s[0] for s in _SIGS]
 
@@ -236,6 +238,26 @@ def ball_attn(q, k, v, perm, ball: int, out=None):
     _check(lib().ball_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), N, ball, H, d,
                            _dtype_code(q), _ptr(out), _stream(q.device)))
     return out
+
+
+def ball_attn_bwd(q, k, v, dout, perm, ball: int, dq=None, dk=None, dv=None):
+    """Gradients (dq, dk, dv) of ball attention for the output gradient dout."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _dev(t, name, q.dtype)
+        if t.shape != q.shape or t.dim() != 3:
+            raise ValueError("q, k, v, dout must share one [N,H,d] shape")
+    if perm is not None:
+        _dev(perm, "perm", torch.int32)
+    N, H, d = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _dev(t, name, q.dtype)
+    _check(lib().ball_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(perm), N, ball, H,
+                               d, _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv),
+                               _stream(q.device)))
+    return dq, dk, dv
 
 
 def bsa_workspace_size(N: int, H: int, d: int, ball: int, block: int, group: int,

@@ -119,6 +119,25 @@ bt_status bt_invert_perm(const int32_t* perm, int64_t N, int32_t* inv,
                          void* stream);
 
 /* ------------------------------------------------------------------------
+ * Backward pass of ball attention (the layers around it are learned: Pith
+ * review of arXiv 2506.12541, "What carries the argument"; Erwin thread,
+ * post 7/N).  For the output gradient dout of ball_attn(q, k, v, perm, ...),
+ * per ball and head, with S = Q K^T / sqrt(d), P = softmax(S), O = P V:
+ *   D_i = dO_i . O_i,  dS = P * (dO V^T - D),
+ *   dq = dS K / sqrt(d),  dk = dS^T Q / sqrt(d),  dv = P^T dO,
+ * in the inputs' order (original order when perm != NULL).  O is recomputed,
+ * so the forward output is not an argument.  fp32 arithmetic; outputs in dt.
+ * Requirements: as ball_attn, with ball <= 1024; dq, dk, dv must not alias
+ * the inputs or each other.  N = 0 is a no-op.  Errors: BT_EINVAL for a
+ * violated requirement or a null pointer with N > 0; BT_EHIP if the launch
+ * fails.  Asynchronous on stream; nothing is allocated.
+ * ---------------------------------------------------------------------- */
+bt_status ball_attn_bwd(const void* q, const void* k, const void* v,
+                        const void* dout, const int32_t* perm, int64_t N,
+                        int32_t ball, int32_t H, int32_t d, bt_dtype dt,
+                        void* dq, void* dk, void* dv, void* stream);
+
+/* ------------------------------------------------------------------------
  * Coarsening and refinement (Erwin thread, post 8/N: the ball tree is
  * coarsened and then refined while the attention ball size stays fixed;
  * post 9/N: every level is contiguous, so these are means over consecutive

@@ -131,3 +131,17 @@ def test_coarsen_refine_reject(L):
         assert f(None, None, 1024, 4, 32, 2, ops.BT_BF16, o, None) == ops.BT_EINVAL
         assert f(x, None, 1024, 4, 32, 2, ops.BT_BF16, x, None) == ops.BT_EINVAL   # overlap
         assert f(None, None, 0, 4, 32, 2, ops.BT_BF16, None, None) == ops.BT_OK    # empty
+
+
+def test_ball_attn_bwd_rejects(L):
+    t = [_fake(1 << 16) for _ in range(7)]
+    def call(N=1024, ball=32, H=4, d=16, dt=ops.BT_F32, ptrs=None):
+        p = t if ptrs is None else ptrs
+        return L.ball_attn_bwd(p[0], p[1], p[2], p[3], None, N, ball, H, d, dt, p[4], p[5], p[6],
+                               None)
+    assert call(ball=2048, N=2048) == ops.BT_EINVAL           # ball above 1024
+    assert call(ball=48) == ops.BT_EINVAL                      # 48 does not divide 1024
+    assert call(d=24) == ops.BT_EINVAL
+    assert call(ptrs=[t[0], t[1], t[2], t[3], t[0], t[5], t[6]]) == ops.BT_EINVAL   # dq aliases q
+    assert call(ptrs=[t[0], t[1], t[2], t[3], t[4], t[4], t[6]]) == ops.BT_EINVAL   # dq is dk
+    assert call(N=0, ptrs=[None] * 7) == ops.BT_OK
