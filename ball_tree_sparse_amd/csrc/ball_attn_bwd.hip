@@ -186,11 +186,273 @@ __global__ __launch_bounds__(kBwdThreads) void ball_attn_bwd_valu(
   }
 }
 
+// --------------------------------------------------------------------------
+// bf16 MFMA kernel (v_mfma_f32_32x32x16_bf16; operand layouts as in the
+// forward kernel: A[i][kk] lane i + 32*(kk/8) element kk%8, B[kk][j] lane
+// j + 32*(kk/8) element kk%8, C[i][j] lane j + 32*((i/4)%2) element
+// (i/8)*4 + i%4).  One workgroup per (ball, head), one wave per 32 rows.
+// Q, K, V, dO of the ball are staged once into LDS, row-major (padded) and,
+// for K, Q and dO, transposed with bits 2 and 3 of the row index swapped
+// inside each group of 16 (the order in which a C tile feeds a B operand).
+//  query pass (lane = query column): S^T = K Q^T -> row max and sum -> P^T;
+//    D_i = sum_j P_ij dP_ij with dP^T = V dO^T (equal to dO_i . O_i, so O is
+//    not needed); then per 32-key block dP^T again, dS^T = P^T (dP^T - D),
+//    and dQ^T += K^T dS^T.
+//  key pass (lane = key column): per 32-query block S = Q K^T, P from the
+//    stored row statistics, dP = dO V^T, dS = P (dP - D); dV^T += dO^T P and
+//    dK^T += Q^T dS.
+// P and dS are rounded to bf16 for the MFMA; everything else is fp32.
+BT_DEV int bswap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+BT_DEV uint32_t bpair(const u32x4& lo, const u32x4& hi, int e) {
+  return __builtin_amdgcn_perm(hi[e >> 1], lo[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+}
+
+template <int D, int BALL>
+struct BwdGeom {
+  static constexpr int NW = BALL / 32, NT = NW * 64;
+  static constexpr int KB = BALL / 32, DS = D / 16, DB = D / 32;
+  static constexpr int RS = D + 8;          // row-major stride (bf16)
+  static constexpr int TS = BALL + 8;       // transposed stride (bf16)
+  static constexpr int CPR = D / 8;         // 16-byte pieces per row
+  static constexpr int PIECES = BALL / 2 * CPR;   // two rows per staging piece
+};
+
+// lane (c, hf) holds C^T[d][c] of a 32-column block for d = db*32 + 8*g +
+// 4*hf + 0..3 in acc[db][g*4 + 0..3]; write row `row` (d contiguous) scaled,
+// as 16-byte runs after one exchange with lane c^32.
+template <int D>
+BT_DEV void store_cols(const f32x16* acc, float f, uint16_t* __restrict__ row) {
+  const int hf = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    u32x2 pg[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      pg[g][0] = pack_bf16x2(acc[db][g * 4 + 0] * f, acc[db][g * 4 + 1] * f);
+      pg[g][1] = pack_bf16x2(acc[db][g * 4 + 2] * f, acc[db][g * 4 + 3] * f);
+    }
+    const u32x2 sa = hf ? pg[0] : pg[1], sb = hf ? pg[2] : pg[3];
+    u32x2 ra, rb;
+    ra[0] = (uint32_t)__shfl_xor((int)sa[0], 32, 64);
+    ra[1] = (uint32_t)__shfl_xor((int)sa[1], 32, 64);
+    rb[0] = (uint32_t)__shfl_xor((int)sb[0], 32, 64);
+    rb[1] = (uint32_t)__shfl_xor((int)sb[1], 32, 64);
+    u32x4 c0, c1;
+    if (hf == 0) {
+      c0 = u32x4{pg[0][0], pg[0][1], ra[0], ra[1]};
+      c1 = u32x4{pg[2][0], pg[2][1], rb[0], rb[1]};
+    } else {
+      c0 = u32x4{ra[0], ra[1], pg[1][0], pg[1][1]};
+      c1 = u32x4{rb[0], rb[1], pg[3][0], pg[3][1]};
+    }
+    *(u32x4*)(row + db * 32 + hf * 8) = c0;
+    *(u32x4*)(row + db * 32 + 16 + hf * 8) = c1;
+  }
+}
+
+template <int D, int BALL>
+__global__ __launch_bounds__(BALL / 32 * 64) void ball_attn_bwd_mfma(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const int32_t* __restrict__ perm, int64_t N, int32_t H, uint16_t* __restrict__ dq,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  using Gm = BwdGeom<D, BALL>;
+  constexpr int NT = Gm::NT, KB = Gm::KB, DS = Gm::DS, DB = Gm::DB, RS = Gm::RS, TS = Gm::TS;
+  constexpr int CPR = Gm::CPR, PIECES = Gm::PIECES;
+  __shared__ __attribute__((aligned(16))) uint16_t ql[BALL * RS], kl[BALL * RS], vl[BALL * RS],
+      dl[BALL * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t qtl[D * TS], ktl[D * TS], dtl[D * TS];
+  __shared__ float smc[BALL], sli[BALL], sdd[BALL];   // m*c2, 1/l, D of every query
+  const int b = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, c = lane & 31;
+  const int64_t base = (int64_t)b * BALL, rs = (int64_t)H * D;
+  auto row_of = [&](int i) -> int64_t { return perm ? perm_index(perm[base + i], N) : base + i; };
+
+  // ---- stage Q, K, V, dO (row-major) and Q^T, K^T, dO^T (transposed) -------
+  for (int it = tid; it < PIECES; it += NT) {
+    const int kq = it / CPR, dc = it - kq * CPR;
+    const int r0 = kq * 2;
+    const int64_t o0 = row_of(r0) * rs + (int64_t)h * D + dc * 8;
+    const int64_t o1 = row_of(r0 + 1) * rs + (int64_t)h * D + dc * 8;
+    const u32x4 q0 = *(const u32x4*)(q + o0), q1 = *(const u32x4*)(q + o1);
+    const u32x4 k0 = *(const u32x4*)(k + o0), k1 = *(const u32x4*)(k + o1);
+    const u32x4 v0 = *(const u32x4*)(v + o0), v1 = *(const u32x4*)(v + o1);
+    const u32x4 d0 = *(const u32x4*)(dout + o0), d1 = *(const u32x4*)(dout + o1);
+    *(u32x4*)&ql[r0 * RS + dc * 8] = q0;  *(u32x4*)&ql[(r0 + 1) * RS + dc * 8] = q1;
+    *(u32x4*)&kl[r0 * RS + dc * 8] = k0;  *(u32x4*)&kl[(r0 + 1) * RS + dc * 8] = k1;
+    *(u32x4*)&vl[r0 * RS + dc * 8] = v0;  *(u32x4*)&vl[(r0 + 1) * RS + dc * 8] = v1;
+    *(u32x4*)&dl[r0 * RS + dc * 8] = d0;  *(u32x4*)&dl[(r0 + 1) * RS + dc * 8] = d1;
+    const int pos0 = (r0 & ~15) + bswap23(r0 & 15);      // keeps bit 0
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      *(uint32_t*)&qtl[(dc * 8 + e) * TS + pos0] = bpair(q0, q1, e);
+      *(uint32_t*)&ktl[(dc * 8 + e) * TS + pos0] = bpair(k0, k1, e);
+      *(uint32_t*)&dtl[(dc * 8 + e) * TS + pos0] = bpair(d0, d1, e);
+    }
+  }
+  __syncthreads();
+  const float c2 = 1.4426950408889634f / sqrtf((float)D);   // log2(e)/sqrt(d)
+  const float scale = 1.0f / sqrtf((float)D);
+
+  // ---- query pass: rows w*32 + c are this lane's query ------------------------
+  {
+    const int qr = w * 32 + c;
+    bf16x8 qf[DS], df[DS];
+#pragma unroll
+    for (int s2 = 0; s2 < DS; ++s2) {
+      qf[s2] = *(const bf16x8*)&ql[qr * RS + s2 * 16 + hf * 8];
+      df[s2] = *(const bf16x8*)&dl[qr * RS + s2 * 16 + hf * 8];
+    }
+    f32x16 pt[KB];                         // S^T, then P^T
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      f32x16 a = {};
+#pragma unroll
+      for (int s2 = 0; s2 < DS; ++s2)
+        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *(const bf16x8*)&kl[(kb * 32 + c) * RS + s2 * 16 + hf * 8], qf[s2], a, 0, 0, 0);
+      pt[kb] = a;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, pt[kb][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float moff = -mx * c2;
+    float sum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(pt[kb][e], c2, moff));
+        pt[kb][e] = p;
+        sum += p;
+      }
+    sum += __shfl_xor(sum, 32, 64);
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pt[kb][e] *= inv;
+    // dP^T = V dO^T, block by block
+    auto dpt_block = [&](int kb) -> f32x16 {
+      f32x16 a = {};
+#pragma unroll
+      for (int s2 = 0; s2 < DS; ++s2)
+        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *(const bf16x8*)&vl[(kb * 32 + c) * RS + s2 * 16 + hf * 8], df[s2], a, 0, 0, 0);
+      return a;
+    };
+    float dsum = 0.f;                      // D_i = sum_j P_ij dP_ij
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const f32x16 dp = dpt_block(kb);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dsum = fmaf(pt[kb][e], dp[e], dsum);
+    }
+    dsum += __shfl_xor(dsum, 32, 64);
+    if (hf == 0) { smc[qr] = -moff; sli[qr] = inv; sdd[qr] = dsum; }
+    f32x16 gq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) gq[db] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const f32x16 dp = dpt_block(kb);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 sf;                         // dS^T operand
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sf[e] = (__bf16)(pt[kb][s2 * 8 + e] * (dp[s2 * 8 + e] - dsum));
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          gq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *(const bf16x8*)&ktl[(db * 32 + c) * TS + (kb * 2 + s2) * 16 + hf * 8], sf, gq[db],
+              0, 0, 0);
+      }
+    }
+    store_cols<D>(gq, scale, dq + row_of(qr) * rs + (int64_t)h * D);
+  }
+  __syncthreads();   // row statistics of every query in LDS
+
+  // ---- key pass: rows w*32 + c are this lane's key ----------------------------
+  {
+    const int kr = w * 32 + c;
+    bf16x8 kf[DS], vf[DS];
+#pragma unroll
+    for (int s2 = 0; s2 < DS; ++s2) {
+      kf[s2] = *(const bf16x8*)&kl[kr * RS + s2 * 16 + hf * 8];
+      vf[s2] = *(const bf16x8*)&vl[kr * RS + s2 * 16 + hf * 8];
+    }
+    f32x16 gk[DB], gv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) { gk[db] = f32x16{}; gv[db] = f32x16{}; }
+#pragma unroll
+    for (int qb = 0; qb < KB; ++qb) {
+      f32x16 sq = {}, dp = {};
+#pragma unroll
+      for (int s2 = 0; s2 < DS; ++s2) {
+        sq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *(const bf16x8*)&ql[(qb * 32 + c) * RS + s2 * 16 + hf * 8], kf[s2], sq, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *(const bf16x8*)&dl[(qb * 32 + c) * RS + s2 * 16 + hf * 8], vf[s2], dp, 0, 0, 0);
+      }
+      // element e is query qb*32 + 8*(e/4) + 4*hf + e%4
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 pf, sf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ee = s2 * 8 + e;
+          const int qi = qb * 32 + 8 * (ee >> 2) + 4 * hf + (ee & 3);
+          const float p = __builtin_amdgcn_exp2f(fmaf(sq[ee], c2, -smc[qi])) * sli[qi];
+          pf[e] = (__bf16)p;
+          sf[e] = (__bf16)(p * (dp[ee] - sdd[qi]));
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          gv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *(const bf16x8*)&dtl[(db * 32 + c) * TS + (qb * 2 + s2) * 16 + hf * 8], pf, gv[db],
+              0, 0, 0);
+          gk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *(const bf16x8*)&qtl[(db * 32 + c) * TS + (qb * 2 + s2) * 16 + hf * 8], sf, gk[db],
+              0, 0, 0);
+        }
+      }
+    }
+    const int64_t orow = row_of(kr) * rs + (int64_t)h * D;
+    store_cols<D>(gk, scale, dk + orow);
+    store_cols<D>(gv, 1.0f, dv + orow);
+  }
+}
+
+bool ball_attn_bwd_uses_mfma(bt_dtype dt, int32_t ball, int32_t d) {
+  return dt == BT_BF16 && ((d == 32 && (ball == 32 || ball == 64 || ball == 128)) ||
+                           (d == 64 && (ball == 32 || ball == 64)));
+}
+
 bt_status ball_attn_bwd_launch(const void* q, const void* k, const void* v, const void* dout,
                                const int32_t* perm, int64_t N, int32_t ball, int32_t H,
                                int32_t d, bt_dtype dt, void* dq, void* dk, void* dv,
                                hipStream_t st) {
-  const dim3 grid((unsigned)((N / ball) * H)), blk(kBwdThreads);
+  const dim3 grid((unsigned)((N / ball) * H));
+  if (ball_attn_bwd_uses_mfma(dt, ball, d)) {
+#define BT_BWDM(DD, BB)                                                                        \
+  hipLaunchKernelGGL((ball_attn_bwd_mfma<DD, BB>), grid, dim3(BB / 32 * 64), 0, st,           \
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,              \
+                     (const uint16_t*)dout, perm, N, H, (uint16_t*)dq, (uint16_t*)dk,         \
+                     (uint16_t*)dv)
+    if (d == 32 && ball == 32) BT_BWDM(32, 32);
+    else if (d == 32 && ball == 64) BT_BWDM(32, 64);
+    else if (d == 32) BT_BWDM(32, 128);
+    else if (ball == 32) BT_BWDM(64, 32);
+    else BT_BWDM(64, 64);
+#undef BT_BWDM
+    return launch_status("ball_attn_bwd_mfma");
+  }
+  const dim3 blk(kBwdThreads);
 #define BT_BWD(TT, DD)                                                                         \
   hipLaunchKernelGGL((ball_attn_bwd_valu<TT, DD>), grid, blk, 0, st, (const TT*)q,            \
                      (const TT*)k, (const TT*)v, (const TT*)dout, perm, N, H, ball, (TT*)dq,   \

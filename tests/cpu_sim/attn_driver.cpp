@@ -1,6 +1,7 @@
-// Runs the ball_attn.hip and bsa.hip kernels on the host under the SIMT
-// emulation.  Inputs and outputs are raw files in the working directory
-// (q.bin, k.bin, v.bin, perm.bin, w.bin -> out.bin, sel.out).
+// Runs the ball_attn.hip, ball_attn_bwd.hip and bsa.hip kernels on the host
+// under the SIMT emulation.  Inputs and outputs are raw files in the working
+// directory (q.bin, k.bin, v.bin, perm.bin, w.bin, do.bin -> out.bin,
+// sel.out, dq.bin, dk.bin, dv.bin).
 #include <cstdarg>
 #include "hip/hip_runtime.h"
 #include "../../ball_tree_sparse_amd/csrc/common.h"
@@ -10,6 +11,7 @@ bt_status launch_status(const char*) { return BT_OK; }
 }
 #include "../../ball_tree_sparse_amd/csrc/ball_attn.hip"
 #include "../../ball_tree_sparse_amd/csrc/bsa.hip"
+#include "../../ball_tree_sparse_amd/csrc/ball_attn_bwd.hip"
 
 template <typename T> std::vector<T> rd(const char* p, size_t n) {
   std::vector<T> v(n); FILE* f = fopen(p, "rb"); fread(v.data(), sizeof(T), n, f); fclose(f); return v; }
@@ -26,6 +28,18 @@ int main(int argc, char** argv) {
        v = rd<unsigned char>("v.bin", ne * es);
   auto perm = rd<int32_t>("perm.bin", N);
   std::vector<unsigned char> out(ne * es, 0xcd);
+  if (mode == "bwd") {
+    auto dout = rd<unsigned char>("do.bin", ne * es);
+    std::vector<unsigned char> g[3];
+    for (auto& x : g) x.assign(ne * es, 0xcd);
+    bt::ball_attn_bwd_launch(q.data(), k.data(), v.data(), dout.data(), perm.data(), N, ball, H,
+                             d, (bt_dtype)dt, g[0].data(), g[1].data(), g[2].data(), nullptr);
+    wr("dq.bin", g[0]);
+    wr("dk.bin", g[1]);
+    wr("dv.bin", g[2]);
+    printf("done bwd %d\n", (int)bt::ball_attn_bwd_uses_mfma((bt_dtype)dt, ball, d));
+    return 0;
+  }
   if (mode == "ball" || mode == "ball_noperm") {
     bt::ball_attn_launch(q.data(), k.data(), v.data(), mode == "ball" ? perm.data() : nullptr, N,
                          ball, H, d, (bt_dtype)dt, out.data(), nullptr);

@@ -18,6 +18,7 @@ import torch
 
 from ball_tree_sparse_amd import synth
 from oracle import attention as A
+from oracle import attention_bwd as AB
 from oracle import bsa as B
 from oracle import tree as T
 
@@ -166,3 +167,27 @@ def test_bsa_kernels(sim, qc):
                        query_compression=bool(qc))
     assert np.array_equal(np.sort(sel, -1), np.sort(parts["sel"], -1))
     assert np.abs(out - ref).max() <= 2e-2
+
+
+@pytest.mark.parametrize("n,H,d,ball,dtype", [(512, 2, 32, 128, "bf16"), (256, 2, 32, 32, "bf16"),
+                                             (256, 1, 64, 64, "bf16"), (384, 2, 32, 64, "bf16"),
+                                             (256, 2, 16, 64, "bf16"), (256, 2, 32, 32, "f32")])
+def test_ball_attn_bwd_kernels(sim, n, H, d, ball, dtype):
+    """Backward: the MFMA kernel (bf16, d 32 or 64, ball up to 128 or 64) and
+    the VALU kernel (the rest)."""
+    d_ = sim["dir"]
+    rng = np.random.default_rng(3 * n + d + ball)
+    q, k, v, do = (synth.normal_features(rng, n, H, d, dtype) for _ in range(4))
+    perm = rng.permutation(n).astype(np.int32)
+    for t, nm in ((q, "q.bin"), (k, "k.bin"), (v, "v.bin"), (do, "do.bin")):
+        _dump(t, d_ / nm)
+    perm.tofile(d_ / "perm.bin")
+    r = subprocess.run([sim["attn"], "bwd", str(n), str(H), str(d), str(ball),
+                        "1" if dtype == "bf16" else "0"], cwd=d_, capture_output=True,
+                       text=True, timeout=600)
+    assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
+    want = AB.ball_attn_bwd(q, k, v, do, perm, ball)
+    for name, w in zip("qkv", want):
+        got = _read_out(d_ / f"d{name}.bin", n, H, d, dtype)
+        err = np.abs(got - w).max()
+        assert err <= (2e-2 if dtype == "bf16" else 2e-5), (name, err)
