@@ -290,6 +290,20 @@ def side_rows(dev, torch, ops, synth):
         "us_per_step": us2, "points_per_s": N / (us2 * 1e-6),
         "tflops": flops2 / (us2 * 1e-6) / 1e12, "speedup_vs_bsa": us / us2}
     del q, k, v, out, bws, bws2
+    # backward of ball attention at the sphere size
+    w = synth.make("sphere")
+    gq, gk, gv = (t.to(dev) for t in (w.q, w.k, w.v))
+    gdo = gq.clone()
+    pb = torch.randperm(w.coords.shape[0], generator=torch.Generator().manual_seed(7)) \
+        .to(torch.int32).to(dev)
+    grads = [torch.empty_like(gq) for _ in range(3)]
+    us_b = _event_us(torch, lambda: ops.ball_attn_bwd(gq, gk, gv, gdo, pb, w.ball, *grads), 10,
+                     warm=2)
+    nb = w.coords.shape[0]
+    bflops = 4 * nb * w.ball * w.d * w.H * 2.5        # S, dP, dV, dQ, dK (2.5x the forward)
+    rows["f4_ball_attn_bwd"] = {"workload": "N=65536, ball 128, H=8, d=32 bf16",
+                                "us": us_b, "tflops": bflops / (us_b * 1e-6) / 1e12}
+    del gq, gk, gv, gdo, grads
     # tree build + fp32 ball attention at 1,024 points
     w = synth.make("tiny")
     c = torch.from_numpy(w.coords).to(dev)
