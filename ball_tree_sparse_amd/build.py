@@ -28,7 +28,10 @@ FLAGS = [
 ]
 # the tree's split rule is defined on fp32 values rounded after every
 # operation, so nothing in that unit may be contracted into an FMA
-PER_FILE = {"tree.hip": ["-ffp-contract=off"]}
+PER_FILE = {"tree.hip": ["-ffp-contract=off"],
+            # MFMA results straight into VGPRs: the backward reads every
+            # accumulator element back, so AGPR copies only cost VALU issue
+            "ball_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _run(cmd):
