@@ -297,8 +297,8 @@ def side_rows(dev, torch, ops, synth):
     pb = torch.randperm(w.coords.shape[0], generator=torch.Generator().manual_seed(7)) \
         .to(torch.int32).to(dev)
     grads = [torch.empty_like(gq) for _ in range(3)]
-    us_b = _event_us(torch, lambda: ops.ball_attn_bwd(gq, gk, gv, gdo, pb, w.ball, *grads), 10,
-                     warm=2)
+    us_b = _event_us(torch, lambda: ops.ball_attn_bwd(gq, gk, gv, gdo, pb, w.ball, *grads), 300,
+                     warm=100)
     nb = w.coords.shape[0]
     bflops = 4 * nb * w.ball * w.d * w.H * 2.5        # S, dP, dV, dQ, dK (2.5x the forward)
     rows["f4_ball_attn_bwd"] = {"workload": "N=65536, ball 128, H=8, d=32 bf16",
