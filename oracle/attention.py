@@ -87,3 +87,28 @@ def full_attn(q, k, v) -> np.ndarray:
     q, k, v = _f64(q), _f64(k), _f64(v)
     o = sdpa(q.transpose(1, 0, 2), k.transpose(1, 0, 2), v.transpose(1, 0, 2))
     return o.transpose(1, 0, 2)
+
+
+def ball_attn_padded(q, k, v, perm, ball: int) -> np.ndarray:
+    """Ball attention on a padded tree (``oracle.tree.build_padded``): ``perm``
+    has one entry per slot, -1 for an unused slot, and the points of a ball are
+    its slots that hold a point.  Each point attends to the points of its own
+    ball (every head); output in original order."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, H, d = q.shape
+    perm = np.asarray(perm, dtype=np.int64)
+    if ball < 1 or len(perm) % ball:
+        raise ValueError("ball must divide the slot count")
+    real = perm[perm >= 0]
+    if len(real) != n or len(np.unique(real)) != n:
+        raise ValueError("the slots must hold every point exactly once")
+    out = np.zeros_like(q)
+    for b0 in range(0, len(perm), ball):
+        ids = perm[b0:b0 + ball]
+        ids = ids[ids >= 0]
+        if len(ids) == 0:
+            continue
+        # [H, m, d] per ball
+        qb, kb, vb = (x[ids].transpose(1, 0, 2) for x in (q, k, v))
+        out[ids] = sdpa(qb, kb, vb).transpose(1, 0, 2)
+    return out

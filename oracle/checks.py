@@ -123,3 +123,54 @@ def check_tree(coords, perm, leaf):
         if not res[0]:
             return False, f"{name}: {res[1]}"
     return True, ""
+
+
+def check_padded_tree(coords, perm, leaf):
+    """The padded tree of an uneven N: slots = the smallest leaf * 2^L >= N;
+    the points fill each leaf's first slots in ascending index, -1 after; at
+    every internal node the left child holds ceil(n/2) of the node's n points,
+    on the axis of largest fp32 spread, all of them before the right child's
+    in (coordinate, index) order."""
+    c = _coords(coords)
+    n = len(c)
+    p = np.asarray(perm)
+    cap = leaf
+    while cap < n:
+        cap *= 2
+    if p.shape != (cap,):
+        return False, f"slot count {p.shape} != ({cap},)"
+    real = p[p >= 0]
+    if np.any(p < -1):
+        return False, "entry below -1"
+    ok, msg = is_bijection(real, n)
+    if not ok:
+        return False, "points: " + msg
+    for j in range(0, cap, leaf):
+        row = p[j:j + leaf]
+        m = int((row >= 0).sum())
+        if np.any(row[:m] < 0) or np.any(np.diff(row[:m]) <= 0):
+            return False, f"leaf at {j}: points not first or not ascending"
+    size = cap
+    while size > leaf:
+        for start in range(0, cap, size):
+            ids = p[start:start + size]
+            ids = ids[ids >= 0]
+            half = size // 2
+            L = p[start:start + half]
+            L = L[L >= 0]
+            R = p[start + half:start + size]
+            R = R[R >= 0]
+            if len(L) != (len(ids) + 1) // 2:
+                return False, f"node at {start}: left holds {len(L)} of {len(ids)}"
+            if len(ids) < 2:
+                continue
+            a = _axis(c[ids])
+            if len(R) == 0:
+                continue
+            lv, rv = c[L, a], c[R, a]
+            if lv.max() > rv.min():
+                return False, f"node at {start}: left {lv.max()} > right {rv.min()}"
+            if lv.max() == rv.min() and L[lv == lv.max()].max() > R[rv == rv.min()].min():
+                return False, f"node at {start}: tie broken wrong"
+        size //= 2
+    return True, ""

@@ -21,6 +21,16 @@ The pages leave the split rule open.  The reading used here:
 
 ``perm[t]`` is the original index of the point at tree position ``t``.
 
+Uneven N (``build_padded``): the sets only need to be of similar size, while
+contiguous storage with equal-size balls at every level is what turns ball
+operations into views and means (posts 6/N and 9/N).  Reading: the tree has
+``leaf * 2^L`` slots, L the smallest with ``leaf * 2^L >= N``; a node of n
+points (and 2c slots) gives its left child the ceil(n/2) smallest points in
+(coordinate, index) order and its right child the rest, each child owning c
+slots; a leaf stores its points first (ascending index) and marks the unused
+slots with -1.  Sibling point counts differ by at most one, and for
+N = leaf * 2^L the result is exactly ``build``.
+
 Rotation: the second tree of a rotated pair is the same tree built on
 coordinates rotated by a caller-supplied 3x3 matrix (Erwin thread: trees are
 rotated, instead of shifting windows as Swin does, so that alternate layers mix
@@ -76,6 +86,42 @@ def build(coords, leaf: int) -> np.ndarray:
         return rec(left) + rec(right)
 
     return np.concatenate(rec(np.arange(n, dtype=np.int64)))
+
+
+def padded_size(n: int, leaf: int) -> int:
+    """Slots of the padded tree: the smallest leaf * 2^L that is >= n."""
+    if leaf < 1 or n < 1:
+        raise ValueError("need N >= 1 and leaf >= 1")
+    cap = leaf
+    while cap < n:
+        cap *= 2
+    return cap
+
+
+def build_padded(coords, leaf: int) -> np.ndarray:
+    """Padded tree permutation (int64, length padded_size(N, leaf)); -1 marks
+    an unused slot."""
+    c = canonical(coords)
+    n = c.shape[0]
+    cap = padded_size(n, leaf)
+
+    def rec(ids: np.ndarray, slots: int) -> list:
+        if slots == leaf:
+            return [ids, np.full(leaf - len(ids), -1, dtype=np.int64)]
+        if len(ids) == 0:
+            return [np.full(slots, -1, dtype=np.int64)]
+        a = split_axis(c[ids])
+        order = np.lexsort((ids, c[ids, a]))          # by (coord, index)
+        nl = (len(ids) + 1) // 2                      # ceil(n/2) go left
+        left = np.sort(ids[order[:nl]])
+        right = np.sort(ids[order[nl:]])
+        return rec(left, slots // 2) + rec(right, slots // 2)
+
+    return np.concatenate(rec(np.arange(n, dtype=np.int64), cap))
+
+
+def rotate_build_padded(coords, leaf: int, R) -> np.ndarray:
+    return build_padded(rotate(coords, R), leaf)
 
 
 def rotate(coords, R) -> np.ndarray:
