@@ -9,12 +9,17 @@ product path never falls back to it.
 
 Modules
 -------
-``tree``       recursive median-split ball tree and the rotated tree.
-``attention``  ball attention (scaled dot-product attention inside each ball)
-               and full attention, in fp64.
+``tree``       recursive median-split ball tree, the rotated tree, and the
+               padded tree of an uneven N.
+``attention``  ball attention (scaled dot-product attention inside each ball),
+               on a padded tree too, and full attention, in fp64.
+``attention_bwd`` gradients of ball attention (dq, dk, dv), in fp64.
 ``bsa``        brute-force Ball Sparse Attention: ball, compression and
-               selection branches merged by sigmoid gates, in fp64.
-``checks``     tree invariant checkers, independent of ``tree``.
+               selection branches merged by sigmoid gates (and the group
+               compression variant), in fp64.
+``pool``       coarsening (means of consecutive tree positions) and refinement.
+``checks``     tree invariant checkers (plain and padded), independent of
+               ``tree``.
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_*.py`` against closed forms, library routines, invariants
