@@ -45,6 +45,17 @@ bt_status coarsen_launch(const void* x, const int32_t* perm, int64_t N, int32_t 
                          bt_dtype dt, void* out, hipStream_t st);
 bt_status refine_launch(const void* xc, const int32_t* perm, int64_t N, int32_t ppr, int32_t s,
                         void* out, hipStream_t st);
+int64_t tree_padded_slots(int64_t n, int leaf);
+size_t tree_padded_workspace_size(int64_t n, int leaf);
+bt_status tree_build_padded_launch(const float* coords, int64_t n, int leaf, const float* R,
+                                   int32_t* perm, void* ws, hipStream_t st);
+bt_status permute_padded_launch(const void* src, const int32_t* perm, int64_t nrows,
+                                int64_t nslots, int64_t row_bytes, bt_perm_mode mode, void* dst,
+                                hipStream_t st);
+bt_status ball_attn_padded_launch(const void* q, const void* k, const void* v,
+                                  const int32_t* perm, int64_t nrows, int64_t nslots,
+                                  int32_t ball, int32_t H, int32_t d, bt_dtype dt, void* out,
+                                  hipStream_t st);
 bt_status bsa_launch(const void* q, const void* k, const void* v, const int32_t* perm, int64_t N,
                      int32_t H, int32_t d, const bsa_params* p, const float* gate_w,
                      const float* gate_b, const float* gate_const, int32_t* sel_out, void* ws,
@@ -240,6 +251,87 @@ bt_status ball_attn_bwd(const void* q, const void* k, const void* v, const void*
   }
   return ball_attn_bwd_launch(q, k, v, dout, perm, N, ball, H, d, dt, dq, dk, dv,
                               (hipStream_t)stream);
+}
+
+int64_t bt_padded_size(int64_t N, int32_t leaf) {
+  if (N < 1 || leaf < 1 || N >= ((int64_t)1 << 31)) return -1;
+  const int64_t s = tree_padded_slots(N, leaf);
+  return s < ((int64_t)1 << 31) ? s : -1;
+}
+
+size_t bt_build_padded_workspace_size(int64_t N, int32_t leaf) {
+  if (bt_padded_size(N, leaf) < 0) return 0;
+  return tree_padded_workspace_size(N, leaf);
+}
+
+bt_status bt_build_padded(const float* coords, int64_t N, int32_t leaf, const float* R_host,
+                          int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
+  BT_REQUIRE(coords && perm, "coords and perm must be non-null");
+  const int64_t S = bt_padded_size(N, leaf);
+  BT_REQUIRE(S > 0, "need N >= 1, leaf >= 1 and fewer than 2^31 slots (N=%lld, leaf=%d)",
+             (long long)N, leaf);
+  BT_REQUIRE(S <= kTreeMaxGpuNode || S == leaf,
+             "bt_build_padded: trees above %lld slots are switched off in this build "
+             "(their global passes faulted the GPU; cause not found); slots=%lld",
+             (long long)kTreeMaxGpuNode, (long long)S);
+  if (R_host) {
+    for (int i = 0; i < 9; ++i)
+      BT_REQUIRE(R_host[i] == R_host[i] && R_host[i] - R_host[i] == 0.0f,
+                 "rotation matrix must be finite");
+  }
+  BT_REQUIRE(ws != nullptr, "workspace must be non-null");
+  BT_REQUIRE(((uintptr_t)ws & 255) == 0, "workspace must be 256-byte aligned");
+  const size_t need = tree_padded_workspace_size(N, leaf);
+  if (ws_bytes < need) {
+    set_error("workspace holds %zu bytes, bt_build_padded needs %zu", ws_bytes, need);
+    return BT_ENOMEM;
+  }
+  return tree_build_padded_launch(coords, N, leaf, R_host, perm, ws, (hipStream_t)stream);
+}
+
+bt_status bt_permute_padded(const void* src, const int32_t* perm, int64_t n_rows,
+                            int64_t n_slots, int64_t row_bytes, bt_perm_mode mode, void* dst,
+                            void* stream) {
+  BT_REQUIRE(n_slots >= 0 && n_slots < ((int64_t)1 << 31), "need 0 <= n_slots < 2^31");
+  BT_REQUIRE(row_bytes > 0 && row_bytes % 4 == 0, "row_bytes must be a positive multiple of 4");
+  BT_REQUIRE(mode == BT_GATHER || mode == BT_SCATTER, "mode must be BT_GATHER or BT_SCATTER");
+  if (n_slots == 0) return BT_OK;
+  BT_REQUIRE(n_rows >= 1 && n_rows <= n_slots, "need 1 <= n_rows <= n_slots (n_rows=%lld)",
+             (long long)n_rows);
+  BT_REQUIRE(src && dst && perm, "src, dst and perm must be non-null");
+  const size_t sb = (size_t)((mode == BT_GATHER ? n_rows : n_slots) * row_bytes);
+  const size_t db = (size_t)((mode == BT_GATHER ? n_slots : n_rows) * row_bytes);
+  BT_REQUIRE(!overlaps(src, sb, dst, db), "src and dst must not overlap");
+  return permute_padded_launch(src, perm, n_rows, n_slots, row_bytes, mode, dst,
+                               (hipStream_t)stream);
+}
+
+bt_status ball_attn_padded(const void* q, const void* k, const void* v, const int32_t* perm,
+                           int64_t n_rows, int64_t n_slots, int32_t ball, int32_t H, int32_t d,
+                           bt_dtype dt, void* out, void* stream) {
+  BT_REQUIRE(dt == BT_F32 || dt == BT_BF16, "dtype must be BT_F32 or BT_BF16");
+  BT_REQUIRE(d == 16 || d == 32 || d == 64, "d must be 16, 32 or 64 (d=%d)", d);
+  BT_REQUIRE(H >= 1, "H must be >= 1");
+  BT_REQUIRE(ball >= 1 && ball <= 4096, "need 1 <= ball <= 4096 (ball=%d)", ball);
+  BT_REQUIRE(n_slots >= 1 && n_slots % ball == 0, "ball must divide n_slots (n_slots=%lld)",
+             (long long)n_slots);
+  BT_REQUIRE(n_rows >= 1 && n_rows <= n_slots, "need 1 <= n_rows <= n_slots (n_rows=%lld)",
+             (long long)n_rows);
+  BT_REQUIRE(q && k && v && out && perm, "q, k, v, out and perm must be non-null");
+  BT_REQUIRE(n_slots * H * d < ((int64_t)1 << 31), "n_slots*H*d must be below 2^31");
+  const size_t bytes = (size_t)(n_rows * H * d) * (dt == BT_F32 ? 4 : 2);
+  BT_REQUIRE(!overlaps(out, bytes, q, bytes) && !overlaps(out, bytes, k, bytes) &&
+                 !overlaps(out, bytes, v, bytes),
+             "out must not alias q, k or v");
+  if (dt == BT_BF16) {
+    BT_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16 == 0,
+               "bf16 tensors must be 16-byte aligned");
+  } else {
+    BT_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 4 == 0,
+               "fp32 tensors must be 4-byte aligned");
+  }
+  return ball_attn_padded_launch(q, k, v, perm, n_rows, n_slots, ball, H, d, dt, out,
+                                 (hipStream_t)stream);
 }
 
 static bt_status check_bsa(int64_t N, int32_t H, int32_t d, const bsa_params* p) {

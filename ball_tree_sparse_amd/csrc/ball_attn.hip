@@ -12,6 +12,9 @@
 //    in the MFMA operand layout; V is staged transposed in LDS.
 //  * ball_attn_valu<T, D>: fp32 arithmetic for any ball, one thread per query,
 //    K/V chunks of 64 keys staged in LDS, exact online softmax with expf.
+// With MASK (the padded tree of an uneven point count) a negative permutation
+// entry marks an unused slot: its key takes no weight and no output row is
+// written for it; row indices are clamped to the nrows input rows.
 #include "common.h"
 
 namespace bt {
@@ -39,13 +42,14 @@ BT_DEV void store_elem<uint16_t>(uint16_t* p, float x) {
 constexpr int kValuThreads = 256;
 constexpr int kValuChunk = 64;
 
-template <typename T, int D>
+template <typename T, int D, bool MASK>
 __global__ __launch_bounds__(kValuThreads) void ball_attn_valu(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ perm, int64_t N, int32_t H, int32_t ball,
     T* __restrict__ out) {
   __shared__ float ks[kValuChunk][D + 1];
   __shared__ float vs[kValuChunk][D + 1];
+  __shared__ uint8_t kok[kValuChunk];       // the key holds a point (MASK)
   const int b = blockIdx.x / H;
   const int h = blockIdx.x - b * H;
   const int64_t base = (int64_t)b * ball;
@@ -55,7 +59,8 @@ __global__ __launch_bounds__(kValuThreads) void ball_attn_valu(
 
   for (int q0 = 0; q0 < ball; q0 += nthr) {
     const int qi = q0 + threadIdx.x;
-    const bool active = qi < ball;
+    bool active = qi < ball;
+    if (MASK && active) active = perm[base + qi] >= 0;
     int64_t pq = 0;
     float qv[D], acc[D];
     float m = -INFINITY, l = 0.f;
@@ -75,6 +80,7 @@ __global__ __launch_bounds__(kValuThreads) void ball_attn_valu(
         const int64_t pk = perm ? perm_index(perm[base + c0 + j], N) : base + c0 + j;
         ks[j][e] = load_elem<T>(k + pk * rs + h * D + e);
         vs[j][e] = load_elem<T>(v + pk * rs + h * D + e);
+        if (MASK && e == 0) kok[j] = perm[base + c0 + j] >= 0;
       }
       __syncthreads();
       if (!active) continue;
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(kValuThreads) void ball_attn_valu(
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
           float t = -INFINITY;
-          if (j0 + jj < nk) {
+          if (j0 + jj < nk && (!MASK || kok[j0 + jj])) {
             t = 0.f;
 #pragma unroll
             for (int e = 0; e < D; ++e) t = fmaf(qv[e], ks[j0 + jj][e], t);
@@ -95,13 +101,14 @@ __global__ __launch_bounds__(kValuThreads) void ball_attn_valu(
           cm = fmaxf(cm, t);
         }
         const float mn = fmaxf(m, cm);
+        if (MASK && mn == -INFINITY) continue;  // no key with a point so far
         const float corr = expf(m - mn);        // 0 on the first sub-chunk
         l *= corr;
 #pragma unroll
         for (int e = 0; e < D; ++e) acc[e] *= corr;
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
-          if (j0 + jj < nk) {
+          if (j0 + jj < nk && (!MASK || kok[j0 + jj])) {
             const float p = expf(sc[jj] - mn);
             l += p;
 #pragma unroll
@@ -181,19 +188,23 @@ struct AttnGeom {
   static_assert((BALL / KPI) * CPR == NT * IPT, "staging pieces tile the threads");
 };
 
-template <int D, int BALL, int HPW, bool PERM, bool PIPE>
+template <int D, int BALL, int HPW, bool PERM, bool PIPE, bool MASK>
 __global__ __launch_bounds__(BALL / 32 * 64)
 BT_WAVES_PER_EU((BALL >= 256 ? 2 : (PIPE ? 3 : 4)), 8)
 void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const int32_t* __restrict__ perm,
-                    int32_t H, int32_t nballs, int32_t xcd_map, uint16_t* __restrict__ out) {
+                    int64_t nrows, int32_t H, int32_t nballs, int32_t xcd_map,
+                    uint16_t* __restrict__ out) {
+  static_assert(PERM || !MASK, "the mask comes from the permutation");
   using Gm = AttnGeom<D, BALL, HPW>;
   constexpr int NT = Gm::NT, KB = Gm::KB, DS = Gm::DS, DB = Gm::DB, VTS = Gm::VTS;
   constexpr int KS = Gm::KS, KPI = Gm::KPI, CPR = Gm::CPR, IPT = Gm::IPT;
   __shared__ __attribute__((aligned(16))) uint16_t ks[HPW][BALL * KS];
   __shared__ __attribute__((aligned(16))) uint16_t vt[HPW][D * VTS];
+  // MASK: 1 where the key slot holds a point (read four keys at a time)
+  __shared__ __attribute__((aligned(16))) uint8_t kok[MASK ? BALL : 4];
 
-  const int64_t N = (int64_t)nballs * BALL;
+  const int64_t N = nrows;
   const int hgroups = H / HPW;
   const int total = nballs * hgroups;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -262,13 +273,19 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       }
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](const Rows& r) {
 #pragma unroll
     for (int ii = 0; ii < IPT; ++ii) {
       const int it = tid + ii * NT;
       const int kq = it / CPR, ch = it - kq * CPR;
       const int hh = ch / (D / 8), dc = ch - hh * (D / 8);
       const int key0 = kq * KPI;
+      if constexpr (MASK) {
+        if (ch == 0) {
+#pragma unroll
+          for (int u = 0; u < KPI; ++u) kok[key0 + u] = r.kv[ii][u] >= 0 ? 1 : 0;
+        }
+      }
 #pragma unroll
       for (int u = 0; u < KPI; ++u) *(u32x4*)&ks[hh][(key0 + u) * KS + dc * 8] = kn[ii][u];
       const int pos0 = (key0 & ~15) + swap23(key0 & 15);   // keeps bits 0,1
@@ -304,6 +321,18 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
           a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qc[hh][s], a, 0, 0, 0);
         }
         sacc[kb] = a;
+      }
+      if constexpr (MASK) {
+        // element e holds key kb*32 + 8*(e/4) + 4*hf + e%4
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint32_t ok4 = *(const uint32_t*)&kok[kb * 32 + 8 * g + 4 * hf];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (!((ok4 >> (8 * i)) & 0xffu)) sacc[kb][g * 4 + i] = -INFINITY;
+          }
       }
       // ---- softmax over the keys of query column c ------------------------
       // Four independent chains for the maximum and the sum.
@@ -370,8 +399,10 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
           c0 = u32x4{ra[0], ra[1], pg[1][0], pg[1][1]};
           c1 = u32x4{rb[0], rb[1], pg[3][0], pg[3][1]};
         }
-        *(u32x4*)(orow + db * 32 + hf * 8) = c0;
-        *(u32x4*)(orow + db * 32 + 16 + hf * 8) = c1;
+        if (!MASK || rc.q >= 0) {          // no output for an unused slot
+          *(u32x4*)(orow + db * 32 + hf * 8) = c0;
+          *(u32x4*)(orow + db * 32 + 16 + hf * 8) = c1;
+        }
       }
     }
   };
@@ -381,7 +412,7 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   if (j >= total) return;                    // uniform over the workgroup
   Rows rc = load_rows(j);
   load_data(rc);
-  stage();
+  stage(rc);
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
@@ -405,7 +436,7 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     attend(rc);
     if (!has_next) break;
     __syncthreads();                         // everyone is done with LDS
-    stage();                                 // waits for the next item's rows
+    stage(rn);                               // waits for the next item's rows
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
@@ -419,17 +450,17 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 // --------------------------------------------------------------------------
 // host launchers
 // --------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool MASK>
 static bt_status launch_valu(const void* q, const void* k, const void* v, const int32_t* perm,
-                             int64_t N, int32_t ball, int32_t H, int32_t d, void* out,
-                             hipStream_t st) {
-  const int nb = (int)(N / ball);
+                             int64_t nrows, int64_t nslots, int32_t ball, int32_t H, int32_t d,
+                             void* out, hipStream_t st) {
+  const int nb = (int)(nslots / ball);
   const int thr = ball >= kValuThreads ? kValuThreads : ((ball + 63) / 64) * 64;
   dim3 grid(nb * H), block(thr);
 #define BT_VALU(DD)                                                                        \
   case DD:                                                                                 \
-    hipLaunchKernelGGL((ball_attn_valu<T, DD>), grid, block, 0, st, (const T*)q,           \
-                       (const T*)k, (const T*)v, perm, N, H, ball, (T*)out);                 \
+    hipLaunchKernelGGL((ball_attn_valu<T, DD, MASK>), grid, block, 0, st, (const T*)q,     \
+                       (const T*)k, (const T*)v, perm, nrows, H, ball, (T*)out);             \
     break;
   switch (d) {
     BT_VALU(16)
@@ -465,25 +496,30 @@ static int attn_grid(int total) {
   return total < g ? total : g;
 }
 
-template <int D, int BB, int HPW>
+template <int D, int BB, int HPW, bool MASK>
 static bt_status launch_mfma(const void* q, const void* k, const void* v, const int32_t* perm,
-                             int64_t N, int32_t H, void* out, hipStream_t st) {
-  const int nb = (int)(N / BB);
+                             int64_t nrows, int64_t nslots, int32_t H, void* out,
+                             hipStream_t st) {
+  const int nb = (int)(nslots / BB);
   const int total = nb * (H / HPW);
   const int xmap = (total % 8 == 0) ? 1 : 0;
-  const int g = attn_grid(total);
+  // the masked kernel runs one item per workgroup: its persistent form would
+  // need more registers than three waves per SIMD allow
+  const int g = MASK ? total : attn_grid(total);
   const bool pipe = g < total;
   dim3 grid(g), block(BB / 32 * 64);
-#define BT_MF(PERM, PIPE)                                                                    \
-  hipLaunchKernelGGL((ball_attn_mfma<D, BB, HPW, PERM, PIPE>), grid, block, 0, st,          \
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, perm, H, nb, \
-                     xmap, (uint16_t*)out)
-  if (perm) {
-    if (pipe) BT_MF(true, true);
-    else BT_MF(true, false);
+#define BT_MF(PERM, PIPE, MK)                                                                \
+  hipLaunchKernelGGL((ball_attn_mfma<D, BB, HPW, PERM, PIPE, MK>), grid, block, 0, st,      \
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, perm, nrows, \
+                     H, nb, xmap, (uint16_t*)out)
+  if constexpr (MASK) {
+    BT_MF(true, false, true);
+  } else if (perm) {
+    if (pipe) BT_MF(true, true, false);
+    else BT_MF(true, false, false);
   } else {
-    if (pipe) BT_MF(false, true);
-    else BT_MF(false, false);
+    if (pipe) BT_MF(false, true, false);
+    else BT_MF(false, false, false);
   }
 #undef BT_MF
   return launch_status("ball_attn_mfma");
@@ -492,22 +528,23 @@ static bt_status launch_mfma(const void* q, const void* k, const void* v, const 
 // Head pairs for balls up to 128 points when H is even; single heads
 // otherwise (a 256-point ball already holds 32 score registers per lane, and
 // a second head's staging registers would spill).
-template <int D>
+template <int D, bool MASK>
 static bt_status launch_mfma_d(const void* q, const void* k, const void* v, const int32_t* perm,
-                               int64_t N, int32_t ball, int32_t H, void* out, hipStream_t st) {
+                               int64_t nrows, int64_t nslots, int32_t ball, int32_t H, void* out,
+                               hipStream_t st) {
   const bool pair = H % 2 == 0;
   switch (ball) {
     case 32:
-      return pair ? launch_mfma<D, 32, 2>(q, k, v, perm, N, H, out, st)
-                  : launch_mfma<D, 32, 1>(q, k, v, perm, N, H, out, st);
+      return pair ? launch_mfma<D, 32, 2, MASK>(q, k, v, perm, nrows, nslots, H, out, st)
+                  : launch_mfma<D, 32, 1, MASK>(q, k, v, perm, nrows, nslots, H, out, st);
     case 64:
-      return pair ? launch_mfma<D, 64, 2>(q, k, v, perm, N, H, out, st)
-                  : launch_mfma<D, 64, 1>(q, k, v, perm, N, H, out, st);
+      return pair ? launch_mfma<D, 64, 2, MASK>(q, k, v, perm, nrows, nslots, H, out, st)
+                  : launch_mfma<D, 64, 1, MASK>(q, k, v, perm, nrows, nslots, H, out, st);
     case 128:
-      return pair ? launch_mfma<D, 128, 2>(q, k, v, perm, N, H, out, st)
-                  : launch_mfma<D, 128, 1>(q, k, v, perm, N, H, out, st);
+      return pair ? launch_mfma<D, 128, 2, MASK>(q, k, v, perm, nrows, nslots, H, out, st)
+                  : launch_mfma<D, 128, 1, MASK>(q, k, v, perm, nrows, nslots, H, out, st);
     case 256:
-      return launch_mfma<D, 256, 1>(q, k, v, perm, N, H, out, st);
+      return launch_mfma<D, 256, 1, MASK>(q, k, v, perm, nrows, nslots, H, out, st);
     default:
       return BT_EINVAL;
   }
@@ -522,11 +559,26 @@ bt_status ball_attn_launch(const void* q, const void* k, const void* v, const in
                            int64_t N, int32_t ball, int32_t H, int32_t d, bt_dtype dt,
                            void* out, hipStream_t st) {
   if (ball_attn_uses_mfma(dt, ball, d)) {
-    if (d == 32) return launch_mfma_d<32>(q, k, v, perm, N, ball, H, out, st);
-    return launch_mfma_d<64>(q, k, v, perm, N, ball, H, out, st);
+    if (d == 32) return launch_mfma_d<32, false>(q, k, v, perm, N, N, ball, H, out, st);
+    return launch_mfma_d<64, false>(q, k, v, perm, N, N, ball, H, out, st);
   }
-  if (dt == BT_F32) return launch_valu<float>(q, k, v, perm, N, ball, H, d, out, st);
-  return launch_valu<uint16_t>(q, k, v, perm, N, ball, H, d, out, st);
+  if (dt == BT_F32) return launch_valu<float, false>(q, k, v, perm, N, N, ball, H, d, out, st);
+  return launch_valu<uint16_t, false>(q, k, v, perm, N, N, ball, H, d, out, st);
+}
+
+// Padded tree: nslots permutation entries (ball | nslots), negative for an
+// unused slot, the others in [0, nrows).
+bt_status ball_attn_padded_launch(const void* q, const void* k, const void* v,
+                                  const int32_t* perm, int64_t nrows, int64_t nslots,
+                                  int32_t ball, int32_t H, int32_t d, bt_dtype dt, void* out,
+                                  hipStream_t st) {
+  if (ball_attn_uses_mfma(dt, ball, d)) {
+    if (d == 32) return launch_mfma_d<32, true>(q, k, v, perm, nrows, nslots, ball, H, out, st);
+    return launch_mfma_d<64, true>(q, k, v, perm, nrows, nslots, ball, H, out, st);
+  }
+  if (dt == BT_F32)
+    return launch_valu<float, true>(q, k, v, perm, nrows, nslots, ball, H, d, out, st);
+  return launch_valu<uint16_t, true>(q, k, v, perm, nrows, nslots, ball, H, d, out, st);
 }
 
 }  // namespace bt

@@ -28,6 +28,29 @@ __global__ __launch_bounds__(256) void permute_rows(const V* __restrict__ src,
   }
 }
 
+// Padded permutation (a padded tree of an uneven point count): nslots
+// entries, negative for an unused slot, the others row indices below nrows.
+//   GATHER  dst[t] = src[perm[t]], a zero row for an unused slot
+//   SCATTER dst[perm[t]] = src[t] for the used slots only
+template <typename V, bool SCATTER>
+__global__ __launch_bounds__(256) void permute_rows_padded(const V* __restrict__ src,
+                                                           const int32_t* __restrict__ perm,
+                                                           int64_t nslots, int64_t nrows, int64_t w,
+                                                           V* __restrict__ dst) {
+  const int64_t total = nslots * w;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / w;
+    const int64_t e = i - t * w;
+    const int32_t raw = perm[t];
+    if (SCATTER) {
+      if (raw >= 0) dst[perm_index(raw, nrows) * w + e] = src[t * w + e];
+    } else {
+      dst[t * w + e] = raw >= 0 ? src[perm_index(raw, nrows) * w + e] : V{};
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void invert_perm_kernel(const int32_t* __restrict__ perm,
                                                           int64_t n, int32_t* __restrict__ inv) {
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n;
@@ -64,6 +87,28 @@ bt_status permute_launch(const void* src, const int32_t* perm, int64_t n, int64_
                          st, (const uint32_t*)src, perm, n, w, (uint32_t*)dst);
   }
   return launch_status("bt_permute");
+}
+
+bt_status permute_padded_launch(const void* src, const int32_t* perm, int64_t nrows,
+                                int64_t nslots, int64_t row_bytes, bt_perm_mode mode, void* dst,
+                                hipStream_t st) {
+  if (nslots == 0) return BT_OK;
+  const bool v16 = (row_bytes % 16 == 0) && ((uintptr_t)src % 16 == 0) &&
+                   ((uintptr_t)dst % 16 == 0);
+  const int64_t w = v16 ? row_bytes / 16 : row_bytes / 4;
+  const dim3 grid(grid_for(nslots * w)), blk(256);
+#define BT_PP(V, SC)                                                                           \
+  hipLaunchKernelGGL((permute_rows_padded<V, SC>), grid, blk, 0, st, (const V*)src, perm,     \
+                     nslots, nrows, w, (V*)dst)
+  if (v16) {
+    if (mode == BT_SCATTER) BT_PP(u32x4, true);
+    else BT_PP(u32x4, false);
+  } else {
+    if (mode == BT_SCATTER) BT_PP(uint32_t, true);
+    else BT_PP(uint32_t, false);
+  }
+#undef BT_PP
+  return launch_status("bt_permute_padded");
 }
 
 bt_status invert_perm_launch(const int32_t* perm, int64_t n, int32_t* inv, hipStream_t st) {

@@ -35,6 +35,10 @@
 //               perm[t] = idx.  With few nodes a 16-wave workgroup owns a
 //               node and its waves split that level's segments in parallel;
 //               otherwise each wave owns a node.
+//   padded      an uneven point count n: the tree has leaf * 2^L slots (the
+//               smallest that holds n); a node of m points gives its left
+//               child the ceil(m/2) smallest, and a leaf's unused slots hold
+//               -1.  Built by one workgroup in LDS (slots <= 1024).
 #include "common.h"
 
 namespace bt {
@@ -365,7 +369,8 @@ __global__ __launch_bounds__(kThreads) void tree_extents(const uint32_t* __restr
 
 // ---------------------------------------------------------------- finish ----
 
-// Split the m-point segment R[0..m) of a wave's LDS node in place.
+// Split the m-point segment R[0..m) of a wave's LDS node in place: the left
+// part takes the ceil(m/2) smallest points (m/2 for the even m of a full tree).
 BT_DEV void wave_split(float4* R, int m, uint32_t* hist, int lane) {
   // extents
   uint32_t mn[3] = {~0u, ~0u, ~0u}, mx[3] = {0u, 0u, 0u};
@@ -385,7 +390,7 @@ BT_DEV void wave_split(float4* R, int m, uint32_t* hist, int lane) {
   // [kmin, kmax], so they share every bit above the highest bit in which
   // kmin and kmax differ; the passes start at the byte holding that bit.
   uint32_t prefix = kmin;
-  uint32_t rank = (uint32_t)(m / 2 - 1);
+  uint32_t rank = (uint32_t)((m + 1) / 2 - 1);
   const uint32_t diff = kmin ^ kmax;
   if (diff) {
     const int top = 31 - __clz((int)diff);
@@ -433,7 +438,7 @@ BT_DEV void wave_split(float4* R, int m, uint32_t* hist, int lane) {
     if (rr * 64 < m && rr * 64 + lane < m) x[rr] = R[rr * 64 + lane];
   __builtin_amdgcn_wave_barrier();
   uint32_t E = 0, Lrun = 0, Rrun = 0;
-  const uint32_t half = (uint32_t)(m / 2);
+  const uint32_t half = (uint32_t)((m + 1) / 2);
 #pragma unroll
   for (int rr = 0; rr < MAXR; ++rr) {
     if (rr * 64 >= m) break;
@@ -497,6 +502,60 @@ __global__ __launch_bounds__(kFinishBlockWaves * 64) void tree_finish_block(
     __syncthreads();
   }
   for (int i = tid; i < nf; i += kFinishBlockWaves * 64) perm[base + i] = __float_as_int(srec[i].w);
+}
+
+// Padded tree: start and point count of segment s at level lev, found by
+// walking down from the root (n points), the left child taking ceil(cnt/2).
+BT_DEV void padded_segment(int n, int lev, int s, int* start, int* cnt) {
+  int st = 0, c = n;
+  for (int i = lev - 1; i >= 0; --i) {
+    const int nl = (c + 1) >> 1;
+    if ((s >> i) & 1) {
+      st += nl;
+      c -= nl;
+    } else {
+      c = nl;
+    }
+  }
+  *start = st;
+  *cnt = c;
+}
+
+// One workgroup builds a padded tree of n <= ncap <= kFinish points: the
+// points stay compacted in LDS (every segment of a level is a contiguous run),
+// each level splits its segments of two or more points in place (the waves
+// take them in turn), then leaf j's points go to slots j*leaf ... in order
+// and the leaf's remaining slots get -1.
+__global__ __launch_bounds__(kFinishBlockWaves * 64) void tree_finish_padded(
+    const float4* __restrict__ rec, int n, int ncap, int leaf, int32_t* __restrict__ perm) {
+  __shared__ float4 srec[kFinish];
+  __shared__ uint32_t shist[kFinishBlockWaves][256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < n; i += kFinishBlockWaves * 64) srec[i] = rec[i];
+  __syncthreads();
+  int lev = 0;
+  for (int slots = ncap; slots > leaf; slots >>= 1, ++lev) {
+    for (int sgi = w; sgi < (1 << lev); sgi += kFinishBlockWaves) {
+      int st, cnt;
+      padded_segment(n, lev, sgi, &st, &cnt);
+      if (cnt >= 2) wave_split(srec + st, cnt, shist[w], lane);
+    }
+    __syncthreads();
+  }
+  for (int t = tid; t < ncap; t += kFinishBlockWaves * 64) {
+    const int j = t / leaf, i = t - j * leaf;
+    int st, cnt;
+    padded_segment(n, lev, j, &st, &cnt);
+    perm[t] = i < cnt ? __float_as_int(srec[st + i].w) : -1;
+  }
+}
+
+// A padded tree that is a single leaf: the points in index order, then -1.
+__global__ __launch_bounds__(kThreads) void tree_single_leaf_padded(int64_t n, int64_t ncap,
+                                                                    int32_t* __restrict__ perm) {
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < ncap;
+       t += (int64_t)gridDim.x * blockDim.x)
+    perm[t] = t < n ? (int32_t)t : -1;
 }
 
 __global__ __launch_bounds__(kThreads) void tree_write_perm(const float4* __restrict__ rec,
@@ -627,6 +686,43 @@ bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const floa
   hipLaunchKernelGGL(tree_finish, dim3((nnodes + kFinishWaves - 1) / kFinishWaves),
                      dim3(kFinishWaves * 64), 0, st, fin, (int)p.nf, leaf, nnodes, perm);
   return launch_status("tree_finish");
+}
+
+int64_t tree_padded_slots(int64_t n, int leaf) {
+  int64_t cap = leaf;
+  while (cap < n) cap *= 2;
+  return cap;
+}
+
+size_t tree_padded_workspace_size(int64_t n, int leaf) {
+  return tree_padded_slots(n, leaf) == leaf ? 256 : align256((size_t)n * 16);
+}
+
+// Padded tree of n points: one leaf of any size, or up to kFinish slots.
+bt_status tree_build_padded_launch(const float* coords, int64_t n, int leaf, const float* R,
+                                   int32_t* perm, void* ws, hipStream_t st) {
+  const int64_t ncap = tree_padded_slots(n, leaf);
+  if (ncap == leaf) {
+    int64_t g = (ncap + kThreads - 1) / kThreads;
+    if (g > 4096) g = 4096;
+    hipLaunchKernelGGL(tree_single_leaf_padded, dim3((int)g), dim3(kThreads), 0, st, n, ncap,
+                       perm);
+    return launch_status("tree_single_leaf_padded");
+  }
+  if (ncap > kFinish) return BT_EINVAL;
+  float4* rec = (float4*)ws;
+  const float* r = R;
+  float rr[9] = {1, 0, 0, 0, 1, 0, 0, 0, 1};
+  if (r) for (int i = 0; i < 9; ++i) rr[i] = r[i];
+  int64_t g = (n + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(tree_ingest, dim3((int)g), dim3(kThreads), 0, st, coords, n, r ? 1 : 0,
+                     rr[0], rr[1], rr[2], rr[3], rr[4], rr[5], rr[6], rr[7], rr[8], rec,
+                     (uint32_t*)nullptr, 0);
+  bt_status s = launch_status("tree_ingest");
+  if (s != BT_OK) return s;
+  hipLaunchKernelGGL(tree_finish_padded, dim3(1), dim3(kFinishBlockWaves * 64), 0, st, rec,
+                     (int)n, (int)ncap, leaf, perm);
+  return launch_status("tree_finish_padded");
 }
 
 }  // namespace bt

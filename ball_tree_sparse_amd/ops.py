@@ -65,6 +65,13 @@ _SIGS = [
                             _P]),
     ("ball_attn_bwd", C.c_int, [_P, _P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32,
                                 C.c_int32, C.c_int, _P, _P, _P, _P]),
+    ("bt_padded_size", C.c_int64, [C.c_int64, C.c_int32]),
+    ("bt_build_padded_workspace_size", C.c_size_t, [C.c_int64, C.c_int32]),
+    ("bt_build_padded", C.c_int, [_P, C.c_int64, C.c_int32, C.POINTER(C.c_float), _P, _P,
+                                  C.c_size_t, _P]),
+    ("bt_permute_padded", C.c_int, [_P, _P, C.c_int64, C.c_int64, C.c_int64, C.c_int, _P, _P]),
+    ("ball_attn_padded", C.c_int, [_P, _P, _P, _P, C.c_int64, C.c_int64, C.c_int32, C.c_int32,
+                                   C.c_int32, C.c_int, _P, _P]),
 ]
 EXPORTS = [s[0] for s in _SIGS]
 
@@ -161,6 +168,34 @@ def bt_rotate_build(coords, leaf: int, R, perm=None, workspace=None):
     return perm
 
 
+def bt_padded_size(N: int, leaf: int) -> int:
+    """Slots of the padded tree of N points (-1 if invalid)."""
+    return lib().bt_padded_size(N, leaf)
+
+
+def bt_build_padded(coords, leaf: int, R=None, perm=None, workspace=None):
+    """Padded tree of an uneven point count: int32 [bt_padded_size(N, leaf)]
+    with -1 in unused slots (R: optional host 3x3 rotation)."""
+    _dev(coords, "coords", torch.float32)
+    N = coords.shape[0]
+    S = lib().bt_padded_size(N, leaf)
+    rarr = None
+    if R is not None:
+        r = torch.as_tensor(R, dtype=torch.float32).reshape(9).cpu().tolist()
+        rarr = (C.c_float * 9)(*r)
+    if perm is None:
+        perm = torch.empty(max(S, 0), dtype=torch.int32, device=coords.device)
+    _dev(perm, "perm", torch.int32)
+    if perm.numel() < S:
+        raise ValueError(f"perm must hold {S} slots")
+    need = lib().bt_build_padded_workspace_size(N, leaf)
+    if workspace is None:
+        workspace = _workspace(need, coords.device)
+    _check(lib().bt_build_padded(_ptr(coords), N, leaf, rarr, _ptr(perm), _ptr(workspace),
+                                 workspace.numel(), _stream(coords.device)))
+    return perm
+
+
 # ------------------------------------------------------------------ permute --
 
 def bt_permute(src, perm, mode: int, dst=None):
@@ -174,6 +209,26 @@ def bt_permute(src, perm, mode: int, dst=None):
     _dev(dst, "dst", src.dtype)
     _check(lib().bt_permute(_ptr(src), _ptr(perm), N, row_bytes, mode, _ptr(dst),
                             _stream(src.device)))
+    return dst
+
+
+def bt_permute_padded(src, perm, n_rows: int, mode: int, dst=None):
+    """Padded permutation (perm: one entry per slot, -1 unused).  GATHER:
+    [n_rows, ...] -> [slots, ...] with zero rows in unused slots; SCATTER:
+    [slots, ...] -> [n_rows, ...] from the used slots."""
+    _dev(src, "src")
+    _dev(perm, "perm", torch.int32)
+    S = perm.numel()
+    row_bytes = math.prod(src.shape[1:]) * src.element_size()
+    if dst is None:
+        rows = S if mode == BT_GATHER else n_rows
+        dst = torch.empty((rows,) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    _dev(dst, "dst", src.dtype)
+    if src.shape[0] != (n_rows if mode == BT_GATHER else S) or \
+            dst.shape[0] != (S if mode == BT_GATHER else n_rows):
+        raise ValueError("src/dst rows do not match n_rows and the slot count")
+    _check(lib().bt_permute_padded(_ptr(src), _ptr(perm), n_rows, S, row_bytes, mode, _ptr(dst),
+                                   _stream(src.device)))
     return dst
 
 
@@ -237,6 +292,23 @@ def ball_attn(q, k, v, perm, ball: int, out=None):
     _dev(out, "out", q.dtype)
     _check(lib().ball_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), N, ball, H, d,
                            _dtype_code(q), _ptr(out), _stream(q.device)))
+    return out
+
+
+def ball_attn_padded(q, k, v, perm, ball: int, out=None):
+    """Ball attention on a padded tree: q, k, v [N,H,d] in original order,
+    perm int32 [slots] with -1 in unused slots."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+        if t.shape != q.shape or t.dim() != 3:
+            raise ValueError("q, k, v must share one [N,H,d] shape")
+    _dev(perm, "perm", torch.int32)
+    N, H, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    _check(lib().ball_attn_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), N, perm.numel(), ball,
+                                  H, d, _dtype_code(q), _ptr(out), _stream(q.device)))
     return out
 
 

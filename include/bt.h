@@ -126,7 +126,10 @@ bt_status bt_invert_perm(const int32_t* perm, int64_t N, int32_t* inv,
  *   D_i = dO_i . O_i,  dS = P * (dO V^T - D),
  *   dq = dS K / sqrt(d),  dk = dS^T Q / sqrt(d),  dv = P^T dO,
  * in the inputs' order (original order when perm != NULL).  O is recomputed,
- * so the forward output is not an argument.  fp32 arithmetic; outputs in dt.
+ * so the forward output is not an argument.  Outputs in dt.  bf16 with d = 32
+ * and ball in {32, 64, 128}, or d = 64 and ball in {32, 64}, runs the MFMA
+ * kernel (bf16 operands with P and dS rounded to bf16; fp32 softmax
+ * statistics and accumulation); every other shape runs in fp32 arithmetic.
  * Requirements: as ball_attn, with ball <= 1024; dq, dk, dv must not alias
  * the inputs or each other.  N = 0 is a no-op.  Errors: BT_EINVAL for a
  * violated requirement or a null pointer with N > 0; BT_EHIP if the launch
@@ -176,6 +179,53 @@ bt_status bt_refine(const void* xc, const int32_t* perm, int64_t N, int32_t H,
 bt_status ball_attn(const void* q, const void* k, const void* v,
                     const int32_t* perm, int64_t N, int32_t ball, int32_t H,
                     int32_t d, bt_dtype dt, void* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Uneven point counts (Erwin thread, post 6/N: the sets are of similar size;
+ * post 9/N: equal contiguous balls make ball operations views and means).
+ * The padded tree of N points has S = bt_padded_size(N, leaf) slots, the
+ * smallest leaf * 2^L >= N.  At every node of m points the split axis is
+ * chosen as in bt_build and the left child takes the ceil(m/2) smallest
+ * points in (coordinate, index) order; a leaf stores its points first, in
+ * ascending index, and -1 in its unused slots.  For N = leaf * 2^L this is
+ * exactly bt_build.
+ *
+ * bt_padded_size: S, or -1 when N < 1, leaf < 1 or S >= 2^31.
+ * bt_build_padded: coords [N,3] fp32 (device); R_host NULL (no rotation) or
+ *   a finite 3x3 row-major fp32 rotation in host memory, applied as in
+ *   bt_rotate_build; writes perm [S] int32 (device).  ws: device workspace of
+ *   bt_build_padded_workspace_size(N, leaf) bytes, 256-byte aligned.  In this
+ *   build S <= 1024 (or S == leaf, a single leaf), for the reason given at
+ *   bt_build.  Errors: BT_EINVAL for null pointers or a violated limit,
+ *   BT_ENOMEM for a short workspace.
+ * bt_permute_padded: perm has n_slots entries, negative for an unused slot,
+ *   the others row indices below n_rows (not checked beyond clamping).
+ *   GATHER:  dst[t] = src[perm[t]] (dst [n_slots] rows, src [n_rows] rows),
+ *            a zero row for an unused slot;
+ *   SCATTER: dst[perm[t]] = src[t] for the used slots (src [n_slots] rows,
+ *            dst [n_rows] rows; rows no slot names are left unchanged).
+ *   Requirements: 1 <= n_rows <= n_slots < 2^31 (n_slots = 0 is a no-op);
+ *   row_bytes a positive multiple of 4; src and dst do not overlap.
+ * ball_attn_padded: ball attention on a padded tree: q, k, v, out [n_rows,
+ *   H, d] in original order; perm [n_slots] as above (required); the keys of
+ *   a ball are its used slots, and out[perm[t]] is written for every used
+ *   slot t only.  Requirements: ball | n_slots; 1 <= n_rows <= n_slots;
+ *   otherwise as ball_attn.  Errors: BT_EINVAL for a violated requirement or
+ *   a null pointer; BT_EHIP if the launch fails.
+ * All three are asynchronous on stream and allocate nothing.
+ * ---------------------------------------------------------------------- */
+int64_t bt_padded_size(int64_t N, int32_t leaf);
+size_t bt_build_padded_workspace_size(int64_t N, int32_t leaf);
+bt_status bt_build_padded(const float* coords, int64_t N, int32_t leaf,
+                          const float* R_host, int32_t* perm, void* ws,
+                          size_t ws_bytes, void* stream);
+bt_status bt_permute_padded(const void* src, const int32_t* perm,
+                            int64_t n_rows, int64_t n_slots, int64_t row_bytes,
+                            bt_perm_mode mode, void* dst, void* stream);
+bt_status ball_attn_padded(const void* q, const void* k, const void* v,
+                           const int32_t* perm, int64_t n_rows, int64_t n_slots,
+                           int32_t ball, int32_t H, int32_t d, bt_dtype dt,
+                           void* out, void* stream);
 
 /* ------------------------------------------------------------------------
  * Ball Sparse Attention (Pith review of arXiv 2506.12541: "What carries the

@@ -26,7 +26,8 @@ int main(int argc, char** argv) {
   size_t ne = (size_t)N * H * d, es = dt == BT_F32 ? 4 : 2;
   auto q = rd<unsigned char>("q.bin", ne * es), k = rd<unsigned char>("k.bin", ne * es),
        v = rd<unsigned char>("v.bin", ne * es);
-  auto perm = rd<int32_t>("perm.bin", N);
+  const long long nslots = mode == "ball_padded" ? atoll(argv[7]) : N;
+  auto perm = rd<int32_t>("perm.bin", nslots);
   std::vector<unsigned char> out(ne * es, 0xcd);
   if (mode == "bwd") {
     auto dout = rd<unsigned char>("do.bin", ne * es);
@@ -40,7 +41,10 @@ int main(int argc, char** argv) {
     printf("done bwd %d\n", (int)bt::ball_attn_bwd_uses_mfma((bt_dtype)dt, ball, d));
     return 0;
   }
-  if (mode == "ball" || mode == "ball_noperm") {
+  if (mode == "ball_padded") {
+    bt::ball_attn_padded_launch(q.data(), k.data(), v.data(), perm.data(), N, nslots, ball, H, d,
+                                (bt_dtype)dt, out.data(), nullptr);
+  } else if (mode == "ball" || mode == "ball_noperm") {
     bt::ball_attn_launch(q.data(), k.data(), v.data(), mode == "ball" ? perm.data() : nullptr, N,
                          ball, H, d, (bt_dtype)dt, out.data(), nullptr);
   } else {

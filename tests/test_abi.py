@@ -145,3 +145,55 @@ def test_ball_attn_bwd_rejects(L):
     assert call(ptrs=[t[0], t[1], t[2], t[3], t[0], t[5], t[6]]) == ops.BT_EINVAL   # dq aliases q
     assert call(ptrs=[t[0], t[1], t[2], t[3], t[4], t[4], t[6]]) == ops.BT_EINVAL   # dq is dk
     assert call(N=0, ptrs=[None] * 7) == ops.BT_OK
+
+
+def test_padded_size_and_workspace(L):
+    assert L.bt_padded_size(972, 32) == 1024
+    assert L.bt_padded_size(1024, 32) == 1024
+    assert L.bt_padded_size(3586, 128) == 4096
+    assert L.bt_padded_size(1, 1) == 1
+    assert L.bt_padded_size(700, 700) == 700
+    assert L.bt_padded_size(0, 4) == -1
+    assert L.bt_padded_size(5, 0) == -1
+    assert L.bt_padded_size((1 << 31) - 1, 3) == -1          # slots would reach 2^31
+    assert L.bt_build_padded_workspace_size(0, 4) == 0
+    assert L.bt_build_padded_workspace_size(972, 32) >= 972 * 16
+
+
+def test_build_padded_rejects(L):
+    f = _fake()
+    assert L.bt_build_padded(None, 10, 2, None, f, f, 1 << 20, None) == ops.BT_EINVAL
+    assert L.bt_build_padded(f, 0, 2, None, f, f, 1 << 20, None) == ops.BT_EINVAL
+    assert L.bt_build_padded(f, 3586, 128, None, f, f, 1 << 20, None) == ops.BT_EINVAL
+    assert b"switched off" in L.bt_last_error()
+    bad = (C.c_float * 9)(1, 0, 0, 0, float("inf"), 0, 0, 0, 1)
+    assert L.bt_build_padded(f, 10, 2, bad, f, f, 1 << 20, None) == ops.BT_EINVAL
+    buf = C.create_string_buffer(4096 + 512)
+    addr = (C.addressof(buf) + 255) & ~255
+    assert L.bt_build_padded(f, 10, 2, None, f, C.c_void_p(addr), 16, None) == ops.BT_ENOMEM
+    assert L.bt_build_padded(f, 10, 2, None, f, C.c_void_p(addr + 8), 4096, None) == \
+        ops.BT_EINVAL
+
+
+def test_permute_padded_rejects(L):
+    f = _fake(4096)
+    assert L.bt_permute_padded(f, f, 5, 8, 6, ops.BT_GATHER, _fake(4096), None) == ops.BT_EINVAL
+    assert L.bt_permute_padded(f, f, 9, 8, 16, ops.BT_GATHER, _fake(4096), None) == ops.BT_EINVAL
+    assert L.bt_permute_padded(f, f, 0, 8, 16, ops.BT_GATHER, _fake(4096), None) == ops.BT_EINVAL
+    assert L.bt_permute_padded(f, f, 5, 8, 16, 7, _fake(4096), None) == ops.BT_EINVAL
+    assert L.bt_permute_padded(f, None, 5, 8, 16, ops.BT_SCATTER, _fake(4096), None) == \
+        ops.BT_EINVAL
+    assert L.bt_permute_padded(f, f, 5, 8, 16, ops.BT_GATHER, f, None) == ops.BT_EINVAL
+    assert L.bt_permute_padded(None, None, 0, 0, 16, ops.BT_GATHER, None, None) == ops.BT_OK
+
+
+def test_ball_attn_padded_rejects(L):
+    a, b, c, o, p = (_fake(1 << 16) for _ in range(5))
+    bf = ops.BT_BF16
+    assert L.ball_attn_padded(a, b, c, p, 100, 96, 32, 2, 32, bf, o, None) == ops.BT_EINVAL
+    assert b"n_rows" in L.bt_last_error()                       # more rows than slots
+    assert L.ball_attn_padded(a, b, c, p, 90, 100, 32, 2, 32, bf, o, None) == ops.BT_EINVAL
+    assert L.ball_attn_padded(a, b, c, None, 90, 96, 32, 2, 32, bf, o, None) == ops.BT_EINVAL
+    assert L.ball_attn_padded(a, b, c, p, 90, 96, 32, 2, 48, bf, o, None) == ops.BT_EINVAL
+    assert L.ball_attn_padded(a, b, c, p, 90, 96, 32, 2, 32, bf, a, None) == ops.BT_EINVAL
+    assert L.ball_attn_padded(a, b, c, p, 0, 96, 32, 2, 32, bf, o, None) == ops.BT_EINVAL

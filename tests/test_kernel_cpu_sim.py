@@ -191,3 +191,60 @@ def test_ball_attn_bwd_kernels(sim, n, H, d, ball, dtype):
         got = _read_out(d_ / f"d{name}.bin", n, H, d, dtype)
         err = np.abs(got - w).max()
         assert err <= (2e-2 if dtype == "bf16" else 2e-5), (name, err)
+
+
+def _tree_padded(sim, coords, leaf, R=None):
+    d = sim["dir"]
+    c = d / "c.bin"
+    np.ascontiguousarray(coords, np.float32).tofile(c)
+    args = [sim["tree"], "padded", str(c), str(len(coords)), str(leaf), str(d / "p.bin")]
+    if R is not None:
+        np.asarray(R, np.float32).tofile(d / "R.bin")
+        args.append(str(d / "R.bin"))
+    r = subprocess.run(args, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
+    return np.fromfile(d / "p.bin", np.int32)
+
+
+@pytest.mark.parametrize("n,leaf", [(972, 32), (1000, 16), (513, 64), (5, 2), (3, 1), (1, 1),
+                                    (2, 1), (700, 700), (1024, 32), (129, 1)])
+def test_padded_tree_kernels_bit_exact(sim, n, leaf):
+    """Uneven N: the padded tree (one workgroup in LDS), bit for bit."""
+    rng = np.random.default_rng(n * 7 + leaf)
+    c = synth.uniform_cube(rng, n)
+    assert np.array_equal(_tree_padded(sim, c, leaf), T.build_padded(c, leaf))
+
+
+def test_padded_tree_kernels_rotated_and_ties(sim):
+    rng = np.random.default_rng(12)
+    c = rng.integers(-1, 2, size=(900, 3)).astype(np.float32)    # many equal keys
+    c[rng.random(c.shape) < 0.5] *= -1.0                          # signed zeros
+    R = synth.random_rotation(rng)
+    assert np.array_equal(_tree_padded(sim, c, 8), T.build_padded(c, 8))
+    w = synth.uniform_cube(rng, 600)
+    assert np.array_equal(_tree_padded(sim, w, 16, R=R), T.rotate_build_padded(w, 16, R))
+
+
+@pytest.mark.parametrize("n,H,d,ball,dtype", [(972, 2, 32, 128, "bf16"), (1000, 3, 64, 64, "bf16"),
+                                             (300, 2, 32, 256, "bf16"), (972, 2, 16, 32, "f32"),
+                                             (500, 2, 16, 64, "bf16")])
+def test_ball_attn_padded_kernels(sim, n, H, d, ball, dtype):
+    """Ball attention on a padded tree: unused slots take no weight and get no
+    output row (the MFMA kernel for bf16 d 32/64, the VALU kernel otherwise)."""
+    d_ = sim["dir"]
+    rng = np.random.default_rng(n + ball)
+    c = synth.uniform_cube(rng, n)
+    perm = T.build_padded(c, 16).astype(np.int32)
+    if len(perm) % ball:
+        perm = np.concatenate([perm, np.full(ball - len(perm) % ball, -1, np.int32)])
+    q, k, v = (synth.normal_features(rng, n, H, d, dtype) for _ in range(3))
+    for t, nm in ((q, "q.bin"), (k, "k.bin"), (v, "v.bin")):
+        _dump(t, d_ / nm)
+    perm.tofile(d_ / "perm.bin")
+    r = subprocess.run([sim["attn"], "ball_padded", str(n), str(H), str(d), str(ball),
+                        "1" if dtype == "bf16" else "0", str(len(perm))], cwd=d_,
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
+    out = _read_out(d_ / "out.bin", n, H, d, dtype)
+    err = np.abs(out - A.ball_attn_padded(q, k, v, perm, ball)).max()
+    assert err <= (2e-2 if dtype == "bf16" else 1e-5), err
