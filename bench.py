@@ -206,8 +206,9 @@ def _event_us(torch, fn, reps, warm=3):
 def side_rows(dev, torch, ops, synth):
     """The other rows of the path, timed in the same run on their own
     workloads: permute (gather and scatter of 512-byte rows at the rotated-
-    pair size), the BSA step, and tree build + fp32 ball attention at the
-    size the GPU tree builder takes (1,024 points)."""
+    pair size), coarsen / refine, the BSA steps, padded ball attention of an
+    uneven N, the backward of ball attention, and tree build + fp32 ball
+    attention at the size the GPU tree builder takes (1,024 points)."""
     rows = {}
     # permute: N = 262,144 rows of H*d bf16 = 512 bytes; three source and
     # destination pairs (805 MB) rotate so that no call finds its rows in the
@@ -290,6 +291,28 @@ def side_rows(dev, torch, ops, synth):
         "us_per_step": us2, "points_per_s": N / (us2 * 1e-6),
         "tflops": flops2 / (us2 * 1e-6) / 1e12, "speedup_vs_bsa": us / us2}
     del q, k, v, out, bws, bws2
+    # uneven N: 65,000 sphere points in 65,536 slots (535 unused slots spread
+    # over the balls), masked ball attention; three input sets rotate
+    n3, slots = 65000, 65536
+    w = synth.make("sphere", n=n3)
+    g3 = torch.Generator().manual_seed(11)
+    pp = torch.full((slots,), -1, dtype=torch.int32)
+    pp[torch.randperm(slots, generator=g3)[:n3]] = torch.randperm(n3, generator=g3).to(torch.int32)
+    pp = pp.to(dev)
+    sets = [tuple(t.to(dev).clone() for t in (w.q, w.k, w.v)) for _ in range(3)]
+    o3 = [torch.empty_like(sets[0][0]) for _ in range(3)]
+    it = [0]
+
+    def call3():
+        i = it[0] % 3
+        it[0] += 1
+        ops.ball_attn_padded(*sets[i], pp, w.ball, out=o3[i])
+    us3 = _event_us(torch, call3, 300, warm=100)
+    nb3 = 4 * n3 * w.H * w.d * 2 + 4 * slots
+    rows["f3_ball_attn_padded"] = {"workload": "N=65,000 in 65,536 slots, ball 128, H=8, d=32 bf16",
+                                   "us": us3, "GBps": nb3 / us3 / 1e3,
+                                   "hbm_frac": nb3 / us3 / 1e3 / HBM_PEAK_GBS}
+    del sets, o3
     # backward of ball attention at the sphere size
     w = synth.make("sphere")
     gq, gk, gv = (t.to(dev) for t in (w.q, w.k, w.v))
@@ -316,6 +339,14 @@ def side_rows(dev, torch, ops, synth):
     us_a = _event_us(torch, lambda: ops.ball_attn(q, k, v, pt, w.ball, out=ot), 200)
     rows["a1_a4_a6_tiny"] = {"workload": "N=1024 uniform cube, leaf = ball 32, H=4, d=16 fp32",
                              "build_us": us_b, "ball_attn_us": us_a}
+    # padded tree of an uneven N: 972 points (the Elasticity cloud size), leaf 32
+    c9 = c[:972].contiguous()
+    tws9 = torch.empty(max(256, ops.lib().bt_build_padded_workspace_size(972, 32)),
+                       dtype=torch.uint8, device=dev)
+    pt9 = torch.empty(ops.bt_padded_size(972, 32), dtype=torch.int32, device=dev)
+    us_p = _event_us(torch, lambda: ops.bt_build_padded(c9, 32, perm=pt9, workspace=tws9), 200)
+    rows["f3_tree_padded"] = {"workload": "N=972 uniform cube in 1,024 slots, leaf 32",
+                              "build_us": us_p}
     return rows
 
 
