@@ -320,13 +320,15 @@ struct Branch {
   float l[4];   // partial sums of the rounded weights
 };
 
-// One online-softmax step over NKB 32-key blocks.  Block kb's keys are rows
-// row0(kb) .. row0(kb)+31 of the head's row-major K (kh) and of its
+// One online-softmax step over NKB 32-key blocks for QB query blocks of 32
+// (qf: QB x D/16 B-operand fragments, br: QB branch states).  Block kb's keys
+// are rows row0(kb) .. row0(kb)+31 of the head's row-major K (kh) and of its
 // transposed V blocks (vh: [rows/32][D][32]); row0(kb) is a multiple of 32.
-// Every K and V fragment of the chunk is requested before the first MFMA.
-template <int D, int NKB, typename RowFn>
+// Every K and V fragment of the chunk is requested before the first MFMA and
+// then serves all QB query blocks, so the cache traffic per query falls by QB.
+template <int D, int NKB, int QB, typename RowFn>
 BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
-                         RowFn row0, const bf16x8* qf, float c2, Branch<D / 32>& br) {
+                         RowFn row0, const bf16x8* qf, float c2, Branch<D / 32>* br) {
   constexpr int DS = D / 16, DB = D / 32;
   const int lane = threadIdx.x & 63, hf = lane >> 5, c = lane & 31;
   bf16x8 kf[NKB][DS], vf[NKB][2][DB];
@@ -343,59 +345,63 @@ BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __rest
       for (int db = 0; db < DB; ++db)
         vf[kb][s2][db] = *(const bf16x8*)(vblk + db * 32 * 32 + s2 * 16);
   }
-  f32x16 sacc[NKB];
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    f32x16 a = {};
+  for (int qb = 0; qb < QB; ++qb) {
+    Branch<DB>& b = br[qb];
+    f32x16 sacc[NKB];
 #pragma unroll
-    for (int s = 0; s < DS; ++s)
-      a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][s], qf[s], a, 0, 0, 0);
-    sacc[kb] = a;
-  }
-  // chunk maximum of the raw scores (scaling by c2 > 0 keeps the order)
-  float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int kb = 0; kb < NKB; ++kb) {
+      f32x16 a = {};
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
-  float cm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * c2;
-  cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-  const float mn = fmaxf(br.m, cm);
-  const float alpha = __builtin_amdgcn_exp2f(br.m - mn);     // 0 on the first chunk
-#pragma unroll
-  for (int i = 0; i < 4; ++i) br.l[i] *= alpha;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) br.o[db][e] *= alpha;
-  br.m = mn;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8 pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pf[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][s2 * 8 + e], c2, -mn));
-      br.l[(kb * 2 + s2) & 3] = bsa_sum8(pf, br.l[(kb * 2 + s2) & 3]);
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        br.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][s2][db], pf, br.o[db], 0, 0, 0);
+      for (int s = 0; s < DS; ++s)
+        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][s], qf[qb * DS + s], a, 0, 0, 0);
+      sacc[kb] = a;
     }
+    // chunk maximum of the raw scores (scaling by c2 > 0 keeps the order)
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
+    float cm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * c2;
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    const float mn = fmaxf(b.m, cm);
+    const float alpha = __builtin_amdgcn_exp2f(b.m - mn);     // 0 on the first chunk
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b.l[i] *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) b.o[db][e] *= alpha;
+    b.m = mn;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pf[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][s2 * 8 + e], c2, -mn));
+        b.l[(kb * 2 + s2) & 3] = bsa_sum8(pf, b.l[(kb * 2 + s2) & 3]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          b.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][s2][db], pf, b.o[db], 0, 0, 0);
+      }
+  }
 }
 
 // Online softmax over keys [0, len) of a branch in kChunk-key chunks (len is
 // a multiple of 32); row0(key) gives the row of the 32-key block at key.
-template <int D, typename RowFn>
+template <int D, int QB, typename RowFn>
 BT_DEV void attend_range(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
-                         RowFn row0, int len, const bf16x8* qf, float c2, Branch<D / 32>& br) {
+                         RowFn row0, int len, const bf16x8* qf, float c2, Branch<D / 32>* br) {
   constexpr int KB = kChunk / 32;
   int k0 = 0;
   for (; k0 + kChunk <= len; k0 += kChunk)
-    attend_chunk<D, KB>(kh, vh, [&](int kb) -> int64_t { return row0(k0 + kb * 32); }, qf, c2,
-                        br);
+    attend_chunk<D, KB, QB>(kh, vh, [&](int kb) -> int64_t { return row0(k0 + kb * 32); }, qf, c2,
+                            br);
   for (; k0 < len; k0 += 32)                 // a tail of 32-key blocks
-    attend_chunk<D, 1>(kh, vh, [&](int kb) -> int64_t { return row0(k0); }, qf, c2, br);
+    attend_chunk<D, 1, QB>(kh, vh, [&](int kb) -> int64_t { return row0(k0); }, qf, c2, br);
 }
 
 template <int D>
@@ -465,8 +471,8 @@ __global__ __launch_bounds__(64) void bsa_qc_cmp(const float* __restrict__ qc,
   const float c2 = 1.4426950408889634f / sqrtf((float)D);
   Branch<D / 32> br;
   branch_init<D>(br);
-  attend_range<D>(kcb + (int64_t)h * nc * D, vct + (int64_t)h * nc * D,
-                  [&](int key) -> int64_t { return key; }, nc, qf, c2, br);
+  attend_range<D, 1>(kcb + (int64_t)h * nc * D, vct + (int64_t)h * nc * D,
+                     [&](int key) -> int64_t { return key; }, nc, qf, c2, &br);
   store_branch<D>(br, true, ocmp + ((int64_t)h * nc + j) * D);
 }
 
@@ -589,8 +595,10 @@ __global__ __launch_bounds__(64) void bsa_qc_slc(const float* __restrict__ qbar,
 // QC (group compression): only the ball branch runs here; the compression
 // and selection results of the token's block and group come from ocmp and
 // oslc (fp32, computed by bsa_qc_cmp / bsa_qc_slc).
-template <int D, int NWV, bool QC>
-__global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(3, 8) void bsa_fused(
+// A workgroup owns one (group, head); each of its NWV waves owns QB blocks of
+// 32 queries (group = NWV * QB * 32).
+template <int D, int NWV, bool QC, int QB>
+__global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3), 8) void bsa_fused(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ perm,
     const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vtt,
     const uint16_t* __restrict__ kcb, const uint16_t* __restrict__ vct,
@@ -606,130 +614,167 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(3, 8) void bsa_fused(
   if (xcd_map) pair = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
   const int h = pair / ngroups;
   const int g = pair - h * ngroups;
-  const int group = NWV * 32;
+  const int group = NWV * QB * 32;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, c = lane & 31;
   const int64_t rs = (int64_t)H * D;
   if (tid < topk)   // block indices are forced into range like perm entries
     ssel[tid] = (int32_t)perm_index(sel[((int64_t)h * ngroups + g) * topk + tid], nc);
 
-  // queries of this wave: tree positions t0 .. t0+31
-  const int64_t t0 = (int64_t)g * group + w * 32;
-  const int64_t pq = perm_index(perm[t0 + c], N);
-  bf16x8 qf[DS];
+  // queries of this wave: tree positions t0 .. t0 + QB*32 - 1, block qb at
+  // t0 + qb*32 + c for lane column c
+  const int64_t t0 = (int64_t)g * group + w * (QB * 32);
+  int64_t pq[QB];
+  bf16x8 qf[QB * DS];
 #pragma unroll
-  for (int s = 0; s < DS; ++s) qf[s] = *(const bf16x8*)(q + pq * rs + (int64_t)h * D + s * 16 + hf * 8);
-
-  // gates: G = sigmoid(W q + b), one W [3, d] for every head
-  float G0 = gc0, G1 = gc1, G2 = gc2;
-  if (gate_w) {
-    float z0 = 0.f, z1 = 0.f, z2 = 0.f;
+  for (int qb = 0; qb < QB; ++qb) {
+    pq[qb] = perm_index(perm[t0 + qb * 32 + c], N);
 #pragma unroll
     for (int s = 0; s < DS; ++s)
+      qf[qb * DS + s] = *(const bf16x8*)(q + pq[qb] * rs + (int64_t)h * D + s * 16 + hf * 8);
+  }
+
+  // gates: G = sigmoid(W q + b), one W [3, d] for every head
+  float G[QB][3];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dd = s * 16 + hf * 8 + e;
-        const float x = (float)qf[s][e];
-        z0 = fmaf(gate_w[dd], x, z0);
-        z1 = fmaf(gate_w[D + dd], x, z1);
-        z2 = fmaf(gate_w[2 * D + dd], x, z2);
-      }
-    z0 += __shfl_xor(z0, 32, 64);
-    z1 += __shfl_xor(z1, 32, 64);
-    z2 += __shfl_xor(z2, 32, 64);
-    if (gate_b) { z0 += gate_b[0]; z1 += gate_b[1]; z2 += gate_b[2]; }
-    G0 = 1.0f / (1.0f + __expf(-z0));
-    G1 = 1.0f / (1.0f + __expf(-z1));
-    G2 = 1.0f / (1.0f + __expf(-z2));
+  for (int qb = 0; qb < QB; ++qb) {
+    G[qb][0] = gc0;
+    G[qb][1] = gc1;
+    G[qb][2] = gc2;
+    if (gate_w) {
+      float z0 = 0.f, z1 = 0.f, z2 = 0.f;
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int dd = s * 16 + hf * 8 + e;
+          const float x = (float)qf[qb * DS + s][e];
+          z0 = fmaf(gate_w[dd], x, z0);
+          z1 = fmaf(gate_w[D + dd], x, z1);
+          z2 = fmaf(gate_w[2 * D + dd], x, z2);
+        }
+      z0 += __shfl_xor(z0, 32, 64);
+      z1 += __shfl_xor(z1, 32, 64);
+      z2 += __shfl_xor(z2, 32, 64);
+      if (gate_b) { z0 += gate_b[0]; z1 += gate_b[1]; z2 += gate_b[2]; }
+      G[qb][0] = 1.0f / (1.0f + __expf(-z0));
+      G[qb][1] = 1.0f / (1.0f + __expf(-z1));
+      G[qb][2] = 1.0f / (1.0f + __expf(-z2));
+    }
   }
   __syncthreads();   // ssel
 
   const float c2 = 1.4426950408889634f / sqrtf((float)D);
   const uint16_t* kh = kt + (int64_t)h * N * D;
   const uint16_t* vh = vtt + (int64_t)h * N * D;
-  f32x16 acc[DB];
+  f32x16 acc[QB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  Branch<DB> br;
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
+  Branch<DB> br[QB];
 
   // ---- ball branch: the ball holding this group (group | ball) ----------
   {
-    branch_init<D>(br);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) branch_init<D>(br[qb]);
     const int64_t b0 = ((int64_t)g * group / ball) * ball;
-    attend_range<D>(kh, vh, [&](int key) -> int64_t { return b0 + key; }, ball, qf, c2, br);
-    branch_merge<D>(br, G0, acc);
+    attend_range<D, QB>(kh, vh, [&](int key) -> int64_t { return b0 + key; }, ball, qf, c2, br);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) branch_merge<D>(br[qb], G[qb][0], acc[qb]);
   }
   if constexpr (QC) {
     // ---- group compression: the token's block and group results --------
-    const int64_t t = t0 + c;
-    const float* rc = ocmp + ((int64_t)h * nc + t / block) * D;
     const float* rsl = oslc + ((int64_t)h * ngroups + g) * D;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int64_t t = t0 + qb * 32 + c;
+      const float* rc = ocmp + ((int64_t)h * nc + t / block) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const float4 a = *(const float4*)(rc + db * 32 + gq * 8 + hf * 4);
+          const float4 b = *(const float4*)(rsl + db * 32 + gq * 8 + hf * 4);
+          f32x16& x = acc[qb][db];
+          x[gq * 4 + 0] = fmaf(G[qb][2], b.x, fmaf(G[qb][1], a.x, x[gq * 4 + 0]));
+          x[gq * 4 + 1] = fmaf(G[qb][2], b.y, fmaf(G[qb][1], a.y, x[gq * 4 + 1]));
+          x[gq * 4 + 2] = fmaf(G[qb][2], b.z, fmaf(G[qb][1], a.z, x[gq * 4 + 2]));
+          x[gq * 4 + 3] = fmaf(G[qb][2], b.w, fmaf(G[qb][1], a.w, x[gq * 4 + 3]));
+        }
+    }
+  } else {
+    // ---- compression branch: every coarse token ---------------------------
+    {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) branch_init<D>(br[qb]);
+      const uint16_t* kch = kcb + (int64_t)h * nc * D;
+      const uint16_t* vch = vct + (int64_t)h * nc * D;
+      attend_range<D, QB>(kch, vch, [&](int key) -> int64_t { return key; }, nc, qf, c2, br);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) branch_merge<D>(br[qb], G[qb][1], acc[qb]);
+    }
+    // ---- selection branch: the union of the selected blocks ---------------
+    {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) branch_init<D>(br[qb]);
+      attend_range<D, QB>(kh, vh,
+                          [&](int key) -> int64_t {
+                            return (int64_t)ssel[key / block] * block + (key % block);
+                          },
+                          topk * block, qf, c2, br);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) branch_merge<D>(br[qb], G[qb][2], acc[qb]);
+    }
+  }
+
+  // ---- store: lane owns d = db*32 + 8*gq + 4*hf + 0..3 of its query -------
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    uint16_t* orow = out + pq[qb] * rs + (int64_t)h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const float4 a = *(const float4*)(rc + db * 32 + gq * 8 + hf * 4);
-        const float4 b = *(const float4*)(rsl + db * 32 + gq * 8 + hf * 4);
-        acc[db][gq * 4 + 0] = fmaf(G2, b.x, fmaf(G1, a.x, acc[db][gq * 4 + 0]));
-        acc[db][gq * 4 + 1] = fmaf(G2, b.y, fmaf(G1, a.y, acc[db][gq * 4 + 1]));
-        acc[db][gq * 4 + 2] = fmaf(G2, b.z, fmaf(G1, a.z, acc[db][gq * 4 + 2]));
-        acc[db][gq * 4 + 3] = fmaf(G2, b.w, fmaf(G1, a.w, acc[db][gq * 4 + 3]));
+        u32x2 pk;
+        pk[0] = pack_bf16x2(acc[qb][db][gq * 4 + 0], acc[qb][db][gq * 4 + 1]);
+        pk[1] = pack_bf16x2(acc[qb][db][gq * 4 + 2], acc[qb][db][gq * 4 + 3]);
+        *(u32x2*)(orow + db * 32 + gq * 8 + hf * 4) = pk;
       }
-  } else {
-    // ---- compression branch: every coarse token ---------------------------
-    {
-      branch_init<D>(br);
-      const uint16_t* kch = kcb + (int64_t)h * nc * D;
-      const uint16_t* vch = vct + (int64_t)h * nc * D;
-      attend_range<D>(kch, vch, [&](int key) -> int64_t { return key; }, nc, qf, c2, br);
-      branch_merge<D>(br, G1, acc);
-    }
-    // ---- selection branch: the union of the selected blocks ---------------
-    {
-      branch_init<D>(br);
-      attend_range<D>(kh, vh,
-                      [&](int key) -> int64_t {
-                        return (int64_t)ssel[key / block] * block + (key % block);
-                      },
-                      topk * block, qf, c2, br);
-      branch_merge<D>(br, G2, acc);
-    }
   }
-
-  // ---- store: lane owns d = db*32 + 8*gq + 4*hf + 0..3 of query c -------
-  uint16_t* orow = out + pq * rs + (int64_t)h * D;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      u32x2 pk;
-      pk[0] = pack_bf16x2(acc[db][gq * 4 + 0], acc[db][gq * 4 + 1]);
-      pk[1] = pack_bf16x2(acc[db][gq * 4 + 2], acc[db][gq * 4 + 3]);
-      *(u32x2*)(orow + db * 32 + gq * 8 + hf * 4) = pk;
-    }
 }
 
 // ------------------------------------------------------------------ host ----
 template <int D, bool QC>
-static void launch_fused(int nwv, dim3 grid, hipStream_t st, const uint16_t* q,
+static void launch_fused(int group, dim3 grid, hipStream_t st, const uint16_t* q,
                          const int32_t* perm, const uint16_t* kt, const uint16_t* vt,
                          const uint16_t* kcb, const uint16_t* vcb, const int32_t* sel,
                          const float* gw, const float* gb, const float* gc, int32_t H, int64_t N,
                          int32_t nc, int32_t ngroups, int32_t ball, int32_t block, int32_t topk,
                          int32_t xmap, const float* ocmp, const float* oslc, uint16_t* out) {
   const float g0 = gc ? gc[0] : 0.f, g1 = gc ? gc[1] : 0.f, g2 = gc ? gc[2] : 0.f;
-#define BT_FUSED(NW)                                                                          \
-  case NW:                                                                                    \
-    hipLaunchKernelGGL((bsa_fused<D, NW, QC>), grid, dim3(NW * 64), 0, st, q, perm, kt, vt,  \
-                       kcb, vcb, sel, gw, gb, g0, g1, g2, H, N, nc, ngroups, ball, block,     \
-                       topk, xmap, ocmp, oslc, out);                                          \
-    break;
-  switch (nwv) {
-    BT_FUSED(1)
-    BT_FUSED(2)
-    BT_FUSED(4)
-    BT_FUSED(8)
-    default:
-      break;
+#define BT_FUSED(NW, QBB)                                                                     \
+  hipLaunchKernelGGL((bsa_fused<D, NW, QC, QBB>), grid, dim3(NW * 64), 0, st, q, perm, kt,    \
+                     vt, kcb, vcb, sel, gw, gb, g0, g1, g2, H, N, nc, ngroups, ball, block,     \
+                     topk, xmap, ocmp, oslc, out)
+  // d = 32 and groups of 64 or more: each wave owns two 32-query blocks, so
+  // every K and V fragment it loads serves 64 queries (at d = 64 the second
+  // block's state would not fit the registers)
+  if constexpr (D == 32) {
+    switch (group) {
+      case 32: BT_FUSED(1, 1); break;
+      case 64: BT_FUSED(1, 2); break;
+      case 128: BT_FUSED(2, 2); break;
+      case 256: BT_FUSED(4, 2); break;
+      default: break;
+    }
+  } else {
+    switch (group) {
+      case 32: BT_FUSED(1, 1); break;
+      case 64: BT_FUSED(2, 1); break;
+      case 128: BT_FUSED(4, 1); break;
+      case 256: BT_FUSED(8, 1); break;
+      default: break;
+    }
   }
 #undef BT_FUSED
 }
@@ -809,11 +854,10 @@ bt_status bsa_launch(const void* q, const void* k, const void* v, const int32_t*
     if (s != BT_OK) return s;
   }
 
-  const int nwv = p->group / 32;
   const int total = ngroups * H;
   const int xmap = (total % 8 == 0) ? 1 : 0;
 #define BT_FUSED_CALL(DD, QCM)                                                                \
-  launch_fused<DD, QCM>(nwv, dim3(total), st, (const uint16_t*)q, perm, kt, vt, kcb, vcb, sel, \
+  launch_fused<DD, QCM>(p->group, dim3(total), st, (const uint16_t*)q, perm, kt, vt, kcb, vcb, sel, \
                         gate_w, gate_b, gate_const, H, N, nc, ngroups, p->ball, p->block,     \
                         p->topk, xmap, ocmp, oslc, (uint16_t*)out)
   if (d == 32) {
