@@ -24,6 +24,7 @@ namespace bt {
 
 constexpr int kChunk = 64;             // keys per online-softmax step
 constexpr int kSelRegs = 16;           // scores per lane held in registers by select
+constexpr int kSelThreads = 512;       // select: eight waves, one group of a tile each
 
 struct BsaLayout {
   size_t kt, vt, kc32, kcb, vcb, qbar, sel;   // vt, vcb: transposed blocks
@@ -214,9 +215,12 @@ BT_DEV void wave_argmax(float& v, int& i) {
 }
 #undef BT_ARGMAX_DPP
 
-// Workgroup = (head, tile of TG groups).  Scores of the tile live in LDS.
+// Workgroup = (head, tile of TG groups).  Scores of the tile live in LDS;
+// the waves take the tile's groups in turn for the top-k (a chain of
+// dependent wave reductions per group, so one group per wave keeps more of
+// them in flight).
 template <int D>
-__global__ __launch_bounds__(256) void bsa_select(const float* __restrict__ qbar,
+__global__ __launch_bounds__(kSelThreads) void bsa_select(const float* __restrict__ qbar,
                                                   const float* __restrict__ kc32, int32_t H,
                                                   int32_t nc, int32_t ngroups,
                                                   int32_t tg, int32_t group, int32_t ball,
@@ -230,12 +234,12 @@ __global__ __launch_bounds__(256) void bsa_select(const float* __restrict__ qbar
   const int g0 = blockIdx.x * tg;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ng = min(tg, ngroups - g0);
-  for (int i = tid; i < ng * d; i += 256)
+  for (int i = tid; i < ng * d; i += kSelThreads)
     qs[i] = qbar[((int64_t)h * ngroups + g0) * d + i];
   __syncthreads();
   const float scale = 1.0f / sqrtf((float)d);
   const float* kh = kc32 + (int64_t)h * D * nc;   // [d][nc]: lanes read consecutive blocks
-  for (int jb = tid; jb < nc; jb += 256) {
+  for (int jb = tid; jb < nc; jb += kSelThreads) {
     float kr[D];
 #pragma unroll
     for (int e = 0; e < D; ++e) kr[e] = kh[(int64_t)e * nc + jb];
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(256) void bsa_select(const float* __restrict__ qbar
     }
   }
   __syncthreads();
-  for (int g = w; g < ng; g += 4) {
+  for (int g = w; g < ng; g += kSelThreads / 64) {
     float* s = sc + g * nc;
     const int gg = g0 + g;
     if (mask) {
@@ -822,10 +826,10 @@ bt_status bsa_launch(const void* q, const void* k, const void* v, const int32_t*
   const size_t smem = (size_t)(tg * d + tg * nc) * sizeof(float);
   const dim3 gs((ngroups + tg - 1) / tg, H);
   if (d == 32)
-    hipLaunchKernelGGL(bsa_select<32>, gs, dim3(256), smem, st, qbar, kc32, H, nc, ngroups, tg,
+    hipLaunchKernelGGL(bsa_select<32>, gs, dim3(kSelThreads), smem, st, qbar, kc32, H, nc, ngroups, tg,
                        p->group, p->ball, p->block, p->topk, p->mask_own_ball, sel);
   else
-    hipLaunchKernelGGL(bsa_select<64>, gs, dim3(256), smem, st, qbar, kc32, H, nc, ngroups, tg,
+    hipLaunchKernelGGL(bsa_select<64>, gs, dim3(kSelThreads), smem, st, qbar, kc32, H, nc, ngroups, tg,
                        p->group, p->ball, p->block, p->topk, p->mask_own_ball, sel);
   s = launch_status("bsa_select");
   if (s != BT_OK) return s;
