@@ -215,6 +215,38 @@ BT_DEV void wave_argmax(float& v, int& i) {
 }
 #undef BT_ARGMAX_DPP
 
+// (score, block) pairs: a is better than b if its score is larger, or equal
+// with a smaller block index.
+BT_DEV bool sel_better(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+
+// Bitonic sort of one (score, block) pair per lane across the wave, best
+// first: lane 0 ends with the best pair.  Pairs must be distinct.
+BT_DEV void wave_sort_best_first(float& v, int& i) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const float ov = __shfl_xor(v, j, 64);
+      const int oi = __shfl_xor(i, j, 64);
+      // the lower lane of a pair keeps the better pair in a best-first run
+      // (lane & k == 0) and the worse one in a worst-first run
+      const bool keep_better = ((lane & j) == 0) == ((lane & k) == 0);
+      const bool ob = sel_better(ov, oi, v, i);
+      if (ob == keep_better) {
+        v = ov;
+        i = oi;
+      }
+    }
+}
+
+// Lanes below this one with their bit of m set.
+BT_DEV uint32_t sel_lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Workgroup = (head, tile of TG groups).  Scores of the tile live in LDS;
 // the waves take the tile's groups in turn for the top-k (a chain of
 // dependent wave reductions per group, so one group per wave keeps more of
@@ -230,6 +262,7 @@ __global__ __launch_bounds__(kSelThreads) void bsa_select(const float* __restric
   constexpr int d = D;
   float* qs = smem;                    // [tg][d]
   float* sc = smem + tg * d;           // [tg][nc]
+  float* cand = sc + tg * nc;          // [waves][128]: top-k candidates of a wave
   const int h = blockIdx.y;
   const int g0 = blockIdx.x * tg;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -269,18 +302,61 @@ __global__ __launch_bounds__(kSelThreads) void bsa_select(const float* __restric
         const int jb = lane + 64 * i;
         r[i] = jb < nc ? s[jb] : -INFINITY;
       }
-      for (int it = 0; it < topk; ++it) {
-        float v = -INFINITY;
-        int i = 0x7fffffff;
+      // Threshold: the topk-th best of the 64 lane maxima.  At least topk
+      // pairs are as good as it, so every one of the topk best pairs is.
+      float lv = r[0];
+      int li = lane;
+#pragma unroll
+      for (int u = 1; u < kSelRegs; ++u)
+        if (r[u] > lv) { lv = r[u]; li = lane + 64 * u; }  // ascending index: first max kept
+      wave_sort_best_first(lv, li);
+      const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), topk - 1));
+      const int ti = __builtin_amdgcn_readlane(li, topk - 1);
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int u = 0; u < kSelRegs; ++u) cnt += !sel_better(tv, ti, r[u], lane + 64 * u);
+      // exclusive prefix of the candidate counts (at most 16: five bits)
+      uint32_t before = 0, total = 0;
+#pragma unroll
+      for (int bit = 0; bit < 5; ++bit) {
+        const uint64_t m = __ballot((cnt >> bit) & 1u);
+        before += sel_lanes_below(m) << bit;
+        total += (uint32_t)__popcll(m) << bit;
+      }
+      if (total <= 64) {
+        // gather the candidates, one per lane, and sort them: the first
+        // topk lanes hold the selection, best first
+        float* cv = cand + w * 128;
+        int* ci = (int*)(cv + 64);
+        uint32_t pos = before;
 #pragma unroll
         for (int u = 0; u < kSelRegs; ++u)
-          if (r[u] > v) { v = r[u]; i = lane + 64 * u; }   // ascending index: first max kept
-        wave_argmax(v, i);
-        if (lane == 0) sel[((int64_t)h * ngroups + gg) * topk + it] = i;
-        if ((i & 63) == lane) {
+          if (!sel_better(tv, ti, r[u], lane + 64 * u)) {
+            cv[pos] = r[u];
+            ci[pos] = lane + 64 * u;
+            ++pos;
+          }
+        __builtin_amdgcn_wave_barrier();
+        float v = (uint32_t)lane < total ? cv[lane] : -INFINITY;
+        int i = (uint32_t)lane < total ? ci[lane] : 0x40000000 + lane;   // after every block
+        __builtin_amdgcn_wave_barrier();
+        wave_sort_best_first(v, i);
+        if (lane < topk) sel[((int64_t)h * ngroups + gg) * topk + lane] = i;
+      } else {
+        // many pairs tie with the threshold: repeated wave arg-max
+        for (int it = 0; it < topk; ++it) {
+          float v = -INFINITY;
+          int i = 0x7fffffff;
 #pragma unroll
           for (int u = 0; u < kSelRegs; ++u)
-            if (u == (i >> 6)) r[u] = -INFINITY;
+            if (r[u] > v) { v = r[u]; i = lane + 64 * u; }   // ascending index: first max kept
+          wave_argmax(v, i);
+          if (lane == 0) sel[((int64_t)h * ngroups + gg) * topk + it] = i;
+          if ((i & 63) == lane) {
+#pragma unroll
+            for (int u = 0; u < kSelRegs; ++u)
+              if (u == (i >> 6)) r[u] = -INFINITY;
+          }
         }
       }
     } else {
@@ -823,7 +899,7 @@ bt_status bsa_launch(const void* q, const void* k, const void* v, const int32_t*
   int tg = 8192 / nc;                  // scores of a tile: <= 32 KB of LDS
   if (tg > 16) tg = 16;
   if (tg < 1) tg = 1;
-  const size_t smem = (size_t)(tg * d + tg * nc) * sizeof(float);
+  const size_t smem = (size_t)(tg * d + tg * nc + kSelThreads / 64 * 128) * sizeof(float);
   const dim3 gs((ngroups + tg - 1) / tg, H);
   if (d == 32)
     hipLaunchKernelGGL(bsa_select<32>, gs, dim3(kSelThreads), smem, st, qbar, kc32, H, nc, ngroups, tg,
