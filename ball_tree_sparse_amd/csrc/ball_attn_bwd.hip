@@ -191,32 +191,61 @@ __global__ __launch_bounds__(kBwdThreads) void ball_attn_bwd_valu(
 // forward kernel: A[i][kk] lane i + 32*(kk/8) element kk%8, B[kk][j] lane
 // j + 32*(kk/8) element kk%8, C[i][j] lane j + 32*((i/4)%2) element
 // (i/8)*4 + i%4).  One workgroup per (ball, head), one wave per 32 rows.
-// Q, K, V, dO of the ball are staged once into LDS, row-major (padded) and,
-// for K, Q and dO, transposed with bits 2 and 3 of the row index swapped
-// inside each group of 16 (the order in which a C tile feeds a B operand).
-//  query pass (lane = query column): S^T = K Q^T -> row max and sum -> P^T;
-//    D_i = sum_j P_ij dP_ij with dP^T = V dO^T (equal to dO_i . O_i, so O is
-//    not needed); then per 32-key block dP^T again, dS^T = P^T (dP^T - D),
-//    and dQ^T += K^T dS^T.
+// Q, K, V and dO of the ball are staged once into LDS as row-major tiles
+// without padding; the 16-byte pieces of a row are permuted by a function of
+// the row (tile_off) so that both access patterns below are free of bank
+// conflicts:
+//  * row reads (ds_read_b128): a lane reads 8 consecutive d of one row, the
+//    A operand of S^T = K Q^T and similar products;
+//  * transposed reads (ds_read_b64_tr_b16, gfx950): in each 16-lane group,
+//    lane l receives element l%4 of the 8-byte runs addressed by lanes l/4,
+//    l/4+4, l/4+8, l/4+12, so four rows x 16 d become 4 keys for each of 16
+//    d: the K^T, Q^T and dO^T operands, read from the same tiles.
+// Key positions inside a 16-key slice follow the order in which a C tile
+// feeds a B operand (bits 2 and 3 of the position swapped), and the
+// transposed reads fetch rows in that order.
+//  query pass (lane = query column): a first sweep over the key blocks forms
+//    the row maximum, the normaliser and D_i = sum_j P_ij dP_ij with
+//    dP^T = V dO^T (equal to dO_i . O_i, so O is not needed) by an online
+//    rescaling; a second sweep recomputes S^T and dP^T per block, forms
+//    dS^T = P^T (dP^T - D) and accumulates dQ^T += K^T dS^T.  The statistics
+//    go to LDS.
 //  key pass (lane = key column): per 32-query block S = Q K^T, P from the
-//    stored row statistics, dP = dO V^T, dS = P (dP - D); dV^T += dO^T P and
+//    stored statistics, dP = dO V^T, dS = P (dP - D); dV^T += dO^T P and
 //    dK^T += Q^T dS.
 // P and dS are rounded to bf16 for the MFMA; everything else is fp32.
-BT_DEV int bswap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-BT_DEV uint32_t bpair(const u32x4& lo, const u32x4& hi, int e) {
-  return __builtin_amdgcn_perm(hi[e >> 1], lo[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+// Element offset of 16-byte piece p of row r in a row-major LDS tile of D
+// columns.  Sixteen consecutive rows put piece p in sixteen different bank
+// groups, and four consecutive rows starting at a multiple of four cover
+// every bank once per 32-column span.
+template <int D>
+BT_DEV int tile_off(int r, int p) {
+  int f;
+  if constexpr (D == 32) f = (r >> 2) & 3;
+  else f = (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  return r * D + ((p ^ f) << 3);
 }
 
-template <int D, int BALL>
-struct BwdGeom {
-  static constexpr int NW = BALL / 32, NT = NW * 64;
-  static constexpr int KB = BALL / 32, DS = D / 16, DB = D / 32;
-  static constexpr int RS = D + 8;          // row-major stride (bf16)
-  static constexpr int TS = BALL + 8;       // transposed stride (bf16)
-  static constexpr int CPR = D / 8;         // 16-byte pieces per row
-  static constexpr int PIECES = BALL / 2 * CPR;   // two rows per staging piece
-};
+// Four bf16 of a 16-lane transposed read (see above); p points at this
+// lane's 8-byte run in LDS.
+BT_DEV s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((BT_LDS_AS s16x4*)p);
+}
+
+// A operand X^T[d][rows] of a 16-row slice (rows sl*16 ...) and the 32-column
+// block db of a tile: lane L holds d = db*32 + L%32 and the rows 8t + 4*(L/32)
+// + e (t = 0, 1; e = 0..3) of the slice, in that element order.
+template <int D>
+BT_DEV bf16x8 tr_operand(const uint16_t* tile, int sl, int db) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4, s = lane & 15;
+  const int col = db * 32 + 16 * (grp & 1) + 4 * (s & 3);     // this lane's 4 columns
+  const int r0 = sl * 16 + 4 * (grp >> 1) + (s >> 2);
+  const s16x4 a = lds_read_tr16(tile + tile_off<D>(r0, col >> 3) + (col & 4));
+  const s16x4 b = lds_read_tr16(tile + tile_off<D>(r0 + 8, col >> 3) + (col & 4));
+  const s16x8 x = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, x);
+}
 
 // lane (c, hf) holds C^T[d][c] of a 32-column block for d = db*32 + 8*g +
 // 4*hf + 0..3 in acc[db][g*4 + 0..3]; write row `row` (d contiguous) scaled,
@@ -257,134 +286,114 @@ __global__ __launch_bounds__(BALL / 32 * 64) void ball_attn_bwd_mfma(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const int32_t* __restrict__ perm, int64_t N, int32_t H, uint16_t* __restrict__ dq,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
-  using Gm = BwdGeom<D, BALL>;
-  constexpr int NT = Gm::NT, KB = Gm::KB, DS = Gm::DS, DB = Gm::DB, RS = Gm::RS, TS = Gm::TS;
-  constexpr int CPR = Gm::CPR, PIECES = Gm::PIECES;
-  __shared__ __attribute__((aligned(16))) uint16_t ql[BALL * RS], kl[BALL * RS], vl[BALL * RS],
-      dl[BALL * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t qtl[D * TS], ktl[D * TS], dtl[D * TS];
-  __shared__ float smc[BALL], sli[BALL], sdd[BALL];   // m*c2, 1/l, D of every query
+  constexpr int NT = BALL / 32 * 64, KB = BALL / 32, DS = D / 16, DB = D / 32, CPR = D / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t ql[BALL * D], kl[BALL * D], vl[BALL * D],
+      dl[BALL * D];
+  __shared__ __attribute__((aligned(16))) float smc[BALL], sli[BALL], sdd[BALL];
   const int b = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, c = lane & 31;
   const int64_t base = (int64_t)b * BALL, rs = (int64_t)H * D;
   auto row_of = [&](int i) -> int64_t { return perm ? perm_index(perm[base + i], N) : base + i; };
 
-  // ---- stage Q, K, V, dO (row-major) and Q^T, K^T, dO^T (transposed) -------
-  for (int it = tid; it < PIECES; it += NT) {
-    const int kq = it / CPR, dc = it - kq * CPR;
-    const int r0 = kq * 2;
-    const int64_t o0 = row_of(r0) * rs + (int64_t)h * D + dc * 8;
-    const int64_t o1 = row_of(r0 + 1) * rs + (int64_t)h * D + dc * 8;
-    const u32x4 q0 = *(const u32x4*)(q + o0), q1 = *(const u32x4*)(q + o1);
-    const u32x4 k0 = *(const u32x4*)(k + o0), k1 = *(const u32x4*)(k + o1);
-    const u32x4 v0 = *(const u32x4*)(v + o0), v1 = *(const u32x4*)(v + o1);
-    const u32x4 d0 = *(const u32x4*)(dout + o0), d1 = *(const u32x4*)(dout + o1);
-    *(u32x4*)&ql[r0 * RS + dc * 8] = q0;  *(u32x4*)&ql[(r0 + 1) * RS + dc * 8] = q1;
-    *(u32x4*)&kl[r0 * RS + dc * 8] = k0;  *(u32x4*)&kl[(r0 + 1) * RS + dc * 8] = k1;
-    *(u32x4*)&vl[r0 * RS + dc * 8] = v0;  *(u32x4*)&vl[(r0 + 1) * RS + dc * 8] = v1;
-    *(u32x4*)&dl[r0 * RS + dc * 8] = d0;  *(u32x4*)&dl[(r0 + 1) * RS + dc * 8] = d1;
-    const int pos0 = (r0 & ~15) + bswap23(r0 & 15);      // keeps bit 0
+  // ---- stage the ball's rows of Q, K, V, dO ----------------------------------
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      *(uint32_t*)&qtl[(dc * 8 + e) * TS + pos0] = bpair(q0, q1, e);
-      *(uint32_t*)&ktl[(dc * 8 + e) * TS + pos0] = bpair(k0, k1, e);
-      *(uint32_t*)&dtl[(dc * 8 + e) * TS + pos0] = bpair(d0, d1, e);
-    }
+  for (int it = tid; it < BALL * CPR; it += NT) {
+    const int r = it / CPR, p = it - r * CPR;
+    const int64_t o = row_of(r) * rs + (int64_t)h * D + p * 8;
+    const u32x4 a0 = *(const u32x4*)(q + o), a1 = *(const u32x4*)(k + o);
+    const u32x4 a2 = *(const u32x4*)(v + o), a3 = *(const u32x4*)(dout + o);
+    const int t = tile_off<D>(r, p);
+    *(u32x4*)&ql[t] = a0;
+    *(u32x4*)&kl[t] = a1;
+    *(u32x4*)&vl[t] = a2;
+    *(u32x4*)&dl[t] = a3;
   }
   __syncthreads();
   const float c2 = 1.4426950408889634f / sqrtf((float)D);   // log2(e)/sqrt(d)
   const float scale = 1.0f / sqrtf((float)D);
 
-  // ---- query pass: rows w*32 + c are this lane's query ------------------------
+  // ---- query pass: row w*32 + c is this lane's query ---------------------------
   {
     const int qr = w * 32 + c;
     bf16x8 qf[DS], df[DS];
 #pragma unroll
     for (int s2 = 0; s2 < DS; ++s2) {
-      qf[s2] = *(const bf16x8*)&ql[qr * RS + s2 * 16 + hf * 8];
-      df[s2] = *(const bf16x8*)&dl[qr * RS + s2 * 16 + hf * 8];
+      qf[s2] = *(const bf16x8*)&ql[tile_off<D>(qr, s2 * 2 + hf)];
+      df[s2] = *(const bf16x8*)&dl[tile_off<D>(qr, s2 * 2 + hf)];
     }
-    f32x16 pt[KB];                         // S^T, then P^T
+    // S^T and dP^T of key block kb for this lane's query
+    auto blocks = [&](int kb, f32x16& sa, f32x16& pa) {
+      sa = f32x16{};
+      pa = f32x16{};
+#pragma unroll
+      for (int s2 = 0; s2 < DS; ++s2) {
+        const int t = tile_off<D>(kb * 32 + c, s2 * 2 + hf);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&kl[t], qf[s2], sa, 0, 0, 0);
+        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&vl[t], df[s2], pa, 0, 0, 0);
+      }
+    };
+    // sweep 1: maximum (log2 units), normaliser and sum_j p_j dP_j, rescaled
+    // as the maximum grows; both lane halves keep the same running maximum
+    float m = -INFINITY, l = 0.f, dacc = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      f32x16 a = {};
+      f32x16 sa, pa;
+      blocks(kb, sa, pa);
+      float bm = sa[0];
 #pragma unroll
-      for (int s2 = 0; s2 < DS; ++s2)
-        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *(const bf16x8*)&kl[(kb * 32 + c) * RS + s2 * 16 + hf * 8], qf[s2], a, 0, 0, 0);
-      pt[kb] = a;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, pt[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float moff = -mx * c2;
-    float sum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int e = 1; e < 16; ++e) bm = fmaxf(bm, sa[e]);
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64)) * c2;
+      const float mn = fmaxf(m, bm);
+      const float sc = __builtin_amdgcn_exp2f(m - mn);      // 0 on the first block
+      l *= sc;
+      dacc *= sc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(pt[kb][e], c2, moff));
-        pt[kb][e] = p;
-        sum += p;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sa[e], c2, -mn));
+        l += p;
+        dacc = fmaf(p, pa[e], dacc);
       }
-    sum += __shfl_xor(sum, 32, 64);
-    const float inv = 1.0f / sum;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) pt[kb][e] *= inv;
-    // dP^T = V dO^T, block by block
-    auto dpt_block = [&](int kb) -> f32x16 {
-      f32x16 a = {};
-#pragma unroll
-      for (int s2 = 0; s2 < DS; ++s2)
-        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *(const bf16x8*)&vl[(kb * 32 + c) * RS + s2 * 16 + hf * 8], df[s2], a, 0, 0, 0);
-      return a;
-    };
-    float dsum = 0.f;                      // D_i = sum_j P_ij dP_ij
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const f32x16 dp = dpt_block(kb);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) dsum = fmaf(pt[kb][e], dp[e], dsum);
+      m = mn;
     }
-    dsum += __shfl_xor(dsum, 32, 64);
-    if (hf == 0) { smc[qr] = -moff; sli[qr] = inv; sdd[qr] = dsum; }
+    l += __shfl_xor(l, 32, 64);
+    dacc += __shfl_xor(dacc, 32, 64);
+    const float inv = 1.0f / l;
+    const float di = dacc * inv;
+    if (hf == 0) { smc[qr] = m; sli[qr] = inv; sdd[qr] = di; }
+    // sweep 2: dS^T per block, dQ^T += K^T dS^T
     f32x16 gq[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) gq[db] = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const f32x16 dp = dpt_block(kb);
+      f32x16 sa, pa;
+      blocks(kb, sa, pa);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         bf16x8 sf;                         // dS^T operand
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sf[e] = (__bf16)(pt[kb][s2 * 8 + e] * (dp[s2 * 8 + e] - dsum));
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sa[s2 * 8 + e], c2, -m)) * inv;
+          sf[e] = (__bf16)(p * (pa[s2 * 8 + e] - di));
+        }
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          gq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              *(const bf16x8*)&ktl[(db * 32 + c) * TS + (kb * 2 + s2) * 16 + hf * 8], sf, gq[db],
-              0, 0, 0);
+          gq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kl, kb * 2 + s2, db), sf,
+                                                           gq[db], 0, 0, 0);
       }
     }
     store_cols<D>(gq, scale, dq + row_of(qr) * rs + (int64_t)h * D);
   }
   __syncthreads();   // row statistics of every query in LDS
 
-  // ---- key pass: rows w*32 + c are this lane's key ----------------------------
+  // ---- key pass: row w*32 + c is this lane's key -------------------------------
   {
     const int kr = w * 32 + c;
     bf16x8 kf[DS], vf[DS];
 #pragma unroll
     for (int s2 = 0; s2 < DS; ++s2) {
-      kf[s2] = *(const bf16x8*)&kl[kr * RS + s2 * 16 + hf * 8];
-      vf[s2] = *(const bf16x8*)&vl[kr * RS + s2 * 16 + hf * 8];
+      kf[s2] = *(const bf16x8*)&kl[tile_off<D>(kr, s2 * 2 + hf)];
+      vf[s2] = *(const bf16x8*)&vl[tile_off<D>(kr, s2 * 2 + hf)];
     }
     f32x16 gk[DB], gv[DB];
 #pragma unroll
@@ -394,31 +403,34 @@ __global__ __launch_bounds__(BALL / 32 * 64) void ball_attn_bwd_mfma(
       f32x16 sq = {}, dp = {};
 #pragma unroll
       for (int s2 = 0; s2 < DS; ++s2) {
-        sq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *(const bf16x8*)&ql[(qb * 32 + c) * RS + s2 * 16 + hf * 8], kf[s2], sq, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *(const bf16x8*)&dl[(qb * 32 + c) * RS + s2 * 16 + hf * 8], vf[s2], dp, 0, 0, 0);
+        const int t = tile_off<D>(qb * 32 + c, s2 * 2 + hf);
+        sq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&ql[t], kf[s2], sq, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&dl[t], vf[s2], dp, 0, 0, 0);
       }
       // element e is query qb*32 + 8*(e/4) + 4*hf + e%4
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         bf16x8 pf, sf;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ee = s2 * 8 + e;
-          const int qi = qb * 32 + 8 * (ee >> 2) + 4 * hf + (ee & 3);
-          const float p = __builtin_amdgcn_exp2f(fmaf(sq[ee], c2, -smc[qi])) * sli[qi];
-          pf[e] = (__bf16)p;
-          sf[e] = (__bf16)(p * (dp[ee] - sdd[qi]));
+        for (int g4 = 0; g4 < 2; ++g4) {
+          const int q0 = qb * 32 + 16 * s2 + 8 * g4 + 4 * hf;
+          const f32x4 mm = *(const f32x4*)&smc[q0];
+          const f32x4 li = *(const f32x4*)&sli[q0];
+          const f32x4 dd = *(const f32x4*)&sdd[q0];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ee = s2 * 8 + g4 * 4 + i;
+            const float p = __builtin_amdgcn_exp2f(fmaf(sq[ee], c2, -mm[i])) * li[i];
+            pf[g4 * 4 + i] = (__bf16)p;
+            sf[g4 * 4 + i] = (__bf16)(p * (dp[ee] - dd[i]));
+          }
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          gv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              *(const bf16x8*)&dtl[(db * 32 + c) * TS + (qb * 2 + s2) * 16 + hf * 8], pf, gv[db],
-              0, 0, 0);
-          gk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              *(const bf16x8*)&qtl[(db * 32 + c) * TS + (qb * 2 + s2) * 16 + hf * 8], sf, gk[db],
-              0, 0, 0);
+          gv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(dl, qb * 2 + s2, db), pf,
+                                                           gv[db], 0, 0, 0);
+          gk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(ql, qb * 2 + s2, db), sf,
+                                                           gk[db], 0, 0, 0);
         }
       }
     }
@@ -429,8 +441,8 @@ __global__ __launch_bounds__(BALL / 32 * 64) void ball_attn_bwd_mfma(
 }
 
 bool ball_attn_bwd_uses_mfma(bt_dtype dt, int32_t ball, int32_t d) {
-  return dt == BT_BF16 && ((d == 32 && (ball == 32 || ball == 64 || ball == 128)) ||
-                           (d == 64 && (ball == 32 || ball == 64)));
+  return dt == BT_BF16 && (d == 32 || d == 64) &&
+         (ball == 32 || ball == 64 || ball == 128 || ball == 256);
 }
 
 bt_status ball_attn_bwd_launch(const void* q, const void* k, const void* v, const void* dout,
@@ -446,9 +458,12 @@ bt_status ball_attn_bwd_launch(const void* q, const void* k, const void* v, cons
                      (uint16_t*)dv)
     if (d == 32 && ball == 32) BT_BWDM(32, 32);
     else if (d == 32 && ball == 64) BT_BWDM(32, 64);
-    else if (d == 32) BT_BWDM(32, 128);
+    else if (d == 32 && ball == 128) BT_BWDM(32, 128);
+    else if (d == 32) BT_BWDM(32, 256);
     else if (ball == 32) BT_BWDM(64, 32);
-    else BT_BWDM(64, 64);
+    else if (ball == 64) BT_BWDM(64, 64);
+    else if (ball == 128) BT_BWDM(64, 128);
+    else BT_BWDM(64, 256);
 #undef BT_BWDM
     return launch_status("ball_attn_bwd_mfma");
   }

@@ -28,6 +28,7 @@
 #define __forceinline__ inline
 #define __launch_bounds__(x)
 #define BT_WAVES_PER_EU(lo, hi)
+#define BT_LDS_AS
 #define __shared__ static
 #define __restrict__
 
@@ -159,6 +160,25 @@ template <class V>
 inline float __builtin_amdgcn_fdot2_f32_bf16(V a, V b, float c, bool) {
   return (float)((double)c + (double)(float)a[0] * (double)(float)b[0] +
                  (double)(float)a[1] * (double)(float)b[1]); }
+
+// ds_read_b64_tr_b16 (gfx950): in each 16-lane group, lane l receives
+// element l%4 of the 8-byte runs addressed by lanes l/4, l/4+4, l/4+8, l/4+12
+// (the layout measured on the device).
+typedef short emu_s16x4 __attribute__((ext_vector_type(4)));
+inline emu_s16x4 __builtin_amdgcn_ds_read_tr16_b64_v4i16(emu_s16x4* p) {
+  const int t = emu_tid(), base = t & ~63, l = t & 63, grp = l & ~15, li = l & 15;
+  uint64_t u;
+  memcpy(&u, p, 8);
+  g_blk->xch[t] = u;
+  emu_wave_sync();
+  emu_s16x4 r;
+  for (int e = 0; e < 4; ++e) {
+    const uint64_t w = g_blk->xch[base + grp + li / 4 + 4 * e];
+    r[e] = (short)((w >> (16 * (li % 4))) & 0xffffu);
+  }
+  emu_wave_sync();
+  return r;
+}
 
 // ---- dynamic LDS -----------------------------------------------------------
 extern unsigned char* g_dyn_lds;

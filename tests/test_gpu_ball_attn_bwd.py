@@ -25,8 +25,11 @@ TOL = {"bf16": 2e-2, "f32": 2e-5}
     (1536, 2, 32, 64, "bf16"),
     (2048, 2, 64, 64, "bf16"),
     (1024, 3, 64, 32, "bf16"),
-    (2048, 2, 64, 256, "bf16"),     # ... VALU kernel again (ball above 64 at d = 64)
-    (1024, 2, 16, 64, "bf16"),
+    (4096, 2, 64, 128, "bf16"),
+    (4096, 2, 32, 256, "bf16"),
+    (2048, 2, 64, 256, "bf16"),
+    (2048, 2, 32, 512, "bf16"),     # ... VALU kernel again (ball above 256)
+    (1024, 2, 16, 64, "bf16"),      # d = 16: VALU kernel
 ])
 def test_parity(n, H, d, ball, dtype):
     dev = gpu()

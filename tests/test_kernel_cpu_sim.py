@@ -171,9 +171,10 @@ def test_bsa_kernels(sim, qc):
 
 @pytest.mark.parametrize("n,H,d,ball,dtype", [(512, 2, 32, 128, "bf16"), (256, 2, 32, 32, "bf16"),
                                              (256, 1, 64, 64, "bf16"), (384, 2, 32, 64, "bf16"),
+                                             (256, 1, 64, 128, "bf16"), (512, 1, 32, 256, "bf16"),
                                              (256, 2, 16, 64, "bf16"), (256, 2, 32, 32, "f32")])
 def test_ball_attn_bwd_kernels(sim, n, H, d, ball, dtype):
-    """Backward: the MFMA kernel (bf16, d 32 or 64, ball up to 128 or 64) and
+    """Backward: the MFMA kernel (bf16, d 32 or 64, balls of 32 to 256) and
     the VALU kernel (the rest)."""
     d_ = sim["dir"]
     rng = np.random.default_rng(3 * n + d + ball)
