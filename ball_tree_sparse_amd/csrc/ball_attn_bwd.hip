@@ -290,7 +290,14 @@ __global__ __launch_bounds__(BALL / 32 * 64) void ball_attn_bwd_mfma(
   __shared__ __attribute__((aligned(16))) uint16_t ql[BALL * D], kl[BALL * D], vl[BALL * D],
       dl[BALL * D];
   __shared__ __attribute__((aligned(16))) float smc[BALL], sli[BALL], sdd[BALL];
-  const int b = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  // Workgroups go round-robin to the 8 XCDs (the grid is a multiple of 8 when
+  // the item count is): XCD x runs items x*total/8 ... in order, so the heads
+  // of one ball, which share the 128-byte lines of its rows, are fetched
+  // through the same L2 at about the same time.
+  const int total = (int)gridDim.x;
+  const int item = (total & 7) ? (int)blockIdx.x
+                               : ((int)blockIdx.x & 7) * (total >> 3) + ((int)blockIdx.x >> 3);
+  const int b = item / H, h = item - (item / H) * H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, c = lane & 31;
   const int64_t base = (int64_t)b * BALL, rs = (int64_t)H * D;
   auto row_of = [&](int i) -> int64_t { return perm ? perm_index(perm[base + i], N) : base + i; };

@@ -406,6 +406,9 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter scaling)")
     ap.add_argument("--copy-probe-mb", type=int, default=128)
+    ap.add_argument("--rows-only", action="store_true",
+                    help="time only the other rows (permute, coarsen/refine, BSA, padded "
+                         "attention, backward, small trees); for kernel traces and counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -416,6 +419,16 @@ def main():
     from ball_tree_sparse_amd import ops, synth
     ops.lib()                                  # fail loudly if the library is missing
     dev = torch.device("cuda:0")
+    if args.rows_only:
+        if args.copy_probe:
+            src = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
+            dst = torch.empty_like(src)
+            for _ in range(4):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+        print(json.dumps({"rows": side_rows(dev, torch, ops, synth)}), flush=True)
+        return
     if args.workload == "bsa":
         line = bench_bsa(args, dev, torch, ops, synth)
     else:
