@@ -190,7 +190,7 @@ struct AttnGeom {
 
 template <int D, int BALL, int HPW, bool PERM, bool PIPE, bool MASK>
 __global__ __launch_bounds__(BALL / 32 * 64)
-BT_WAVES_PER_EU((BALL >= 256 ? 2 : (PIPE ? 3 : 4)), 8)
+BT_WAVES_PER_EU((BALL >= 256 ? (D == 32 ? 4 : 2) : (PIPE ? 3 : 4)), 8)
 void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const int32_t* __restrict__ perm,
                     int64_t nrows, int32_t H, int32_t nballs, int32_t xcd_map,
@@ -310,67 +310,93 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     uint16_t* orow0 = out + row_of(rc.q) * rs + (int64_t)rc.h0 * D;
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      // ---- S^T = K Q^T ----------------------------------------------------
-      f32x16 sacc[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        f32x16 a = {};
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          const bf16x8 kf = *(const bf16x8*)&ks[hh][(kb * 32 + c) * KS + s * 16 + hf * 8];
-          a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qc[hh][s], a, 0, 0, 0);
-        }
-        sacc[kb] = a;
-      }
-      if constexpr (MASK) {
-        // element e holds key kb*32 + 8*(e/4) + 4*hf + e%4
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const uint32_t ok4 = *(const uint32_t*)&kok[kb * 32 + 8 * g + 4 * hf];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (!((ok4 >> (8 * i)) & 0xffu)) sacc[kb][g * 4 + i] = -INFINITY;
-          }
-      }
-      // ---- softmax over the keys of query column c ------------------------
-      // Four independent chains for the maximum and the sum.
-      float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
-      float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float moff = -mx * c2;
-      bf16x8 pf[KB][2];                // P^T operands, rounded once
-      float s4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pf[kb][s2][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][s2 * 8 + e], c2, moff));
-          s4[(kb * 2 + s2) & 3] = sum_bf16x8(pf[kb][s2], s4[(kb * 2 + s2) & 3]);
-        }
-      float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-      sum += __shfl_xor(sum, 32, 64);
-      // ---- O^T = V^T P^T ----------------------------------------------------
+      // Keys go in chunks of CH 32-key blocks with an online softmax: one
+      // chunk for balls up to 128; 64-key chunks for 256-point balls keep a
+      // wave's score and probability registers small enough for two
+      // workgroups per CU.
+      constexpr int CH = BALL >= 256 ? 2 : KB;
       f32x16 oacc[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};   // four chains of the normaliser
+      float mrun = -INFINITY;               // running maximum (raw scores)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int c0 = 0; c0 < KB; c0 += CH) {
+        // ---- S^T = K Q^T --------------------------------------------------
+        f32x16 sacc[CH];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+        for (int kb = 0; kb < CH; ++kb) {
+          f32x16 a = {};
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 vf =
-                *(const bf16x8*)&vt[hh][(db * 32 + c) * VTS + (kb * 2 + s2) * 16 + hf * 8];
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][s2], oacc[db], 0, 0, 0);
+          for (int s = 0; s < DS; ++s) {
+            const bf16x8 kf =
+                *(const bf16x8*)&ks[hh][((c0 + kb) * 32 + c) * KS + s * 16 + hf * 8];
+            a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qc[hh][s], a, 0, 0, 0);
           }
+          sacc[kb] = a;
+        }
+        if constexpr (MASK) {
+          // element e holds key kb*32 + 8*(e/4) + 4*hf + e%4
+#pragma unroll
+          for (int kb = 0; kb < CH; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const uint32_t ok4 = *(const uint32_t*)&kok[(c0 + kb) * 32 + 8 * g + 4 * hf];
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (!((ok4 >> (8 * i)) & 0xffu)) sacc[kb][g * 4 + i] = -INFINITY;
+            }
+        }
+        // ---- softmax over the keys of query column c ----------------------
+        // Four independent chains for the maximum and the sum.
+        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int kb = 0; kb < CH; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
+        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float moff = -mx * c2;
+        if constexpr (CH < KB) {
+          const float mn = fmaxf(mrun, mx);
+          // nothing to rescale before the first chunk with a key; a chunk
+          // whose keys are all unused slots leaves the maximum at -inf
+          const float alpha =
+              mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mrun - mn) * c2);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s4[i] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+          mrun = mn;
+          moff = mn == -INFINITY ? 0.f : -mn * c2;
+        }
+        bf16x8 pf[CH][2];                // P^T operands, rounded once
+#pragma unroll
+        for (int kb = 0; kb < CH; ++kb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              pf[kb][s2][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][s2 * 8 + e], c2, moff));
+            s4[(kb * 2 + s2) & 3] = sum_bf16x8(pf[kb][s2], s4[(kb * 2 + s2) & 3]);
+          }
+        // ---- O^T += V^T P^T -------------------------------------------------
+#pragma unroll
+        for (int kb = 0; kb < CH; ++kb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const bf16x8 vf = *(const bf16x8*)&vt[hh][(db * 32 + c) * VTS +
+                                                        ((c0 + kb) * 2 + s2) * 16 + hf * 8];
+              oacc[db] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][s2], oacc[db], 0, 0, 0);
+            }
+      }
+      float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      sum += __shfl_xor(sum, 32, 64);
       // ---- normalise, regroup across the lane halves, store 16-byte runs ---
       // Lane (c, hf) holds d = db*32 + 8*g + 4*hf + 0..3 for g = 0..3.  After
       // one exchange with lane c^32, the hf = 0 lane holds d 0-7 and 16-23
@@ -503,9 +529,10 @@ static bt_status launch_mfma(const void* q, const void* k, const void* v, const 
   const int nb = (int)(nslots / BB);
   const int total = nb * (H / HPW);
   const int xmap = (total % 8 == 0) ? 1 : 0;
-  // the masked kernel runs one item per workgroup: its persistent form would
-  // need more registers than three waves per SIMD allow
-  const int g = MASK ? total : attn_grid(total);
+  // the masked kernel and 256-point balls run one item per workgroup: their
+  // persistent form would need more registers than the waves per SIMD that
+  // hide the gathers allow (256-point balls: two 8-wave workgroups per CU)
+  const int g = (MASK || BB >= 256) ? total : attn_grid(total);
   const bool pipe = g < total;
   dim3 grid(g), block(BB / 32 * 64);
 #define BT_MF(PERM, PIPE, MK)                                                                \
@@ -514,6 +541,9 @@ static bt_status launch_mfma(const void* q, const void* k, const void* v, const 
                      H, nb, xmap, (uint16_t*)out)
   if constexpr (MASK) {
     BT_MF(true, false, true);
+  } else if constexpr (BB >= 256) {
+    if (perm) BT_MF(true, false, false);
+    else BT_MF(false, false, false);
   } else if (perm) {
     if (pipe) BT_MF(true, true, false);
     else BT_MF(true, false, false);
