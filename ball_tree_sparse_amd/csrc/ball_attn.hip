@@ -555,9 +555,8 @@ static bt_status launch_mfma(const void* q, const void* k, const void* v, const 
   return launch_status("ball_attn_mfma");
 }
 
-// Head pairs for balls up to 128 points when H is even; single heads
-// otherwise (a 256-point ball already holds 32 score registers per lane, and
-// a second head's staging registers would spill).
+// Head pairs when H is even (for 256-point balls only at d = 32); single
+// heads otherwise.
 template <int D, bool MASK>
 static bt_status launch_mfma_d(const void* q, const void* k, const void* v, const int32_t* perm,
                                int64_t nrows, int64_t nslots, int32_t ball, int32_t H, void* out,
@@ -573,7 +572,10 @@ static bt_status launch_mfma_d(const void* q, const void* k, const void* v, cons
     case 128:
       return pair ? launch_mfma<D, 128, 2, MASK>(q, k, v, perm, nrows, nslots, H, out, st)
                   : launch_mfma<D, 128, 1, MASK>(q, k, v, perm, nrows, nslots, H, out, st);
-    case 256:
+    case 256:   // head pairs at d = 32 (at d = 64 their LDS would leave one workgroup per CU)
+      if constexpr (D == 32) {
+        if (pair) return launch_mfma<D, 256, 2, MASK>(q, k, v, perm, nrows, nslots, H, out, st);
+      }
       return launch_mfma<D, 256, 1, MASK>(q, k, v, perm, nrows, nslots, H, out, st);
     default:
       return BT_EINVAL;

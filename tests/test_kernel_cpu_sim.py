@@ -106,6 +106,7 @@ def _read_out(path, n, H, d, dtype):
 
 
 @pytest.mark.parametrize("n,H,d,ball,dtype", [(1024, 2, 32, 128, "bf16"), (1024, 1, 32, 256, "bf16"),
+                                             (512, 2, 32, 256, "bf16"),
                                              (256, 3, 32, 32, "bf16"), (512, 1, 64, 256, "bf16"),
                                              (512, 2, 64, 64, "bf16"), (2048, 4, 32, 64, "bf16"),
                                              (1024, 6, 64, 128, "bf16"),
