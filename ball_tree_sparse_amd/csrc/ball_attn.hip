@@ -506,17 +506,28 @@ static bt_status launch_valu(const void* q, const void* k, const void* v, const 
 // per CU measured best among 3 to 8 in steps of a half.
 constexpr int kGridPerCu = 5;
 
-static int attn_grid(int total) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
+// CU count of the current device, cached per device (a relaxed atomic per
+// slot: concurrent first calls store the same value).
+static int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static int cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    const int c = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (c > 0) return c;
   }
-  int g = cus * kGridPerCu;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  if (cached) __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+  return n;
+}
+
+static int attn_grid(int total) {
+  int g = device_cus() * kGridPerCu;
   g -= g % 8;
   if (g < 8) g = 8;
   return total < g ? total : g;

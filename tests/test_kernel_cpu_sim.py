@@ -250,3 +250,24 @@ def test_ball_attn_padded_kernels(sim, n, H, d, ball, dtype):
     out = _read_out(d_ / "out.bin", n, H, d, dtype)
     err = np.abs(out - A.ball_attn_padded(q, k, v, perm, ball)).max()
     assert err <= (2e-2 if dtype == "bf16" else 1e-5), err
+
+
+@pytest.mark.parametrize("mode,ball,dtype", [("ball", 128, "bf16"), ("ball", 64, "f32"),
+                                             ("bwd", 128, "bf16"), ("bwd", 32, "f32")])
+def test_out_of_range_perm_stays_in_bounds(sim, mode, ball, dtype):
+    """A 'permutation' with entries far outside [0, N) (negative and huge):
+    every kernel that reads rows through it forces the indices into range,
+    so AddressSanitizer sees no access outside q/k/v/dO or the outputs."""
+    d_ = sim["dir"]
+    n, H, d = 512, 2, 32
+    rng = np.random.default_rng(77)
+    ts = [synth.normal_features(rng, n, H, d, dtype) for _ in range(4)]
+    for t, nm in zip(ts, ("q.bin", "k.bin", "v.bin", "do.bin")):
+        _dump(t, d_ / nm)
+    perm = rng.integers(-2**31, 2**31 - 1, size=n, dtype=np.int64).astype(np.int32)
+    perm[:8] = [-1, n, n + 1, 2**31 - 1, -2**31, 0, n - 1, 7]
+    perm.tofile(d_ / "perm.bin")
+    r = subprocess.run([sim["attn"], mode, str(n), str(H), str(d), str(ball),
+                        "1" if dtype == "bf16" else "0"], cwd=d_, capture_output=True,
+                       text=True, timeout=600)
+    assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
