@@ -72,6 +72,8 @@ def _run(q, k, v, perm, W, ball, block, group, topk, mask, gate_const=None, qc=F
     (8192, 2, 32, 64, 32, 32, 5, True, None),
     (4096, 1, 32, 128, 32, 64, 64, True, None),       # 64 blocks selected
     (65536, 1, 32, 64, 32, 32, 8, True, None),        # 2,048 blocks: scores kept in LDS
+    (8192, 2, 32, 256, 64, 128, 8, True, None),       # two 64-query waves per group
+    (8192, 2, 32, 256, 128, 256, 4, False, None),     # four 64-query waves per group
 ])
 def test_parity(n, H, d, ball, block, group, topk, mask, gates):
     _, q, k, v, W, perm = _setup(n, H, d, seed=n + H + d + topk, leaf=block)

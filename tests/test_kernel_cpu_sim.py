@@ -144,11 +144,12 @@ def test_ball_attn_kernel_tree_order_input(sim):
     assert np.abs(out - A.ball_attn(q, k, v, None, ball)).max() <= 2e-2
 
 
-@pytest.mark.parametrize("qc", [0, 1])
-def test_bsa_kernels(sim, qc):
-    """BSA, and BSA with group compression (qc = 1)."""
+@pytest.mark.parametrize("qc,group", [(0, 64), (1, 64), (0, 128)])
+def test_bsa_kernels(sim, qc, group):
+    """BSA, and BSA with group compression (qc = 1); group 128 runs two waves
+    of 64 queries per workgroup."""
     d_ = sim["dir"]
-    n, H, d, ball, block, group, topk = 2048, 2, 32, 128, 64, 64, 4
+    n, H, d, ball, block, topk = 2048, 2, 32, 128, 64, 4
     rng = np.random.default_rng(5)
     c = synth.deformed_sphere(rng, n)
     q, k, v = (synth.normal_features(rng, n, H, d, "bf16") for _ in range(3))
