@@ -518,42 +518,69 @@ BT_DEV void pooled_query_frags(const float* __restrict__ row, bf16x8* qf) {
   }
 }
 
-// O / l of a finished branch for the lane's query column, written as fp32
-// where `write` holds (every lane takes part in the exchange): lane (c, hf)
-// holds d = db*32 + 8*g + 4*hf + 0..3.
-template <int D>
-BT_DEV void store_branch(const Branch<D / 32>& br, bool write, float* __restrict__ row) {
-  const int hf = (threadIdx.x & 63) >> 5;
-  float l = (br.l[0] + br.l[1]) + (br.l[2] + br.l[3]);
-  l += __shfl_xor(l, 32, 64);
-  const float f = __builtin_amdgcn_rcpf(l);
-  if (!write) return;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *(float4*)(row + db * 32 + g * 8 + hf * 4) =
-          make_float4(br.o[db][g * 4] * f, br.o[db][g * 4 + 1] * f, br.o[db][g * 4 + 2] * f,
-                      br.o[db][g * 4 + 3] * f);
-}
+// Compression branch of group compression: 32 block-mean queries of a head
+// per workgroup, all attending to every coarse token.  The coarse tokens are
+// split into kQcWaves contiguous ranges (multiples of 32), one per wave, and
+// the waves' partial results (running maximum, normaliser, unnormalised
+// output) are merged through LDS.  Grid (nc/32, H).
+constexpr int kQcWaves = 4;
 
-// Compression branch of group compression: one wave per 32 block-mean
-// queries of a head, all attending to every coarse token.  Grid (nc/32, H).
 template <int D>
-__global__ __launch_bounds__(64) void bsa_qc_cmp(const float* __restrict__ qc,
-                                                 const uint16_t* __restrict__ kcb,
-                                                 const uint16_t* __restrict__ vct, int32_t nc,
-                                                 float* __restrict__ ocmp) {
-  const int h = blockIdx.y, c = threadIdx.x & 31;
+__global__ __launch_bounds__(kQcWaves * 64) void bsa_qc_cmp(const float* __restrict__ qc,
+                                                            const uint16_t* __restrict__ kcb,
+                                                            const uint16_t* __restrict__ vct,
+                                                            int32_t nc,
+                                                            float* __restrict__ ocmp) {
+  constexpr int DB = D / 32;
+  __shared__ float pm[kQcWaves][64], pl[kQcWaves][64], po[kQcWaves][DB * 16][64];
+  const int h = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31;
   const int64_t j = (int64_t)blockIdx.x * 32 + c;          // this lane's coarse query
   bf16x8 qf[D / 16];
   pooled_query_frags<D>(qc + ((int64_t)h * nc + j) * D, qf);
   const float c2 = 1.4426950408889634f / sqrtf((float)D);
-  Branch<D / 32> br;
+  Branch<DB> br;
   branch_init<D>(br);
+  const int seg = ((nc / 32 + kQcWaves - 1) / kQcWaves) * 32;  // keys per wave
+  const int k0 = w * seg, len = max(0, min(nc - k0, seg));
   attend_range<D, 1>(kcb + (int64_t)h * nc * D, vct + (int64_t)h * nc * D,
-                     [&](int key) -> int64_t { return key; }, nc, qf, c2, &br);
-  store_branch<D>(br, true, ocmp + ((int64_t)h * nc + j) * D);
+                     [&](int key) -> int64_t { return k0 + key; }, len, qf, c2, &br);
+  float l = (br.l[0] + br.l[1]) + (br.l[2] + br.l[3]);
+  l += __shfl_xor(l, 32, 64);
+  pm[w][lane] = br.m;
+  pl[w][lane] = l;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) po[w][db * 16 + e][lane] = br.o[db][e];
+  __syncthreads();
+  if (w != 0) return;
+  float mt = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kQcWaves; ++u) mt = fmaxf(mt, pm[u][lane]);
+  float lt = 0.f, f[kQcWaves];
+#pragma unroll
+  for (int u = 0; u < kQcWaves; ++u) {
+    // a wave without keys has m = -inf and contributes nothing
+    f[u] = pm[u][lane] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pm[u][lane] - mt);
+    lt = fmaf(f[u], pl[u][lane], lt);
+  }
+  const float inv = __builtin_amdgcn_rcpf(lt);
+  const int hf = lane >> 5;
+  float* row = ocmp + ((int64_t)h * nc + j) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a = 0.f;
+#pragma unroll
+        for (int u = 0; u < kQcWaves; ++u) a = fmaf(f[u], po[u][db * 16 + g * 4 + i][lane], a);
+        x[i] = a * inv;
+      }
+      *(float4*)(row + db * 32 + g * 8 + hf * 4) = make_float4(x[0], x[1], x[2], x[3]);
+    }
 }
 
 // Selection branch of group compression: one wave per (group, head) and a
@@ -922,11 +949,11 @@ bt_status bsa_launch(const void* q, const void* k, const void* v, const int32_t*
                        qc);
     const dim3 gcm(nc / 32, H), gsl(ngroups, H);
     if (d == 32) {
-      hipLaunchKernelGGL(bsa_qc_cmp<32>, gcm, dim3(64), 0, st, qc, kcb, vcb, nc, ocmp);
+      hipLaunchKernelGGL(bsa_qc_cmp<32>, gcm, dim3(kQcWaves * 64), 0, st, qc, kcb, vcb, nc, ocmp);
       hipLaunchKernelGGL(bsa_qc_slc<32>, gsl, dim3(64), 0, st, qbar, kt, vt, sel, N, nc, ngroups,
                          p->block, p->topk, oslc);
     } else {
-      hipLaunchKernelGGL(bsa_qc_cmp<64>, gcm, dim3(64), 0, st, qc, kcb, vcb, nc, ocmp);
+      hipLaunchKernelGGL(bsa_qc_cmp<64>, gcm, dim3(kQcWaves * 64), 0, st, qc, kcb, vcb, nc, ocmp);
       hipLaunchKernelGGL(bsa_qc_slc<64>, gsl, dim3(64), 0, st, qbar, kt, vt, sel, N, nc, ngroups,
                          p->block, p->topk, oslc);
     }
