@@ -324,8 +324,12 @@ def side_rows(dev, torch, ops, synth):
                      warm=100)
     nb = w.coords.shape[0]
     bflops = 4 * nb * w.ball * w.d * w.H * 2.5        # S, dP, dV, dQ, dK (2.5x the forward)
+    bbytes = 7 * nb * w.H * w.d * 2 + 4 * nb     # q, k, v, dO gathered; dq, dk, dv scattered
     rows["f4_ball_attn_bwd"] = {"workload": "N=65536, ball 128, H=8, d=32 bf16",
-                                "us": us_b, "tflops": bflops / (us_b * 1e-6) / 1e12}
+                                "us": us_b, "tflops": bflops / (us_b * 1e-6) / 1e12,
+                                "GBps": bbytes / us_b / 1e3,
+                                "hbm_frac": bbytes / us_b / 1e3 / HBM_PEAK_GBS,
+                                "mfma_frac": bflops / (us_b * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
     del gq, gk, gv, gdo, grads
     # tree build + fp32 ball attention at 1,024 points
     w = synth.make("tiny")
@@ -338,7 +342,8 @@ def side_rows(dev, torch, ops, synth):
     us_b = _event_us(torch, lambda: ops.bt_build(c, w.leaf, perm=pt, workspace=tws), 200)
     us_a = _event_us(torch, lambda: ops.ball_attn(q, k, v, pt, w.ball, out=ot), 200)
     rows["a1_a4_a6_tiny"] = {"workload": "N=1024 uniform cube, leaf = ball 32, H=4, d=16 fp32",
-                             "build_us": us_b, "ball_attn_us": us_a}
+                             "build_us": us_b, "ball_attn_us": us_a,
+                             "bound": "latency (one workgroup; 16 KB of records)"}
     # padded tree of an uneven N: 972 points (the Elasticity cloud size), leaf 32
     c9 = c[:972].contiguous()
     tws9 = torch.empty(max(256, ops.lib().bt_build_padded_workspace_size(972, 32)),
@@ -346,7 +351,7 @@ def side_rows(dev, torch, ops, synth):
     pt9 = torch.empty(ops.bt_padded_size(972, 32), dtype=torch.int32, device=dev)
     us_p = _event_us(torch, lambda: ops.bt_build_padded(c9, 32, perm=pt9, workspace=tws9), 200)
     rows["f3_tree_padded"] = {"workload": "N=972 uniform cube in 1,024 slots, leaf 32",
-                              "build_us": us_p}
+                              "build_us": us_p, "bound": "latency (one workgroup)"}
     return rows
 
 
