@@ -566,13 +566,15 @@ static bt_status launch_mfma(const void* q, const void* k, const void* v, const 
   return launch_status("ball_attn_mfma");
 }
 
-// Head pairs when H is even (for 256-point balls only at d = 32); single
-// heads otherwise.
+// Head pairs when H is even: at d = 32 two heads' slices of a row are one
+// 128-byte line.  At d = 64 one head's slice already is a line, and from
+// 128-point balls on a pair's registers leave one wave per SIMD, so single
+// heads run there (65,536 points, 8 heads, ball 128: 69 us against 84 us).
 template <int D, bool MASK>
 static bt_status launch_mfma_d(const void* q, const void* k, const void* v, const int32_t* perm,
                                int64_t nrows, int64_t nslots, int32_t ball, int32_t H, void* out,
                                hipStream_t st) {
-  const bool pair = H % 2 == 0;
+  const bool pair = H % 2 == 0 && (D == 32 || ball <= 64);
   switch (ball) {
     case 32:
       return pair ? launch_mfma<D, 32, 2, MASK>(q, k, v, perm, nrows, nslots, H, out, st)
