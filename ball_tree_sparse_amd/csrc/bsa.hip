@@ -25,6 +25,7 @@ namespace bt {
 constexpr int kChunk = 64;             // keys per online-softmax step
 constexpr int kSelRegs = 16;           // scores per lane held in registers by select
 constexpr int kSelThreads = 512;       // select: eight waves, one group of a tile each
+constexpr float kLazyLog2 = 8.0f;      // online softmax: rescale only past 2^8
 
 struct BsaLayout {
   size_t kt, vt, kc32, kcb, vcb, qbar, sel;   // vt, vcb: transposed blocks
@@ -445,15 +446,22 @@ BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __rest
       for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
     float cm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * c2;
     cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-    const float mn = fmaxf(b.m, cm);
-    const float alpha = __builtin_amdgcn_exp2f(b.m - mn);     // 0 on the first chunk
+    // The running maximum is raised (and the state rescaled) only when a
+    // chunk maximum exceeds it by more than kLazyLog2, for every lane of the
+    // wave at once; the weights then stay below 2^kLazyLog2, and the
+    // normalised result is the same up to rounding.
+    if (__ballot(cm > b.m + kLazyLog2)) {
+      const float mn = fmaxf(b.m, cm);
+      const float alpha = __builtin_amdgcn_exp2f(b.m - mn);   // 0 on the first chunk
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b.l[i] *= alpha;
+      for (int i = 0; i < 4; ++i) b.l[i] *= alpha;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) b.o[db][e] *= alpha;
-    b.m = mn;
+        for (int e = 0; e < 16; ++e) b.o[db][e] *= alpha;
+      b.m = mn;
+    }
+    const float mn = b.m;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
