@@ -154,6 +154,17 @@ def bench_ball(args, dev, torch, ops, synth):
     g1.record()
     torch.cuda.synchronize()
     graph_us = g0.elapsed_time(g1) * 1e3 / (reps * len(sets))
+    # single launches, each between its own pair of events with the device
+    # idle before it: median and minimum of 60 (no back-to-back overlap)
+    single = []
+    for i in range(60):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        step(i)
+        a1.record()
+        torch.cuda.synchronize()
+        single.append(a0.elapsed_time(a1) * 1e3)
+    single.sort()
 
     esize = 2 if w.dtype == "bf16" else 4
     attn_bytes = 4 * N * H * d * esize + 4 * N
@@ -177,6 +188,7 @@ def bench_ball(args, dev, torch, ops, synth):
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": attn_bytes},
         "ball_attn": {"us": attn_us, "us_graph_replay": graph_us,
+                      "us_single_median": single[len(single) // 2], "us_single_min": single[0],
                       "points_per_s": N / (attn_us * 1e-6),
                       "tflops": attn_flops / (attn_us * 1e-6) / 1e12,
                       "mfma_frac": attn_flops / (attn_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
