@@ -15,8 +15,9 @@
 //   per level while the node size n is above kFinish (= 1024 points):
 //     hist<p>     radix-select of the median key on the split axis, 11/11/10
 //                 bit digits of the order-preserving uint32 key (p = 0,1,2).
-//                 Workgroups own 1-4K point chunks of one node, build an LDS
-//                 histogram and add it to the node's global histogram.
+//                 Workgroups own equal chunks of one node (the node halved
+//                 down to at most 1-4K points while its size is even), build
+//                 an LDS histogram and add it to the node's global histogram.
 //     select<p>   one workgroup per node scans that histogram, fixes the next
 //                 digit of the pivot (and, at p = 0, the split axis) and
 //                 clears the histogram.
@@ -281,9 +282,13 @@ __global__ __launch_bounds__(kThreads) void tree_scatter(
   uint32_t rmin[3] = {~0u, ~0u, ~0u}, rmax[3] = {0u, 0u, 0u};
   const float4* r = rec + (int64_t)c * chunk;
   for (int base = 0; base < chunk; base += kThreads) {
-    const float4 x = r[base + tid];
+    // a chunk need not be a multiple of the workgroup: the valid lanes of
+    // the last round are its first chunk - base threads
+    const bool valid = base + tid < chunk;
+    const int nvalid = min(kThreads, chunk - base);
+    const float4 x = valid ? r[base + tid] : make_float4(0.f, 0.f, 0.f, 0.f);
     const uint32_t key = float_key(comp(x, axis));
-    const bool is_lt = key < pivot, is_eq = key == pivot;
+    const bool is_lt = valid && key < pivot, is_eq = valid && key == pivot;
     const uint64_t blt = __ballot(is_lt), beq = __ballot(is_eq);
     const uint32_t lt_ex = mbcnt64(blt);
     const uint32_t eq_ex = mbcnt64(beq);
@@ -304,15 +309,16 @@ __global__ __launch_bounds__(kThreads) void tree_scatter(
                               : nstart + half + Rrun + ((uint32_t)tid - left_p);
     // ranks are consistent by construction; the guard keeps a broken
     // invariant from ever writing outside the node
-    if (dest >= nstart && dest < nstart + nsize) out[dest] = x;
+    if (valid && dest >= nstart && dest < nstart + nsize) out[dest] = x;
     const uint32_t k3[3] = {float_key(x.x), float_key(x.y), float_key(x.z)};
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
+      if (!valid) continue;
       if (left) { lmin[a] = min(lmin[a], k3[a]); lmax[a] = max(lmax[a], k3[a]); }
       else { rmin[a] = min(rmin[a], k3[a]); rmax[a] = max(rmax[a], k3[a]); }
     }
     Lrun += left_tot;
-    Rrun += kThreads - left_tot;
+    Rrun += (uint32_t)nvalid - left_tot;
     E += eqt;
     __syncthreads();
   }
@@ -725,11 +731,15 @@ struct TreePlan {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Points per chunk of a node of nsize = leaf * 2^k points: nsize halved while
+// it is even and above the target, so that the chunks tile every node
+// exactly.  A chunk is above half the target, or odd and above it.
 static int chunk_for(int64_t n_total, int64_t nsize) {
-  int64_t c = 1024;
-  if (n_total >= (int64_t)1 << 19) c = 4096;
-  else if (n_total >= (int64_t)1 << 18) c = 2048;
-  if (c > nsize) c = nsize;
+  int64_t target = 1024;
+  if (n_total >= (int64_t)1 << 19) target = 4096;
+  else if (n_total >= (int64_t)1 << 18) target = 2048;
+  int64_t c = nsize;
+  while (c > target && (c & 1) == 0) c >>= 1;
   return (int)c;
 }
 
@@ -753,7 +763,11 @@ static TreePlan plan_tree(int64_t n, int leaf) {
   p.off_ext1 = o; o = align256(o + nodes_next * 6 * 4);
   p.off_hist = o; o = align256(o + nodes_max * kBins * 4);
   p.off_state = o; o = align256(o + nodes_max * sizeof(NodeState));
-  const size_t max_chunks = (size_t)(n / 1024 + 1);
+  size_t max_chunks = 1;
+  for (int lev = 0; lev < G; ++lev) {
+    const size_t nc = (size_t)(n / chunk_for(n, n >> lev));
+    if (nc > max_chunks) max_chunks = nc;
+  }
   p.off_counts = o; o = align256(o + max_chunks * 8);
   p.off_part = o; o = align256(o + max_chunks * 12 * 4);
   p.total = o;

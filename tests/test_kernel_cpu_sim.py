@@ -65,7 +65,8 @@ def _tree(sim, coords, leaf, R=None):
 
 
 @pytest.mark.parametrize("case", ["cube4k_leaf32", "lattice2k_leaf8", "signed_zeros2k_leaf2",
-                                  "mixture4k_leaf16", "leaf2048"])
+                                  "mixture4k_leaf16", "leaf2048", "cube3k_leaf3",
+                                  "cube4000_leaf1000"])
 def test_tree_kernels_bit_exact(sim, case):
     rng = np.random.default_rng(31)
     if case == "cube4k_leaf32":
@@ -79,8 +80,12 @@ def test_tree_kernels_bit_exact(sim, case):
         leaf = 2
     elif case == "mixture4k_leaf16":
         c, leaf = synth.gaussian_mixture(rng, 4096, k=16), 16
-    else:
+    elif case == "leaf2048":
         c, leaf = synth.uniform_cube(rng, 4096), 2048
+    elif case == "cube3k_leaf3":          # 1,536-point nodes: not a multiple of 1,024
+        c, leaf = synth.uniform_cube(rng, 3 << 10), 3
+    else:                                 # chunks that are not a multiple of 256
+        c, leaf = synth.uniform_cube(rng, 4000), 1000
     assert np.array_equal(_tree(sim, c, leaf), T.build(c, leaf))
 
 
