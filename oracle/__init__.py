@@ -17,6 +17,7 @@ Modules
 ``bsa``        brute-force Ball Sparse Attention: ball, compression and
                selection branches merged by sigmoid gates (and the group
                compression variant), in fp64.
+``bsa_bwd``    gradients of BSA (dq, dk, dv and the gate parameters), in fp64.
 ``pool``       coarsening (means of consecutive tree positions) and refinement.
 ``checks``     tree invariant checkers (plain and padded), independent of
                ``tree``.
