@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbtsparse.so")
 SOURCES = ["api.hip", "ball_attn.hip", "ball_attn_bwd.hip", "permute.hip", "tree.hip", "bsa.hip",
-           "pool.hip"]
+           "bsa_bwd.hip", "pool.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

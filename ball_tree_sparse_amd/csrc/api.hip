@@ -61,6 +61,13 @@ bt_status bsa_launch(const void* q, const void* k, const void* v, const int32_t*
                      const float* gate_b, const float* gate_const, int32_t* sel_out, void* ws,
                      void* out, hipStream_t st);
 
+size_t bsa_bwd_ws_size(int64_t N, int32_t H, int32_t d, const bsa_params* p);
+bt_status bsa_bwd_launch(const void* q, const void* k, const void* v, const int32_t* perm,
+                         const void* dout, int64_t N, int32_t H, int32_t d, const bsa_params* p,
+                         const float* gate_w, const float* gate_b, const float* gate_const,
+                         void* dq, void* dk, void* dv, float* dgate_w, float* dgate_b, void* ws,
+                         hipStream_t st);
+
 static bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 // Largest N that bt_build / bt_rotate_build accept (see build_common).
@@ -395,6 +402,54 @@ bt_status bsa_attn(const void* q, const void* k, const void* v, const int32_t* p
   }
   return bsa_launch(q, k, v, perm, N, H, d, p, gate_w, gate_b, gate_const_host, sel_out, ws, out,
                     (hipStream_t)stream);
+}
+
+size_t bsa_attn_bwd_workspace_size(int64_t N, int32_t H, int32_t d, const bsa_params* p) {
+  if (check_bsa(N, H, d, p) != BT_OK || p->query_compression != 0) return 0;
+  return bsa_bwd_ws_size(N, H, d, p);
+}
+
+bt_status bsa_attn_bwd(const void* q, const void* k, const void* v, const int32_t* perm,
+                       const void* dout, int64_t N, int32_t H, int32_t d, bt_dtype dt,
+                       const bsa_params* p, const float* gate_w, const float* gate_b,
+                       const float* gate_const_host, void* dq, void* dk, void* dv,
+                       float* dgate_w, float* dgate_b, void* ws, size_t ws_bytes, void* stream) {
+  BT_REQUIRE(q && k && v && perm && dout && dq && dk && dv,
+             "q, k, v, perm, dout, dq, dk and dv must be non-null");
+  BT_REQUIRE(dt == BT_BF16, "bsa_attn_bwd supports bf16 inputs");
+  bt_status s = check_bsa(N, H, d, p);
+  if (s != BT_OK) return s;
+  BT_REQUIRE(p->query_compression == 0,
+             "bsa_attn_bwd does not cover group compression (query_compression must be 0)");
+  BT_REQUIRE((gate_w == nullptr) != (gate_const_host == nullptr),
+             "give exactly one of gate_w and gate_const");
+  BT_REQUIRE(gate_w || (dgate_w == nullptr && dgate_b == nullptr),
+             "constant gates have no parameter gradients: dgate_w and dgate_b must be NULL");
+  if (gate_const_host)
+    for (int i = 0; i < 3; ++i)
+      BT_REQUIRE(gate_const_host[i] == gate_const_host[i], "gate_const must not be NaN");
+  const size_t bytes = (size_t)(N * H * d) * 2;
+  const void* ins[5] = {q, k, v, dout, nullptr};
+  void* outs[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      BT_REQUIRE(!overlaps(outs[i], bytes, ins[j], bytes),
+                 "dq, dk and dv must not alias q, k, v or dout");
+    for (int j = i + 1; j < 3; ++j)
+      BT_REQUIRE(!overlaps(outs[i], bytes, outs[j], bytes), "dq, dk and dv must not overlap");
+  }
+  BT_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)dout | (uintptr_t)dq |
+              (uintptr_t)dk | (uintptr_t)dv) % 16 == 0,
+             "bf16 tensors must be 16-byte aligned");
+  BT_REQUIRE(ws != nullptr && ((uintptr_t)ws & 255) == 0,
+             "workspace must be non-null and 256-byte aligned");
+  const size_t need = bsa_bwd_ws_size(N, H, d, p);
+  if (ws_bytes < need) {
+    set_error("workspace holds %zu bytes, bsa_attn_bwd needs %zu", ws_bytes, need);
+    return BT_ENOMEM;
+  }
+  return bsa_bwd_launch(q, k, v, perm, dout, N, H, d, p, gate_w, gate_b, gate_const_host, dq, dk,
+                        dv, dgate_w, dgate_b, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

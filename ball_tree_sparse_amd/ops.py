@@ -65,6 +65,11 @@ _SIGS = [
                             _P]),
     ("ball_attn_bwd", C.c_int, [_P, _P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32,
                                 C.c_int32, C.c_int, _P, _P, _P, _P]),
+    ("bsa_attn_bwd_workspace_size", C.c_size_t, [C.c_int64, C.c_int32, C.c_int32,
+                                                 C.POINTER(BsaParams)]),
+    ("bsa_attn_bwd", C.c_int, [_P, _P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int,
+                               C.POINTER(BsaParams), _P, _P, C.POINTER(C.c_float), _P, _P, _P,
+                               _P, _P, _P, C.c_size_t, _P]),
     ("bt_padded_size", C.c_int64, [C.c_int64, C.c_int32]),
     ("bt_build_padded_workspace_size", C.c_size_t, [C.c_int64, C.c_int32]),
     ("bt_build_padded", C.c_int, [_P, C.c_int64, C.c_int32, C.POINTER(C.c_float), _P, _P,
@@ -340,6 +345,12 @@ def bsa_workspace_size(N: int, H: int, d: int, ball: int, block: int, group: int
     return lib().bsa_workspace_size(N, H, d, C.byref(p))
 
 
+def bsa_attn_bwd_workspace_size(N: int, H: int, d: int, ball: int, block: int, group: int,
+                                topk: int, mask_own_ball: bool = True) -> int:
+    p = BsaParams(ball, block, group, topk, int(bool(mask_own_ball)), 0)
+    return lib().bsa_attn_bwd_workspace_size(N, H, d, C.byref(p))
+
+
 def bsa_attn(q, k, v, perm, ball: int, block: int, group: int, topk: int,
              mask_own_ball: bool = True, gate_w=None, gate_b=None, gate_const=None,
              return_sel: bool = False, out=None, workspace=None,
@@ -373,3 +384,45 @@ def bsa_attn(q, k, v, perm, ball: int, block: int, group: int, topk: int,
                           C.byref(p), _ptr(gate_w), _ptr(gate_b), gc, _ptr(sel),
                           _ptr(workspace), workspace.numel(), _ptr(out), _stream(q.device)))
     return (out, sel) if return_sel else out
+
+
+def bsa_attn_bwd(q, k, v, perm, dout, ball: int, block: int, group: int, topk: int,
+                 mask_own_ball: bool = True, gate_w=None, gate_b=None, gate_const=None,
+                 grads=None, workspace=None):
+    """Backward of BSA (without group compression): returns (dq, dk, dv,
+    dgate_w, dgate_b); the gate gradients are None with ``gate_const``.
+    ``grads`` optionally gives the (dq, dk, dv) tensors to write."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _dev(t, name, q.dtype)
+        if t.shape != q.shape or t.dim() != 3:
+            raise ValueError("q, k, v, dout must share one [N,H,d] shape")
+    _dev(perm, "perm", torch.int32)
+    N, H, d = q.shape
+    p = BsaParams(ball, block, group, topk, int(bool(mask_own_ball)), 0)
+    if gate_w is not None:
+        _dev(gate_w, "gate_w", torch.float32)
+    if gate_b is not None:
+        _dev(gate_b, "gate_b", torch.float32)
+    gc = None
+    dgw = dgb = None
+    if gate_const is not None:
+        gc = (C.c_float * 3)(*[float(x) for x in gate_const])
+    else:
+        dgw = torch.empty((3, d), dtype=torch.float32, device=q.device)
+        dgb = torch.empty(3, dtype=torch.float32, device=q.device)
+    if grads is None:
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    else:
+        dq, dk, dv = grads
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            _dev(t, name, q.dtype)
+            if t.shape != q.shape:
+                raise ValueError(f"{name} must have the shape of q")
+    need = lib().bsa_attn_bwd_workspace_size(N, H, d, C.byref(p))
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    _check(lib().bsa_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(dout), N, H, d,
+                              _dtype_code(q), C.byref(p), _ptr(gate_w), _ptr(gate_b), gc,
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgw), _ptr(dgb),
+                              _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return dq, dk, dv, dgw, dgb

@@ -302,7 +302,21 @@ def side_rows(dev, torch, ops, synth):
         "workload": "as a7_a11_bsa, queries pooled before compression and selection",
         "us_per_step": us2, "points_per_s": N / (us2 * 1e-6),
         "tflops": flops2 / (us2 * 1e-6) / 1e12, "speedup_vs_bsa": us / us2}
-    del q, k, v, out, bws, bws2
+    # backward of BSA (no group compression) at the same size
+    bdo = q.clone()
+    bgr = [torch.empty_like(q) for _ in range(3)]
+    bws3 = torch.empty(ops.bsa_attn_bwd_workspace_size(N, H, d, w.ball, x["block"], x["group"],
+                                                       x["topk"]),
+                       dtype=torch.uint8, device=dev)
+    us4 = _event_us(torch, lambda: ops.bsa_attn_bwd(q, k, v, p, bdo, w.ball, x["block"],
+                                                    x["group"], x["topk"], x["mask_own_ball"],
+                                                    gate_w=Wg, grads=bgr, workspace=bws3),
+                    30, warm=5)
+    rows["f4_bsa_bwd"] = {"workload": "as a7_a11_bsa: dq, dk, dv and the gate gradients",
+                          "us": us4, "tflops": 2.5 * flops / (us4 * 1e-6) / 1e12,
+                          "mfma_frac": 2.5 * flops / (us4 * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+                          "vs_forward": us4 / us}
+    del q, k, v, out, bws, bws2, bws3, bdo, bgr
     # uneven N: 65,000 sphere points in 65,536 slots (535 unused slots spread
     # over the balls), masked ball attention; three input sets rotate
     n3, slots = 65000, 65536

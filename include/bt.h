@@ -268,6 +268,39 @@ bt_status bsa_attn(const void* q, const void* k, const void* v,
                    int32_t* sel_out, void* ws, size_t ws_bytes, void* out,
                    void* stream);
 
+/* ------------------------------------------------------------------------
+ * Backward of BSA without group compression (the branches and the gates are
+ * learned: Pith review of arXiv 2506.12541, "What carries the argument").
+ * For the output gradient dout [N,H,d] (original order, bf16) it writes
+ *   dq, dk, dv [N,H,d] bf16 in original order, and with learned gates
+ *   dgate_w [3,d] and dgate_b [3] (fp32 device; either may be NULL to skip
+ *   it; both must be NULL with gate_const).
+ * Every branch is softmax attention with output gradient G_i dout; the
+ * gates give dG_i = dout . O_i and, when learned, dz_i = dG_i G_i (1 - G_i)
+ * with dq += sum_i dz_i W[i], dW[i] = sum_{t,h} dz_i q_{t,h} and db[i] =
+ * sum_{t,h} dz_i.  Compression passes dKc[j] / block to every token of block
+ * j; selected blocks collect the gradient of every group that selected them.
+ * The top-k selection passes no gradient: it is recomputed exactly as the
+ * forward's and held fixed.  P, dS and G*P are rounded to bf16 for the
+ * matrix products; everything else accumulates in fp32.
+ * Arguments and requirements as bsa_attn, plus p->query_compression == 0;
+ * dq, dk and dv must not overlap each other or q, k, v, dout, and must be
+ * 16-byte aligned.  ws: device workspace of at least
+ * bsa_attn_bwd_workspace_size() bytes (0 for invalid parameters), 256-byte
+ * aligned.  Errors: BT_EINVAL for a violated requirement or a null pointer;
+ * BT_ENOMEM for a short workspace; BT_EHIP if a launch fails.  Asynchronous
+ * on stream; allocates nothing.
+ * ---------------------------------------------------------------------- */
+size_t bsa_attn_bwd_workspace_size(int64_t N, int32_t H, int32_t d,
+                                   const bsa_params* p);
+bt_status bsa_attn_bwd(const void* q, const void* k, const void* v,
+                       const int32_t* perm, const void* dout, int64_t N,
+                       int32_t H, int32_t d, bt_dtype dt, const bsa_params* p,
+                       const float* gate_w, const float* gate_b,
+                       const float* gate_const_host, void* dq, void* dk,
+                       void* dv, float* dgate_w, float* dgate_b, void* ws,
+                       size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

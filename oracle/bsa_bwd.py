@@ -54,12 +54,14 @@ def attn_bwd(Q, K, V, dO):
 
 
 def bsa_bwd(q, k, v, dout, perm, ball: int, block: int, group: int, topk: int,
-            mask_own_ball: bool = True, W=None, b=None, gate_const=None):
+            mask_own_ball: bool = True, W=None, b=None, gate_const=None, sel_override=None):
     """(dq, dk, dv, dW, db) of BSA (without group compression) for ``dout``.
 
     Inputs and gradients are [N,H,d] in original order (``perm`` is the tree
     permutation, or None for tree order).  dW [3,d] and db [3] are None with
-    constant gates.
+    constant gates.  ``sel_override`` ([H, N/g, k*]) replaces the oracle's own
+    top-k choice, as in ``oracle.bsa.bsa`` (a numerical near-tie admits
+    another valid set).
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
     n, H, d = q.shape
@@ -102,7 +104,10 @@ def bsa_bwd(q, k, v, dout, perm, ball: int, block: int, group: int, topk: int,
     dvt += np.repeat(th(dVc), block, axis=0) / block
 
     # selection branch: each group over the union of its selected blocks
-    sel, _ = select(qt, kc, ball, block, group, topk, mask_own_ball)
+    if sel_override is None:
+        sel, _ = select(qt, kc, ball, block, group, topk, mask_own_ball)
+    else:
+        sel = np.asarray(sel_override)
     dO2 = G[..., 2:3] * dot
     r = np.arange(block)
     for h in range(H):

@@ -16,7 +16,7 @@ void emu_launch(dim3 grid, dim3 block, size_t shm, const std::function<void()>& 
   // launch; workgroups run one after another
   std::barrier<> outer(nt + 1);
   std::vector<std::unique_ptr<EmuBlock>> blocks;
-  const unsigned nblk = grid.x * grid.y;
+  const unsigned nblk = grid.x * grid.y * grid.z;
   for (unsigned b = 0; b < nblk; ++b) {
     auto eb = std::make_unique<EmuBlock>();
     eb->block_bar = std::make_unique<std::barrier<>>(nt);
@@ -31,7 +31,7 @@ void emu_launch(dim3 grid, dim3 block, size_t shm, const std::function<void()>& 
       for (unsigned b = 0; b < nblk; ++b) {
         outer.arrive_and_wait();                 // workgroup b may start
         threadIdx = {t, 0, 0};
-        blockIdx = {b % grid.x, b / grid.x, 0};
+        blockIdx = {b % grid.x, (b / grid.x) % grid.y, b / (grid.x * grid.y)};
         body();
         // a finished thread leaves this workgroup's barriers
         g_blk->block_bar->arrive_and_drop();

@@ -121,6 +121,37 @@ def test_bsa_rejects(L):
     assert L.bsa_workspace_size(4096, 2, 32, C.byref(P(100, 64, 64, 4, 1))) == 0
 
 
+def test_bsa_bwd_rejects(L):
+    # distinct, 256-byte aligned stand-ins, each as large as a [4096, 2, 32] bf16 tensor
+    bufs = [C.create_string_buffer(4096 * 2 * 32 * 2 + 512) for _ in range(9)]
+    a = [C.c_void_p((C.addressof(b) + 255) & ~255) for b in bufs]
+    q, k, v, perm, do, dq, dk, dv, ws = a
+    P = ops.BsaParams
+    gc = (C.c_float * 3)(1, 0, 0)
+    gw = _fake(3 * 32 * 4)
+
+    def call(params=None, N=4096, H=2, d=32, dt=ops.BT_BF16, gates=(None, gc), grads=(None, None),
+             outs=(dq, dk, dv), wsb=1 << 30):
+        params = params or P(128, 64, 64, 4, 1, 0)
+        return L.bsa_attn_bwd(q, k, v, perm, do, N, H, d, dt, C.byref(params), gates[0], None,
+                              gates[1], outs[0], outs[1], outs[2], grads[0], grads[1], ws, wsb,
+                              None)
+    assert call(dt=ops.BT_F32) == ops.BT_EINVAL
+    assert call(P(128, 64, 64, 4, 1, 1)) == ops.BT_EINVAL          # group compression
+    assert call(P(128, 48, 64, 4, 1, 0)) == ops.BT_EINVAL          # block not multiple of 32
+    assert call(d=16) == ops.BT_EINVAL
+    assert call(gates=(gw, gc)) == ops.BT_EINVAL                   # both gates given
+    assert call(gates=(None, None)) == ops.BT_EINVAL               # no gate
+    assert call(grads=(gw, None)) == ops.BT_EINVAL                 # constant gates: no dW
+    assert call(outs=(q, dk, dv)) == ops.BT_EINVAL                 # dq is q
+    assert call(outs=(dq, dq, dv)) == ops.BT_EINVAL                # dk is dq
+    assert call(outs=(dq, dk, None)) == ops.BT_EINVAL
+    assert call(wsb=4096) == ops.BT_ENOMEM
+    assert L.bsa_attn_bwd_workspace_size(4096, 2, 32, C.byref(P(128, 64, 64, 4, 1, 0))) > \
+        L.bsa_workspace_size(4096, 2, 32, C.byref(P(128, 64, 64, 4, 1, 0)))
+    assert L.bsa_attn_bwd_workspace_size(4096, 2, 32, C.byref(P(128, 64, 64, 4, 1, 1))) == 0
+
+
 def test_coarsen_refine_reject(L):
     x, o = _fake(1 << 16), _fake(1 << 16)
     for f in (L.bt_coarsen, L.bt_refine):

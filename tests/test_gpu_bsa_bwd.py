@@ -1,0 +1,112 @@
+"""GPU parity of bsa_attn_bwd (BSA backward, no group compression) against
+the fp64 oracle.  The backward recomputes the forward's selection; where the
+GPU's top-k set differs from the oracle's it must be a near-tie (as in the
+forward's tests) and the oracle then uses the GPU's set."""
+import numpy as np
+import pytest
+import torch
+
+from ball_tree_sparse_amd import ops, synth
+from oracle import bsa as B
+from oracle import bsa_bwd as BB
+from oracle import tree as T
+from tests.helpers import gpu, max_abs, say
+from tests.test_gpu_bsa import _check_sel
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _setup(n, H, d, seed, leaf, wscale=0.2):
+    rng = np.random.default_rng(seed)
+    c = synth.deformed_sphere(rng, n)
+    q, k, v, do = [synth.normal_features(rng, n, H, d, "bf16") for _ in range(4)]
+    W = (wscale * rng.standard_normal((3, d))).astype(np.float32)
+    b = (0.5 * rng.standard_normal(3)).astype(np.float32)
+    perm = T.build(c, leaf)
+    return q, k, v, do, W, b, perm
+
+
+def _run(q, k, v, do, perm, W, b, ball, block, group, topk, mask, gate_const):
+    dev = gpu()
+    qd, kd, vd, dd = (t.to(dev) for t in (q, k, v, do))
+    pd = torch.from_numpy(np.asarray(perm, np.int32)).to(dev)
+    Wd = None if gate_const is not None else torch.from_numpy(W).to(dev)
+    bd = None if (gate_const is not None or b is None) else torch.from_numpy(b).to(dev)
+    _, sel = ops.bsa_attn(qd, kd, vd, pd, ball, block, group, topk, mask, gate_w=Wd, gate_b=bd,
+                          gate_const=gate_const, return_sel=True)
+    g = ops.bsa_attn_bwd(qd, kd, vd, pd, dd, ball, block, group, topk, mask, gate_w=Wd,
+                         gate_b=bd, gate_const=gate_const)
+    torch.cuda.synchronize()
+    return [x.cpu() if x is not None else None for x in g], sel.cpu().numpy()
+
+
+def _selection(q, k, v, perm, W, b, ball, block, group, topk, mask, gate_const, sel_gpu):
+    _, parts = B.bsa(q, k, v, perm, ball, block, group, topk, mask,
+                     W=None if gate_const is not None else W,
+                     b=None if gate_const is not None else b, gate_const=gate_const,
+                     return_parts=True)
+    use, amb = _check_sel(sel_gpu, parts, topk)
+    return use, amb
+
+
+@pytest.mark.parametrize("n,H,d,ball,block,group,topk,mask,gates", [
+    (4096, 2, 32, 128, 64, 64, 4, True, None),
+    (4096, 2, 32, 128, 64, 64, 4, True, (0.3, 0.5, 0.7)),
+    (4096, 2, 32, 128, 64, 64, 4, True, (0.0, 1.0, 0.0)),    # compression only
+    (4096, 2, 32, 128, 64, 64, 4, True, (0.0, 0.0, 1.0)),    # selection only
+    (4096, 3, 32, 128, 32, 32, 6, False, None),              # one-wave groups, no mask
+    (8192, 2, 32, 256, 64, 256, 5, True, None),              # eight-wave groups
+    (4096, 2, 64, 128, 64, 128, 4, True, None),              # d = 64
+    (2048, 1, 64, 64, 32, 64, 3, True, (1.0, 0.0, 0.0)),     # ball only
+])
+def test_parity(n, H, d, ball, block, group, topk, mask, gates):
+    q, k, v, do, W, b, perm = _setup(n, H, d, seed=n + 7 * H + d + topk, leaf=block)
+    say("bsa_attn_bwd", n, H, d, ball, block, group, topk, mask, gates)
+    (dq, dk, dv, dw, db), sel = _run(q, k, v, do, perm, W, b, ball, block, group, topk, mask,
+                                     gates)
+    use, amb = _selection(q, k, v, perm, W, b, ball, block, group, topk, mask, gates, sel)
+    want = BB.bsa_bwd(q, k, v, do, perm, ball, block, group, topk, mask,
+                      W=None if gates else W, b=None if gates else b, gate_const=gates,
+                      sel_override=use)
+    for name, got, w in zip("qkv", (dq, dk, dv), want[:3]):
+        assert max_abs(got, w) <= TOL, name
+    if gates is None:
+        for got, w in ((dw, want[3]), (db, want[4])):
+            assert np.abs(got.numpy() - w).max() <= TOL * max(1.0, np.abs(w).max())
+    else:
+        assert dw is None and db is None
+
+
+def test_deterministic():
+    q, k, v, do, W, b, perm = _setup(4096, 2, 32, seed=3, leaf=64)
+    say("bsa_attn_bwd determinism")
+    a, _ = _run(q, k, v, do, perm, W, b, 128, 64, 64, 4, True, None)
+    c, _ = _run(q, k, v, do, perm, W, b, 128, 64, 64, 4, True, None)
+    for x, y in zip(a, c):
+        assert torch.equal(x, y)
+
+
+def test_bsa_workload_full_size_two_heads():
+    """The 65,536-point BSA workload (ball 128, block 64, group 64, top-16,
+    W ~ N(0, 0.02^2)) on all 8 heads; heads 0 and 5 are compared element by
+    element with the oracle run on those heads alone (heads are independent;
+    dW and db sum over every head and are covered by the smaller cases)."""
+    w = synth.make("bsa")
+    x = w.extra
+    rng = np.random.default_rng(1234)
+    do = synth.normal_features(rng, w.coords.shape[0], w.H, w.d, "bf16")
+    perm = T.build(w.coords, w.leaf)
+    say("bsa_attn_bwd full size")
+    (dq, dk, dv, _, _), sel = _run(w.q, w.k, w.v, do, perm, w.gate_w, None, w.ball, x["block"],
+                                   x["group"], x["topk"], True, None)
+    hs = [0, 5]
+    sub = lambda t: t[:, hs].contiguous()
+    use, amb = _selection(sub(w.q), sub(w.k), sub(w.v), perm, w.gate_w, None, w.ball, x["block"],
+                          x["group"], x["topk"], True, None, sel[hs])
+    print(f"ambiguous top-k rows: {amb}")
+    want = BB.bsa_bwd(sub(w.q), sub(w.k), sub(w.v), sub(do), perm, w.ball, x["block"],
+                      x["group"], x["topk"], True, W=w.gate_w, sel_override=use)
+    for name, got, ref in zip("qkv", (dq, dk, dv), want[:3]):
+        assert max_abs(got[:, hs], ref) <= TOL, name

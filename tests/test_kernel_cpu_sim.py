@@ -20,6 +20,7 @@ from ball_tree_sparse_amd import synth
 from oracle import attention as A
 from oracle import attention_bwd as AB
 from oracle import bsa as B
+from oracle import bsa_bwd as BB
 from oracle import tree as T
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,13 +34,14 @@ def sim(tmp_path_factory):
     if not os.path.exists(CXX):
         pytest.skip("clang++ not available")
     d = tmp_path_factory.mktemp("cpu_sim")
-    flags = ["-std=c++20", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer",
+    flags = ["-std=c++20", "-O1", "-fsanitize=address", "-fno-omit-frame-pointer",
              "-I", SIM, "-I", os.path.join(ROOT, "include")]
     bins = {}
     procs = []
-    for name, src in (("tree", "tree_driver.cpp"), ("attn", "attn_driver.cpp")):
+    for name, src, extra in (("tree", "tree_driver.cpp", []), ("attn", "attn_driver.cpp", []),
+                             ("bsa_bwd", "attn_driver.cpp", ["-DBT_SIM_BSA_BWD"])):
         out = str(d / name)
-        procs.append(subprocess.Popen([CXX, *flags, os.path.join(SIM, src),
+        procs.append(subprocess.Popen([CXX, *flags, *extra, os.path.join(SIM, src),
                                        os.path.join(SIM, "emu.cpp"), "-o", out, "-lpthread"],
                                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
                                       text=True))
@@ -65,8 +67,8 @@ def _tree(sim, coords, leaf, R=None):
 
 
 @pytest.mark.parametrize("case", ["cube4k_leaf32", "lattice2k_leaf8", "signed_zeros2k_leaf2",
-                                  "mixture4k_leaf16", "leaf2048", "cube3k_leaf3",
-                                  "cube4000_leaf1000"])
+                                  "mixture4k_leaf16", "leaf2048", "cube1536_leaf3",
+                                  "cube2000_leaf1000"])
 def test_tree_kernels_bit_exact(sim, case):
     rng = np.random.default_rng(31)
     if case == "cube4k_leaf32":
@@ -82,10 +84,10 @@ def test_tree_kernels_bit_exact(sim, case):
         c, leaf = synth.gaussian_mixture(rng, 4096, k=16), 16
     elif case == "leaf2048":
         c, leaf = synth.uniform_cube(rng, 4096), 2048
-    elif case == "cube3k_leaf3":          # 1,536-point nodes: not a multiple of 1,024
-        c, leaf = synth.uniform_cube(rng, 3 << 10), 3
+    elif case == "cube1536_leaf3":        # a 1,536-point node: not a multiple of 1,024
+        c, leaf = synth.uniform_cube(rng, 3 << 9), 3
     else:                                 # chunks that are not a multiple of 256
-        c, leaf = synth.uniform_cube(rng, 4000), 1000
+        c, leaf = synth.uniform_cube(rng, 2000), 1000
     assert np.array_equal(_tree(sim, c, leaf), T.build(c, leaf))
 
 
@@ -174,6 +176,45 @@ def test_bsa_kernels(sim, qc, group):
                        query_compression=bool(qc))
     assert np.array_equal(np.sort(sel, -1), np.sort(parts["sel"], -1))
     assert np.abs(out - ref).max() <= 2e-2
+
+
+@pytest.mark.parametrize("n,d,block,group,gm", [(1024, 32, 32, 64, 0), (1024, 32, 32, 32, 1),
+                                               (1024, 64, 32, 128, 0)])
+def test_bsa_bwd_kernels(sim, n, d, block, group, gm):
+    """BSA backward: learned gates (gm 0, with dW and db) and constant gates
+    (gm 1); groups of one, two and four waves."""
+    d_ = sim["dir"]
+    H, ball, topk = 2, 128, 4
+    rng = np.random.default_rng(11 + d + group)
+    c = synth.deformed_sphere(rng, n)
+    q, k, v, do = (synth.normal_features(rng, n, H, d, "bf16") for _ in range(4))
+    W = (0.2 * rng.standard_normal((3, d))).astype(np.float32)
+    b = (0.5 * rng.standard_normal(3)).astype(np.float32)
+    perm = T.build(c, block).astype(np.int32)
+    for t, nm in ((q, "q.bin"), (k, "k.bin"), (v, "v.bin"), (do, "do.bin")):
+        _dump(t, d_ / nm)
+    perm.tofile(d_ / "perm.bin")
+    W.tofile(d_ / "w.bin")
+    b.tofile(d_ / "b.bin")
+    r = subprocess.run([sim["bsa_bwd"], "bsa_bwd", str(n), str(H), str(d), str(ball), "1",
+                        str(block), str(group), str(topk), "1", str(gm)], cwd=d_,
+                       capture_output=True, text=True, timeout=900)
+    assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
+    if gm == 0:
+        want = BB.bsa_bwd(q, k, v, do, perm, ball, block, group, topk, True, W=W, b=b)
+    else:
+        want = BB.bsa_bwd(q, k, v, do, perm, ball, block, group, topk, True,
+                          gate_const=(0.3, 0.5, 0.7))
+    for name, w in zip("qkv", want[:3]):
+        got = _read_out(d_ / f"d{name}.bin", n, H, d, "bf16")
+        err = np.abs(got - w).max()
+        assert err <= 2e-2, (name, err)
+    if gm == 0:
+        # sums over all N*H tokens: 2e-2 relative to the largest entry
+        dw = np.fromfile(d_ / "dw.bin", np.float32).reshape(3, d)
+        db = np.fromfile(d_ / "db.bin", np.float32)
+        assert np.abs(dw - want[3]).max() <= 2e-2 * max(1.0, np.abs(want[3]).max())
+        assert np.abs(db - want[4]).max() <= 2e-2 * max(1.0, np.abs(want[4]).max())
 
 
 @pytest.mark.parametrize("n,H,d,ball,dtype", [(512, 2, 32, 128, "bf16"), (256, 2, 32, 32, "bf16"),
