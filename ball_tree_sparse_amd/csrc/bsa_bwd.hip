@@ -47,13 +47,14 @@ constexpr int kIdxChunk = 64;     // groups per chunk of the selection index
 
 struct BsaBwdLayout {
   BsaLayout f;                      // the forward's workspace
-  size_t vr, ktt, qtt, dott;        // [h][t][d] row-major V; [h][t/32][d][32] transposed
+  size_t vr, qr, dor;               // [h][t][d] row-major V, Q and dO
+  size_t ktt, qtt, dott;            // [h][t/32][d][32]: K, Q and dO transposed
   size_t vcr, kctt;                 // coarse tokens: Vc row-major, Kc transposed
   size_t stats;                     // [h][3][t] float4 (m, 1/l, G_i, D_i)
   size_t dkacc, dvacc;              // [h][t][d] fp32
   size_t cpart;                     // [part][2][h][nc][d] fp32
   size_t dkc, dvc;                  // [h][nc][d] fp32
-  size_t gpart;                     // [waves][3][d + 1] fp32
+  size_t gpart;                     // [3][d + 1][H * N/32] fp32
   size_t cntc, basec, off, list;    // selection index
   size_t total;
 };
@@ -66,6 +67,8 @@ static BsaBwdLayout bsa_bwd_layout(int64_t N, int32_t H, int32_t d, const bsa_pa
   const size_t rows = (size_t)N * H * d;
   size_t o = L.f.total;
   L.vr = o; o = a256(o + rows * 2);
+  L.qr = o; o = a256(o + rows * 2);
+  L.dor = o; o = a256(o + rows * 2);
   L.ktt = o; o = a256(o + rows * 2);
   L.qtt = o; o = a256(o + rows * 2);
   L.dott = o; o = a256(o + rows * 2);
@@ -92,7 +95,7 @@ size_t bsa_bwd_ws_size(int64_t N, int32_t H, int32_t d, const bsa_params* p) {
 
 // ------------------------------------------------------------ layouts ----
 // Grid (N/32 row blocks, H), one wave: rows t0 .. t0+31 of head h gathered
-// through perm.  V is written row-major; K, Q and dO transposed per block,
+// through perm.  V, Q and dO are written row-major; K, Q and dO transposed per block,
 // position p of a [d][32] row holding row tpos(p) (the key order of the
 // forward's transposed V).
 template <int D>
@@ -102,6 +105,8 @@ __global__ __launch_bounds__(64) void bsa_bwd_prep(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ dout,
                                                    const int32_t* __restrict__ perm, int32_t H,
                                                    int64_t N, uint16_t* __restrict__ vr,
+                                                   uint16_t* __restrict__ qr,
+                                                   uint16_t* __restrict__ dor,
                                                    uint16_t* __restrict__ ktt,
                                                    uint16_t* __restrict__ qtt,
                                                    uint16_t* __restrict__ dott) {
@@ -115,11 +120,14 @@ __global__ __launch_bounds__(64) void bsa_bwd_prep(const uint16_t* __restrict__ 
   for (int it = lane; it < 32 * CPR; it += 64) {
     const int r = it / CPR, ch = it - r * CPR;
     const int64_t src = perm_index(perm[t0 + r], N) * rs + (int64_t)h * D + ch * 8;
-    const u32x4 xv = *(const u32x4*)(v + src);
-    *(u32x4*)(vr + ((int64_t)h * N + t0 + r) * D + ch * 8) = xv;
+    const int64_t dst = ((int64_t)h * N + t0 + r) * D + ch * 8;
+    const u32x4 xq = *(const u32x4*)(q + src), xd = *(const u32x4*)(dout + src);
+    *(u32x4*)(vr + dst) = *(const u32x4*)(v + src);
+    *(u32x4*)(qr + dst) = xq;
+    *(u32x4*)(dor + dst) = xd;
     *(u32x4*)&tl[0][r * D + ch * 8] = *(const u32x4*)(k + src);
-    *(u32x4*)&tl[1][r * D + ch * 8] = *(const u32x4*)(q + src);
-    *(u32x4*)&tl[2][r * D + ch * 8] = *(const u32x4*)(dout + src);
+    *(u32x4*)&tl[1][r * D + ch * 8] = xq;
+    *(u32x4*)&tl[2][r * D + ch * 8] = xd;
   }
   __syncthreads();
   uint16_t* outs[3] = {ktt, qtt, dott};
@@ -242,13 +250,18 @@ __global__ __launch_bounds__(64) void bsa_bwd_sel_fill(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------- query pass ----
-// Second sweep of one branch for the lane's query: dQ^T += K^T dS^T over the
-// branch's keys in 32-key blocks; rows: row0(key) of the 32-key block at key.
-template <int D, typename RowFn>
+// Per-query statistics of one branch for query block qb of a wave.
+struct QStat {
+  float m, linv, g, dv;
+};
+
+// Second sweep of one branch for the wave's QB query blocks: dQ^T += K^T dS^T
+// over the branch's keys in 32-key blocks (rows row0(key) of the block at
+// key); every K, V and K^T fragment of a block serves all QB query blocks.
+template <int D, int QB, typename RowFn>
 BT_DEV void dq_sweep(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vrh,
                      const uint16_t* __restrict__ kth, RowFn row0, int len, const bf16x8* qf,
-                     const bf16x8* dof, float c2, float m, float linv, float g, float dv,
-                     f32x16* dqa) {
+                     const bf16x8* dof, float c2, const QStat* st, f32x16 (*dqa)[D / 32]) {
   constexpr int DS = D / 16, DB = D / 32;
   const int lane = threadIdx.x & 63, hf = lane >> 5, c = lane & 31;
   for (int key = 0; key < len; key += 32) {
@@ -265,29 +278,32 @@ BT_DEV void dq_sweep(const uint16_t* __restrict__ kh, const uint16_t* __restrict
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int db = 0; db < DB; ++db) tf[s2][db] = *(const bf16x8*)(tb + db * 32 * 32 + s2 * 16);
-    f32x16 sa = {}, pa = {};
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sa, 0, 0, 0);
-      pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], dof[s], pa, 0, 0, 0);
-    }
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16 sa = {}, pa = {};
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8 dsf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sa[s2 * 8 + e], c2, -m)) * linv;
-        dsf[e] = (__bf16)(p * fmaf(g, pa[s2 * 8 + e], -dv));
+      for (int s = 0; s < DS; ++s) {
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[qb * DS + s], sa, 0, 0, 0);
+        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], dof[qb * DS + s], pa, 0, 0, 0);
       }
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[s2][db], dsf, dqa[db], 0, 0, 0);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 dsf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sa[s2 * 8 + e], c2, -st[qb].m)) * st[qb].linv;
+          dsf[e] = (__bf16)(p * fmaf(st[qb].g, pa[s2 * 8 + e], -st[qb].dv));
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          dqa[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[s2][db], dsf, dqa[qb][db], 0, 0, 0);
+      }
     }
   }
 }
 
-// Grid (groups x H), NWV waves of 32 queries (group = 32 * NWV).
-template <int D, int NWV>
+// Grid (groups x H), NWV waves of QB blocks of 32 queries (group = 32 * NWV * QB).
+template <int D, int NWV, int QB>
 __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(2, 8) void bsa_bwd_q(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
     const int32_t* __restrict__ perm, const uint16_t* __restrict__ kt,
@@ -306,52 +322,47 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(2, 8) void bsa_bwd_q(
   if (xcd_map) pair = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
   const int h = pair / ngroups;
   const int g = pair - h * ngroups;
-  const int group = NWV * 32;
+  const int group = NWV * QB * 32;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, c = lane & 31;
   const int64_t rs = (int64_t)H * D;
   if (tid < topk)
     ssel[tid] = (int32_t)perm_index(sel[((int64_t)h * ngroups + g) * topk + tid], nc);
 
-  const int64_t t0 = (int64_t)g * group + w * 32;
-  const int64_t t = t0 + c;
-  const int64_t pq = perm_index(perm[t], N);
-  const uint16_t* qrow = q + pq * rs + (int64_t)h * D;
-  const uint16_t* drow = dout + pq * rs + (int64_t)h * D;
-  bf16x8 qf[DS], dof[DS];
+  // query block qb of this wave: tree positions t0 + qb*32 + c
+  const int64_t t0 = (int64_t)g * group + w * (QB * 32);
+  int64_t pq[QB];
+  bf16x8 qf[QB * DS], dof[QB * DS];
+  float G[QB][3];
 #pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    qf[s] = *(const bf16x8*)(qrow + s * 16 + hf * 8);
-    dof[s] = *(const bf16x8*)(drow + s * 16 + hf * 8);
-  }
-  // dO in the accumulator layout: element e of block db is d = db*32 + 8*(e/4) + 4*hf + e%4
-  float dov[DB][16];
+  for (int qb = 0; qb < QB; ++qb) {
+    pq[qb] = perm_index(perm[t0 + qb * 32 + c], N);
+    const uint16_t* qrow = q + pq[qb] * rs + (int64_t)h * D;
+    const uint16_t* drow = dout + pq[qb] * rs + (int64_t)h * D;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const u32x2 x = *(const u32x2*)(drow + db * 32 + gq * 8 + hf * 4);
-      dov[db][gq * 4 + 0] = bf16_to_f32((uint16_t)(x[0] & 0xffffu));
-      dov[db][gq * 4 + 1] = bf16_to_f32((uint16_t)(x[0] >> 16));
-      dov[db][gq * 4 + 2] = bf16_to_f32((uint16_t)(x[1] & 0xffffu));
-      dov[db][gq * 4 + 3] = bf16_to_f32((uint16_t)(x[1] >> 16));
+    for (int s = 0; s < DS; ++s) {
+      qf[qb * DS + s] = *(const bf16x8*)(qrow + s * 16 + hf * 8);
+      dof[qb * DS + s] = *(const bf16x8*)(drow + s * 16 + hf * 8);
     }
-  float G[3] = {gc0, gc1, gc2};
-  if (gate_w) {
-    float z[3] = {0.f, 0.f, 0.f};
+    G[qb][0] = gc0;
+    G[qb][1] = gc1;
+    G[qb][2] = gc2;
+    if (gate_w) {
+      float z[3] = {0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < DS; ++s)
+      for (int s = 0; s < DS; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dd = s * 16 + hf * 8 + e;
-        const float x = (float)qf[s][e];
+        for (int e = 0; e < 8; ++e) {
+          const int dd = s * 16 + hf * 8 + e;
+          const float x = (float)qf[qb * DS + s][e];
 #pragma unroll
-        for (int i = 0; i < 3; ++i) z[i] = fmaf(gate_w[i * D + dd], x, z[i]);
+          for (int i = 0; i < 3; ++i) z[i] = fmaf(gate_w[i * D + dd], x, z[i]);
+        }
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        z[i] += __shfl_xor(z[i], 32, 64);
+        if (gate_b) z[i] += gate_b[i];
+        G[qb][i] = 1.0f / (1.0f + __expf(-z[i]));
       }
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      z[i] += __shfl_xor(z[i], 32, 64);
-      if (gate_b) z[i] += gate_b[i];
-      G[i] = 1.0f / (1.0f + __expf(-z[i]));
     }
   }
   __syncthreads();   // ssel
@@ -372,254 +383,304 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(2, 8) void bsa_bwd_q(
     return (int64_t)ssel[key / block] * block + (key % block);
   };
 
-  f32x16 dqa[DB];
+  f32x16 dqa[QB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
-  float dG[3];
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dqa[qb][db] = f32x16{};
+  float dG[QB][3];
 #pragma unroll
   for (int br = 0; br < 3; ++br) {
-    // forward sweep: m, l and O_i of the branch
-    Branch<DB> B;
-    branch_init<D>(B);
-    if (br == 0) attend_range<D, 1>(kh, vth, row_ball, ball, qf, c2, &B);
-    else if (br == 1) attend_range<D, 1>(kch, vcth, row_cmp, nc, qf, c2, &B);
-    else attend_range<D, 1>(kh, vth, row_slc, topk * block, qf, c2, &B);
-    float l = (B.l[0] + B.l[1]) + (B.l[2] + B.l[3]);
-    l += __shfl_xor(l, 32, 64);
-    const float linv = __builtin_amdgcn_rcpf(l);
-    float dg = 0.f;
+    // forward sweep: m, l and O_i of the branch for every query block
+    Branch<DB> B[QB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int qb = 0; qb < QB; ++qb) branch_init<D>(B[qb]);
+    if (br == 0) attend_range<D, QB>(kh, vth, row_ball, ball, qf, c2, B);
+    else if (br == 1) attend_range<D, QB>(kch, vcth, row_cmp, nc, qf, c2, B);
+    else attend_range<D, QB>(kh, vth, row_slc, topk * block, qf, c2, B);
+    QStat st[QB];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) dg = fmaf(dov[db][e], B.o[db][e], dg);
-    dg *= linv;
-    dg += __shfl_xor(dg, 32, 64);
-    dG[br] = dg;
-    const float dv = G[br] * dg;
-    if (br == 0) dq_sweep<D>(kh, vrh, kth, row_ball, ball, qf, dof, c2, B.m, linv, G[br], dv, dqa);
-    else if (br == 1) dq_sweep<D>(kch, vcrh, kcth, row_cmp, nc, qf, dof, c2, B.m, linv, G[br], dv, dqa);
-    else dq_sweep<D>(kh, vrh, kth, row_slc, topk * block, qf, dof, c2, B.m, linv, G[br], dv, dqa);
-    if (hf == 0) stats[((int64_t)h * 3 + br) * N + t] = make_float4(B.m, linv, G[br], dv);
+    for (int qb = 0; qb < QB; ++qb) {
+      float l = (B[qb].l[0] + B[qb].l[1]) + (B[qb].l[2] + B[qb].l[3]);
+      l += __shfl_xor(l, 32, 64);
+      const float linv = __builtin_amdgcn_rcpf(l);
+      // dG_i = dO . O_i: dO in the accumulator layout, d = db*32 + 8*(e/4) + 4*hf + e%4
+      const uint16_t* drow = dout + pq[qb] * rs + (int64_t)h * D;
+      float dg = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const u32x2 x = *(const u32x2*)(drow + db * 32 + gq * 8 + hf * 4);
+          dg = fmaf(bf16_to_f32((uint16_t)(x[0] & 0xffffu)), B[qb].o[db][gq * 4 + 0], dg);
+          dg = fmaf(bf16_to_f32((uint16_t)(x[0] >> 16)), B[qb].o[db][gq * 4 + 1], dg);
+          dg = fmaf(bf16_to_f32((uint16_t)(x[1] & 0xffffu)), B[qb].o[db][gq * 4 + 2], dg);
+          dg = fmaf(bf16_to_f32((uint16_t)(x[1] >> 16)), B[qb].o[db][gq * 4 + 3], dg);
+        }
+      dg *= linv;
+      dg += __shfl_xor(dg, 32, 64);
+      dG[qb][br] = dg;
+      st[qb] = QStat{B[qb].m, linv, G[qb][br], G[qb][br] * dg};
+      if (hf == 0)
+        stats[((int64_t)h * 3 + br) * N + t0 + qb * 32 + c] =
+            make_float4(st[qb].m, st[qb].linv, st[qb].g, st[qb].dv);
+    }
+    if (br == 0) dq_sweep<D, QB>(kh, vrh, kth, row_ball, ball, qf, dof, c2, st, dqa);
+    else if (br == 1) dq_sweep<D, QB>(kch, vcrh, kcth, row_cmp, nc, qf, dof, c2, st, dqa);
+    else dq_sweep<D, QB>(kh, vrh, kth, row_slc, topk * block, qf, dof, c2, st, dqa);
   }
 
   // dq = dQ / sqrt(d) + sum_i dz_i W[i]
   const float scale = 1.0f / sqrtf((float)D);
-  float dz[3] = {0.f, 0.f, 0.f};
-  if (gate_w) {
 #pragma unroll
-    for (int i = 0; i < 3; ++i) dz[i] = dG[i] * G[i] * (1.0f - G[i]);
-  }
-  uint16_t* orow = dq + pq * rs + (int64_t)h * D;
+  for (int qb = 0; qb < QB; ++qb) {
+    float dz[3] = {0.f, 0.f, 0.f};
+    if (gate_w) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      float x[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int dd = db * 32 + gq * 8 + hf * 4 + e;
-        x[e] = dqa[db][gq * 4 + e] * scale;
-        if (gate_w)
-          x[e] = fmaf(dz[0], gate_w[dd], fmaf(dz[1], gate_w[D + dd], fmaf(dz[2], gate_w[2 * D + dd], x[e])));
-      }
-      u32x2 pk;
-      pk[0] = pack_bf16x2(x[0], x[1]);
-      pk[1] = pack_bf16x2(x[2], x[3]);
-      *(u32x2*)(orow + db * 32 + gq * 8 + hf * 4) = pk;
+      for (int i = 0; i < 3; ++i) dz[i] = dG[qb][i] * G[qb][i] * (1.0f - G[qb][i]);
     }
-
-  // gate parameters: this wave's sums of dz_i q[d] and dz_i over its 32 queries
-  if (gate_w && gpart) {
-    const int64_t wv = ((int64_t)h * ngroups + g) * NWV + w;
-    float* gp = gpart + wv * 3 * (D + 1);
+    uint16_t* orow = dq + pq[qb] * rs + (int64_t)h * D;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int s = 0; s < DS; ++s)
+      for (int gq = 0; gq < 4; ++gq) {
+        float x[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float x = dz[i] * (float)qf[s][e];
-#pragma unroll
-          for (int m = 1; m < 32; m <<= 1) x += __shfl_xor(x, m, 64);
-          if (c == 0) gp[i * (D + 1) + s * 16 + hf * 8 + e] = x;
+        for (int e = 0; e < 4; ++e) {
+          const int dd = db * 32 + gq * 8 + hf * 4 + e;
+          x[e] = dqa[qb][db][gq * 4 + e] * scale;
+          if (gate_w)
+            x[e] = fmaf(dz[0], gate_w[dd],
+                        fmaf(dz[1], gate_w[D + dd], fmaf(dz[2], gate_w[2 * D + dd], x[e])));
         }
-      float y = dz[i];
+        u32x2 pk;
+        pk[0] = pack_bf16x2(x[0], x[1]);
+        pk[1] = pack_bf16x2(x[2], x[3]);
+        *(u32x2*)(orow + db * 32 + gq * 8 + hf * 4) = pk;
+      }
+
+    // gate parameters: this block's sums of dz_i q[d] and dz_i over its 32
+    // queries, output-major ([3*(d+1)][blocks]) so the final sums read
+    // contiguous memory
+    if (gate_w && gpart) {
+      const int64_t nblk = (int64_t)H * (N / 32);
+      const int64_t wv = (int64_t)h * (N / 32) + (t0 / 32) + qb;
 #pragma unroll
-      for (int m = 1; m < 32; m <<= 1) y += __shfl_xor(y, m, 64);
-      if (lane == 0) gp[i * (D + 1) + D] = y;
+      for (int i = 0; i < 3; ++i) {
+#pragma unroll
+        for (int s = 0; s < DS; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float x = dz[i] * (float)qf[qb * DS + s][e];
+#pragma unroll
+            for (int m = 1; m < 32; m <<= 1) x += __shfl_xor(x, m, 64);
+            if (c == 0) gpart[(int64_t)(i * (D + 1) + s * 16 + hf * 8 + e) * nblk + wv] = x;
+          }
+        float y = dz[i];
+#pragma unroll
+        for (int m = 1; m < 32; m <<= 1) y += __shfl_xor(y, m, 64);
+        if (lane == 0) gpart[(int64_t)(i * (D + 1) + D) * nblk + wv] = y;
+      }
     }
   }
 }
 
 // ------------------------------------------------------------ key pass ----
-// One wave per 32 keys (rows r0 .. r0+31 of the key source): over the query
-// blocks given by qblock(i) (tree position of the block's first query) for
-// i < nqb, accumulate dK^T and dV^T of branch BR; returns them in acc[0..DB)
-// (dK^T, scaled) and acc[DB..2DB) (dV^T).
-template <int D, int BR, typename QFn>
-BT_DEV void kv_sweep(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
-                     const int32_t* __restrict__ perm, const uint16_t* __restrict__ qtt,
-                     const uint16_t* __restrict__ dott, const float4* __restrict__ stats,
-                     const uint16_t* __restrict__ krow, const uint16_t* __restrict__ vrow,
-                     int32_t H, int64_t N, int h, int nqb, QFn qblock, f32x16* acc) {
+// One wave per NKB blocks of 32 keys (rows r0 .. r0 + 32*NKB - 1 of the key
+// source, row-major): over the query blocks given by qblock(i) (tree
+// position of the block's first query) for i < nqb, accumulate dK^T and dV^T
+// of branch BR into acc[kb][0..DB) (dK^T, scaled) and acc[kb][DB..2DB)
+// (dV^T).  The query rows come from the tree-ordered copies qr and dor, so a
+// block is one contiguous run; its loads serve all NKB key blocks.
+template <int D, int BR, int NKB, typename QFn>
+BT_DEV void kv_sweep(const uint16_t* __restrict__ qr, const uint16_t* __restrict__ dor,
+                     const uint16_t* __restrict__ qtt, const uint16_t* __restrict__ dott,
+                     const float4* __restrict__ stats, const uint16_t* __restrict__ krow,
+                     const uint16_t* __restrict__ vrow, int64_t N, int h, int nqb, QFn qblock,
+                     f32x16 (*acc)[2 * (D / 32)]) {
   constexpr int DS = D / 16, DB = D / 32;
   const int lane = threadIdx.x & 63, hf = lane >> 5, c = lane & 31;
-  const int64_t rs = (int64_t)H * D;
   const float c2 = 1.4426950408889634f / sqrtf((float)D);
-  bf16x8 kB[DS], vB[DS];
+  bf16x8 kB[NKB][DS], vB[NKB][DS];
 #pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    kB[s] = *(const bf16x8*)(krow + c * D + hf * 8 + s * 16);
-    vB[s] = *(const bf16x8*)(vrow + c * D + hf * 8 + s * 16);
-  }
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-  for (int i = 0; i < 2 * DB; ++i) acc[i] = f32x16{};
+    for (int s = 0; s < DS; ++s) {
+      kB[kb][s] = *(const bf16x8*)(krow + (kb * 32 + c) * D + hf * 8 + s * 16);
+      vB[kb][s] = *(const bf16x8*)(vrow + (kb * 32 + c) * D + hf * 8 + s * 16);
+    }
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 2 * DB; ++i) acc[kb][i] = f32x16{};
   const float4* sh = stats + ((int64_t)h * 3 + BR) * N;
+  const uint16_t* qh = qr + (int64_t)h * N * D;
+  const uint16_t* dh = dor + (int64_t)h * N * D;
   for (int i = 0; i < nqb; ++i) {
     const int64_t q0 = qblock(i);
-    const int64_t pq = perm_index(perm[q0 + c], N);
     bf16x8 qA[DS], dA[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      qA[s] = *(const bf16x8*)(q + pq * rs + (int64_t)h * D + s * 16 + hf * 8);
-      dA[s] = *(const bf16x8*)(dout + pq * rs + (int64_t)h * D + s * 16 + hf * 8);
+      qA[s] = *(const bf16x8*)(qh + (q0 + c) * D + s * 16 + hf * 8);
+      dA[s] = *(const bf16x8*)(dh + (q0 + c) * D + s * 16 + hf * 8);
     }
-    f32x16 sa = {}, pa = {};
+    f32x16 sa[NKB], pa[NKB];
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qA[s], kB[s], sa, 0, 0, 0);
-      pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA[s], vB[s], pa, 0, 0, 0);
+    for (int kb = 0; kb < NKB; ++kb) {
+      sa[kb] = f32x16{};
+      pa[kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qA[s], kB[kb][s], sa[kb], 0, 0, 0);
+        pa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA[s], vB[kb][s], pa[kb], 0, 0, 0);
+      }
     }
     // element e holds query 8*(e/4) + 4*hf + e%4 of the block
     const uint16_t* qtb = qtt + ((int64_t)h * (N / 32) + q0 / 32) * D * 32 + c * 32 + hf * 8;
     const uint16_t* dtb = dott + ((int64_t)h * (N / 32) + q0 / 32) * D * 32 + c * 32 + hf * 8;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8 gpf, dsf;
+      bf16x8 gpf[NKB], dsf[NKB];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int ee = s2 * 8 + e;
         const float4 st = sh[q0 + 8 * (ee / 4) + 4 * hf + (ee % 4)];   // (m, 1/l, G, D)
-        const float p = __builtin_amdgcn_exp2f(fmaf(sa[ee], c2, -st.x)) * st.y;
-        gpf[e] = (__bf16)(st.z * p);
-        dsf[e] = (__bf16)(p * fmaf(st.z, pa[ee], -st.w));
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sa[kb][ee], c2, -st.x)) * st.y;
+          gpf[kb][e] = (__bf16)(st.z * p);
+          dsf[kb][e] = (__bf16)(p * fmaf(st.z, pa[kb][ee], -st.w));
+        }
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const bf16x8 qT = *(const bf16x8*)(qtb + db * 32 * 32 + s2 * 16);
         const bf16x8 dT = *(const bf16x8*)(dtb + db * 32 * 32 + s2 * 16);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, dsf, acc[db], 0, 0, 0);
-        acc[DB + db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dT, gpf, acc[DB + db], 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          acc[kb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, dsf[kb], acc[kb][db], 0, 0, 0);
+          acc[kb][DB + db] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(dT, gpf[kb], acc[kb][DB + db], 0, 0, 0);
+        }
       }
     }
   }
   const float scale = 1.0f / sqrtf((float)D);
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] *= scale;
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[kb][db] *= scale;
 }
 
-// Writes (ADD = false) or adds the wave's dK^T / dV^T into [.][rows][D] fp32
-// at rows r0 .. r0+31 (lane c owns row r0 + c).
-template <int D, bool ADD>
-BT_DEV void kv_store(const f32x16* acc, int64_t r0, float* __restrict__ dk,
+// Writes (ADD = false) or adds a wave's dK^T / dV^T (acc as kv_sweep leaves
+// it) into [.][rows][D] fp32 at rows r0 .. r0 + 32*NKB - 1.
+template <int D, int NKB, bool ADD>
+BT_DEV void kv_store(f32x16 (*acc)[2 * (D / 32)], int64_t r0, float* __restrict__ dk,
                      float* __restrict__ dv) {
   constexpr int DB = D / 32;
   const int lane = threadIdx.x & 63, hf = lane >> 5, c = lane & 31;
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    float* base = (x == 0 ? dk : dv) + (r0 + c) * D;
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int x = 0; x < 2; ++x) {
+      float* base = (x == 0 ? dk : dv) + (r0 + kb * 32 + c) * D;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        float4* p = (float4*)(base + db * 32 + gq * 8 + hf * 4);
-        const f32x16& a = acc[x * DB + db];
-        float4 v = make_float4(a[gq * 4 + 0], a[gq * 4 + 1], a[gq * 4 + 2], a[gq * 4 + 3]);
-        if (ADD) {
-          const float4 o = *p;
-          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float4* p = (float4*)(base + db * 32 + gq * 8 + hf * 4);
+          const f32x16& a = acc[kb][x * DB + db];
+          float4 v = make_float4(a[gq * 4 + 0], a[gq * 4 + 1], a[gq * 4 + 2], a[gq * 4 + 3]);
+          if (ADD) {
+            const float4 o = *p;
+            v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+          }
+          *p = v;
         }
-        *p = v;
-      }
-  }
+    }
 }
 
-// Ball branch: grid (balls, H), ball/32 waves; wave w owns keys w*32.. of the
-// ball and visits the ball's query blocks.
+// Key blocks per wave of the key passes: two at d = 32 (their loads of a
+// query block are shared), one at d = 64 (register budget).
 template <int D>
+constexpr int kv_nkb() { return D == 32 ? 2 : 1; }
+
+// Ball branch: grid (balls, H), ball/(32*NKB) waves; wave w owns keys
+// w*32*NKB.. of the ball and visits the ball's query blocks.
+template <int D, int NKB>
 __global__ __launch_bounds__(512) void bsa_bwd_kv_ball(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
-    const int32_t* __restrict__ perm, const uint16_t* __restrict__ qtt,
-    const uint16_t* __restrict__ dott, const float4* __restrict__ stats,
-    const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vr, int32_t H, int64_t N,
-    int32_t ball, float* __restrict__ dkacc, float* __restrict__ dvacc) {
+    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ dor,
+    const uint16_t* __restrict__ qtt, const uint16_t* __restrict__ dott,
+    const float4* __restrict__ stats, const uint16_t* __restrict__ kt,
+    const uint16_t* __restrict__ vr, int64_t N, int32_t ball, float* __restrict__ dkacc,
+    float* __restrict__ dvacc) {
   constexpr int DB = D / 32;
   const int w = threadIdx.x >> 6, h = blockIdx.y;
   const int64_t b0 = (int64_t)blockIdx.x * ball;
-  const int64_t r0 = b0 + w * 32;
-  f32x16 acc[2 * DB];
-  kv_sweep<D, 0>(q, dout, perm, qtt, dott, stats, kt + ((int64_t)h * N + r0) * D,
-                 vr + ((int64_t)h * N + r0) * D, H, N, h, ball / 32,
-                 [&](int i) -> int64_t { return b0 + i * 32; }, acc);
-  kv_store<D, false>(acc, r0, dkacc + (int64_t)h * N * D, dvacc + (int64_t)h * N * D);
+  const int64_t r0 = b0 + w * 32 * NKB;
+  f32x16 acc[NKB][2 * DB];
+  kv_sweep<D, 0, NKB>(qr, dor, qtt, dott, stats, kt + ((int64_t)h * N + r0) * D,
+                      vr + ((int64_t)h * N + r0) * D, N, h, ball / 32,
+                      [&](int i) -> int64_t { return b0 + i * 32; }, acc);
+  kv_store<D, NKB, false>(acc, r0, dkacc + (int64_t)h * N * D, dvacc + (int64_t)h * N * D);
 }
 
-// Selection branch: grid (blocks, H), block/32 waves; wave w owns keys w*32..
-// of block j and visits the query blocks of every group that selected j.
-template <int D>
+// Selection branch: grid (blocks, H), block/(32*NKB) waves; wave w owns keys
+// w*32*NKB.. of block j and visits the query blocks of every group that
+// selected j.
+template <int D, int NKB>
 __global__ __launch_bounds__(512) void bsa_bwd_kv_slc(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
-    const int32_t* __restrict__ perm, const uint16_t* __restrict__ qtt,
-    const uint16_t* __restrict__ dott, const float4* __restrict__ stats,
-    const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vr,
-    const uint32_t* __restrict__ off, const int32_t* __restrict__ list, int32_t H, int64_t N,
-    int32_t nc, int32_t ngroups, int32_t group, int32_t block, int32_t topk,
-    float* __restrict__ dkacc, float* __restrict__ dvacc) {
+    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ dor,
+    const uint16_t* __restrict__ qtt, const uint16_t* __restrict__ dott,
+    const float4* __restrict__ stats, const uint16_t* __restrict__ kt,
+    const uint16_t* __restrict__ vr, const uint32_t* __restrict__ off,
+    const int32_t* __restrict__ list, int64_t N, int32_t nc, int32_t ngroups, int32_t group,
+    int32_t block, int32_t topk, float* __restrict__ dkacc, float* __restrict__ dvacc) {
   constexpr int DB = D / 32;
   const int w = threadIdx.x >> 6, h = blockIdx.y;
   const int64_t j = blockIdx.x;
-  const int64_t r0 = j * block + w * 32;
+  const int64_t r0 = j * block + w * 32 * NKB;
   const int64_t cap = (int64_t)ngroups * topk;
   const uint32_t* oh = off + (int64_t)h * (nc + 1);
   const int64_t e0 = min((int64_t)oh[j], cap), e1 = min((int64_t)oh[j + 1], cap);
   const int32_t* lh = list + (int64_t)h * cap;
   const int per = group / 32;
   const int nqb = e1 > e0 ? (int)(e1 - e0) * per : 0;
-  f32x16 acc[2 * DB];
-  kv_sweep<D, 2>(q, dout, perm, qtt, dott, stats, kt + ((int64_t)h * N + r0) * D,
-                 vr + ((int64_t)h * N + r0) * D, H, N, h, nqb,
-                 [&](int i) -> int64_t {
-                   const int e = i / per, qb = i - e * per;
-                   const int64_t gg = perm_index(lh[e0 + e], ngroups);
-                   return gg * group + qb * 32;
-                 },
-                 acc);
-  kv_store<D, true>(acc, r0, dkacc + (int64_t)h * N * D, dvacc + (int64_t)h * N * D);
+  f32x16 acc[NKB][2 * DB];
+  kv_sweep<D, 2, NKB>(qr, dor, qtt, dott, stats, kt + ((int64_t)h * N + r0) * D,
+                      vr + ((int64_t)h * N + r0) * D, N, h, nqb,
+                      [&](int i) -> int64_t {
+                        const int e = i / per, qb = i - e * per;
+                        const int64_t gg = perm_index(lh[e0 + e], ngroups);
+                        return gg * group + qb * 32;
+                      },
+                      acc);
+  kv_store<D, NKB, true>(acc, r0, dkacc + (int64_t)h * N * D, dvacc + (int64_t)h * N * D);
 }
 
-// Compression branch: grid (nc/32, H, kCmpParts/4), 4 waves; wave w takes
-// query partition z*4 + w of all N/32 query blocks for coarse tokens jb*32..
-// and writes its partial dKc / dVc.
-template <int D>
+// Compression branch: grid (nc/(32*NKB), H, kCmpParts/4), 4 waves; wave w
+// takes query partition z*4 + w of all N/32 query blocks for the coarse
+// tokens jb*32*NKB.. and writes its partial dKc / dVc.
+template <int D, int NKB>
 __global__ __launch_bounds__(256) void bsa_bwd_kv_cmp(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
-    const int32_t* __restrict__ perm, const uint16_t* __restrict__ qtt,
-    const uint16_t* __restrict__ dott, const float4* __restrict__ stats,
-    const uint16_t* __restrict__ kcb, const uint16_t* __restrict__ vcr, int32_t H, int64_t N,
-    int32_t nc, float* __restrict__ cpart) {
+    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ dor,
+    const uint16_t* __restrict__ qtt, const uint16_t* __restrict__ dott,
+    const float4* __restrict__ stats, const uint16_t* __restrict__ kcb,
+    const uint16_t* __restrict__ vcr, int32_t H, int64_t N, int32_t nc,
+    float* __restrict__ cpart) {
   constexpr int DB = D / 32;
   const int w = threadIdx.x >> 6, h = blockIdx.y;
   const int part = blockIdx.z * 4 + w;
-  const int64_t r0 = (int64_t)blockIdx.x * 32;
+  const int64_t r0 = (int64_t)blockIdx.x * 32 * NKB;
   const int64_t nqb = N / 32;
   const int64_t i0 = nqb * part / kCmpParts, i1 = nqb * (part + 1) / kCmpParts;
-  f32x16 acc[2 * DB];
-  kv_sweep<D, 1>(q, dout, perm, qtt, dott, stats, kcb + ((int64_t)h * nc + r0) * D,
-                 vcr + ((int64_t)h * nc + r0) * D, H, N, h, (int)(i1 - i0),
-                 [&](int i) -> int64_t { return (i0 + i) * 32; }, acc);
+  f32x16 acc[NKB][2 * DB];
+  kv_sweep<D, 1, NKB>(qr, dor, qtt, dott, stats, kcb + ((int64_t)h * nc + r0) * D,
+                      vcr + ((int64_t)h * nc + r0) * D, N, h, (int)(i1 - i0),
+                      [&](int i) -> int64_t { return (i0 + i) * 32; }, acc);
   float* pk = cpart + (((int64_t)part * 2 + 0) * H + h) * nc * D;
   float* pv = cpart + (((int64_t)part * 2 + 1) * H + h) * nc * D;
-  kv_store<D, false>(acc, r0, pk, pv);
+  kv_store<D, NKB, false>(acc, r0, pk, pv);
 }
 
 // dKc, dVc [h][j][d] = the sum of the partitions' partials, in order.
@@ -675,16 +736,16 @@ __global__ __launch_bounds__(256) void bsa_bwd_finish(const float* __restrict__ 
 }
 
 // Grid (3 * (D + 1)), 256 threads: output o of (dW [3][D], db [3]) summed over
-// the per-wave partials in a fixed order.
+// the per-block partials (gpart[o][block], contiguous) in a fixed order.
 __global__ __launch_bounds__(256) void bsa_bwd_gate_reduce(const float* __restrict__ gpart,
-                                                           int64_t nwaves, int32_t d,
+                                                           int64_t nblk, int32_t d,
                                                            float* __restrict__ dgw,
                                                            float* __restrict__ dgb) {
   __shared__ float red[256];
   const int o = blockIdx.x, tid = threadIdx.x;
-  const int stride = 3 * (d + 1);
+  const float* src = gpart + (int64_t)o * nblk;
   float s = 0.f;
-  for (int64_t wv = tid; wv < nwaves; wv += 256) s += gpart[wv * stride + o];
+  for (int64_t i = tid; i < nblk; i += 256) s += src[i];
   red[tid] = s;
   __syncthreads();
   for (int m = 128; m > 0; m >>= 1) {
@@ -716,6 +777,8 @@ static bt_status bwd_launch_d(const void* q, const void* k, const void* v, const
   const uint16_t* kcb = (const uint16_t*)(b + L.f.kcb);
   const uint16_t* vct = (const uint16_t*)(b + L.f.vcb);
   uint16_t* vr = (uint16_t*)(b + L.vr);
+  uint16_t* qr = (uint16_t*)(b + L.qr);
+  uint16_t* dor = (uint16_t*)(b + L.dor);
   uint16_t* ktt = (uint16_t*)(b + L.ktt);
   uint16_t* qtt = (uint16_t*)(b + L.qtt);
   uint16_t* dott = (uint16_t*)(b + L.dott);
@@ -737,8 +800,8 @@ static bt_status bwd_launch_d(const void* q, const void* k, const void* v, const
 
   const dim3 w1(64);
   hipLaunchKernelGGL((bsa_bwd_prep<D>), dim3((unsigned)(N / 32), H), w1, 0, st,
-                     (const uint16_t*)q, kin, vin, (const uint16_t*)dout, perm, H, N, vr, ktt, qtt,
-                     dott);
+                     (const uint16_t*)q, kin, vin, (const uint16_t*)dout, perm, H, N, vr, qr, dor,
+                     ktt, qtt, dott);
   hipLaunchKernelGGL((bsa_bwd_prep_coarse<D>), dim3(nc / 32, H), w1, 0, st, kcb, vct, nc, vcr,
                      kctt);
   const size_t idx_lds = (size_t)nc * 4;
@@ -755,30 +818,52 @@ static bt_status bwd_launch_d(const void* q, const void* k, const void* v, const
   const int total = ngroups * H;
   const int xmap = (total % 8 == 0) ? 1 : 0;
   float* gp = (gate_w && (dgate_w || dgate_b)) ? gpart : nullptr;
-#define BT_BWDQ(NW)                                                                            \
-  hipLaunchKernelGGL((bsa_bwd_q<D, NW>), dim3(total), dim3(NW * 64), 0, st, (const uint16_t*)q, \
-                     (const uint16_t*)dout, perm, kt, vtt, vr, ktt, kcb, vct, vcr, kctt, sel,    \
-                     gate_w, gate_b, g0, g1, g2, H, N, nc, ngroups, p->ball, p->block, p->topk,  \
-                     xmap, stats, gp, (uint16_t*)dq)
-  switch (p->group) {
-    case 32: BT_BWDQ(1); break;
-    case 64: BT_BWDQ(2); break;
-    case 128: BT_BWDQ(4); break;
-    default: BT_BWDQ(8); break;
+#define BT_BWDQ(NW, QBB)                                                                       \
+  hipLaunchKernelGGL((bsa_bwd_q<D, NW, QBB>), dim3(total), dim3(NW * 64), 0, st,                \
+                     (const uint16_t*)q, (const uint16_t*)dout, perm, kt, vtt, vr, ktt, kcb, vct, \
+                     vcr, kctt, sel, gate_w, gate_b, g0, g1, g2, H, N, nc, ngroups, p->ball,     \
+                     p->block, p->topk, xmap, stats, gp, (uint16_t*)dq)
+  // two query blocks per wave at d = 32 (their key fragments are shared)
+  if constexpr (D == 32) {
+    switch (p->group) {
+      case 32: BT_BWDQ(1, 1); break;
+      case 64: BT_BWDQ(1, 2); break;
+      case 128: BT_BWDQ(2, 2); break;
+      default: BT_BWDQ(4, 2); break;
+    }
+  } else {
+    switch (p->group) {
+      case 32: BT_BWDQ(1, 1); break;
+      case 64: BT_BWDQ(2, 1); break;
+      case 128: BT_BWDQ(4, 1); break;
+      default: BT_BWDQ(8, 1); break;
+    }
   }
 #undef BT_BWDQ
   s = launch_status("bsa_bwd_q");
   if (s != BT_OK) return s;
 
-  hipLaunchKernelGGL((bsa_bwd_kv_ball<D>), dim3((unsigned)(N / p->ball), H),
-                     dim3(p->ball / 32 * 64), 0, st, (const uint16_t*)q, (const uint16_t*)dout,
-                     perm, qtt, dott, stats, kt, vr, H, N, p->ball, dkacc, dvacc);
-  hipLaunchKernelGGL((bsa_bwd_kv_slc<D>), dim3(nc, H), dim3(p->block / 32 * 64), 0, st,
-                     (const uint16_t*)q, (const uint16_t*)dout, perm, qtt, dott, stats, kt, vr,
-                     off, list, H, N, nc, ngroups, p->group, p->block, p->topk, dkacc, dvacc);
-  hipLaunchKernelGGL((bsa_bwd_kv_cmp<D>), dim3(nc / 32, H, kCmpParts / 4), dim3(256), 0, st,
-                     (const uint16_t*)q, (const uint16_t*)dout, perm, qtt, dott, stats, kcb, vcr,
-                     H, N, nc, cpart);
+  // two key blocks per wave where the block sizes allow it
+  constexpr int NK = kv_nkb<D>();
+  const bool ball2 = NK == 2 && p->ball % 64 == 0, blk2 = NK == 2 && p->block % 64 == 0,
+             cmp2 = NK == 2 && nc % 64 == 0;
+#define BT_KVB(K)                                                                             \
+  hipLaunchKernelGGL((bsa_bwd_kv_ball<D, K>), dim3((unsigned)(N / p->ball), H),               \
+                     dim3(p->ball / (32 * K) * 64), 0, st, qr, dor, qtt, dott, stats, kt, vr, N, \
+                     p->ball, dkacc, dvacc)
+#define BT_KVS(K)                                                                             \
+  hipLaunchKernelGGL((bsa_bwd_kv_slc<D, K>), dim3(nc, H), dim3(p->block / (32 * K) * 64), 0, st, \
+                     qr, dor, qtt, dott, stats, kt, vr, off, list, N, nc, ngroups, p->group,      \
+                     p->block, p->topk, dkacc, dvacc)
+#define BT_KVC(K)                                                                             \
+  hipLaunchKernelGGL((bsa_bwd_kv_cmp<D, K>), dim3(nc / (32 * K), H, kCmpParts / 4), dim3(256), \
+                     0, st, qr, dor, qtt, dott, stats, kcb, vcr, H, N, nc, cpart)
+  if (ball2) BT_KVB(NK); else BT_KVB(1);
+  if (blk2) BT_KVS(NK); else BT_KVS(1);
+  if (cmp2) BT_KVC(NK); else BT_KVC(1);
+#undef BT_KVB
+#undef BT_KVS
+#undef BT_KVC
   s = launch_status("bsa_bwd keys");
   if (s != BT_OK) return s;
 

@@ -178,11 +178,12 @@ def test_bsa_kernels(sim, qc, group):
     assert np.abs(out - ref).max() <= 2e-2
 
 
-@pytest.mark.parametrize("n,d,block,group,gm", [(1024, 32, 32, 64, 0), (1024, 32, 32, 32, 1),
+@pytest.mark.parametrize("n,d,block,group,gm", [(2048, 32, 64, 64, 0), (2048, 32, 32, 32, 1),
                                                (1024, 64, 32, 128, 0)])
 def test_bsa_bwd_kernels(sim, n, d, block, group, gm):
     """BSA backward: learned gates (gm 0, with dW and db) and constant gates
-    (gm 1); groups of one, two and four waves."""
+    (gm 1); groups of one, two and four waves; key passes with two key blocks
+    per wave (ball and 64-key blocks; 64 coarse tokens) and with one."""
     d_ = sim["dir"]
     H, ball, topk = 2, 128, 4
     rng = np.random.default_rng(11 + d + group)
