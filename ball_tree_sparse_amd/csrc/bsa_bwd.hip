@@ -14,14 +14,15 @@
 //   index     for every (head, block) the groups that selected the block, in
 //             ascending group order (a per-chunk count, a scan and an
 //             in-order fill, so the result is deterministic).
-//   queries   one wave per 32 queries: per branch, a forward sweep (the
-//             forward's online softmax) gives the maximum m, the normaliser l
-//             and O_i, hence dG_i = dO . O_i and D_i = G_i dG_i; a second
-//             sweep forms S^T, P^T = exp(S - m) / l, dP^T = V dO^T, dS^T =
-//             P^T (G_i dP^T - D_i) and dQ^T += K^T dS^T.  The gate term
-//             sum_i dz_i W[i] with dz_i = dG_i G_i (1 - G_i) is added, dq is
-//             written in original order, and (m, 1/l, G_i, D_i) are kept.
-//   keys      one wave per 32 keys: for every query block that attends to
+//   queries   one wave per 32 or 64 queries, one sweep per branch: with
+//             p = exp(S - m) under an online maximum m, it sums l = sum p,
+//             c = sum p dP, A = K^T (p dP) and Bv = K^T p, so that dG_i =
+//             dO . O_i = c / l, D_i = G_i dG_i and dQ^T = (G_i A - D_i Bv) / l
+//             (S^T = K Q^T and dP^T = V dO^T are formed once per key).  The
+//             gate term sum_i dz_i W[i] with dz_i = dG_i G_i (1 - G_i) is
+//             added, dq is written in original order, and (m, 1/l, G_i, D_i)
+//             are kept.
+//   keys      one wave per 32 or 64 keys: for every query block that attends to
 //             them, S = Q K^T, dP = dO V^T, P from the kept statistics, dS =
 //             P (G dP - D), dV^T += dO^T (G P) and dK^T += Q^T dS.  Ball keys
 //             see their ball's queries; selected blocks see the groups that
@@ -32,8 +33,8 @@
 //             parameter gradients are summed from per-wave partials.
 //
 // Products run on v_mfma_f32_32x32x16_bf16 in the operand layouts of the
-// forward: P, dS and G P are rounded to bf16 for the MFMA, statistics and
-// accumulators are fp32.
+// forward: p, p dP, dS and G P are rounded to bf16 for the MFMA; statistics
+// and accumulators are fp32.
 #include "bsa_common.h"
 
 namespace bt {
@@ -250,66 +251,140 @@ __global__ __launch_bounds__(64) void bsa_bwd_sel_fill(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------- query pass ----
-// Per-query statistics of one branch for query block qb of a wave.
-struct QStat {
-  float m, linv, g, dv;
+// One sweep per branch.  With p_k = exp(s_k - m) (online maximum m), l =
+// sum p_k, c = sum p_k dP_k, A = sum p_k dP_k K_k and Bv = sum p_k K_k, the
+// branch gives dG = dO . O = c / l, D = G dG and dQ = sum_k P_k (G dP_k - D)
+// K_k = (G A - D Bv) / l, so S, dP and both K products are formed once per
+// key (A and Bv as K^T products of the bf16-rounded p dP and p).
+template <int DB>
+struct QState {
+  f32x16 a[DB], bv[DB];   // A^T, Bv^T: lane = query column, d in the accumulator layout
+  float m;                // running maximum, log2-scaled units
+  float l[2], c[2];       // partial sums of p and p dP
 };
 
-// Second sweep of one branch for the wave's QB query blocks: dQ^T += K^T dS^T
-// over the branch's keys in 32-key blocks (rows row0(key) of the block at
-// key); every K, V and K^T fragment of a block serves all QB query blocks.
-template <int D, int QB, typename RowFn>
-BT_DEV void dq_sweep(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vrh,
-                     const uint16_t* __restrict__ kth, RowFn row0, int len, const bf16x8* qf,
-                     const bf16x8* dof, float c2, const QStat* st, f32x16 (*dqa)[D / 32]) {
+template <int DB>
+BT_DEV void qstate_init(QState<DB>& q) {
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    q.a[db] = f32x16{};
+    q.bv[db] = f32x16{};
+  }
+  q.m = -INFINITY;
+  q.l[0] = q.l[1] = q.c[0] = q.c[1] = 0.f;
+}
+
+// NKB blocks of 32 keys (rows row0(kb) .. + 31) for the wave's QB query
+// blocks; every K, V and K^T fragment serves all QB blocks.
+template <int D, int NKB, int QB, typename RowFn>
+BT_DEV void bwd_chunk(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vrh,
+                      const uint16_t* __restrict__ kth, RowFn row0, const bf16x8* qf,
+                      const bf16x8* dof, float c2, QState<D / 32>* st) {
   constexpr int DS = D / 16, DB = D / 32;
   const int lane = threadIdx.x & 63, hf = lane >> 5, c = lane & 31;
-  for (int key = 0; key < len; key += 32) {
-    const int64_t r0 = row0(key);
-    bf16x8 kf[DS], vf[DS];
+  bf16x8 kf[NKB][DS], vf[NKB][DS], tf[NKB][2][DB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const int64_t r0 = row0(kb);
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      kf[s] = *(const bf16x8*)(kh + (r0 + c) * D + hf * 8 + s * 16);
-      vf[s] = *(const bf16x8*)(vrh + (r0 + c) * D + hf * 8 + s * 16);
+      kf[kb][s] = *(const bf16x8*)(kh + (r0 + c) * D + hf * 8 + s * 16);
+      vf[kb][s] = *(const bf16x8*)(vrh + (r0 + c) * D + hf * 8 + s * 16);
     }
-    bf16x8 tf[2][DB];
     const uint16_t* tb = kth + r0 * D + c * 32 + hf * 8;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) tf[s2][db] = *(const bf16x8*)(tb + db * 32 * 32 + s2 * 16);
+      for (int db = 0; db < DB; ++db)
+        tf[kb][s2][db] = *(const bf16x8*)(tb + db * 32 * 32 + s2 * 16);
+  }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x16 sa = {}, pa = {};
+  for (int qb = 0; qb < QB; ++qb) {
+    QState<DB>& b = st[qb];
+    f32x16 sa[NKB], pa[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      sa[kb] = f32x16{};
+      pa[kb] = f32x16{};
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[qb * DS + s], sa, 0, 0, 0);
-        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], dof[qb * DS + s], pa, 0, 0, 0);
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 dsf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sa[s2 * 8 + e], c2, -st[qb].m)) * st[qb].linv;
-          dsf[e] = (__bf16)(p * fmaf(st[qb].g, pa[s2 * 8 + e], -st[qb].dv));
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          dqa[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[s2][db], dsf, dqa[qb][db], 0, 0, 0);
+        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][s], qf[qb * DS + s], sa[kb], 0, 0, 0);
+        pa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][s], dof[qb * DS + s], pa[kb], 0, 0, 0);
       }
     }
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sa[kb][e]);
+    float cm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * c2;
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    // lazy rescale, as in the forward: only when a chunk maximum passes the
+    // running one by more than 2^kLazyLog2, for the whole wave at once
+    if (__ballot(cm > b.m + kLazyLog2)) {
+      const float mn = fmaxf(b.m, cm);
+      const float alpha = __builtin_amdgcn_exp2f(b.m - mn);   // 0 on the first chunk
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        b.l[i] *= alpha;
+        b.c[i] *= alpha;
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        b.a[db] *= alpha;
+        b.bv[db] *= alpha;
+      }
+      b.m = mn;
+    }
+    const float mn = b.m;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 pb, pdb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sa[kb][s2 * 8 + e], c2, -mn));
+          const float pd = pv * pa[kb][s2 * 8 + e];
+          b.l[s2] += pv;
+          b.c[s2] += pd;
+          pb[e] = (__bf16)pv;
+          pdb[e] = (__bf16)pd;
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          b.a[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[kb][s2][db], pdb, b.a[db], 0, 0, 0);
+          b.bv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[kb][s2][db], pb, b.bv[db], 0, 0, 0);
+        }
+      }
   }
 }
 
-// Grid (groups x H), NWV waves of QB blocks of 32 queries (group = 32 * NWV * QB).
-template <int D, int NWV, int QB>
+// The branch's keys [0, len) (len a multiple of 32) in chunks of NKB blocks
+// and a tail of single blocks; row0(key) gives the row of the block at key.
+template <int D, int NKB, int QB, typename RowFn>
+BT_DEV void bwd_range(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vrh,
+                      const uint16_t* __restrict__ kth, RowFn row0, int len, const bf16x8* qf,
+                      const bf16x8* dof, float c2, QState<D / 32>* st) {
+  int k0 = 0;
+  for (; k0 + 32 * NKB <= len; k0 += 32 * NKB)
+    bwd_chunk<D, NKB, QB>(kh, vrh, kth, [&](int kb) -> int64_t { return row0(k0 + kb * 32); },
+                          qf, dof, c2, st);
+  if constexpr (NKB > 1) {
+    for (; k0 < len; k0 += 32)
+      bwd_chunk<D, 1, QB>(kh, vrh, kth, [&](int) -> int64_t { return row0(k0); }, qf, dof, c2,
+                          st);
+  }
+}
+
+// Grid (groups x H), NWV waves of QB blocks of 32 queries (group = 32 * NWV * QB);
+// keys in chunks of NKB blocks of 32.
+template <int D, int NWV, int QB, int NKB>
 __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(2, 8) void bsa_bwd_q(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
     const int32_t* __restrict__ perm, const uint16_t* __restrict__ kt,
-    const uint16_t* __restrict__ vtt, const uint16_t* __restrict__ vr,
-    const uint16_t* __restrict__ ktt, const uint16_t* __restrict__ kcb,
-    const uint16_t* __restrict__ vct, const uint16_t* __restrict__ vcr,
+    const uint16_t* __restrict__ vr, const uint16_t* __restrict__ ktt,
+    const uint16_t* __restrict__ kcb, const uint16_t* __restrict__ vcr,
     const uint16_t* __restrict__ kctt, const int32_t* __restrict__ sel,
     const float* __restrict__ gate_w, const float* __restrict__ gate_b, float gc0, float gc1,
     float gc2, int32_t H, int64_t N, int32_t nc, int32_t ngroups, int32_t ball, int32_t block,
@@ -369,11 +444,9 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(2, 8) void bsa_bwd_q(
 
   const float c2 = 1.4426950408889634f / sqrtf((float)D);
   const uint16_t* kh = kt + (int64_t)h * N * D;
-  const uint16_t* vth = vtt + (int64_t)h * N * D;
   const uint16_t* vrh = vr + (int64_t)h * N * D;
   const uint16_t* kth = ktt + (int64_t)h * N * D;
   const uint16_t* kch = kcb + (int64_t)h * nc * D;
-  const uint16_t* vcth = vct + (int64_t)h * nc * D;
   const uint16_t* vcrh = vcr + (int64_t)h * nc * D;
   const uint16_t* kcth = kctt + (int64_t)h * nc * D;
   const int64_t b0 = ((int64_t)g * group / ball) * ball;
@@ -383,51 +456,43 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(2, 8) void bsa_bwd_q(
     return (int64_t)ssel[key / block] * block + (key % block);
   };
 
-  f32x16 dqa[QB][DB];
+  // dQ^T per lane, kept in LDS between branches (registers go to the
+  // branch state); lane-consecutive words, so free of bank conflicts
+  __shared__ float sdq[NWV][QB][DB][16][64];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) dqa[qb][db] = f32x16{};
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sdq[w][qb][db][e][lane] = 0.f;
   float dG[QB][3];
 #pragma unroll
   for (int br = 0; br < 3; ++br) {
-    // forward sweep: m, l and O_i of the branch for every query block
-    Branch<DB> B[QB];
+    QState<DB> S[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) branch_init<D>(B[qb]);
-    if (br == 0) attend_range<D, QB>(kh, vth, row_ball, ball, qf, c2, B);
-    else if (br == 1) attend_range<D, QB>(kch, vcth, row_cmp, nc, qf, c2, B);
-    else attend_range<D, QB>(kh, vth, row_slc, topk * block, qf, c2, B);
-    QStat st[QB];
+    for (int qb = 0; qb < QB; ++qb) qstate_init<DB>(S[qb]);
+    if (br == 0) bwd_range<D, NKB, QB>(kh, vrh, kth, row_ball, ball, qf, dof, c2, S);
+    else if (br == 1) bwd_range<D, NKB, QB>(kch, vcrh, kcth, row_cmp, nc, qf, dof, c2, S);
+    else bwd_range<D, NKB, QB>(kh, vrh, kth, row_slc, topk * block, qf, dof, c2, S);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float l = (B[qb].l[0] + B[qb].l[1]) + (B[qb].l[2] + B[qb].l[3]);
+      float l = S[qb].l[0] + S[qb].l[1];
+      float cc = S[qb].c[0] + S[qb].c[1];
       l += __shfl_xor(l, 32, 64);
+      cc += __shfl_xor(cc, 32, 64);
       const float linv = __builtin_amdgcn_rcpf(l);
-      // dG_i = dO . O_i: dO in the accumulator layout, d = db*32 + 8*(e/4) + 4*hf + e%4
-      const uint16_t* drow = dout + pq[qb] * rs + (int64_t)h * D;
-      float dg = 0.f;
+      const float dg = cc * linv;                 // dO . O_i
+      const float gi = G[qb][br], dv = gi * dg;
+      dG[qb][br] = dg;
+      const float fa = gi * linv, fb = dv * linv;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const u32x2 x = *(const u32x2*)(drow + db * 32 + gq * 8 + hf * 4);
-          dg = fmaf(bf16_to_f32((uint16_t)(x[0] & 0xffffu)), B[qb].o[db][gq * 4 + 0], dg);
-          dg = fmaf(bf16_to_f32((uint16_t)(x[0] >> 16)), B[qb].o[db][gq * 4 + 1], dg);
-          dg = fmaf(bf16_to_f32((uint16_t)(x[1] & 0xffffu)), B[qb].o[db][gq * 4 + 2], dg);
-          dg = fmaf(bf16_to_f32((uint16_t)(x[1] >> 16)), B[qb].o[db][gq * 4 + 3], dg);
-        }
-      dg *= linv;
-      dg += __shfl_xor(dg, 32, 64);
-      dG[qb][br] = dg;
-      st[qb] = QStat{B[qb].m, linv, G[qb][br], G[qb][br] * dg};
+        for (int e = 0; e < 16; ++e)
+          sdq[w][qb][db][e][lane] += fa * S[qb].a[db][e] - fb * S[qb].bv[db][e];
       if (hf == 0)
-        stats[((int64_t)h * 3 + br) * N + t0 + qb * 32 + c] =
-            make_float4(st[qb].m, st[qb].linv, st[qb].g, st[qb].dv);
+        stats[((int64_t)h * 3 + br) * N + t0 + qb * 32 + c] = make_float4(S[qb].m, linv, gi, dv);
     }
-    if (br == 0) dq_sweep<D, QB>(kh, vrh, kth, row_ball, ball, qf, dof, c2, st, dqa);
-    else if (br == 1) dq_sweep<D, QB>(kch, vcrh, kcth, row_cmp, nc, qf, dof, c2, st, dqa);
-    else dq_sweep<D, QB>(kh, vrh, kth, row_slc, topk * block, qf, dof, c2, st, dqa);
   }
 
   // dq = dQ / sqrt(d) + sum_i dz_i W[i]
@@ -448,7 +513,7 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(2, 8) void bsa_bwd_q(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int dd = db * 32 + gq * 8 + hf * 4 + e;
-          x[e] = dqa[qb][db][gq * 4 + e] * scale;
+          x[e] = sdq[w][qb][db][gq * 4 + e][lane] * scale;
           if (gate_w)
             x[e] = fmaf(dz[0], gate_w[dd],
                         fmaf(dz[1], gate_w[D + dd], fmaf(dz[2], gate_w[2 * D + dd], x[e])));
@@ -773,7 +838,6 @@ static bt_status bwd_launch_d(const void* q, const void* k, const void* v, const
   const int32_t nc = (int32_t)(N / p->block), ngroups = (int32_t)(N / p->group);
   const int nchunk = (ngroups + kIdxChunk - 1) / kIdxChunk;
   const uint16_t* kt = (const uint16_t*)(b + L.f.kt);
-  const uint16_t* vtt = (const uint16_t*)(b + L.f.vt);
   const uint16_t* kcb = (const uint16_t*)(b + L.f.kcb);
   const uint16_t* vct = (const uint16_t*)(b + L.f.vcb);
   uint16_t* vr = (uint16_t*)(b + L.vr);
@@ -819,10 +883,11 @@ static bt_status bwd_launch_d(const void* q, const void* k, const void* v, const
   const int xmap = (total % 8 == 0) ? 1 : 0;
   float* gp = (gate_w && (dgate_w || dgate_b)) ? gpart : nullptr;
 #define BT_BWDQ(NW, QBB)                                                                       \
-  hipLaunchKernelGGL((bsa_bwd_q<D, NW, QBB>), dim3(total), dim3(NW * 64), 0, st,                \
-                     (const uint16_t*)q, (const uint16_t*)dout, perm, kt, vtt, vr, ktt, kcb, vct, \
-                     vcr, kctt, sel, gate_w, gate_b, g0, g1, g2, H, N, nc, ngroups, p->ball,     \
+  hipLaunchKernelGGL((bsa_bwd_q<D, NW, QBB, QNKB>), dim3(total), dim3(NW * 64), 0, st,                \
+                     (const uint16_t*)q, (const uint16_t*)dout, perm, kt, vr, ktt, kcb, vcr,    \
+                     kctt, sel, gate_w, gate_b, g0, g1, g2, H, N, nc, ngroups, p->ball,     \
                      p->block, p->topk, xmap, stats, gp, (uint16_t*)dq)
+  constexpr int QNKB = 1;   // 64-key chunks measured no faster
   // two query blocks per wave at d = 32 (their key fragments are shared)
   if constexpr (D == 32) {
     switch (p->group) {

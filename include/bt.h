@@ -281,8 +281,9 @@ bt_status bsa_attn(const void* q, const void* k, const void* v,
  * sum_{t,h} dz_i.  Compression passes dKc[j] / block to every token of block
  * j; selected blocks collect the gradient of every group that selected them.
  * The top-k selection passes no gradient: it is recomputed exactly as the
- * forward's and held fixed.  P, dS and G*P are rounded to bf16 for the
- * matrix products; everything else accumulates in fp32.
+ * forward's and held fixed.  The softmax weights, their products with dP,
+ * dS and G*P are rounded to bf16 for the matrix products; everything else
+ * accumulates in fp32.
  * Arguments and requirements as bsa_attn, plus p->query_compression == 0;
  * dq, dk and dv must not overlap each other or q, k, v, dout, and must be
  * 16-byte aligned.  ws: device workspace of at least
