@@ -60,6 +60,7 @@ def _selection(q, k, v, perm, W, b, ball, block, group, topk, mask, gate_const, 
     (8192, 2, 32, 256, 64, 256, 5, True, None),              # eight-wave groups
     (4096, 2, 64, 128, 64, 128, 4, True, None),              # d = 64
     (2048, 1, 64, 64, 32, 64, 3, True, (1.0, 0.0, 0.0)),     # ball only
+    (8192, 2, 64, 256, 64, 256, 4, True, None),              # d = 64, eight-wave groups
 ])
 def test_parity(n, H, d, ball, block, group, topk, mask, gates):
     q, k, v, do, W, b, perm = _setup(n, H, d, seed=n + 7 * H + d + topk, leaf=block)
