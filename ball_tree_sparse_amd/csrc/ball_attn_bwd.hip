@@ -16,7 +16,7 @@
 //   key pass (thread per key): a sweep over the queries (staged in LDS with
 //     their dO rows) accumulates dK_j and dV_j.
 // Rows are staged through LDS in chunks of 64 as fp32.
-#include "common.h"
+#include "lds_tile.h"
 
 namespace bt {
 
@@ -214,38 +214,6 @@ __global__ __launch_bounds__(kBwdThreads) void ball_attn_bwd_valu(
 //    stored statistics, dP = dO V^T, dS = P (dP - D); dV^T += dO^T P and
 //    dK^T += Q^T dS.
 // P and dS are rounded to bf16 for the MFMA; everything else is fp32.
-
-// Element offset of 16-byte piece p of row r in a row-major LDS tile of D
-// columns.  Sixteen consecutive rows put piece p in sixteen different bank
-// groups, and four consecutive rows starting at a multiple of four cover
-// every bank once per 32-column span.
-template <int D>
-BT_DEV int tile_off(int r, int p) {
-  int f;
-  if constexpr (D == 32) f = (r >> 2) & 3;
-  else f = (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  return r * D + ((p ^ f) << 3);
-}
-
-// Four bf16 of a 16-lane transposed read (see above); p points at this
-// lane's 8-byte run in LDS.
-BT_DEV s16x4 lds_read_tr16(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((BT_LDS_AS s16x4*)p);
-}
-
-// A operand X^T[d][rows] of a 16-row slice (rows sl*16 ...) and the 32-column
-// block db of a tile: lane L holds d = db*32 + L%32 and the rows 8t + 4*(L/32)
-// + e (t = 0, 1; e = 0..3) of the slice, in that element order.
-template <int D>
-BT_DEV bf16x8 tr_operand(const uint16_t* tile, int sl, int db) {
-  const int lane = threadIdx.x & 63, grp = lane >> 4, s = lane & 15;
-  const int col = db * 32 + 16 * (grp & 1) + 4 * (s & 3);     // this lane's 4 columns
-  const int r0 = sl * 16 + 4 * (grp >> 1) + (s >> 2);
-  const s16x4 a = lds_read_tr16(tile + tile_off<D>(r0, col >> 3) + (col & 4));
-  const s16x4 b = lds_read_tr16(tile + tile_off<D>(r0 + 8, col >> 3) + (col & 4));
-  const s16x8 x = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, x);
-}
 
 // lane (c, hf) holds C^T[d][c] of a 32-column block for d = db*32 + 8*g +
 // 4*hf + 0..3 in acc[db][g*4 + 0..3]; write row `row` (d contiguous) scaled,

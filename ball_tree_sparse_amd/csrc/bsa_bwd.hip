@@ -36,6 +36,7 @@
 // forward: p, p dP, dS and G P are rounded to bf16 for the MFMA; statistics
 // and accumulators are fp32.
 #include "bsa_common.h"
+#include "lds_tile.h"
 
 namespace bt {
 
@@ -49,7 +50,7 @@ constexpr int kIdxChunk = 64;     // groups per chunk of the selection index
 struct BsaBwdLayout {
   BsaLayout f;                      // the forward's workspace
   size_t vr, qr, dor;               // [h][t][d] row-major V, Q and dO
-  size_t ktt, qtt, dott;            // [h][t/32][d][32]: K, Q and dO transposed
+  size_t ktt;                       // [h][t/32][d][32]: K transposed
   size_t vcr, kctt;                 // coarse tokens: Vc row-major, Kc transposed
   size_t stats;                     // [h][3][t] float4 (m, 1/l, G_i, D_i)
   size_t dkacc, dvacc;              // [h][t][d] fp32
@@ -71,8 +72,6 @@ static BsaBwdLayout bsa_bwd_layout(int64_t N, int32_t H, int32_t d, const bsa_pa
   L.qr = o; o = a256(o + rows * 2);
   L.dor = o; o = a256(o + rows * 2);
   L.ktt = o; o = a256(o + rows * 2);
-  L.qtt = o; o = a256(o + rows * 2);
-  L.dott = o; o = a256(o + rows * 2);
   L.vcr = o; o = a256(o + nc * H * d * 2);
   L.kctt = o; o = a256(o + nc * H * d * 2);
   L.stats = o; o = a256(o + (size_t)N * H * 3 * 16);
@@ -96,9 +95,9 @@ size_t bsa_bwd_ws_size(int64_t N, int32_t H, int32_t d, const bsa_params* p) {
 
 // ------------------------------------------------------------ layouts ----
 // Grid (N/32 row blocks, H), one wave: rows t0 .. t0+31 of head h gathered
-// through perm.  V, Q and dO are written row-major; K, Q and dO transposed per block,
-// position p of a [d][32] row holding row tpos(p) (the key order of the
-// forward's transposed V).
+// through perm.  V, Q and dO are written row-major, K also transposed per
+// block, position p of a [d][32] row holding row tpos(p) (the key order of
+// the forward's transposed V).
 template <int D>
 __global__ __launch_bounds__(64) void bsa_bwd_prep(const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ k,
@@ -108,11 +107,9 @@ __global__ __launch_bounds__(64) void bsa_bwd_prep(const uint16_t* __restrict__ 
                                                    int64_t N, uint16_t* __restrict__ vr,
                                                    uint16_t* __restrict__ qr,
                                                    uint16_t* __restrict__ dor,
-                                                   uint16_t* __restrict__ ktt,
-                                                   uint16_t* __restrict__ qtt,
-                                                   uint16_t* __restrict__ dott) {
+                                                   uint16_t* __restrict__ ktt) {
   constexpr int CPR = D / 8;                     // 16-byte pieces per row
-  __shared__ __attribute__((aligned(16))) uint16_t tl[3][32 * D];   // K, Q, dO
+  __shared__ __attribute__((aligned(16))) uint16_t tl[32 * D];
   const int lane = threadIdx.x;
   const int64_t blk = blockIdx.x;
   const int h = blockIdx.y;
@@ -122,28 +119,21 @@ __global__ __launch_bounds__(64) void bsa_bwd_prep(const uint16_t* __restrict__ 
     const int r = it / CPR, ch = it - r * CPR;
     const int64_t src = perm_index(perm[t0 + r], N) * rs + (int64_t)h * D + ch * 8;
     const int64_t dst = ((int64_t)h * N + t0 + r) * D + ch * 8;
-    const u32x4 xq = *(const u32x4*)(q + src), xd = *(const u32x4*)(dout + src);
     *(u32x4*)(vr + dst) = *(const u32x4*)(v + src);
-    *(u32x4*)(qr + dst) = xq;
-    *(u32x4*)(dor + dst) = xd;
-    *(u32x4*)&tl[0][r * D + ch * 8] = *(const u32x4*)(k + src);
-    *(u32x4*)&tl[1][r * D + ch * 8] = xq;
-    *(u32x4*)&tl[2][r * D + ch * 8] = xd;
+    *(u32x4*)(qr + dst) = *(const u32x4*)(q + src);
+    *(u32x4*)(dor + dst) = *(const u32x4*)(dout + src);
+    *(u32x4*)&tl[r * D + ch * 8] = *(const u32x4*)(k + src);
   }
   __syncthreads();
-  uint16_t* outs[3] = {ktt, qtt, dott};
+  for (int it = lane; it < 4 * D; it += 64) {
+    const int dd = it >> 2, q8 = it & 3;
+    u32x4 o;
 #pragma unroll
-  for (int x = 0; x < 3; ++x) {
-    for (int it = lane; it < 4 * D; it += 64) {
-      const int dd = it >> 2, q8 = it & 3;
-      u32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r0 = tpos(q8 * 8 + 2 * e), r1 = tpos(q8 * 8 + 2 * e + 1);
-        o[e] = uint32_t(tl[x][r0 * D + dd]) | (uint32_t(tl[x][r1 * D + dd]) << 16);
-      }
-      *(u32x4*)(outs[x] + (((int64_t)h * (N / 32) + blk) * D + dd) * 32 + q8 * 8) = o;
+    for (int e = 0; e < 4; ++e) {
+      const int r0 = tpos(q8 * 8 + 2 * e), r1 = tpos(q8 * 8 + 2 * e + 1);
+      o[e] = uint32_t(tl[r0 * D + dd]) | (uint32_t(tl[r1 * D + dd]) << 16);
     }
+    *(u32x4*)(ktt + (((int64_t)h * (N / 32) + blk) * D + dd) * 32 + q8 * 8) = o;
   }
 }
 
@@ -555,15 +545,18 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(2, 8) void bsa_bwd_q(
 // source, row-major): over the query blocks given by qblock(i) (tree
 // position of the block's first query) for i < nqb, accumulate dK^T and dV^T
 // of branch BR into acc[kb][0..DB) (dK^T, scaled) and acc[kb][DB..2DB)
-// (dV^T).  The query rows come from the tree-ordered copies qr and dor, so a
-// block is one contiguous run; its loads serve all NKB key blocks.
+// (dV^T).  A query block's Q and dO rows (one contiguous run each in the
+// tree-ordered copies qr, dor) are staged in the wave's LDS tiles tq, td:
+// row reads give the A operands of S = Q K^T and dP = dO V^T, transposed
+// reads the Q^T and dO^T operands.  The tiles are private to the wave, whose
+// LDS accesses complete in program order, so wave barriers (which only keep
+// the compiler from moving accesses across them) suffice.
 template <int D, int BR, int NKB, typename QFn>
 BT_DEV void kv_sweep(const uint16_t* __restrict__ qr, const uint16_t* __restrict__ dor,
-                     const uint16_t* __restrict__ qtt, const uint16_t* __restrict__ dott,
                      const float4* __restrict__ stats, const uint16_t* __restrict__ krow,
                      const uint16_t* __restrict__ vrow, int64_t N, int h, int nqb, QFn qblock,
-                     f32x16 (*acc)[2 * (D / 32)]) {
-  constexpr int DS = D / 16, DB = D / 32;
+                     uint16_t* tq, uint16_t* td, f32x16 (*acc)[2 * (D / 32)]) {
+  constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
   const int lane = threadIdx.x & 63, hf = lane >> 5, c = lane & 31;
   const float c2 = 1.4426950408889634f / sqrtf((float)D);
   bf16x8 kB[NKB][DS], vB[NKB][DS];
@@ -583,11 +576,20 @@ BT_DEV void kv_sweep(const uint16_t* __restrict__ qr, const uint16_t* __restrict
   const uint16_t* dh = dor + (int64_t)h * N * D;
   for (int i = 0; i < nqb; ++i) {
     const int64_t q0 = qblock(i);
+    __builtin_amdgcn_wave_barrier();   // the wave's reads of the last block came first
+#pragma unroll
+    for (int it = lane; it < 32 * CPR; it += 64) {
+      const int r = it / CPR, p = it - r * CPR;
+      const int t = tile_off<D>(r, p);
+      *(u32x4*)&tq[t] = *(const u32x4*)(qh + (q0 + r) * D + p * 8);
+      *(u32x4*)&td[t] = *(const u32x4*)(dh + (q0 + r) * D + p * 8);
+    }
+    __builtin_amdgcn_wave_barrier();
     bf16x8 qA[DS], dA[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      qA[s] = *(const bf16x8*)(qh + (q0 + c) * D + s * 16 + hf * 8);
-      dA[s] = *(const bf16x8*)(dh + (q0 + c) * D + s * 16 + hf * 8);
+      qA[s] = *(const bf16x8*)&tq[tile_off<D>(c, s * 2 + hf)];
+      dA[s] = *(const bf16x8*)&td[tile_off<D>(c, s * 2 + hf)];
     }
     f32x16 sa[NKB], pa[NKB];
 #pragma unroll
@@ -601,8 +603,6 @@ BT_DEV void kv_sweep(const uint16_t* __restrict__ qr, const uint16_t* __restrict
       }
     }
     // element e holds query 8*(e/4) + 4*hf + e%4 of the block
-    const uint16_t* qtb = qtt + ((int64_t)h * (N / 32) + q0 / 32) * D * 32 + c * 32 + hf * 8;
-    const uint16_t* dtb = dott + ((int64_t)h * (N / 32) + q0 / 32) * D * 32 + c * 32 + hf * 8;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       bf16x8 gpf[NKB], dsf[NKB];
@@ -619,8 +619,8 @@ BT_DEV void kv_sweep(const uint16_t* __restrict__ qr, const uint16_t* __restrict
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 qT = *(const bf16x8*)(qtb + db * 32 * 32 + s2 * 16);
-        const bf16x8 dT = *(const bf16x8*)(dtb + db * 32 * 32 + s2 * 16);
+        const bf16x8 qT = tr_operand<D>(tq, s2, db);
+        const bf16x8 dT = tr_operand<D>(td, s2, db);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           acc[kb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, dsf[kb], acc[kb][db], 0, 0, 0);
@@ -675,7 +675,6 @@ constexpr int kv_nkb() { return D == 32 ? 2 : 1; }
 template <int D, int NKB>
 __global__ __launch_bounds__(512) void bsa_bwd_kv_ball(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ dor,
-    const uint16_t* __restrict__ qtt, const uint16_t* __restrict__ dott,
     const float4* __restrict__ stats, const uint16_t* __restrict__ kt,
     const uint16_t* __restrict__ vr, int64_t N, int32_t ball, float* __restrict__ dkacc,
     float* __restrict__ dvacc) {
@@ -684,9 +683,11 @@ __global__ __launch_bounds__(512) void bsa_bwd_kv_ball(
   const int64_t b0 = (int64_t)blockIdx.x * ball;
   const int64_t r0 = b0 + w * 32 * NKB;
   f32x16 acc[NKB][2 * DB];
-  kv_sweep<D, 0, NKB>(qr, dor, qtt, dott, stats, kt + ((int64_t)h * N + r0) * D,
+  HIP_DYNAMIC_SHARED(uint16_t, tiles)
+  uint16_t* tq = tiles + (size_t)w * 2 * 32 * D;
+  kv_sweep<D, 0, NKB>(qr, dor, stats, kt + ((int64_t)h * N + r0) * D,
                       vr + ((int64_t)h * N + r0) * D, N, h, ball / 32,
-                      [&](int i) -> int64_t { return b0 + i * 32; }, acc);
+                      [&](int i) -> int64_t { return b0 + i * 32; }, tq, tq + 32 * D, acc);
   kv_store<D, NKB, false>(acc, r0, dkacc + (int64_t)h * N * D, dvacc + (int64_t)h * N * D);
 }
 
@@ -696,7 +697,6 @@ __global__ __launch_bounds__(512) void bsa_bwd_kv_ball(
 template <int D, int NKB>
 __global__ __launch_bounds__(512) void bsa_bwd_kv_slc(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ dor,
-    const uint16_t* __restrict__ qtt, const uint16_t* __restrict__ dott,
     const float4* __restrict__ stats, const uint16_t* __restrict__ kt,
     const uint16_t* __restrict__ vr, const uint32_t* __restrict__ off,
     const int32_t* __restrict__ list, int64_t N, int32_t nc, int32_t ngroups, int32_t group,
@@ -712,14 +712,16 @@ __global__ __launch_bounds__(512) void bsa_bwd_kv_slc(
   const int per = group / 32;
   const int nqb = e1 > e0 ? (int)(e1 - e0) * per : 0;
   f32x16 acc[NKB][2 * DB];
-  kv_sweep<D, 2, NKB>(qr, dor, qtt, dott, stats, kt + ((int64_t)h * N + r0) * D,
+  HIP_DYNAMIC_SHARED(uint16_t, tiles)
+  uint16_t* tq = tiles + (size_t)w * 2 * 32 * D;
+  kv_sweep<D, 2, NKB>(qr, dor, stats, kt + ((int64_t)h * N + r0) * D,
                       vr + ((int64_t)h * N + r0) * D, N, h, nqb,
                       [&](int i) -> int64_t {
                         const int e = i / per, qb = i - e * per;
                         const int64_t gg = perm_index(lh[e0 + e], ngroups);
                         return gg * group + qb * 32;
                       },
-                      acc);
+                      tq, tq + 32 * D, acc);
   kv_store<D, NKB, true>(acc, r0, dkacc + (int64_t)h * N * D, dvacc + (int64_t)h * N * D);
 }
 
@@ -729,7 +731,6 @@ __global__ __launch_bounds__(512) void bsa_bwd_kv_slc(
 template <int D, int NKB>
 __global__ __launch_bounds__(256) void bsa_bwd_kv_cmp(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ dor,
-    const uint16_t* __restrict__ qtt, const uint16_t* __restrict__ dott,
     const float4* __restrict__ stats, const uint16_t* __restrict__ kcb,
     const uint16_t* __restrict__ vcr, int32_t H, int64_t N, int32_t nc,
     float* __restrict__ cpart) {
@@ -740,9 +741,11 @@ __global__ __launch_bounds__(256) void bsa_bwd_kv_cmp(
   const int64_t nqb = N / 32;
   const int64_t i0 = nqb * part / kCmpParts, i1 = nqb * (part + 1) / kCmpParts;
   f32x16 acc[NKB][2 * DB];
-  kv_sweep<D, 1, NKB>(qr, dor, qtt, dott, stats, kcb + ((int64_t)h * nc + r0) * D,
+  HIP_DYNAMIC_SHARED(uint16_t, tiles)
+  uint16_t* tq = tiles + (size_t)w * 2 * 32 * D;
+  kv_sweep<D, 1, NKB>(qr, dor, stats, kcb + ((int64_t)h * nc + r0) * D,
                       vcr + ((int64_t)h * nc + r0) * D, N, h, (int)(i1 - i0),
-                      [&](int i) -> int64_t { return (i0 + i) * 32; }, acc);
+                      [&](int i) -> int64_t { return (i0 + i) * 32; }, tq, tq + 32 * D, acc);
   float* pk = cpart + (((int64_t)part * 2 + 0) * H + h) * nc * D;
   float* pv = cpart + (((int64_t)part * 2 + 1) * H + h) * nc * D;
   kv_store<D, NKB, false>(acc, r0, pk, pv);
@@ -844,8 +847,6 @@ static bt_status bwd_launch_d(const void* q, const void* k, const void* v, const
   uint16_t* qr = (uint16_t*)(b + L.qr);
   uint16_t* dor = (uint16_t*)(b + L.dor);
   uint16_t* ktt = (uint16_t*)(b + L.ktt);
-  uint16_t* qtt = (uint16_t*)(b + L.qtt);
-  uint16_t* dott = (uint16_t*)(b + L.dott);
   uint16_t* vcr = (uint16_t*)(b + L.vcr);
   uint16_t* kctt = (uint16_t*)(b + L.kctt);
   float4* stats = (float4*)(b + L.stats);
@@ -865,7 +866,7 @@ static bt_status bwd_launch_d(const void* q, const void* k, const void* v, const
   const dim3 w1(64);
   hipLaunchKernelGGL((bsa_bwd_prep<D>), dim3((unsigned)(N / 32), H), w1, 0, st,
                      (const uint16_t*)q, kin, vin, (const uint16_t*)dout, perm, H, N, vr, qr, dor,
-                     ktt, qtt, dott);
+                     ktt);
   hipLaunchKernelGGL((bsa_bwd_prep_coarse<D>), dim3(nc / 32, H), w1, 0, st, kcb, vct, nc, vcr,
                      kctt);
   const size_t idx_lds = (size_t)nc * 4;
@@ -912,17 +913,19 @@ static bt_status bwd_launch_d(const void* q, const void* k, const void* v, const
   constexpr int NK = kv_nkb<D>();
   const bool ball2 = NK == 2 && p->ball % 64 == 0, blk2 = NK == 2 && p->block % 64 == 0,
              cmp2 = NK == 2 && nc % 64 == 0;
+  // each wave stages a query block's Q and dO rows in two tiles of its own
+  const size_t tl_bytes = (size_t)2 * 32 * D * sizeof(uint16_t);
 #define BT_KVB(K)                                                                             \
   hipLaunchKernelGGL((bsa_bwd_kv_ball<D, K>), dim3((unsigned)(N / p->ball), H),               \
-                     dim3(p->ball / (32 * K) * 64), 0, st, qr, dor, qtt, dott, stats, kt, vr, N, \
-                     p->ball, dkacc, dvacc)
+                     dim3(p->ball / (32 * K) * 64), p->ball / (32 * K) * tl_bytes, st, qr, dor, \
+                     stats, kt, vr, N, p->ball, dkacc, dvacc)
 #define BT_KVS(K)                                                                             \
-  hipLaunchKernelGGL((bsa_bwd_kv_slc<D, K>), dim3(nc, H), dim3(p->block / (32 * K) * 64), 0, st, \
-                     qr, dor, qtt, dott, stats, kt, vr, off, list, N, nc, ngroups, p->group,      \
-                     p->block, p->topk, dkacc, dvacc)
+  hipLaunchKernelGGL((bsa_bwd_kv_slc<D, K>), dim3(nc, H), dim3(p->block / (32 * K) * 64),     \
+                     p->block / (32 * K) * tl_bytes, st, qr, dor, stats, kt, vr, off, list, N, nc, \
+                     ngroups, p->group, p->block, p->topk, dkacc, dvacc)
 #define BT_KVC(K)                                                                             \
   hipLaunchKernelGGL((bsa_bwd_kv_cmp<D, K>), dim3(nc / (32 * K), H, kCmpParts / 4), dim3(256), \
-                     0, st, qr, dor, qtt, dott, stats, kcb, vcr, H, N, nc, cpart)
+                     4 * tl_bytes, st, qr, dor, stats, kcb, vcr, H, N, nc, cpart)
   if (ball2) BT_KVB(NK); else BT_KVB(1);
   if (blk2) BT_KVS(NK); else BT_KVS(1);
   if (cmp2) BT_KVC(NK); else BT_KVC(1);
