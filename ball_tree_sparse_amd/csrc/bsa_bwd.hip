@@ -546,9 +546,11 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU(2, 8) void bsa_bwd_q(
 // position of the block's first query) for i < nqb, accumulate dK^T and dV^T
 // of branch BR into acc[kb][0..DB) (dK^T, scaled) and acc[kb][DB..2DB)
 // (dV^T).  A query block's Q and dO rows (one contiguous run each in the
-// tree-ordered copies qr, dor) are staged in the wave's LDS tiles tq, td:
-// row reads give the A operands of S = Q K^T and dP = dO V^T, transposed
-// reads the Q^T and dO^T operands.  The tiles are private to the wave, whose
+// tree-ordered copies qr, dor) are staged in the wave's LDS tiles tq, td
+// (td is followed by the block's 32 statistics): row reads give the A
+// operands of S = Q K^T and dP = dO V^T, transposed reads the Q^T and dO^T
+// operands.  The next block's rows and statistics are fetched into
+// registers while the current one is computed.  The tiles are private to the wave, whose
 // LDS accesses complete in program order, so wave barriers (which only keep
 // the compiler from moving accesses across them) suffice.
 template <int D, int BR, int NKB, typename QFn>
@@ -574,17 +576,34 @@ BT_DEV void kv_sweep(const uint16_t* __restrict__ qr, const uint16_t* __restrict
   const float4* sh = stats + ((int64_t)h * 3 + BR) * N;
   const uint16_t* qh = qr + (int64_t)h * N * D;
   const uint16_t* dh = dor + (int64_t)h * N * D;
+  // the next block's rows and statistics are fetched into registers while
+  // the current one is computed, then put into the wave's LDS tiles
+  constexpr int PPL = 32 * CPR / 64;            // 16-byte pieces per lane and tensor
+  float4* sst = (float4*)(td + 32 * D);          // statistics of the block's 32 queries
+  u32x4 fq[PPL], fd[PPL];
+  float4 fs = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fetch = [&](int64_t q0) {
+#pragma unroll
+    for (int u = 0; u < PPL; ++u) {
+      const int it = lane + u * 64, r = it / CPR, p = it - r * CPR;
+      fq[u] = *(const u32x4*)(qh + (q0 + r) * D + p * 8);
+      fd[u] = *(const u32x4*)(dh + (q0 + r) * D + p * 8);
+    }
+    if (lane < 32) fs = sh[q0 + lane];
+  };
+  if (nqb > 0) fetch(qblock(0));
   for (int i = 0; i < nqb; ++i) {
-    const int64_t q0 = qblock(i);
     __builtin_amdgcn_wave_barrier();   // the wave's reads of the last block came first
 #pragma unroll
-    for (int it = lane; it < 32 * CPR; it += 64) {
-      const int r = it / CPR, p = it - r * CPR;
+    for (int u = 0; u < PPL; ++u) {
+      const int it = lane + u * 64, r = it / CPR, p = it - r * CPR;
       const int t = tile_off<D>(r, p);
-      *(u32x4*)&tq[t] = *(const u32x4*)(qh + (q0 + r) * D + p * 8);
-      *(u32x4*)&td[t] = *(const u32x4*)(dh + (q0 + r) * D + p * 8);
+      *(u32x4*)&tq[t] = fq[u];
+      *(u32x4*)&td[t] = fd[u];
     }
+    if (lane < 32) sst[lane] = fs;
     __builtin_amdgcn_wave_barrier();
+    if (i + 1 < nqb) fetch(qblock(i + 1));
     bf16x8 qA[DS], dA[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
@@ -609,7 +628,7 @@ BT_DEV void kv_sweep(const uint16_t* __restrict__ qr, const uint16_t* __restrict
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int ee = s2 * 8 + e;
-        const float4 st = sh[q0 + 8 * (ee / 4) + 4 * hf + (ee % 4)];   // (m, 1/l, G, D)
+        const float4 st = sst[8 * (ee / 4) + 4 * hf + (ee % 4)];   // (m, 1/l, G, D)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sa[kb][ee], c2, -st.x)) * st.y;
@@ -684,7 +703,7 @@ __global__ __launch_bounds__(512) void bsa_bwd_kv_ball(
   const int64_t r0 = b0 + w * 32 * NKB;
   f32x16 acc[NKB][2 * DB];
   HIP_DYNAMIC_SHARED(uint16_t, tiles)
-  uint16_t* tq = tiles + (size_t)w * 2 * 32 * D;
+  uint16_t* tq = tiles + (size_t)w * (2 * 32 * D + 256);
   kv_sweep<D, 0, NKB>(qr, dor, stats, kt + ((int64_t)h * N + r0) * D,
                       vr + ((int64_t)h * N + r0) * D, N, h, ball / 32,
                       [&](int i) -> int64_t { return b0 + i * 32; }, tq, tq + 32 * D, acc);
@@ -713,7 +732,7 @@ __global__ __launch_bounds__(512) void bsa_bwd_kv_slc(
   const int nqb = e1 > e0 ? (int)(e1 - e0) * per : 0;
   f32x16 acc[NKB][2 * DB];
   HIP_DYNAMIC_SHARED(uint16_t, tiles)
-  uint16_t* tq = tiles + (size_t)w * 2 * 32 * D;
+  uint16_t* tq = tiles + (size_t)w * (2 * 32 * D + 256);
   kv_sweep<D, 2, NKB>(qr, dor, stats, kt + ((int64_t)h * N + r0) * D,
                       vr + ((int64_t)h * N + r0) * D, N, h, nqb,
                       [&](int i) -> int64_t {
@@ -728,8 +747,9 @@ __global__ __launch_bounds__(512) void bsa_bwd_kv_slc(
 // Compression branch: grid (nc/(32*NKB), H, kCmpParts/4), 4 waves; wave w
 // takes query partition z*4 + w of all N/32 query blocks for the coarse
 // tokens jb*32*NKB.. and writes its partial dKc / dVc.
+// (two waves per SIMD at d = 32: 7 registers spill, and it still beats one wave)
 template <int D, int NKB>
-__global__ __launch_bounds__(256) void bsa_bwd_kv_cmp(
+__global__ __launch_bounds__(256) BT_WAVES_PER_EU(D == 32 ? 2 : 1, 8) void bsa_bwd_kv_cmp(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ dor,
     const float4* __restrict__ stats, const uint16_t* __restrict__ kcb,
     const uint16_t* __restrict__ vcr, int32_t H, int64_t N, int32_t nc,
@@ -742,7 +762,7 @@ __global__ __launch_bounds__(256) void bsa_bwd_kv_cmp(
   const int64_t i0 = nqb * part / kCmpParts, i1 = nqb * (part + 1) / kCmpParts;
   f32x16 acc[NKB][2 * DB];
   HIP_DYNAMIC_SHARED(uint16_t, tiles)
-  uint16_t* tq = tiles + (size_t)w * 2 * 32 * D;
+  uint16_t* tq = tiles + (size_t)w * (2 * 32 * D + 256);
   kv_sweep<D, 1, NKB>(qr, dor, stats, kcb + ((int64_t)h * nc + r0) * D,
                       vcr + ((int64_t)h * nc + r0) * D, N, h, (int)(i1 - i0),
                       [&](int i) -> int64_t { return (i0 + i) * 32; }, tq, tq + 32 * D, acc);
@@ -913,8 +933,9 @@ static bt_status bwd_launch_d(const void* q, const void* k, const void* v, const
   constexpr int NK = kv_nkb<D>();
   const bool ball2 = NK == 2 && p->ball % 64 == 0, blk2 = NK == 2 && p->block % 64 == 0,
              cmp2 = NK == 2 && nc % 64 == 0;
-  // each wave stages a query block's Q and dO rows in two tiles of its own
-  const size_t tl_bytes = (size_t)2 * 32 * D * sizeof(uint16_t);
+  // each wave stages a query block's Q and dO rows in two tiles of its own,
+  // followed by the block's statistics
+  const size_t tl_bytes = (size_t)2 * 32 * D * sizeof(uint16_t) + 32 * sizeof(float4);
 #define BT_KVB(K)                                                                             \
   hipLaunchKernelGGL((bsa_bwd_kv_ball<D, K>), dim3((unsigned)(N / p->ball), H),               \
                      dim3(p->ball / (32 * K) * 64), p->ball / (32 * K) * tl_bytes, st, qr, dor, \
