@@ -120,7 +120,7 @@ static bt_status build_common(const float* coords, int64_t N, int32_t leaf, cons
   // testing and the cause has not been found, so they are switched off:
   // only trees whose root fits the one-wave LDS finisher are built.
   BT_REQUIRE(N <= kTreeMaxGpuNode || N == leaf,
-             "bt_build: trees with nodes above %lld points are switched off in this build "
+             "bt_build: trees with nodes above %lld points are switched off in this version "
              "(their global passes faulted the GPU; cause not found); N=%lld",
              (long long)kTreeMaxGpuNode, (long long)N);
   BT_REQUIRE(ws != nullptr, "workspace must be non-null");
@@ -278,7 +278,7 @@ bt_status bt_build_padded(const float* coords, int64_t N, int32_t leaf, const fl
   BT_REQUIRE(S > 0, "need N >= 1, leaf >= 1 and fewer than 2^31 slots (N=%lld, leaf=%d)",
              (long long)N, leaf);
   BT_REQUIRE(S <= kTreeMaxGpuNode || S == leaf,
-             "bt_build_padded: trees above %lld slots are switched off in this build "
+             "bt_build_padded: trees above %lld slots are switched off in this version "
              "(their global passes faulted the GPU; cause not found); slots=%lld",
              (long long)kTreeMaxGpuNode, (long long)S);
   if (R_host) {

@@ -4,7 +4,7 @@
 One step = one ball-attention pass (ball_attn) over one synthetic point cloud
 of the measured shape, gathering q/k/v through a tree permutation and
 scattering the result back to original order.  The GPU tree builder is
-limited to 1,024 points in this build, so the permutation is a seeded random
+limited to 1,024 points in this version, so the permutation is a seeded random
 one: the synthetic clouds are in random original order, so a tree order is a
 random gather pattern too, and the kernel's work does not depend on which
 permutation it is.  Inputs are resident in HBM before the timed region
@@ -26,7 +26,7 @@ Prints ONE JSON line.  Besides the required fields it carries:
                 own workloads: permute gather/scatter of 512-byte rows at the
                 rotated-pair size, the BSA step (also with group compression),
                 and tree build + fp32 ball attention at 1,024 points (the
-                largest tree the GPU builder takes in this build).
+                largest tree the GPU builder takes in this version).
 
 Other workloads (--workload bsa | cosmo | rotpair) print their own line and
 are not the default measurement.
@@ -442,8 +442,8 @@ def main():
                          "attention, backward, small trees); for kernel traces and counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
 

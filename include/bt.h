@@ -80,7 +80,7 @@ const char* bt_version(void);
  *   N < 2^31; writes perm [N] int32 (device).  ws: device workspace of at
  *   least bt_build_workspace_size(N, leaf) bytes, 256-byte aligned.
  *   Coordinates must be finite (not checked).
- *   In this build N is limited to 1024 (or N == leaf): the passes that split
+ *   In this version N is limited to 1024 (or N == leaf): the passes that split
  *   larger nodes are switched off after they faulted the GPU in testing.
  *   Errors: BT_EINVAL for null pointers, N not leaf*2^L, N >= 2^31, N above
  *   the limit; BT_ENOMEM for a short workspace.
