@@ -23,13 +23,15 @@ def _work(q, k, v, perm):
     b = ops.bsa_attn(q, k, v, perm, 128, 64, 64, 8, True,
                      gate_const=(0.5, 0.25, 0.25))
     g = ops.ball_attn_bwd(q, k, v, a, perm, 128)
-    return [a, b, *g]
+    gb = ops.bsa_attn_bwd(q, k, v, perm, a, 128, 64, 64, 8, True,
+                          gate_const=(0.5, 0.25, 0.25))
+    return [a, b, *g, *gb[:3]]
 
 
 def test_two_streams_match_serial_runs():
     dev = gpu()
     x1, x2 = _inputs(dev, 1), _inputs(dev, 2)
-    say("two streams: ball_attn, bsa_attn, ball_attn_bwd")
+    say("two streams: ball_attn, bsa_attn, ball_attn_bwd, bsa_attn_bwd")
     ref1 = _work(*x1)
     ref2 = _work(*x2)
     torch.cuda.synchronize()
