@@ -231,6 +231,8 @@ bt_status ball_attn(const void* q, const void* k, const void* v, const int32_t* 
     BT_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 4 == 0,
                "fp32 tensors must be 4-byte aligned");
   }
+  // the MFMA kernel reads a ball's permutation entries 2 or 4 at a time
+  BT_REQUIRE(((uintptr_t)perm & 15) == 0, "perm must be 16-byte aligned");
   return ball_attn_launch(q, k, v, perm, N, ball, H, d, dt, out, (hipStream_t)stream);
 }
 
@@ -337,6 +339,7 @@ bt_status ball_attn_padded(const void* q, const void* k, const void* v, const in
     BT_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 4 == 0,
                "fp32 tensors must be 4-byte aligned");
   }
+  BT_REQUIRE(((uintptr_t)perm & 15) == 0, "perm must be 16-byte aligned");
   return ball_attn_padded_launch(q, k, v, perm, n_rows, n_slots, ball, H, d, dt, out,
                                  (hipStream_t)stream);
 }

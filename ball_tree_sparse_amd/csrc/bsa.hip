@@ -9,8 +9,13 @@
 //           like V) over blocks of l tree positions; Q -> fp32 group means
 //           qbar (the pooled query).
 //   select  s[g, j] = qbar_g . Kc_j / sqrt(d) in fp32; blocks inside the
-//           group's own ball are excluded; top-k per (group, head) by
-//           repeated wave arg-max (ties to the smaller block index).
+//           group's own ball are excluded; top-k per (group, head), ties to
+//           the smaller block index: a wave bitonic sort of the 64 lane
+//           maxima gives the k-th best of them, a lower bound of the k-th
+//           score; the (score, block) pairs at least that good (k or a few
+//           more) are gathered through LDS and sorted the same way, best
+//           first.  Only when more than 64 pairs tie with the bound does the
+//           wave fall back to repeated arg-max.
 //   fused   one workgroup per (group, head), one wave per 32 queries: the
 //           ball, compression and selection branches run one after another
 //           as online-softmax attention over 64-key chunks (S^T = K Q^T and

@@ -788,8 +788,9 @@ bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const floa
   uint32_t* part = (uint32_t*)(b + p.off_part);
 
   if (p.G > 0) {
-    // zero every histogram and completion counter once; the last workgroup of
-    // each node clears what it used, so they stay zero between passes
+    // zero the histogram region once and set the root extents; afterwards
+    // each tree_select<p> clears its node's histogram after reading it, so
+    // the histograms are zero at the start of every radix pass
     const int64_t nwords = (int64_t)((p.off_state - p.off_hist) / 4);
     hipLaunchKernelGGL(tree_init, dim3(64), dim3(256), 0, st, hist, nwords, ext[0]);
     bt_status s = launch_status("tree_init");

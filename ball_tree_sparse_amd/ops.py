@@ -131,6 +131,38 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _coords(coords):
+    _dev(coords, "coords", torch.float32)
+    if coords.dim() != 2 or coords.shape[1] != 3:
+        raise ValueError(f"coords must be [N,3], got {tuple(coords.shape)}")
+    return coords.shape[0]
+
+
+def _perm(perm, n, name="perm"):
+    """A permutation argument: int32, 1-D, n entries (checked before any
+    launch, so a short array never reaches a kernel)."""
+    _dev(perm, name, torch.int32)
+    if perm.dim() != 1 or perm.numel() != n:
+        raise ValueError(f"{name} must be int32 [{n}], got {tuple(perm.shape)}")
+    return perm
+
+
+def _same_shape(t, ref, name):
+    if tuple(t.shape) != tuple(ref.shape):
+        raise ValueError(f"{name} must have shape {tuple(ref.shape)}, got {tuple(t.shape)}")
+
+
+def _gates(gate_w, gate_b, d):
+    if gate_w is not None:
+        _dev(gate_w, "gate_w", torch.float32)
+        if tuple(gate_w.shape) != (3, d):
+            raise ValueError(f"gate_w must be [3,{d}], got {tuple(gate_w.shape)}")
+    if gate_b is not None:
+        _dev(gate_b, "gate_b", torch.float32)
+        if tuple(gate_b.shape) != (3,):
+            raise ValueError(f"gate_b must be [3], got {tuple(gate_b.shape)}")
+
+
 # --------------------------------------------------------------------- tree --
 
 def bt_build_workspace_size(N: int, leaf: int) -> int:
@@ -143,11 +175,10 @@ def _workspace(nbytes, device):
 
 def bt_build(coords, leaf: int, perm=None, workspace=None):
     """Tree permutation of ``coords`` [N,3] fp32 -> int32 [N] (device)."""
-    _dev(coords, "coords", torch.float32)
-    N = coords.shape[0]
+    N = _coords(coords)
     if perm is None:
         perm = torch.empty(N, dtype=torch.int32, device=coords.device)
-    _dev(perm, "perm", torch.int32)
+    _perm(perm, N)
     need = lib().bt_build_workspace_size(N, leaf)
     if workspace is None:
         workspace = _workspace(need, coords.device)
@@ -158,13 +189,12 @@ def bt_build(coords, leaf: int, perm=None, workspace=None):
 
 def bt_rotate_build(coords, leaf: int, R, perm=None, workspace=None):
     """Tree of the coordinates rotated by the 3x3 matrix R (host values)."""
-    _dev(coords, "coords", torch.float32)
-    N = coords.shape[0]
+    N = _coords(coords)
     r = torch.as_tensor(R, dtype=torch.float32).reshape(9).cpu().tolist()
     rarr = (C.c_float * 9)(*r)
     if perm is None:
         perm = torch.empty(N, dtype=torch.int32, device=coords.device)
-    _dev(perm, "perm", torch.int32)
+    _perm(perm, N)
     need = lib().bt_build_workspace_size(N, leaf)
     if workspace is None:
         workspace = _workspace(need, coords.device)
@@ -181,8 +211,7 @@ def bt_padded_size(N: int, leaf: int) -> int:
 def bt_build_padded(coords, leaf: int, R=None, perm=None, workspace=None):
     """Padded tree of an uneven point count: int32 [bt_padded_size(N, leaf)]
     with -1 in unused slots (R: optional host 3x3 rotation)."""
-    _dev(coords, "coords", torch.float32)
-    N = coords.shape[0]
+    N = _coords(coords)
     S = lib().bt_padded_size(N, leaf)
     rarr = None
     if R is not None:
@@ -191,8 +220,8 @@ def bt_build_padded(coords, leaf: int, R=None, perm=None, workspace=None):
     if perm is None:
         perm = torch.empty(max(S, 0), dtype=torch.int32, device=coords.device)
     _dev(perm, "perm", torch.int32)
-    if perm.numel() < S:
-        raise ValueError(f"perm must hold {S} slots")
+    if perm.dim() != 1 or perm.numel() != S:
+        raise ValueError(f"perm must be int32 [{S}] (the slot count)")
     need = lib().bt_build_padded_workspace_size(N, leaf)
     if workspace is None:
         workspace = _workspace(need, coords.device)
@@ -206,12 +235,15 @@ def bt_build_padded(coords, leaf: int, R=None, perm=None, workspace=None):
 def bt_permute(src, perm, mode: int, dst=None):
     """GATHER dst[t] = src[perm[t]]; SCATTER dst[perm[t]] = src[t] (rows)."""
     _dev(src, "src")
-    _dev(perm, "perm", torch.int32)
+    if src.dim() < 1:
+        raise ValueError("src must have a row axis")
     N = src.shape[0]
+    _perm(perm, N)
     row_bytes = math.prod(src.shape[1:]) * src.element_size()
     if dst is None:
         dst = torch.empty_like(src)
     _dev(dst, "dst", src.dtype)
+    _same_shape(dst, src, "dst")
     _check(lib().bt_permute(_ptr(src), _ptr(perm), N, row_bytes, mode, _ptr(dst),
                             _stream(src.device)))
     return dst
@@ -223,6 +255,8 @@ def bt_permute_padded(src, perm, n_rows: int, mode: int, dst=None):
     [slots, ...] -> [n_rows, ...] from the used slots."""
     _dev(src, "src")
     _dev(perm, "perm", torch.int32)
+    if perm.dim() != 1:
+        raise ValueError("perm must be 1-D (one entry per slot)")
     S = perm.numel()
     row_bytes = math.prod(src.shape[1:]) * src.element_size()
     if dst is None:
@@ -239,8 +273,11 @@ def bt_permute_padded(src, perm, n_rows: int, mode: int, dst=None):
 
 def bt_invert_perm(perm, inv=None):
     _dev(perm, "perm", torch.int32)
+    if perm.dim() != 1:
+        raise ValueError("perm must be 1-D")
     if inv is None:
         inv = torch.empty_like(perm)
+    _perm(inv, perm.numel(), "inv")
     _check(lib().bt_invert_perm(_ptr(perm), perm.numel(), _ptr(inv), _stream(perm.device)))
     return inv
 
@@ -253,12 +290,14 @@ def bt_coarsen(x, perm, s: int, out=None):
     _dev(x, "x")
     if x.dim() != 3:
         raise ValueError("x must be [N,H,d]")
-    if perm is not None:
-        _dev(perm, "perm", torch.int32)
     N, H, d = x.shape
+    if perm is not None:
+        _perm(perm, N)
     if out is None:
         out = torch.empty((N // s if s > 0 else 0, H, d), dtype=x.dtype, device=x.device)
     _dev(out, "out", x.dtype)
+    if s > 0 and tuple(out.shape) != (N // s, H, d):
+        raise ValueError(f"out must be [{N // s},{H},{d}]")
     _check(lib().bt_coarsen(_ptr(x), _ptr(perm), N, H, d, s, _dtype_code(x), _ptr(out),
                             _stream(x.device)))
     return out
@@ -270,12 +309,14 @@ def bt_refine(xc, perm, s: int, out=None):
     _dev(xc, "xc")
     if xc.dim() != 3:
         raise ValueError("xc must be [N/s,H,d]")
-    if perm is not None:
-        _dev(perm, "perm", torch.int32)
     Nc, H, d = xc.shape
+    if perm is not None:
+        _perm(perm, Nc * s)
     if out is None:
         out = torch.empty((Nc * s, H, d), dtype=xc.dtype, device=xc.device)
     _dev(out, "out", xc.dtype)
+    if tuple(out.shape) != (Nc * s, H, d):
+        raise ValueError(f"out must be [{Nc * s},{H},{d}]")
     _check(lib().bt_refine(_ptr(xc), _ptr(perm), Nc * s, H, d, s, _dtype_code(xc), _ptr(out),
                            _stream(xc.device)))
     return out
@@ -289,12 +330,13 @@ def ball_attn(q, k, v, perm, ball: int, out=None):
         _dev(t, name, q.dtype)
         if t.shape != q.shape or t.dim() != 3:
             raise ValueError("q, k, v must share one [N,H,d] shape")
-    if perm is not None:
-        _dev(perm, "perm", torch.int32)
     N, H, d = q.shape
+    if perm is not None:
+        _perm(perm, N)
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype)
+    _same_shape(out, q, "out")
     _check(lib().ball_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), N, ball, H, d,
                            _dtype_code(q), _ptr(out), _stream(q.device)))
     return out
@@ -308,10 +350,13 @@ def ball_attn_padded(q, k, v, perm, ball: int, out=None):
         if t.shape != q.shape or t.dim() != 3:
             raise ValueError("q, k, v must share one [N,H,d] shape")
     _dev(perm, "perm", torch.int32)
+    if perm.dim() != 1:
+        raise ValueError("perm must be 1-D (one entry per slot)")
     N, H, d = q.shape
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype)
+    _same_shape(out, q, "out")
     _check(lib().ball_attn_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), N, perm.numel(), ball,
                                   H, d, _dtype_code(q), _ptr(out), _stream(q.device)))
     return out
@@ -323,14 +368,15 @@ def ball_attn_bwd(q, k, v, dout, perm, ball: int, dq=None, dk=None, dv=None):
         _dev(t, name, q.dtype)
         if t.shape != q.shape or t.dim() != 3:
             raise ValueError("q, k, v, dout must share one [N,H,d] shape")
-    if perm is not None:
-        _dev(perm, "perm", torch.int32)
     N, H, d = q.shape
+    if perm is not None:
+        _perm(perm, N)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         _dev(t, name, q.dtype)
+        _same_shape(t, q, name)
     _check(lib().ball_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(perm), N, ball, H,
                                d, _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv),
                                _stream(q.device)))
@@ -361,14 +407,11 @@ def bsa_attn(q, k, v, perm, ball: int, block: int, group: int, topk: int,
         _dev(t, name, q.dtype)
         if t.shape != q.shape or t.dim() != 3:
             raise ValueError("q, k, v must share one [N,H,d] shape")
-    _dev(perm, "perm", torch.int32)
     N, H, d = q.shape
+    _perm(perm, N)
     p = BsaParams(ball, block, group, topk, int(bool(mask_own_ball)),
                   int(bool(query_compression)))
-    if gate_w is not None:
-        _dev(gate_w, "gate_w", torch.float32)
-    if gate_b is not None:
-        _dev(gate_b, "gate_b", torch.float32)
+    _gates(gate_w, gate_b, d)
     gc = None
     if gate_const is not None:
         gc = (C.c_float * 3)(*[float(x) for x in gate_const])
@@ -377,6 +420,8 @@ def bsa_attn(q, k, v, perm, ball: int, block: int, group: int, topk: int,
         sel = torch.empty((H, N // group, topk), dtype=torch.int32, device=q.device)
     if out is None:
         out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    _same_shape(out, q, "out")
     need = lib().bsa_workspace_size(N, H, d, C.byref(p))
     if workspace is None:
         workspace = _workspace(need, q.device)
@@ -396,13 +441,10 @@ def bsa_attn_bwd(q, k, v, perm, dout, ball: int, block: int, group: int, topk: i
         _dev(t, name, q.dtype)
         if t.shape != q.shape or t.dim() != 3:
             raise ValueError("q, k, v, dout must share one [N,H,d] shape")
-    _dev(perm, "perm", torch.int32)
     N, H, d = q.shape
+    _perm(perm, N)
     p = BsaParams(ball, block, group, topk, int(bool(mask_own_ball)), 0)
-    if gate_w is not None:
-        _dev(gate_w, "gate_w", torch.float32)
-    if gate_b is not None:
-        _dev(gate_b, "gate_b", torch.float32)
+    _gates(gate_w, gate_b, d)
     gc = None
     dgw = dgb = None
     if gate_const is not None:

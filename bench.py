@@ -2,31 +2,41 @@
 """Benchmark of the ball-tree + ball-attention hot path on one MI355X.
 
 One step = one ball-attention pass (ball_attn) over one synthetic point cloud
-of the measured shape, gathering q/k/v through a tree permutation and
-scattering the result back to original order.  The GPU tree builder is
-limited to 1,024 points in this version, so the permutation is a seeded random
-one: the synthetic clouds are in random original order, so a tree order is a
-random gather pattern too, and the kernel's work does not depend on which
-permutation it is.  Inputs are resident in HBM before the timed region
-starts.  The q/k/v/out tensors rotate over several copies
-(default 4, 540 MB in all) so that no step finds its inputs in the 256 MB
-Infinity Cache left behind by the previous one.
+of the measured shape, gathering q/k/v through a permutation into ball order
+and scattering the result back to original order.  The GPU tree builder
+refuses trees above 1,024 points in this version, so the step's permutation
+is a seeded random one (the config says so): the synthetic clouds are in
+random original order, so a tree order is a random gather pattern too, and
+the kernel's work does not depend on which permutation it is.  Inputs are
+resident in HBM before the timed region starts.  The q/k/v/out tensors rotate
+over several copies (default 4, 540 MB in all) so that no step finds its
+inputs in the 256 MB Infinity Cache left behind by the previous one.
+
+Timing: before the W warmup steps the kernel runs back to back for about
+0.3 s so that the clocks settle (reported as config.settle_launches); then
+the K timed steps run back to back between two HIP events recorded on the
+launching stream.  `value`, `ms_per_step` and `roofline.achieved` all come
+from that one event interval.
 
 Prints ONE JSON line.  Besides the required fields it carries:
   roofline      for the ball-attention kernel: algorithmic bytes per launch
                 (q, k, v read once, out written once, perm read once) over the
-                mean launch time measured with HIP events on the launching
-                stream, against the 8 TB/s HBM peak; `traffic` is the HBM
-                byte count of the kernel per launch from rocprofv3 FETCH_SIZE +
-                WRITE_SIZE counters (profiles/), or null if the kernel source
-                changed since they were taken;
+                mean launch time, against the 8 TB/s HBM peak (source in
+                peak_source); `traffic` is the HBM byte count of the kernel
+                per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters
+                (profiles/), or null if the kernel source changed since they
+                were taken; `measured_copy_GBps` is a timed 128 MiB
+                device-to-device copy in the same run, a secondary reference;
   cpu_baseline  the CPU oracle (NumPy fp64 ball attention) timed on this
-                host on whole steps of the same workload;
+                host on whole steps of the same workload, with the CPU model
+                and the BLAS thread count;
   rows          the other rows of the path timed in the same run on their
                 own workloads: permute gather/scatter of 512-byte rows at the
-                rotated-pair size, the BSA step (also with group compression),
-                and tree build + fp32 ball attention at 1,024 points (the
-                largest tree the GPU builder takes in this version).
+                rotated-pair size, coarsen/refine, the BSA step (also with
+                group compression) with the count of top-k rows whose
+                selection differs from the oracle's (near ties), padded
+                attention, the backward passes, and tree build + fp32 ball
+                attention at 1,024 points.
 
 Other workloads (--workload bsa | cosmo | rotpair) print their own line and
 are not the default measurement.
@@ -46,6 +56,19 @@ sys.path.insert(0, ROOT)
 METRIC = "ball-attn points/sec + TFLOP/s (% roofline) at N=65,536, ball 128, H=8 d=32"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_SOURCE = ("AMD Instinct MI355X public specification: HBM3E 8.0 TB/s; dense bf16 "
+               "MFMA 2.5 PFLOP/s (without sparsity); 256 CUs at 2.4 GHz")
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _src_hash(names):
@@ -69,8 +92,11 @@ def _traffic(kernel_key, src_names):
     return t.get("bytes_per_launch")
 
 
-def _cpu_baseline(w, budget_s):
-    """The oracle on whole steps of the workload until the budget is spent."""
+def _cpu_baseline(w, budget_s, sel_check=None):
+    """The oracle on whole steps of the workload until the budget is spent.
+    With sel_check (the BSA row's inputs and the GPU's selections), the
+    oracle's top-k selection is computed too and the rows whose selected set
+    differs from the GPU's are counted (near ties of fp32 scores)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -85,10 +111,41 @@ def _cpu_baseline(w, budget_s):
         if el >= budget_s:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": steps * n / el, "unit": "points/s", "cores": threads, "kind": "oracle",
-            "sample": f"{steps} whole steps (fp64 ball attention over all balls) of the "
-                      f"{n}-point workload in {el:.1f} s, through {threads}-thread BLAS on "
-                      f"{len(os.sched_getaffinity(0))} host cores"}
+    out = {"value": steps * n / el, "unit": "points/s", "cores": threads, "kind": "oracle",
+           "cpu_model": _cpu_model(), "host_cores_visible": len(os.sched_getaffinity(0)),
+           "sample": f"{steps} whole steps (fp64 ball attention over all balls) of the "
+                     f"{n}-point workload in {el:.1f} s, through {threads}-thread BLAS"}
+    if sel_check is not None:
+        out["bsa_topk_rows_differing"] = _sel_differences(**sel_check)
+    return out
+
+
+def _sel_differences(wb, perm, sel_gpu, tau_rel=1e-4):
+    """Rows (head, group) whose GPU top-k set differs from the oracle's, and
+    how many of those differ only by near ties (every differing block's
+    fp64 score within tau_rel * max|s| of the oracle's k-th score)."""
+    import numpy as np
+
+    from oracle import bsa as B
+    x = wb.extra
+    qt = np.asarray(wb.q.float().numpy(), np.float64)[perm]
+    kt = np.asarray(wb.k.float().numpy(), np.float64)[perm]
+    kc = B.pool_blocks(kt, x["block"])
+    sel, s = B.select(qt, kc, wb.ball, x["block"], x["group"], x["topk"], x["mask_own_ball"])
+    diff = near = 0
+    H, G, K = sel.shape
+    for h in range(H):
+        for g in range(G):
+            a, b = set(sel[h, g].tolist()), set(sel_gpu[h, g].tolist())
+            if a == b:
+                continue
+            diff += 1
+            sc = s[g, h]
+            kth = sc[sel[h, g][-1]]
+            tau = tau_rel * np.max(np.abs(sc[np.isfinite(sc)]))
+            near += all(abs(sc[j] - kth) <= tau for j in a ^ b)
+    return {"rows": H * G, "differing": diff, "differing_by_near_ties": near,
+            "tau": f"{tau_rel} * max|s| of the row"}
 
 
 def bench_ball(args, dev, torch, ops, synth):
@@ -108,34 +165,41 @@ def bench_ball(args, dev, torch, ops, synth):
     for i in range(len(sets)):                 # load the kernel, touch every set
         step(i)
     torch.cuda.synchronize()
-    if args.copy_probe:
-        # a plain device copy of known size, for scaling HBM byte counters
-        src = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+    # a plain device-to-device copy of known size: a measured bandwidth
+    # reference, and the scale for HBM byte counters
+    src = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    copy_us = _event_us(torch, lambda: dst.copy_(src), 20, warm=4)
+    copy_gbs = 2 * src.numel() / copy_us / 1e3
+    del src, dst
     if args.eager:
         for i in range(args.steps):
             step(i)
         torch.cuda.synchronize()
         print(json.dumps({"eager_launches": args.steps}), flush=True)
         return None
-    # warmup: back-to-back launches until the clocks have settled
+    # clock settle: back-to-back launches for about 0.3 s, then the warmup
+    settle, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < args.settle_seconds:
+        for i in range(50):
+            step(i)
+        settle += 50
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: back-to-back launches on the current stream, HIP events
-    # recorded on that stream around them
+    # timed region: exactly `steps` back-to-back launches on the current
+    # stream (the one the library launches on), HIP events on that stream
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     nsteps = args.steps
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
     for i in range(nsteps):
         step(i)
     e1.record()
     torch.cuda.synchronize()
-    el = time.perf_counter() - t0
+    host_el = time.perf_counter() - t0
     attn_us = e0.elapsed_time(e1) * 1e3 / nsteps
     # the same launches replayed from a HIP graph (one launch per input set),
     # for comparison: replays add a gap between kernels
@@ -171,32 +235,40 @@ def bench_ball(args, dev, torch, ops, synth):
     attn_flops = 4 * N * ball * d * H
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
     traffic = _traffic(f"ball_attn/{args.workload}", ["ball_attn.hip", "common.h"])
-    ms = el / nsteps * 1e3
+    ms = attn_us * 1e-3
     line = {
         "metric": METRIC, "value": N / (ms * 1e-3), "unit": "points/s", "n_gpus": 1,
         "steps": nsteps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"{args.workload}: ball attention over a tree permutation, "
-                               f"N={N}, ball {ball}, H={H}, d={d}, {w.dtype}",
+        "config": {"workload": f"{args.workload}: ball attention over a seeded random "
+                               f"permutation (gather through it, scatter back; the GPU tree "
+                               f"builder refuses {N} points in this version), N={N}, "
+                               f"ball {ball}, H={H}, d={d}, {w.dtype}",
                    "N": N, "ball": ball, "leaf": leaf, "H": H, "d": d,
-                   "input_sets_rotated": len(sets),
-                   "timing": "back-to-back launches on one stream; HIP events on that "
-                             "stream around the timed launches"},
+                   "input_sets_rotated": len(sets), "settle_launches": settle,
+                   "timing": "exactly `steps` back-to-back launches on one stream between "
+                             "two HIP events on that stream; value, ms_per_step and "
+                             "roofline.achieved all come from that interval",
+                   "host_wall_ms_per_step": host_el / nsteps * 1e3},
         "roofline": {"kernel": "ball_attn_mfma" if w.dtype == "bf16" else "ball_attn_valu",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes": attn_bytes},
+                     "traffic": traffic, "algorithmic_bytes": attn_bytes,
+                     "peak_source": PEAK_SOURCE,
+                     "measured_copy_GBps": copy_gbs,
+                     "frac_of_measured_copy": achieved / copy_gbs},
         "ball_attn": {"us": attn_us, "us_graph_replay": graph_us,
                       "us_single_median": single[len(single) // 2], "us_single_min": single[0],
                       "points_per_s": N / (attn_us * 1e-6),
                       "tflops": attn_flops / (attn_us * 1e-6) / 1e12,
                       "mfma_frac": attn_flops / (attn_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
     }
+    sel_check = {}
     if not args.no_side_rows:
-        line["rows"] = side_rows(dev, torch, ops, synth)
+        line["rows"] = side_rows(dev, torch, ops, synth, sel_check)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = _cpu_baseline(w, args.cpu_seconds)
+        line["cpu_baseline"] = _cpu_baseline(w, args.cpu_seconds, sel_check or None)
     return line
 
 
@@ -215,7 +287,7 @@ def _event_us(torch, fn, reps, warm=3):
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
-def side_rows(dev, torch, ops, synth):
+def side_rows(dev, torch, ops, synth, sel_check=None):
     """The other rows of the path, timed in the same run on their own
     workloads: permute (gather and scatter of 512-byte rows at the rotated-
     pair size), coarsen / refine, the BSA steps, padded ball attention of an
@@ -283,6 +355,11 @@ def side_rows(dev, torch, ops, synth):
                                                x["topk"], x["mask_own_ball"], gate_w=Wg,
                                                out=out, workspace=bws), 100, warm=20)
     flops = 4 * N * H * d * (w.ball + N // x["block"] + x["topk"] * x["block"])
+    if sel_check is not None:
+        _, sel = ops.bsa_attn(q, k, v, p, w.ball, x["block"], x["group"], x["topk"],
+                              x["mask_own_ball"], gate_w=Wg, out=out, workspace=bws,
+                              return_sel=True)
+        sel_check.update(wb=w, perm=p.cpu().numpy(), sel_gpu=sel.cpu().numpy())
     rows["a7_a11_bsa"] = {"workload": "N=65536 deformed sphere, ball 128, block 64, group 64, "
                                       "top-16, H=8, d=32 bf16",
                           "us_per_step": us, "points_per_s": N / (us * 1e-6),
@@ -435,8 +512,11 @@ def main():
     ap.add_argument("--eager", action="store_true",
                     help="only launch the kernels (for counter collection)")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a plain device copy of known size (counter scaling)")
+                    help="with --rows-only: also run a plain device copy of known size "
+                         "(counter scaling; the default line always times one)")
     ap.add_argument("--copy-probe-mb", type=int, default=128)
+    ap.add_argument("--settle-seconds", type=float, default=0.3,
+                    help="back-to-back launches before the warmup, for the clocks")
     ap.add_argument("--rows-only", action="store_true",
                     help="time only the other rows (permute, coarsen/refine, BSA, padded "
                          "attention, backward, small trees); for kernel traces and counters")

@@ -170,8 +170,8 @@ bt_status bt_refine(const void* xc, const int32_t* perm, int64_t N, int32_t H,
  * no mask, no bias, non-causal.  out[perm[t]] = O[t] (out in the same order
  * and dtype as the inputs).
  * Requirements: ball >= 1 divides N; 1 <= H; d in {16, 32, 64};
- * ball <= 4096; N*H*d < 2^31; out does not alias q, k or v.  N = 0 is a
- * no-op (pointers are not used).  Errors: BT_EINVAL for a violated
+ * ball <= 4096; N*H*d < 2^31; out does not alias q, k or v; perm (when
+ * given) 16-byte aligned.  N = 0 is a no-op (pointers are not used).  Errors: BT_EINVAL for a violated
  * requirement or a null pointer with N > 0; BT_EHIP if the launch fails.
  * bf16 with d in {32, 64} and ball a multiple of 32 up to 256 runs the MFMA
  * kernel; every other supported shape runs the fp32-VALU kernel.
@@ -210,7 +210,7 @@ bt_status ball_attn(const void* q, const void* k, const void* v,
  *   H, d] in original order; perm [n_slots] as above (required); the keys of
  *   a ball are its used slots, and out[perm[t]] is written for every used
  *   slot t only.  Requirements: ball | n_slots; 1 <= n_rows <= n_slots;
- *   otherwise as ball_attn.  Errors: BT_EINVAL for a violated requirement or
+ *   perm 16-byte aligned; otherwise as ball_attn.  Errors: BT_EINVAL for a violated requirement or
  *   a null pointer; BT_EHIP if the launch fails.
  * All three are asynchronous on stream and allocate nothing.
  * ---------------------------------------------------------------------- */

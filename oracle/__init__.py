@@ -19,6 +19,8 @@ Modules
                compression variant), in fp64.
 ``bsa_bwd``    gradients of BSA (dq, dk, dv and the gate parameters), in fp64.
 ``pool``       coarsening (means of consecutive tree positions) and refinement.
+``permute``    row gather / scatter between original and tree order, the
+               inverse permutation, and their padded forms.
 ``checks``     tree invariant checkers (plain and padded), independent of
                ``tree``.
 

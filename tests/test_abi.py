@@ -98,6 +98,10 @@ def test_ball_attn_rejects(L):
     assert call(args(out=q)) == ops.BT_EINVAL            # aliasing
     assert call(args(q=None)) == ops.BT_EINVAL
     assert call(args(ball=8192, N=8192)) == ops.BT_EINVAL
+    buf = C.create_string_buffer(64)
+    pa = (C.addressof(buf) + 15) & ~15
+    assert call(args(perm=C.c_void_p(pa + 4), N=64)) == ops.BT_EINVAL    # perm misaligned
+    assert b"aligned" in L.bt_last_error()
     # no points: a no-op that touches no pointer; shape checks still apply
     assert call(args(N=0, q=None, k=None, v=None, out=None)) == ops.BT_OK
     assert call(args(N=0, d=24, q=None, k=None, v=None, out=None)) == ops.BT_EINVAL

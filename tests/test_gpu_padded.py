@@ -5,6 +5,7 @@ import pytest
 
 from ball_tree_sparse_amd import ops, synth
 from oracle import attention as A
+from oracle import permute as P
 from oracle import checks as CK
 from oracle import tree as T
 from tests.helpers import gpu, max_abs, say
@@ -69,11 +70,10 @@ def test_permute_padded(n, shape, dtype):
     g = ops.bt_permute_padded(x.to(dev), pd, n, ops.BT_GATHER)
     back = ops.bt_permute_padded(g, pd, n, ops.BT_SCATTER)
     torch.cuda.synchronize()
-    want = torch.zeros((slots,) + shape, dtype=dtype)
-    used = torch.from_numpy(perm >= 0)
-    want[used] = x[torch.from_numpy(perm[perm >= 0]).long()]
-    assert torch.equal(g.cpu(), want)
-    assert torch.equal(back.cpu(), x)
+    as_np = lambda t: (t.cpu().view(torch.int16) if t.dtype == torch.bfloat16 else t.cpu()).numpy()
+    assert np.array_equal(as_np(g), P.gather_padded(as_np(x), perm))
+    assert np.array_equal(as_np(back), P.scatter_padded(as_np(g), perm, n))
+    assert np.array_equal(as_np(back), as_np(x))
 
 
 @pytest.mark.parametrize("n,leaf,H,d,ball,dtype", [

@@ -5,10 +5,17 @@ import torch
 
 from ball_tree_sparse_amd import ops, synth
 from oracle import attention as A
+from oracle import permute as P
 from oracle import tree as T
 from tests.helpers import gpu, max_abs, say
 
 pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    """Host copy as a NumPy array of the same bytes (bf16 viewed as int16)."""
+    t = t.cpu()
+    return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t).numpy()
 
 
 @pytest.mark.parametrize("n,shape,dtype", [
@@ -19,6 +26,8 @@ pytestmark = pytest.mark.gpu
     (262144, (8, 32), torch.bfloat16),   # the rotated-pair size
 ])
 def test_gather_scatter_identities(n, shape, dtype):
+    """Byte-exact against oracle/permute.py, plus the identities
+    scatter(gather(x, p), p) == x and gather(x, inv(p)) == scatter(x, p)."""
     dev = gpu()
     g = torch.Generator().manual_seed(n)
     x = torch.randn((n,) + shape, generator=g).to(dtype) if dtype != torch.int32 else \
@@ -32,12 +41,12 @@ def test_gather_scatter_identities(n, shape, dtype):
     inv = ops.bt_invert_perm(pd)
     ga_inv = ops.bt_permute(xd, inv, ops.BT_GATHER)
     torch.cuda.synchronize()
-    assert torch.equal(ga.cpu(), x[perm.long()])
-    ref = torch.empty_like(x); ref[perm.long()] = x
-    assert torch.equal(sc.cpu(), ref)
-    assert torch.equal(back.cpu(), x)
-    assert torch.equal(ga_inv.cpu(), sc.cpu())
-    assert torch.equal(inv.cpu(), torch.argsort(perm.long()).to(torch.int32))
+    xn, pn = _np(x), perm.numpy()
+    assert np.array_equal(_np(ga), P.gather(xn, pn))
+    assert np.array_equal(_np(sc), P.scatter(xn, pn))
+    assert np.array_equal(_np(back), xn)
+    assert np.array_equal(_np(ga_inv), _np(sc))
+    assert np.array_equal(inv.cpu().numpy(), P.invert(pn))
 
 
 def _rotated_pair(n, leaf):
