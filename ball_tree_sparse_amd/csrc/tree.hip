@@ -725,8 +725,20 @@ struct TreePlan {
   int L;         // total levels
   int G;         // levels split by the global passes
   int64_t nf;    // node size handed to the finisher
+  size_t nodes_next, nodes_max, max_chunks;
   size_t off_rec0, off_rec1, off_ext0, off_ext1, off_hist, off_state, off_counts,
       off_part, total;
+};
+
+// The workspace arrays of one build, with their capacities in elements.
+struct TreeBufs {
+  float4* rec[2];
+  uint32_t* ext[2];
+  uint32_t* hist;
+  NodeState* state;
+  uint2* counts;
+  uint32_t* part;
+  size_t n_rec, n_ext, n_hist, n_state, n_counts, n_part;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -754,45 +766,82 @@ static TreePlan plan_tree(int64_t n, int leaf) {
   while (G < L && (n >> G) > kFinish) ++G;
   p.G = G;
   p.nf = n >> G;
+  p.nodes_next = (size_t)1 << G;                       // children of the last global level
+  p.nodes_max = G ? ((size_t)1 << (G - 1)) : 1;        // nodes of the last global level
+  p.max_chunks = 1;
+  for (int lev = 0; lev < G; ++lev) {
+    const size_t nc = (size_t)(n / chunk_for(n, n >> lev));
+    if (nc > p.max_chunks) p.max_chunks = nc;
+  }
   size_t o = 0;
   p.off_rec0 = o; o = align256(o + (size_t)n * 16);
   p.off_rec1 = o; o = align256(o + (size_t)n * 16);
-  const size_t nodes_next = (size_t)1 << G;            // children of the last global level
-  const size_t nodes_max = G ? ((size_t)1 << (G - 1)) : 1;
-  p.off_ext0 = o; o = align256(o + nodes_next * 6 * 4);
-  p.off_ext1 = o; o = align256(o + nodes_next * 6 * 4);
-  p.off_hist = o; o = align256(o + nodes_max * kBins * 4);
-  p.off_state = o; o = align256(o + nodes_max * sizeof(NodeState));
-  size_t max_chunks = 1;
-  for (int lev = 0; lev < G; ++lev) {
-    const size_t nc = (size_t)(n / chunk_for(n, n >> lev));
-    if (nc > max_chunks) max_chunks = nc;
-  }
-  p.off_counts = o; o = align256(o + max_chunks * 8);
-  p.off_part = o; o = align256(o + max_chunks * 12 * 4);
+  p.off_ext0 = o; o = align256(o + p.nodes_next * 6 * 4);
+  p.off_ext1 = o; o = align256(o + p.nodes_next * 6 * 4);
+  p.off_hist = o; o = align256(o + p.nodes_max * kBins * 4);
+  p.off_state = o; o = align256(o + p.nodes_max * sizeof(NodeState));
+  p.off_counts = o; o = align256(o + p.max_chunks * 8);
+  p.off_part = o; o = align256(o + p.max_chunks * 12 * 4);
   p.total = o;
   return p;
 }
 
 size_t tree_workspace_size(int64_t n, int leaf) { return plan_tree(n, leaf).total; }
 
-bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const float* R,
-                            int32_t* perm, void* ws, hipStream_t st) {
-  const TreePlan p = plan_tree(n, leaf);
+static TreeBufs carve_tree(const TreePlan& p, void* ws) {
   char* b = (char*)ws;
-  float4* rec[2] = {(float4*)(b + p.off_rec0), (float4*)(b + p.off_rec1)};
-  uint32_t* ext[2] = {(uint32_t*)(b + p.off_ext0), (uint32_t*)(b + p.off_ext1)};
-  uint32_t* hist = (uint32_t*)(b + p.off_hist);
-  NodeState* state = (NodeState*)(b + p.off_state);
-  uint2* counts = (uint2*)(b + p.off_counts);
-  uint32_t* part = (uint32_t*)(b + p.off_part);
+  TreeBufs t{};
+  t.rec[0] = (float4*)(b + p.off_rec0);
+  t.rec[1] = (float4*)(b + p.off_rec1);
+  t.ext[0] = (uint32_t*)(b + p.off_ext0);
+  t.ext[1] = (uint32_t*)(b + p.off_ext1);
+  t.hist = (uint32_t*)(b + p.off_hist);
+  t.state = (NodeState*)(b + p.off_state);
+  t.counts = (uint2*)(b + p.off_counts);
+  t.part = (uint32_t*)(b + p.off_part);
+  t.n_rec = (size_t)p.n;
+  t.n_ext = p.nodes_next * 6;
+  t.n_hist = p.nodes_max * kBins;
+  t.n_state = p.nodes_max;
+  t.n_counts = p.max_chunks;
+  t.n_part = p.max_chunks * 12;
+  return t;
+}
 
+// Host check, before any launch of a level, that every index the level's
+// kernels derive from their grid fits the array it addresses: chunk c of
+// node c / cpn reads rec[c * chunk + i] (i < chunk) and writes counts[c] and
+// part[12 c + j] (j < 12); node k uses hist[k * kBins + b] (b < kBins),
+// state[k] and ext[6 k + a] (a < 6), and its scatter writes rec[k * nsize +
+// i] (i < nsize); tree_extents writes ext[12 k + j] of the next level.  The
+// plan makes these hold by construction; a violation is reported, never
+// launched.
+static bool level_fits(const TreePlan& p, const TreeBufs& b, int lev, int64_t nsize, int chunk,
+                       int cpn, int nchunks, int nodes) {
+  const bool tiles = chunk > 0 && (int64_t)chunk * cpn == nsize && (int64_t)nodes * nsize == p.n &&
+                     nchunks == nodes * cpn;
+  return tiles && (size_t)nchunks * chunk <= b.n_rec && (size_t)nodes * nsize <= b.n_rec &&
+         (size_t)nchunks <= b.n_counts && (size_t)nchunks * 12 <= b.n_part &&
+         (size_t)nodes * kBins <= b.n_hist && (size_t)nodes <= b.n_state &&
+         (size_t)nodes * 6 <= b.n_ext && (size_t)nodes * 12 <= b.n_ext && lev < p.G;
+}
+
+// Runs the build on the arrays of b (carved from one workspace by
+// tree_build_launch; given separately by tests).
+bt_status tree_build_bufs(const TreePlan& p, const TreeBufs& b, const float* coords,
+                          const float* R, int32_t* perm, hipStream_t st) {
+  const int64_t n = p.n;
+  const int leaf = p.leaf;
+  if (b.n_rec < (size_t)n) {
+    set_error("tree: record arrays hold %zu points, the build needs %lld", b.n_rec,
+              (long long)n);
+    return BT_EINVAL;
+  }
   if (p.G > 0) {
     // zero the histogram region once and set the root extents; afterwards
     // each tree_select<p> clears its node's histogram after reading it, so
     // the histograms are zero at the start of every radix pass
-    const int64_t nwords = (int64_t)((p.off_state - p.off_hist) / 4);
-    hipLaunchKernelGGL(tree_init, dim3(64), dim3(256), 0, st, hist, nwords, ext[0]);
+    hipLaunchKernelGGL(tree_init, dim3(64), dim3(256), 0, st, b.hist, (int64_t)b.n_hist, b.ext[0]);
     bt_status s = launch_status("tree_init");
     if (s != BT_OK) return s;
   }
@@ -803,8 +852,8 @@ bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const floa
     float rr[9] = {1, 0, 0, 0, 1, 0, 0, 0, 1};
     if (r) for (int i = 0; i < 9; ++i) rr[i] = r[i];
     hipLaunchKernelGGL(tree_ingest, dim3((int)g), dim3(kThreads), 0, st, coords, n, r ? 1 : 0,
-                       rr[0], rr[1], rr[2], rr[3], rr[4], rr[5], rr[6], rr[7], rr[8], rec[0],
-                       ext[0], p.G > 0 ? 1 : 0);
+                       rr[0], rr[1], rr[2], rr[3], rr[4], rr[5], rr[6], rr[7], rr[8], b.rec[0],
+                       b.ext[0], p.G > 0 ? 1 : 0);
     bt_status s = launch_status("tree_ingest");
     if (s != BT_OK) return s;
   }
@@ -814,10 +863,19 @@ bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const floa
     const int cpn = (int)(nsize / chunk);
     const int nchunks = (int)(n / chunk);
     const int nodes = 1 << lev;
-    float4* cur = rec[lev & 1];
-    float4* nxt = rec[(lev + 1) & 1];
-    uint32_t* ec = ext[lev & 1];
-    uint32_t* en = ext[(lev + 1) & 1];
+    if (!level_fits(p, b, lev, nsize, chunk, cpn, nchunks, nodes)) {
+      set_error("tree: level %d geometry does not fit the workspace (nsize %lld, chunk %d)", lev,
+                (long long)nsize, chunk);
+      return BT_EINVAL;
+    }
+    float4* cur = b.rec[lev & 1];
+    float4* nxt = b.rec[(lev + 1) & 1];
+    uint32_t* ec = b.ext[lev & 1];
+    uint32_t* en = b.ext[(lev + 1) & 1];
+    uint32_t* hist = b.hist;
+    NodeState* state = b.state;
+    uint2* counts = b.counts;
+    uint32_t* part = b.part;
     const dim3 gc(nchunks), gn(nodes), blk(kThreads);
     hipLaunchKernelGGL(tree_hist<0>, gc, blk, 0, st, cur, chunk, cpn, ec, state, hist);
     hipLaunchKernelGGL(tree_select<0>, gn, blk, 0, st, nsize, ec, state, hist);
@@ -832,7 +890,7 @@ bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const floa
     bt_status s = launch_status("tree level");
     if (s != BT_OK) return s;
   }
-  const float4* fin = rec[p.G & 1];
+  const float4* fin = b.rec[p.G & 1];
   if (p.nf == leaf) {
     int64_t g = (n + kThreads - 1) / kThreads;
     if (g > 4096) g = 4096;
@@ -840,6 +898,11 @@ bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const floa
     return launch_status("tree_write_perm");
   }
   const int nnodes = (int)(n / p.nf);
+  if (p.nf > kFinish || (int64_t)nnodes * p.nf != n) {
+    set_error("tree: finisher nodes of %lld points do not tile %lld", (long long)p.nf,
+              (long long)n);
+    return BT_EINVAL;
+  }
   if (nnodes <= 256) {                       // few nodes: a workgroup per node
     hipLaunchKernelGGL(tree_finish_block, dim3(nnodes), dim3(kFinishBlockWaves * 64), 0, st,
                        fin, (int)p.nf, leaf, perm);
@@ -848,6 +911,12 @@ bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const floa
   hipLaunchKernelGGL(tree_finish, dim3((nnodes + kFinishWaves - 1) / kFinishWaves),
                      dim3(kFinishWaves * 64), 0, st, fin, (int)p.nf, leaf, nnodes, perm);
   return launch_status("tree_finish");
+}
+
+bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const float* R,
+                            int32_t* perm, void* ws, hipStream_t st) {
+  const TreePlan p = plan_tree(n, leaf);
+  return tree_build_bufs(p, carve_tree(p, ws), coords, R, perm, st);
 }
 
 int64_t tree_padded_slots(int64_t n, int leaf) {

@@ -25,11 +25,27 @@ void emu_launch(dim3 grid, dim3 block, size_t shm, const std::function<void()>& 
     eb->xch.assign(nt, 0);
     blocks.push_back(std::move(eb));
   }
+  // With EMU_SHUFFLE=<seed> the workgroups run in a seeded random order (a
+  // different order in every launch): results must not depend on it.
+  std::vector<unsigned> order(nblk);
+  for (unsigned b = 0; b < nblk; ++b) order[b] = b;
+  if (const char* sh = getenv("EMU_SHUFFLE")) {
+    static unsigned long long state = 0;
+    if (state == 0) state = 0x9e3779b97f4a7c15ull ^ strtoull(sh, nullptr, 10);
+    for (unsigned b = nblk; b > 1; --b) {        // Fisher-Yates, splitmix64 draws
+      unsigned long long z = (state += 0x9e3779b97f4a7c15ull);
+      z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+      z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+      z ^= z >> 31;
+      std::swap(order[b - 1], order[z % b]);
+    }
+  }
   std::vector<std::thread> th;
   for (unsigned t = 0; t < nt; ++t)
     th.emplace_back([&, t]() {
-      for (unsigned b = 0; b < nblk; ++b) {
-        outer.arrive_and_wait();                 // workgroup b may start
+      for (unsigned bi = 0; bi < nblk; ++bi) {
+        outer.arrive_and_wait();                 // workgroup order[bi] may start
+        const unsigned b = order[bi];
         threadIdx = {t, 0, 0};
         blockIdx = {b % grid.x, (b / grid.x) % grid.y, b / (grid.x * grid.y)};
         body();
@@ -39,8 +55,8 @@ void emu_launch(dim3 grid, dim3 block, size_t shm, const std::function<void()>& 
         outer.arrive_and_wait();                 // workgroup b done
       }
     });
-  for (unsigned b = 0; b < nblk; ++b) {
-    g_blk = blocks[b].get();
+  for (unsigned bi = 0; bi < nblk; ++bi) {
+    g_blk = blocks[order[bi]].get();
     outer.arrive_and_wait();
     outer.arrive_and_wait();
   }

@@ -7,7 +7,8 @@
 // 32x32x16 bf16 MFMA is computed wave-wide in its lane layout:
 //   A[i][k] in lane i + 32*(k/8), element k%8; B[k][j] in lane j + 32*(k/8),
 //   element k%8; D[i][j] in lane j + 32*((i/4)%2), element (i/8)*4 + i%4.
-// Workgroups of a launch run one after another.
+// Workgroups of a launch run one after another (in a seeded random order
+// when EMU_SHUFFLE is set).
 #pragma once
 #include <atomic>
 #include <barrier>

@@ -39,7 +39,8 @@ def sim(tmp_path_factory):
     bins = {}
     procs = []
     for name, src, extra in (("tree", "tree_driver.cpp", []), ("attn", "attn_driver.cpp", []),
-                             ("bsa_bwd", "attn_driver.cpp", ["-DBT_SIM_BSA_BWD"])):
+                             ("bsa_bwd", "attn_driver.cpp", ["-DBT_SIM_BSA_BWD"]),
+                             ("pipeline", "pipeline_driver.cpp", [])):
         out = str(d / name)
         procs.append(subprocess.Popen([CXX, *flags, *extra, os.path.join(SIM, src),
                                        os.path.join(SIM, "emu.cpp"), "-o", out, "-lpthread"],
@@ -53,7 +54,20 @@ def sim(tmp_path_factory):
     return bins
 
 
-def _tree(sim, coords, leaf, R=None):
+# Cases that take minutes of emulation run only with BT_SIM_SLOW=1 (their
+# results are recorded with the tree notes of the design document).
+SLOW = pytest.mark.skipif(os.environ.get("BT_SIM_SLOW") != "1",
+                          reason="long emulation: set BT_SIM_SLOW=1")
+
+
+def _env(shuffle):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0")
+    if shuffle is not None:
+        env["EMU_SHUFFLE"] = str(shuffle)
+    return env
+
+
+def _tree(sim, coords, leaf, R=None, shuffle=None, timeout=600):
     d = sim["dir"]
     c = d / "c.bin"
     np.ascontiguousarray(coords, np.float32).tofile(c)
@@ -61,7 +75,7 @@ def _tree(sim, coords, leaf, R=None):
     if R is not None:
         np.asarray(R, np.float32).tofile(d / "R.bin")
         args.append(str(d / "R.bin"))
-    r = subprocess.run(args, capture_output=True, text=True, timeout=600)
+    r = subprocess.run(args, capture_output=True, text=True, timeout=timeout, env=_env(shuffle))
     assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
     return np.fromfile(d / "p.bin", np.int32)
 
@@ -95,6 +109,73 @@ def test_rotated_tree_kernels_bit_exact(sim):
     w = synth.make("rotpair", n=4096, features=False)
     assert np.array_equal(_tree(sim, w.coords, 64, R=w.R),
                           T.rotate_build(w.coords, 64, w.R))
+
+
+@pytest.mark.parametrize("shuffle", [1, 2])
+def test_tree_kernels_shuffled_workgroups(sim, shuffle):
+    """Workgroups of every launch in a seeded random order: the result does
+    not depend on the order (no workgroup reads what another one of the same
+    launch writes; the histogram atomics commute)."""
+    w = synth.make("rotpair", n=4096, features=False)
+    assert np.array_equal(_tree(sim, w.coords, 128, R=w.R, shuffle=shuffle),
+                          T.rotate_build(w.coords, 128, w.R))
+
+
+def _pipeline(sim, n, H, shuffle):
+    """The rotated-pair pipeline of the rotated-pair workload's recipe at n
+    points, every array in an allocation of its own (AddressSanitizer
+    catches an access past any of them), compared with the oracle."""
+    from oracle import permute as P
+    d_ = sim["dir"]
+    w = synth.make("rotpair", n=n, features=False)
+    rng = np.random.default_rng(n)
+    q, k, v = (synth.normal_features(rng, n, H, 32, "bf16") for _ in range(3))
+    w.coords.astype(np.float32).tofile(d_ / "coords.bin")
+    w.R.astype(np.float32).tofile(d_ / "R.bin")
+    for t, nm in ((q, "q.bin"), (k, "k.bin"), (v, "v.bin")):
+        _dump(t, d_ / nm)
+    r = subprocess.run([sim["pipeline"], str(n), str(w.leaf), str(w.ball), str(H), "32"],
+                       cwd=d_, capture_output=True, text=True, timeout=3600, env=_env(shuffle))
+    assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
+    pa, pb = (np.fromfile(d_ / f, np.int32) for f in ("pa.bin", "pb.bin"))
+    pa_ref, pb_ref = T.build(w.coords, w.leaf), T.rotate_build(w.coords, w.leaf, w.R)
+    assert np.array_equal(pa, pa_ref) and np.array_equal(pb, pb_ref)
+    assert np.array_equal(np.fromfile(d_ / "inv.bin", np.int32), P.invert(pb_ref))
+    o1 = torch.from_numpy(_read_out(d_ / "o1.bin", n, H, 32, "bf16")).to(torch.bfloat16)
+    assert np.abs(o1.float().numpy() - A.ball_attn(q, k, v, pa_ref, w.ball)).max() <= 2e-2
+    o2 = _read_out(d_ / "o2.bin", n, H, 32, "bf16")
+    assert np.abs(o2 - A.ball_attn(q, k, o1, pb_ref, w.ball)).max() <= 2e-2
+
+
+def test_rotated_pair_pipeline(sim):
+    """4,096 points, leaf = ball 128: two global levels, then the finisher;
+    ball attention in tree A, gather into tree B, attention, scatter back."""
+    _pipeline(sim, 4096, 2, shuffle=5)
+
+
+@SLOW
+def test_rotated_pair_pipeline_16k_8_heads(sim):
+    """The inputs of the pipeline case that faulted the GPU: the rotated-pair
+    recipe at 16,384 points, leaf = ball 128, 8 heads of 32."""
+    _pipeline(sim, 16384, 8, shuffle=7)
+
+
+@SLOW
+@pytest.mark.parametrize("leaf", [128, 64])
+def test_sphere_65536_tree(sim, leaf):
+    w = synth.make("sphere", features=False)
+    assert np.array_equal(_tree(sim, w.coords, leaf, shuffle=leaf, timeout=3600),
+                          T.build(w.coords, leaf))
+
+
+@SLOW
+def test_tree_finish_many_nodes(sim):
+    """524,288 points, leaf 128: 512 finisher nodes of 1,024 points, so the
+    one-wave-per-node finisher (tree_finish) runs, after nine global levels
+    with 4,096-point chunks."""
+    w = synth.make("rotpair", n=524288, features=False)
+    assert np.array_equal(_tree(sim, w.coords, 128, shuffle=11, timeout=7200),
+                          T.build(w.coords, 128))
 
 
 def _dump(t, path):
