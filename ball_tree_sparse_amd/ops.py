@@ -70,6 +70,10 @@ _SIGS = [
     ("bsa_attn_bwd", C.c_int, [_P, _P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int,
                                C.POINTER(BsaParams), _P, _P, C.POINTER(C.c_float), _P, _P, _P,
                                _P, _P, _P, C.c_size_t, _P]),
+    ("bsa_attn_noalloc_max_bytes", C.c_size_t, []),
+    ("bsa_attn_noalloc", C.c_int, [_P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int,
+                                   C.POINTER(BsaParams), _P, _P, C.POINTER(C.c_float), _P, _P,
+                                   _P]),
     ("bt_padded_size", C.c_int64, [C.c_int64, C.c_int32]),
     ("bt_build_padded_workspace_size", C.c_size_t, [C.c_int64, C.c_int32]),
     ("bt_build_padded", C.c_int, [_P, C.c_int64, C.c_int32, C.POINTER(C.c_float), _P, _P,
@@ -428,6 +432,36 @@ def bsa_attn(q, k, v, perm, ball: int, block: int, group: int, topk: int,
     _check(lib().bsa_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), N, H, d, _dtype_code(q),
                           C.byref(p), _ptr(gate_w), _ptr(gate_b), gc, _ptr(sel),
                           _ptr(workspace), workspace.numel(), _ptr(out), _stream(q.device)))
+    return (out, sel) if return_sel else out
+
+
+def bsa_attn_noalloc(q, k, v, perm, ball: int, block: int, group: int, topk: int,
+                     mask_own_ball: bool = True, gate_w=None, gate_b=None, gate_const=None,
+                     return_sel: bool = False, out=None, query_compression: bool = False):
+    """bsa_attn with the library's static workspace (no device allocation by
+    the library; ``out`` and ``sel`` are allocated here unless given)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+        if t.shape != q.shape or t.dim() != 3:
+            raise ValueError("q, k, v must share one [N,H,d] shape")
+    N, H, d = q.shape
+    _perm(perm, N)
+    p = BsaParams(ball, block, group, topk, int(bool(mask_own_ball)),
+                  int(bool(query_compression)))
+    _gates(gate_w, gate_b, d)
+    gc = None
+    if gate_const is not None:
+        gc = (C.c_float * 3)(*[float(x) for x in gate_const])
+    sel = None
+    if return_sel:
+        sel = torch.empty((H, N // group, topk), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    _same_shape(out, q, "out")
+    _check(lib().bsa_attn_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), N, H, d,
+                                  _dtype_code(q), C.byref(p), _ptr(gate_w), _ptr(gate_b), gc,
+                                  _ptr(sel), _ptr(out), _stream(q.device)))
     return (out, sel) if return_sel else out
 
 

@@ -269,6 +269,27 @@ bt_status bsa_attn(const void* q, const void* k, const void* v,
                    void* stream);
 
 /* ------------------------------------------------------------------------
+ * bsa_attn without allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same computation, arguments, requirements and errors
+ * as bsa_attn, without the workspace arguments: the workspace is a static
+ * device array of bsa_attn_noalloc_max_bytes() bytes (80 MiB) that the
+ * library holds on every GPU it runs on until the process ends.  A call whose
+ * bsa_workspace_size() exceeds it returns BT_EINVAL (the BSA workload of
+ * 65,536 points, 8 heads of 32 needs 67.5 MiB, 70.5 MiB with group
+ * compression).  Calls on one GPU share the array: calls that overlap on one
+ * GPU (other streams, other threads) race.  Allocates nothing; asynchronous
+ * on stream.
+ * ---------------------------------------------------------------------- */
+size_t bsa_attn_noalloc_max_bytes(void);
+bt_status bsa_attn_noalloc(const void* q, const void* k, const void* v,
+                           const int32_t* perm, int64_t N, int32_t H, int32_t d,
+                           bt_dtype dt, const bsa_params* p,
+                           const float* gate_w, const float* gate_b,
+                           const float* gate_const_host, int32_t* sel_out,
+                           void* out, void* stream);
+
+/* ------------------------------------------------------------------------
  * Backward of BSA without group compression (the branches and the gates are
  * learned: Pith review of arXiv 2506.12541, "What carries the argument").
  * For the output gradient dout [N,H,d] (original order, bf16) it writes
