@@ -189,25 +189,47 @@ BT_DEV bool sel_better(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
 
+// The value of lane (this lane) ^ J.  Distances 1 and 2 are DPP quad
+// permutes and 4, 8, 16 ds_swizzle bit-mask moves inside each half-wave, so
+// only distance 32 goes through ds_bpermute.
+template <int J>
+BT_DEV int lane_xor(int x) {
+  if constexpr (J == 1) return __builtin_amdgcn_mov_dpp(x, 0xb1, 0xf, 0xf, false);  // [1,0,3,2]
+  else if constexpr (J == 2) return __builtin_amdgcn_mov_dpp(x, 0x4e, 0xf, 0xf, false);  // [2,3,0,1]
+  else if constexpr (J < 32) return __builtin_amdgcn_ds_swizzle(x, (J << 10) | 0x1f);
+  else return __shfl_xor(x, J, 64);
+}
+
+template <int K, int J>
+BT_DEV void sort_step(float& v, int& i, int lane) {
+  const float ov = __int_as_float(lane_xor<J>(__float_as_int(v)));
+  const int oi = lane_xor<J>(i);
+  // the lower lane of a pair keeps the better pair in a best-first run
+  // (lane & K == 0) and the worse one in a worst-first run
+  const bool keep_better = ((lane & J) == 0) == ((lane & K) == 0);
+  const bool ob = sel_better(ov, oi, v, i);
+  if (ob == keep_better) {
+    v = ov;
+    i = oi;
+  }
+}
+
+template <int K, int J>
+BT_DEV void sort_stage(float& v, int& i, int lane) {
+  sort_step<K, J>(v, i, lane);
+  if constexpr (J > 1) sort_stage<K, J / 2>(v, i, lane);
+}
+
 // Bitonic sort of one (score, block) pair per lane across the wave, best
 // first: lane 0 ends with the best pair.  Pairs must be distinct.
 BT_DEV void wave_sort_best_first(float& v, int& i) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1)
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const float ov = __shfl_xor(v, j, 64);
-      const int oi = __shfl_xor(i, j, 64);
-      // the lower lane of a pair keeps the better pair in a best-first run
-      // (lane & k == 0) and the worse one in a worst-first run
-      const bool keep_better = ((lane & j) == 0) == ((lane & k) == 0);
-      const bool ob = sel_better(ov, oi, v, i);
-      if (ob == keep_better) {
-        v = ov;
-        i = oi;
-      }
-    }
+  sort_stage<2, 1>(v, i, lane);
+  sort_stage<4, 2>(v, i, lane);
+  sort_stage<8, 4>(v, i, lane);
+  sort_stage<16, 8>(v, i, lane);
+  sort_stage<32, 16>(v, i, lane);
+  sort_stage<64, 32>(v, i, lane);
 }
 
 // Lanes below this one with their bit of m set.
@@ -228,26 +250,26 @@ __global__ __launch_bounds__(kSelThreads) void bsa_select(const float* __restric
                                                   int32_t* __restrict__ sel) {
   HIP_DYNAMIC_SHARED(float, smem)
   constexpr int d = D;
-  float* qs = smem;                    // [tg][d]
-  float* sc = smem + tg * d;           // [tg][nc]
+  float* sc = smem + tg * d;           // [tg][nc] (after tg*d floats kept for the layout)
   float* cand = sc + tg * nc;          // [waves][128]: top-k candidates of a wave
   const int h = blockIdx.y;
   const int g0 = blockIdx.x * tg;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ng = min(tg, ngroups - g0);
-  for (int i = tid; i < ng * d; i += kSelThreads)
-    qs[i] = qbar[((int64_t)h * ngroups + g0) * d + i];
-  __syncthreads();
   const float scale = 1.0f / sqrtf((float)d);
   const float* kh = kc32 + (int64_t)h * D * nc;   // [d][nc]: lanes read consecutive blocks
+  // the pooled query of a group is the same for every lane: it is read with
+  // scalar loads (SGPR operands of the FMAs), not from LDS once per lane
+  const float* qh = qbar + ((int64_t)h * ngroups + g0) * d;
   for (int jb = tid; jb < nc; jb += kSelThreads) {
     float kr[D];
 #pragma unroll
     for (int e = 0; e < D; ++e) kr[e] = kh[(int64_t)e * nc + jb];
     for (int g = 0; g < ng; ++g) {
+      const float* qg = qh + g * D;
       float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < D; ++e) s = fmaf(qs[g * D + e], kr[e], s);
+      for (int e = 0; e < D; ++e) s = fmaf(qg[e], kr[e], s);
       sc[g * nc + jb] = s * scale;
     }
   }

@@ -94,15 +94,16 @@ template <typename T> inline T __shfl(T v, int src, int w = 64) { return emu_shf
 template <typename T> inline T __shfl_up(T v, unsigned d, int w = 64) {
   int l = emu_tid() & 63; int s = l >= (int)d ? l - (int)d : l; return emu_shfl_from(v, s); }
 // DPP move with the old value kept where the source lane is invalid or the
-// row is masked off (bound_ctrl off, all banks).  Controls: row_shr:1-15,
-// row_bcast:15, row_bcast:31.
+// row is masked off (bound_ctrl off, all banks).  Controls: quad_perm,
+// row_shr:1-15, row_bcast:15, row_bcast:31.
 inline int __builtin_amdgcn_update_dpp(int old, int src, int ctrl, int row_mask, int bank_mask,
                                        bool bound_ctrl) {
   const int t = emu_tid(), base = t & ~63, l = t & 63, row = l >> 4, x = l & 15;
   g_blk->xch[t] = (uint32_t)src;
   emu_wave_sync();
   int from = -1;
-  if (ctrl >= 0x111 && ctrl <= 0x11f) { const int k = ctrl - 0x110; if (x >= k) from = l - k; }
+  if (ctrl >= 0 && ctrl <= 0xff) from = (l & ~3) | ((ctrl >> (2 * (l & 3))) & 3);  // quad_perm
+  else if (ctrl >= 0x111 && ctrl <= 0x11f) { const int k = ctrl - 0x110; if (x >= k) from = l - k; }
   else if (ctrl == 0x142) { if (row >= 1) from = 16 * row - 1; }
   else if (ctrl == 0x143) { if (row >= 2) from = 31; }
   else { fprintf(stderr, "emulator: DPP control %#x not modelled\n", ctrl); abort(); }
@@ -112,6 +113,17 @@ inline int __builtin_amdgcn_update_dpp(int old, int src, int ctrl, int row_mask,
   emu_wave_sync();
   (void)bound_ctrl;
   return r;
+}
+inline int __builtin_amdgcn_mov_dpp(int src, int ctrl, int row_mask, int bank_mask,
+                                    bool bound_ctrl) {
+  return __builtin_amdgcn_update_dpp(0, src, ctrl, row_mask, bank_mask, bound_ctrl);
+}
+// ds_swizzle_b32 in bit-mask mode (offset bit 15 clear): inside each group of
+// 32 lanes, lane l reads lane ((l & and) | or) ^ xor.
+inline int __builtin_amdgcn_ds_swizzle(int src, int pattern) {
+  if (pattern & 0x8000) { fprintf(stderr, "emulator: ds_swizzle mode not modelled\n"); abort(); }
+  const int l = emu_tid() & 63, a = pattern & 31, o = (pattern >> 5) & 31, x = (pattern >> 10) & 31;
+  return emu_shfl_from(src, (l & 32) | (((l & a) | o) ^ x));
 }
 inline int __builtin_amdgcn_readlane(int v, int lane) { return emu_shfl_from(v, lane); }
 inline unsigned long long __ballot(int p) {
