@@ -369,16 +369,18 @@ __global__ __launch_bounds__(kSelThreads) void bsa_select(const float* __restric
 }
 
 // ------------------------------------------------------ group compression ----
-// Pooled (fp32) query rows -> the B operand of S^T = K Q^T, rounded to bf16.
+// Pooled (fp32) query rows times scale -> the B operand of S^T = K Q^T,
+// rounded to bf16 once.
 template <int D>
-BT_DEV void pooled_query_frags(const float* __restrict__ row, bf16x8* qf) {
+BT_DEV void pooled_query_frags(const float* __restrict__ row, float scale, bf16x8* qf) {
   const int hf = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     const float4 a = *(const float4*)(row + s * 16 + hf * 8);
     const float4 b = *(const float4*)(row + s * 16 + hf * 8 + 4);
-    qf[s] = bf16x8{(__bf16)a.x, (__bf16)a.y, (__bf16)a.z, (__bf16)a.w,
-                   (__bf16)b.x, (__bf16)b.y, (__bf16)b.z, (__bf16)b.w};
+    qf[s] = bf16x8{(__bf16)(a.x * scale), (__bf16)(a.y * scale), (__bf16)(a.z * scale),
+                   (__bf16)(a.w * scale), (__bf16)(b.x * scale), (__bf16)(b.y * scale),
+                   (__bf16)(b.z * scale), (__bf16)(b.w * scale)};
   }
 }
 
@@ -400,14 +402,13 @@ __global__ __launch_bounds__(kQcWaves * 64) void bsa_qc_cmp(const float* __restr
   const int h = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31;
   const int64_t j = (int64_t)blockIdx.x * 32 + c;          // this lane's coarse query
   bf16x8 qf[D / 16];
-  pooled_query_frags<D>(qc + ((int64_t)h * nc + j) * D, qf);
-  const float c2 = 1.4426950408889634f / sqrtf((float)D);
+  pooled_query_frags<D>(qc + ((int64_t)h * nc + j) * D, log2_score_scale(D), qf);
   Branch<DB> br;
   branch_init<D>(br);
   const int seg = ((nc / 32 + kQcWaves - 1) / kQcWaves) * 32;  // keys per wave
   const int k0 = w * seg, len = max(0, min(nc - k0, seg));
   attend_range<D, 1>(kcb + (int64_t)h * nc * D, vct + (int64_t)h * nc * D,
-                     [&](int key) -> int64_t { return k0 + key; }, len, qf, c2, &br);
+                     [&](int key) -> int64_t { return k0 + key; }, len, qf, &br);
   float l = (br.l[0] + br.l[1]) + (br.l[2] + br.l[3]);
   l += __shfl_xor(l, 32, 64);
   pm[w][lane] = br.m;
@@ -633,8 +634,10 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3
     }
   }
   __syncthreads();   // ssel
+  // from here on the queries are scaled: their scores come out in log2 units
+#pragma unroll
+  for (int i = 0; i < QB * DS; ++i) qf[i] = scale_query(qf[i], log2_score_scale(D));
 
-  const float c2 = 1.4426950408889634f / sqrtf((float)D);
   const uint16_t* kh = kt + (int64_t)h * N * D;
   const uint16_t* vh = vtt + (int64_t)h * N * D;
   f32x16 acc[QB][DB];
@@ -649,7 +652,7 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) branch_init<D>(br[qb]);
     const int64_t b0 = ((int64_t)g * group / ball) * ball;
-    attend_range<D, QB>(kh, vh, [&](int key) -> int64_t { return b0 + key; }, ball, qf, c2, br);
+    attend_range<D, QB>(kh, vh, [&](int key) -> int64_t { return b0 + key; }, ball, qf, br);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) branch_merge<D>(br[qb], G[qb][0], acc[qb]);
   }
@@ -680,7 +683,7 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3
       for (int qb = 0; qb < QB; ++qb) branch_init<D>(br[qb]);
       const uint16_t* kch = kcb + (int64_t)h * nc * D;
       const uint16_t* vch = vct + (int64_t)h * nc * D;
-      attend_range<D, QB>(kch, vch, [&](int key) -> int64_t { return key; }, nc, qf, c2, br);
+      attend_range<D, QB>(kch, vch, [&](int key) -> int64_t { return key; }, nc, qf, br);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) branch_merge<D>(br[qb], G[qb][1], acc[qb]);
     }
@@ -692,7 +695,7 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3
                           [&](int key) -> int64_t {
                             return (int64_t)ssel[key / block] * block + (key % block);
                           },
-                          topk * block, qf, c2, br);
+                          topk * block, qf, br);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) branch_merge<D>(br[qb], G[qb][2], acc[qb]);
     }

@@ -65,19 +65,55 @@ BT_DEV float bsa_sum8(bf16x8 x, float acc) {
 template <int DB>
 struct Branch {
   f32x16 o[DB];
-  float m;      // running max in log2-scaled units
+  float m;      // running max in log2-scaled units (-inf before the first chunk)
   float l[4];   // partial sums of the rounded weights
+  s16x4 shf;    // shift_frag(m)
 };
 
+// The scores reach the exponential without a pass over them on the VALU:
+// the queries are multiplied by log2(e)/sqrt(d) before their rounding to bf16
+// (scale_query), so S^T = K Q^T is already in log2 units, and the running
+// maximum m is subtracted inside the MFMAs.  A 32x32x8 MFMA of a fragment of
+// ones with shift_frag(m) puts -m in every row of a lane's column; the score
+// MFMAs accumulate onto it.  shift_frag splits -m into three bf16 pieces,
+// which between them hold all 24 bits of its significand, in the k rows of
+// the lanes of the lower half (the lanes of the upper half hold zeros), so
+// the sum over k is -m exactly.
+BT_DEV bf16x8 scale_query(bf16x8 x, float scale) {
+  bf16x8 y;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = (__bf16)((float)x[e] * scale);
+  return y;
+}
+BT_DEV float log2_score_scale(int d) { return 1.4426950408889634f / sqrtf((float)d); }
+
+BT_DEV s16x4 ones_frag() { return s16x4{0x3f80, 0x3f80, 0x3f80, 0x3f80}; }
+BT_DEV s16x4 shift_frag(float m) {
+  const float x = -m;
+  const float hi = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
+  const float r = x - hi;                                      // exact
+  const float mid = __uint_as_float(__float_as_uint(r) & 0xffff0000u);
+  const float lo = r - mid;                                    // exact, at most 8 bits
+  const bool lower = ((threadIdx.x >> 5) & 1) == 0;
+  s16x4 f;
+  f[0] = lower ? (short)(__float_as_uint(hi) >> 16) : (short)0;
+  f[1] = lower ? (short)(__float_as_uint(mid) >> 16) : (short)0;
+  f[2] = lower ? (short)(__float_as_uint(lo) >> 16) : (short)0;
+  f[3] = 0;
+  return f;
+}
+
 // One online-softmax step over NKB 32-key blocks for QB query blocks of 32
-// (qf: QB x D/16 B-operand fragments, br: QB branch states).  Block kb's keys
-// are rows row0(kb) .. row0(kb)+31 of the head's row-major K (kh) and of its
-// transposed V blocks (vh: [rows/32][D][32]); row0(kb) is a multiple of 32.
-// Every K and V fragment of the chunk is requested before the first MFMA and
-// then serves all QB query blocks, so the cache traffic per query falls by QB.
-template <int D, int NKB, int QB, typename RowFn>
+// (qf: QB x D/16 B-operand fragments of scaled queries, br: QB branch
+// states).  Block kb's keys are rows row0(kb) .. row0(kb)+31 of the head's
+// row-major K (kh) and of its transposed V blocks (vh: [rows/32][D][32]);
+// row0(kb) is a multiple of 32.  Every K and V fragment of the chunk is
+// requested before the first MFMA and then serves all QB query blocks, so the
+// cache traffic per query falls by QB.  FIRST: the branch's first chunk (its
+// maximum sets m; nothing is accumulated yet).
+template <int D, int NKB, int QB, bool FIRST, typename RowFn>
 BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
-                         RowFn row0, const bf16x8* qf, float c2, Branch<D / 32>* br) {
+                         RowFn row0, const bf16x8* qf, Branch<D / 32>* br) {
   constexpr int DS = D / 16, DB = D / 32;
   const int lane = threadIdx.x & 63, hf = lane >> 5, c = lane & 31;
   bf16x8 kf[NKB][DS], vf[NKB][2][DB];
@@ -101,43 +137,55 @@ BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __rest
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16 a = {};
+      if constexpr (!FIRST)
+        a = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ones_frag(), b.shf, a, 0, 0, 0);
 #pragma unroll
       for (int s = 0; s < DS; ++s)
         a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][s], qf[qb * DS + s], a, 0, 0, 0);
       sacc[kb] = a;
     }
-    // chunk maximum of the raw scores (scaling by c2 > 0 keeps the order)
+    // chunk maximum of the shifted scores (of the scores on the first chunk)
     float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
-    float cm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * c2;
+    float cm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
     // The running maximum is raised (and the state rescaled) only when a
     // chunk maximum exceeds it by more than kLazyLog2, for every lane of the
     // wave at once; the weights then stay below 2^kLazyLog2, and the
     // normalised result is the same up to rounding.
-    if (__ballot(cm > b.m + kLazyLog2)) {
-      const float mn = fmaxf(b.m, cm);
-      const float alpha = __builtin_amdgcn_exp2f(b.m - mn);   // 0 on the first chunk
+    if (FIRST || __ballot(cm > kLazyLog2)) {
+      float delta;                                  // taken off this chunk's scores
+      if constexpr (FIRST) {
+        delta = cm;
+        b.m = cm;
+      } else {
+        const float mn = b.m + fmaxf(cm, 0.f);
+        delta = mn - b.m;
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) b.l[i] *= alpha;
+        for (int i = 0; i < 4; ++i) b.l[i] *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) b.o[db][e] *= alpha;
-      b.m = mn;
+          for (int e = 0; e < 16; ++e) b.o[db][e] *= alpha;
+        b.m = mn;
+      }
+      b.shf = shift_frag(b.m);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kb][e] -= delta;
     }
-    const float mn = b.m;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         bf16x8 pf;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pf[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][s2 * 8 + e], c2, -mn));
+        for (int e = 0; e < 8; ++e) pf[e] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][s2 * 8 + e]);
         b.l[(kb * 2 + s2) & 3] = bsa_sum8(pf, b.l[(kb * 2 + s2) & 3]);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -150,14 +198,22 @@ BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __rest
 // a multiple of 32); row0(key) gives the row of the 32-key block at key.
 template <int D, int QB, typename RowFn>
 BT_DEV void attend_range(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
-                         RowFn row0, int len, const bf16x8* qf, float c2, Branch<D / 32>* br) {
+                         RowFn row0, int len, const bf16x8* qf, Branch<D / 32>* br) {
   constexpr int KB = kChunk / 32;
   int k0 = 0;
+  if (len >= kChunk) {
+    attend_chunk<D, KB, QB, true>(kh, vh, [&](int kb) -> int64_t { return row0(kb * 32); }, qf,
+                                  br);
+    k0 = kChunk;
+  } else if (len > 0) {
+    attend_chunk<D, 1, QB, true>(kh, vh, [&](int kb) -> int64_t { return row0(0); }, qf, br);
+    k0 = 32;
+  }
   for (; k0 + kChunk <= len; k0 += kChunk)
-    attend_chunk<D, KB, QB>(kh, vh, [&](int kb) -> int64_t { return row0(k0 + kb * 32); }, qf, c2,
-                            br);
+    attend_chunk<D, KB, QB, false>(kh, vh,
+                                   [&](int kb) -> int64_t { return row0(k0 + kb * 32); }, qf, br);
   for (; k0 < len; k0 += 32)                 // a tail of 32-key blocks
-    attend_chunk<D, 1, QB>(kh, vh, [&](int kb) -> int64_t { return row0(k0); }, qf, c2, br);
+    attend_chunk<D, 1, QB, false>(kh, vh, [&](int kb) -> int64_t { return row0(k0); }, qf, br);
 }
 
 template <int D>
@@ -167,6 +223,7 @@ BT_DEV void branch_init(Branch<D / 32>& br) {
   br.m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) br.l[i] = 0.f;
+  br.shf = s16x4{0, 0, 0, 0};
 }
 
 template <int D>

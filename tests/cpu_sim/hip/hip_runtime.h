@@ -223,6 +223,35 @@ inline emu_f32x16 __builtin_amdgcn_mfma_f32_32x32x16_bf16(emu_bf16x8 a, emu_bf16
   return d;
 }
 
+// ---- MFMA 32x32x8 bf16 (bf16 operands as raw 16-bit patterns) ------------
+typedef short emu_s16x4 __attribute__((ext_vector_type(4)));
+inline float emu_bf16_bits(short h) {
+  uint32_t u = (uint32_t)(uint16_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+inline emu_f32x16 __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(emu_s16x4 a, emu_s16x4 b, emu_f32x16 c,
+                                                          int, int, int) {
+  const int t = emu_tid(), base = t & ~63, l = t & 63;
+  for (int e = 0; e < 4; ++e) { g_mfma[t].a[e] = emu_bf16_bits(a[e]); g_mfma[t].b[e] = emu_bf16_bits(b[e]); }
+  emu_wave_sync();
+  emu_f32x16 d = c;
+  const int j = l & 31, hf = l >> 5;
+  for (int e = 0; e < 16; ++e) {
+    const int i = (e / 4) * 8 + hf * 4 + (e % 4);
+    float acc = 0.f;
+    for (int k = 0; k < 8; ++k) {
+      const float av = g_mfma[base + i + 32 * (k / 4)].a[k % 4];
+      const float bv = g_mfma[base + j + 32 * (k / 4)].b[k % 4];
+      acc += av * bv;
+    }
+    d[e] = c[e] + acc;
+  }
+  emu_wave_sync();
+  return d;
+}
+
 // ---- launches ------------------------------------------------------------
 // Runs every workgroup of the grid one after another, each with blockDim
 // host threads.
