@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kQcWaves * 64) void bsa_qc_cmp(const float* __restr
   const int k0 = w * seg, len = max(0, min(nc - k0, seg));
   attend_range<D, 1>(kcb + (int64_t)h * nc * D, vct + (int64_t)h * nc * D,
                      [&](int key) -> int64_t { return k0 + key; }, len, qf, &br);
-  float l = (br.l[0] + br.l[1]) + (br.l[2] + br.l[3]);
+  float l = branch_l(br);
   l += __shfl_xor(l, 32, 64);
   pm[w][lane] = br.m;
   pl[w][lane] = l;
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(64) void bsa_qc_slc(const float* __restrict__ qbar,
 // A workgroup owns one (group, head); each of its NWV waves owns QB blocks of
 // 32 queries (group = NWV * QB * 32).
 template <int D, int NWV, bool QC, int QB>
-__global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3), 8) void bsa_fused(
+__global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((D > 32 ? 2 : 3), 8) void bsa_fused(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ perm,
     const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vtt,
     const uint16_t* __restrict__ kcb, const uint16_t* __restrict__ vct,
@@ -581,6 +581,11 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3
     uint16_t* __restrict__ out) {
   constexpr int DS = D / 16, DB = D / 32;
   __shared__ int32_t ssel[64];
+  // The merged output and the gates of a wave's queries wait in LDS while the
+  // branches run (lane-major, conflict-free), so the registers hold only the
+  // branch state: three waves per SIMD instead of two.
+  __shared__ float sacc_out[NWV][QB][DB * 16][64];
+  __shared__ float sgate[NWV][QB][3][64];
   const int total = ngroups * H;
   int pair = blockIdx.x;
   if (xcd_map) pair = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
@@ -595,14 +600,13 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3
   // queries of this wave: tree positions t0 .. t0 + QB*32 - 1, block qb at
   // t0 + qb*32 + c for lane column c
   const int64_t t0 = (int64_t)g * group + w * (QB * 32);
-  int64_t pq[QB];
   bf16x8 qf[QB * DS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    pq[qb] = perm_index(perm[t0 + qb * 32 + c], N);
+    const int64_t pq = perm_index(perm[t0 + qb * 32 + c], N);
 #pragma unroll
     for (int s = 0; s < DS; ++s)
-      qf[qb * DS + s] = *(const bf16x8*)(q + pq[qb] * rs + (int64_t)h * D + s * 16 + hf * 8);
+      qf[qb * DS + s] = *(const bf16x8*)(q + pq * rs + (int64_t)h * D + s * 16 + hf * 8);
   }
 
   // gates: G = sigmoid(W q + b), one W [3, d] for every head
@@ -632,6 +636,8 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3
       G[qb][1] = 1.0f / (1.0f + __expf(-z1));
       G[qb][2] = 1.0f / (1.0f + __expf(-z2));
     }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) sgate[w][qb][i][lane] = G[qb][i];
   }
   __syncthreads();   // ssel
   // from here on the queries are scaled: their scores come out in log2 units
@@ -640,12 +646,23 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3
 
   const uint16_t* kh = kt + (int64_t)h * N * D;
   const uint16_t* vh = vtt + (int64_t)h * N * D;
-  f32x16 acc[QB][DB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
   Branch<DB> br[QB];
+  // out_slot = (first ? 0 : out_slot) + gate * o / l for every query block
+  auto merge = [&](int gi, bool first) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float l = branch_l(br[qb]);
+      l += __shfl_xor(l, 32, 64);
+      const float f = sgate[w][qb][gi][lane] * __builtin_amdgcn_rcpf(l);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float& x = sacc_out[w][qb][db * 16 + e][lane];
+          x = first ? br[qb].o[db][e] * f : fmaf(br[qb].o[db][e], f, x);
+        }
+    }
+  };
 
   // ---- ball branch: the ball holding this group (group | ball) ----------
   {
@@ -653,8 +670,7 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3
     for (int qb = 0; qb < QB; ++qb) branch_init<D>(br[qb]);
     const int64_t b0 = ((int64_t)g * group / ball) * ball;
     attend_range<D, QB>(kh, vh, [&](int key) -> int64_t { return b0 + key; }, ball, qf, br);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) branch_merge<D>(br[qb], G[qb][0], acc[qb]);
+    merge(0, true);
   }
   if constexpr (QC) {
     // ---- group compression: the token's block and group results --------
@@ -669,11 +685,12 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3
         for (int gq = 0; gq < 4; ++gq) {
           const float4 a = *(const float4*)(rc + db * 32 + gq * 8 + hf * 4);
           const float4 b = *(const float4*)(rsl + db * 32 + gq * 8 + hf * 4);
-          f32x16& x = acc[qb][db];
-          x[gq * 4 + 0] = fmaf(G[qb][2], b.x, fmaf(G[qb][1], a.x, x[gq * 4 + 0]));
-          x[gq * 4 + 1] = fmaf(G[qb][2], b.y, fmaf(G[qb][1], a.y, x[gq * 4 + 1]));
-          x[gq * 4 + 2] = fmaf(G[qb][2], b.z, fmaf(G[qb][1], a.z, x[gq * 4 + 2]));
-          x[gq * 4 + 3] = fmaf(G[qb][2], b.w, fmaf(G[qb][1], a.w, x[gq * 4 + 3]));
+          const float g1 = sgate[w][qb][1][lane], g2 = sgate[w][qb][2][lane];
+          float* x = &sacc_out[w][qb][db * 16 + gq * 4][lane];
+          x[0] = fmaf(g2, b.x, fmaf(g1, a.x, x[0]));
+          x[64] = fmaf(g2, b.y, fmaf(g1, a.y, x[64]));
+          x[128] = fmaf(g2, b.z, fmaf(g1, a.z, x[128]));
+          x[192] = fmaf(g2, b.w, fmaf(g1, a.w, x[192]));
         }
     }
   } else {
@@ -684,8 +701,7 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3
       const uint16_t* kch = kcb + (int64_t)h * nc * D;
       const uint16_t* vch = vct + (int64_t)h * nc * D;
       attend_range<D, QB>(kch, vch, [&](int key) -> int64_t { return key; }, nc, qf, br);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) branch_merge<D>(br[qb], G[qb][1], acc[qb]);
+      merge(1, false);
     }
     // ---- selection branch: the union of the selected blocks ---------------
     {
@@ -696,22 +712,24 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QB > 1 || D > 32 ? 2 : 3
                             return (int64_t)ssel[key / block] * block + (key % block);
                           },
                           topk * block, qf, br);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) branch_merge<D>(br[qb], G[qb][2], acc[qb]);
+      merge(2, false);
     }
   }
 
   // ---- store: lane owns d = db*32 + 8*gq + 4*hf + 0..3 of its query -------
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    uint16_t* orow = out + pq[qb] * rs + (int64_t)h * D;
+    const int64_t pq = perm_index(perm[t0 + qb * 32 + c], N);
+    uint16_t* orow = out + pq * rs + (int64_t)h * D;
+    const float* x = &sacc_out[w][qb][0][lane];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
+        const int e0 = (db * 16 + gq * 4) * 64;
         u32x2 pk;
-        pk[0] = pack_bf16x2(acc[qb][db][gq * 4 + 0], acc[qb][db][gq * 4 + 1]);
-        pk[1] = pack_bf16x2(acc[qb][db][gq * 4 + 2], acc[qb][db][gq * 4 + 3]);
+        pk[0] = pack_bf16x2(x[e0], x[e0 + 64]);
+        pk[1] = pack_bf16x2(x[e0 + 128], x[e0 + 192]);
         *(u32x2*)(orow + db * 32 + gq * 8 + hf * 4) = pk;
       }
   }

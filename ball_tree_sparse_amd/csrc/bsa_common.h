@@ -11,6 +11,7 @@ constexpr int kChunk = 64;             // keys per online-softmax step
 constexpr int kSelRegs = 16;           // scores per lane held in registers by select
 constexpr int kSelThreads = 512;       // select: eight waves, one group of a tile each
 constexpr float kLazyLog2 = 8.0f;      // online softmax: rescale only past 2^8
+constexpr int kLChains = 2;            // chains of the softmax normaliser
 
 struct BsaLayout {
   size_t kt, vt, kc32, kcb, vcb, qbar, sel;   // vt, vcb: transposed blocks
@@ -61,12 +62,12 @@ BT_DEV float bsa_sum8(bf16x8 x, float acc) {
 
 // Running state of one branch for the lane's query column.  The softmax
 // weights are rounded once to bf16 for the P V product and the normaliser
-// sums those rounded weights (four chains, lane-local until the merge).
+// sums those rounded weights (kLChains chains, lane-local until the merge).
 template <int DB>
 struct Branch {
   f32x16 o[DB];
   float m;      // running max in log2-scaled units (-inf before the first chunk)
-  float l[4];   // partial sums of the rounded weights
+  float l[kLChains];   // partial sums of the rounded weights
   s16x4 shf;    // shift_frag(m)
 };
 
@@ -166,7 +167,7 @@ BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __rest
         delta = mn - b.m;
         const float alpha = __builtin_amdgcn_exp2f(-delta);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b.l[i] *= alpha;
+        for (int i = 0; i < kLChains; ++i) b.l[i] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -186,7 +187,7 @@ BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __rest
         bf16x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pf[e] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][s2 * 8 + e]);
-        b.l[(kb * 2 + s2) & 3] = bsa_sum8(pf, b.l[(kb * 2 + s2) & 3]);
+        b.l[(kb * 2 + s2) % kLChains] = bsa_sum8(pf, b.l[(kb * 2 + s2) % kLChains]);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
           b.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][s2][db], pf, b.o[db], 0, 0, 0);
@@ -216,19 +217,28 @@ BT_DEV void attend_range(const uint16_t* __restrict__ kh, const uint16_t* __rest
     attend_chunk<D, 1, QB, false>(kh, vh, [&](int kb) -> int64_t { return row0(k0); }, qf, br);
 }
 
+// The lane's part of a branch's normaliser (the chains added in order).
+template <int DB>
+BT_DEV float branch_l(const Branch<DB>& br) {
+  float l = br.l[0];
+#pragma unroll
+  for (int i = 1; i < kLChains; ++i) l += br.l[i];
+  return l;
+}
+
 template <int D>
 BT_DEV void branch_init(Branch<D / 32>& br) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) br.o[db] = f32x16{};
   br.m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) br.l[i] = 0.f;
+  for (int i = 0; i < kLChains; ++i) br.l[i] = 0.f;
   br.shf = s16x4{0, 0, 0, 0};
 }
 
 template <int D>
 BT_DEV void branch_merge(const Branch<D / 32>& br, float gate, f32x16* acc) {
-  float l = (br.l[0] + br.l[1]) + (br.l[2] + br.l[3]);
+  float l = branch_l(br);
   l += __shfl_xor(l, 32, 64);
   const float f = gate * __builtin_amdgcn_rcpf(l);
 #pragma unroll
