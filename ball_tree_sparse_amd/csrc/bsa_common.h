@@ -3,6 +3,8 @@
 // online-softmax attention over 32-key blocks read straight from the
 // tree-ordered K and transposed V.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 
 namespace bt {
@@ -104,117 +106,173 @@ BT_DEV s16x4 shift_frag(float m) {
   return f;
 }
 
-// One online-softmax step over NKB 32-key blocks for QB query blocks of 32
-// (qf: QB x D/16 B-operand fragments of scaled queries, br: QB branch
-// states).  Block kb's keys are rows row0(kb) .. row0(kb)+31 of the head's
-// row-major K (kh) and of its transposed V blocks (vh: [rows/32][D][32]);
-// row0(kb) is a multiple of 32.  Every K and V fragment of the chunk is
-// requested before the first MFMA and then serves all QB query blocks, so the
-// cache traffic per query falls by QB.  FIRST: the branch's first chunk (its
-// maximum sets m; nothing is accumulated yet).
-template <int D, int NKB, int QB, bool FIRST, typename RowFn>
-BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
-                         RowFn row0, const bf16x8* qf, Branch<D / 32>* br) {
-  constexpr int DS = D / 16, DB = D / 32;
+// Fragments of NKB 32-key blocks: block kb's keys are rows row0(kb) ..
+// row0(kb)+31 of the head's row-major K (kh) and of its transposed V blocks
+// (vh: [rows/32][D][32]); row0(kb) is a multiple of 32.  kf are A operands of
+// S^T = K Q^T, vf A operands of O^T = V^T P^T.
+template <int D, int NKB, typename RowFn>
+BT_DEV void load_kfrags(const uint16_t* __restrict__ kh, RowFn row0, bf16x8 (&kf)[NKB][D / 16]) {
   const int lane = threadIdx.x & 63, hf = lane >> 5, c = lane & 31;
-  bf16x8 kf[NKB][DS], vf[NKB][2][DB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    const int64_t r0 = row0(kb);
-    const uint16_t* krow = kh + (r0 + c) * D + hf * 8;
+    const uint16_t* krow = kh + (row0(kb) + c) * D + hf * 8;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) kf[kb][s] = *(const bf16x8*)(krow + s * 16);
-    const uint16_t* vblk = vh + r0 * D + c * 32 + hf * 8;
+    for (int s = 0; s < D / 16; ++s) kf[kb][s] = *(const bf16x8*)(krow + s * 16);
+  }
+}
+template <int D, int NKB, typename RowFn>
+BT_DEV void load_vfrags(const uint16_t* __restrict__ vh, RowFn row0,
+                        bf16x8 (&vf)[NKB][2][D / 32]) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5, c = lane & 31;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const uint16_t* vblk = vh + row0(kb) * D + c * 32 + hf * 8;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < D / 32; ++db)
         vf[kb][s2][db] = *(const bf16x8*)(vblk + db * 32 * 32 + s2 * 16);
-  }
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    Branch<DB>& b = br[qb];
-    f32x16 sacc[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      f32x16 a = {};
-      if constexpr (!FIRST)
-        a = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ones_frag(), b.shf, a, 0, 0, 0);
-#pragma unroll
-      for (int s = 0; s < DS; ++s)
-        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][s], qf[qb * DS + s], a, 0, 0, 0);
-      sacc[kb] = a;
-    }
-    // chunk maximum of the shifted scores (of the scores on the first chunk)
-    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
-    float cm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-    // The running maximum is raised (and the state rescaled) only when a
-    // chunk maximum exceeds it by more than kLazyLog2, for every lane of the
-    // wave at once; the weights then stay below 2^kLazyLog2, and the
-    // normalised result is the same up to rounding.
-    if (FIRST || __ballot(cm > kLazyLog2)) {
-      float delta;                                  // taken off this chunk's scores
-      if constexpr (FIRST) {
-        delta = cm;
-        b.m = cm;
-      } else {
-        const float mn = b.m + fmaxf(cm, 0.f);
-        delta = mn - b.m;
-        const float alpha = __builtin_amdgcn_exp2f(-delta);
-#pragma unroll
-        for (int i = 0; i < kLChains; ++i) b.l[i] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) b.o[db][e] *= alpha;
-        b.m = mn;
-      }
-      b.shf = shift_frag(b.m);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[kb][e] -= delta;
-    }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][s2 * 8 + e]);
-        b.l[(kb * 2 + s2) % kLChains] = bsa_sum8(pf, b.l[(kb * 2 + s2) % kLChains]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          b.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][s2][db], pf, b.o[db], 0, 0, 0);
-      }
   }
 }
 
-// Online softmax over keys [0, len) of a branch in kChunk-key chunks (len is
-// a multiple of 32); row0(key) gives the row of the 32-key block at key.
+// S^T of NKB key blocks for one query block (qf: its D/16 B-operand
+// fragments of scaled queries), shifted by -m (not on the branch's first
+// chunk, FIRST).
+template <int D, int NKB, bool FIRST>
+BT_DEV void chunk_scores(const bf16x8 (&kf)[NKB][D / 16], const bf16x8* qf,
+                         const Branch<D / 32>& b, f32x16 (&sacc)[NKB]) {
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    f32x16 a = {};
+    if constexpr (!FIRST)
+      a = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ones_frag(), b.shf, a, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][s], qf[s], a, 0, 0, 0);
+    sacc[kb] = a;
+  }
+}
+
+// The online-softmax update of one query block's branch state with the
+// chunk's scores, and O^T += V^T P^T.  FIRST: the branch's first chunk (its
+// maximum sets m; nothing is accumulated yet).
+template <int D, int NKB, bool FIRST>
+BT_DEV void chunk_softmax_pv(f32x16 (&sacc)[NKB], const bf16x8 (&vf)[NKB][2][D / 32],
+                             Branch<D / 32>& b) {
+  constexpr int DB = D / 32;
+  // chunk maximum of the shifted scores (of the scores on the first chunk)
+  float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
+  float cm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+  cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+  // The running maximum is raised (and the state rescaled) only when a
+  // chunk maximum exceeds it by more than kLazyLog2, for every lane of the
+  // wave at once; the weights then stay below 2^kLazyLog2, and the
+  // normalised result is the same up to rounding.
+  if (FIRST || __ballot(cm > kLazyLog2)) {
+    float delta;                                  // taken off this chunk's scores
+    if constexpr (FIRST) {
+      delta = cm;
+      b.m = cm;
+    } else {
+      const float mn = b.m + fmaxf(cm, 0.f);
+      delta = mn - b.m;
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+      for (int i = 0; i < kLChains; ++i) b.l[i] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) b.o[db][e] *= alpha;
+      b.m = mn;
+    }
+    b.shf = shift_frag(b.m);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] -= delta;
+  }
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][s2 * 8 + e]);
+      b.l[(kb * 2 + s2) % kLChains] = bsa_sum8(pf, b.l[(kb * 2 + s2) % kLChains]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        b.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][s2][db], pf, b.o[db], 0, 0, 0);
+    }
+}
+
+// One online-softmax step over NKB 32-key blocks for QB query blocks of 32
+// (qf: QB x D/16 fragments, br: QB branch states), its fragments loaded here.
+// Every K and V fragment of the chunk serves all QB query blocks, so the
+// cache traffic per query falls by QB.
+template <int D, int NKB, int QB, bool FIRST, typename RowFn>
+BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
+                         RowFn row0, const bf16x8* qf, Branch<D / 32>* br) {
+  bf16x8 kf[NKB][D / 16], vf[NKB][2][D / 32];
+  load_kfrags<D, NKB>(kh, row0, kf);
+  load_vfrags<D, NKB>(vh, row0, vf);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    f32x16 sacc[NKB];
+    chunk_scores<D, NKB, FIRST>(kf, qf + qb * (D / 16), br[qb], sacc);
+    chunk_softmax_pv<D, NKB, FIRST>(sacc, vf, br[qb]);
+  }
+}
+
+// Online softmax over keys [0, len) of a branch (len a multiple of 32);
+// row0(key) gives the row of the 32-key block at key.  Full kChunk-key chunks
+// are software-pipelined without extra registers: the next chunk's K
+// fragments are requested as soon as the last query block's score MFMAs have
+// taken theirs, and its V fragments once the last P V MFMAs have, so each
+// load is in flight while part of a chunk is computed.  A tail of 32-key
+// blocks follows unpipelined.
 template <int D, int QB, typename RowFn>
 BT_DEV void attend_range(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
                          RowFn row0, int len, const bf16x8* qf, Branch<D / 32>* br) {
-  constexpr int KB = kChunk / 32;
+  constexpr int KB = kChunk / 32, DS = D / 16;
+  const int nfull = len / kChunk;
   int k0 = 0;
-  if (len >= kChunk) {
-    attend_chunk<D, KB, QB, true>(kh, vh, [&](int kb) -> int64_t { return row0(kb * 32); }, qf,
-                                  br);
-    k0 = kChunk;
-  } else if (len > 0) {
-    attend_chunk<D, 1, QB, true>(kh, vh, [&](int kb) -> int64_t { return row0(0); }, qf, br);
-    k0 = 32;
+  if (nfull > 0) {
+    bf16x8 kf[KB][DS], vf[KB][2][D / 32];
+    load_kfrags<D, KB>(kh, [&](int kb) -> int64_t { return row0(kb * 32); }, kf);
+    load_vfrags<D, KB>(vh, [&](int kb) -> int64_t { return row0(kb * 32); }, vf);
+    // The loads are unconditional (the last chunk requests itself again,
+    // from the cache, and the values go unused): with loads under a branch
+    // the compiler's wait counts at the loop head also covered the V loads
+    // just issued.
+    auto step = [&](auto first, int ci) {
+      constexpr bool FIRST = decltype(first)::value;
+      const int kn = min(ci + 1, nfull - 1) * kChunk;   // the next chunk's first key
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x16 sacc[KB];
+        chunk_scores<D, KB, FIRST>(kf, qf + qb * DS, br[qb], sacc);
+        if (qb == QB - 1)                      // the last scores have taken kf
+          load_kfrags<D, KB>(kh, [&](int kb) -> int64_t { return row0(kn + kb * 32); }, kf);
+        chunk_softmax_pv<D, KB, FIRST>(sacc, vf, br[qb]);
+      }
+      load_vfrags<D, KB>(vh, [&](int kb) -> int64_t { return row0(kn + kb * 32); }, vf);
+    };
+    step(std::true_type{}, 0);
+    for (int ci = 1; ci < nfull; ++ci) step(std::false_type{}, ci);
+    k0 = nfull * kChunk;
   }
-  for (; k0 + kChunk <= len; k0 += kChunk)
-    attend_chunk<D, KB, QB, false>(kh, vh,
-                                   [&](int kb) -> int64_t { return row0(k0 + kb * 32); }, qf, br);
-  for (; k0 < len; k0 += 32)                 // a tail of 32-key blocks
-    attend_chunk<D, 1, QB, false>(kh, vh, [&](int kb) -> int64_t { return row0(k0); }, qf, br);
+  if (k0 < len) {                            // a tail of 32-key blocks
+    if (k0 == 0)
+      attend_chunk<D, 1, QB, true>(kh, vh, [&](int kb) -> int64_t { return row0(0); }, qf, br);
+    else
+      attend_chunk<D, 1, QB, false>(kh, vh, [&](int kb) -> int64_t { return row0(k0); }, qf, br);
+    for (k0 += 32; k0 < len; k0 += 32)
+      attend_chunk<D, 1, QB, false>(kh, vh, [&](int kb) -> int64_t { return row0(k0); }, qf, br);
+  }
 }
 
 // The lane's part of a branch's normaliser (the chains added in order).
