@@ -197,7 +197,10 @@ BT_DEV int lane_xor(int x) {
   if constexpr (J == 1) return __builtin_amdgcn_mov_dpp(x, 0xb1, 0xf, 0xf, false);  // [1,0,3,2]
   else if constexpr (J == 2) return __builtin_amdgcn_mov_dpp(x, 0x4e, 0xf, 0xf, false);  // [2,3,0,1]
   else if constexpr (J < 32) return __builtin_amdgcn_ds_swizzle(x, (J << 10) | 0x1f);
-  else return __shfl_xor(x, J, 64);
+  else {   // lanes 32 apart: the two halves swapped on the VALU
+    const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    return (int)((threadIdx.x & 32) ? r[0] : r[1]);
+  }
 }
 
 template <int K, int J>
@@ -409,8 +412,7 @@ __global__ __launch_bounds__(kQcWaves * 64) void bsa_qc_cmp(const float* __restr
   const int k0 = w * seg, len = max(0, min(nc - k0, seg));
   attend_range<D, 1>(kcb + (int64_t)h * nc * D, vct + (int64_t)h * nc * D,
                      [&](int key) -> int64_t { return k0 + key; }, len, qf, &br);
-  float l = branch_l(br);
-  l += __shfl_xor(l, 32, 64);
+  const float l = xor32_sum(branch_l(br));
   pm[w][lane] = br.m;
   pl[w][lane] = l;
 #pragma unroll
@@ -651,8 +653,7 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((D > 32 ? 2 : 3), 8) void
   auto merge = [&](int gi, bool first) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float l = branch_l(br[qb]);
-      l += __shfl_xor(l, 32, 64);
+      const float l = xor32_sum(branch_l(br[qb]));
       const float f = sgate[w][qb][gi][lane] * __builtin_amdgcn_rcpf(l);
 #pragma unroll
       for (int db = 0; db < DB; ++db)

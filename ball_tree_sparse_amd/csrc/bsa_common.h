@@ -53,6 +53,21 @@ BT_DEV int tpos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 // ----------------------------------------------------------------- fused ----
 typedef __bf16 bsa_bf16x2 __attribute__((ext_vector_type(2)));
 
+// x combined with its value in lane ^ 32, through gfx950's v_permlane32_swap
+// (a VALU exchange of the wave's two halves) rather than an LDS permute.
+// With both operands x, the swap returns each lane's own value and its
+// partner's, so the max and the sum are the same in both lanes of a pair.
+BT_DEV float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+BT_DEV float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum of the eight bf16 values of an MFMA operand, added to acc.
 BT_DEV float bsa_sum8(bf16x8 x, float acc) {
   const bsa_bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -166,8 +181,7 @@ BT_DEV void chunk_softmax_pv(f32x16 (&sacc)[NKB], const bf16x8 (&vf)[NKB][2][D /
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
-  float cm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-  cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+  const float cm = xor32_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
   // The running maximum is raised (and the state rescaled) only when a
   // chunk maximum exceeds it by more than kLazyLog2, for every lane of the
   // wave at once; the weights then stay below 2^kLazyLog2, and the
@@ -296,8 +310,7 @@ BT_DEV void branch_init(Branch<D / 32>& br) {
 
 template <int D>
 BT_DEV void branch_merge(const Branch<D / 32>& br, float gate, f32x16* acc) {
-  float l = branch_l(br);
-  l += __shfl_xor(l, 32, 64);
+  const float l = xor32_sum(branch_l(br));
   const float f = gate * __builtin_amdgcn_rcpf(l);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)

@@ -223,6 +223,18 @@ inline emu_f32x16 __builtin_amdgcn_mfma_f32_32x32x16_bf16(emu_bf16x8 a, emu_bf16
   return d;
 }
 
+// ---- v_permlane32_swap: lanes 32-63 of the first operand trade places with
+// lanes 0-31 of the second; returns the two operands after the swap ----------
+typedef unsigned emu_u32x2 __attribute__((ext_vector_type(2)));
+inline emu_u32x2 __builtin_amdgcn_permlane32_swap(unsigned a, unsigned b, bool, bool) {
+  const int l = emu_tid() & 63;
+  const unsigned a_x = emu_shfl_from(a, l ^ 32), b_x = emu_shfl_from(b, l ^ 32);
+  emu_u32x2 r;
+  r[0] = l < 32 ? a : b_x;      // upper half of a takes the lower half of b
+  r[1] = l < 32 ? a_x : b;      // lower half of b takes the upper half of a
+  return r;
+}
+
 // ---- MFMA 32x32x8 bf16 (bf16 operands as raw 16-bit patterns) ------------
 typedef short emu_s16x4 __attribute__((ext_vector_type(4)));
 inline float emu_bf16_bits(short h) {
