@@ -572,7 +572,7 @@ __global__ __launch_bounds__(64) void bsa_qc_slc(const float* __restrict__ qbar,
 // A workgroup owns one (group, head); each of its NWV waves owns QB blocks of
 // 32 queries (group = NWV * QB * 32).
 template <int D, int NWV, bool QC, int QB>
-__global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((D > 32 ? 2 : 3), 8) void bsa_fused(
+__global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QC || D > 32 ? 2 : 3), 8) void bsa_fused(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ perm,
     const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vtt,
     const uint16_t* __restrict__ kcb, const uint16_t* __restrict__ vct,
@@ -583,11 +583,14 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((D > 32 ? 2 : 3), 8) void
     uint16_t* __restrict__ out) {
   constexpr int DS = D / 16, DB = D / 32;
   __shared__ int32_t ssel[64];
-  // The merged output and the gates of a wave's queries wait in LDS while the
-  // branches run (lane-major, conflict-free), so the registers hold only the
-  // branch state: three waves per SIMD instead of two.
-  __shared__ float sacc_out[NWV][QB][DB * 16][64];
+  // Without group compression the merged output and the gates of a wave's
+  // queries wait in LDS while the three branches run (lane-major,
+  // conflict-free), so the registers hold only the branch state: three waves
+  // per SIMD instead of two.  With it (one branch, then the block and group
+  // results) the merged output stays in registers.
+  __shared__ float sacc_out[QC ? 1 : NWV][QC ? 1 : QB][QC ? 1 : DB * 16][64];
   __shared__ float sgate[NWV][QB][3][64];
+  f32x16 accr[QC ? QB : 1][QC ? DB : 1];
   const int total = ngroups * H;
   int pair = blockIdx.x;
   if (xcd_map) pair = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
@@ -659,8 +662,12 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((D > 32 ? 2 : 3), 8) void
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float& x = sacc_out[w][qb][db * 16 + e][lane];
-          x = first ? br[qb].o[db][e] * f : fmaf(br[qb].o[db][e], f, x);
+          if constexpr (QC) {
+            accr[qb][db][e] = br[qb].o[db][e] * f;      // QC: the ball branch only
+          } else {
+            float& x = sacc_out[w][qb][db * 16 + e][lane];
+            x = first ? br[qb].o[db][e] * f : fmaf(br[qb].o[db][e], f, x);
+          }
         }
     }
   };
@@ -686,12 +693,12 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((D > 32 ? 2 : 3), 8) void
         for (int gq = 0; gq < 4; ++gq) {
           const float4 a = *(const float4*)(rc + db * 32 + gq * 8 + hf * 4);
           const float4 b = *(const float4*)(rsl + db * 32 + gq * 8 + hf * 4);
-          const float g1 = sgate[w][qb][1][lane], g2 = sgate[w][qb][2][lane];
-          float* x = &sacc_out[w][qb][db * 16 + gq * 4][lane];
-          x[0] = fmaf(g2, b.x, fmaf(g1, a.x, x[0]));
-          x[64] = fmaf(g2, b.y, fmaf(g1, a.y, x[64]));
-          x[128] = fmaf(g2, b.z, fmaf(g1, a.z, x[128]));
-          x[192] = fmaf(g2, b.w, fmaf(g1, a.w, x[192]));
+          const float g1 = G[qb][1], g2 = G[qb][2];
+          f32x16& x = accr[qb][db];
+          x[gq * 4 + 0] = fmaf(g2, b.x, fmaf(g1, a.x, x[gq * 4 + 0]));
+          x[gq * 4 + 1] = fmaf(g2, b.y, fmaf(g1, a.y, x[gq * 4 + 1]));
+          x[gq * 4 + 2] = fmaf(g2, b.z, fmaf(g1, a.z, x[gq * 4 + 2]));
+          x[gq * 4 + 3] = fmaf(g2, b.w, fmaf(g1, a.w, x[gq * 4 + 3]));
         }
     }
   } else {
@@ -722,15 +729,19 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((D > 32 ? 2 : 3), 8) void
   for (int qb = 0; qb < QB; ++qb) {
     const int64_t pq = perm_index(perm[t0 + qb * 32 + c], N);
     uint16_t* orow = out + pq * rs + (int64_t)h * D;
-    const float* x = &sacc_out[w][qb][0][lane];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int e0 = (db * 16 + gq * 4) * 64;
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (QC) y[r] = accr[qb][db][gq * 4 + r];
+          else y[r] = sacc_out[w][qb][db * 16 + gq * 4 + r][lane];
+        }
         u32x2 pk;
-        pk[0] = pack_bf16x2(x[e0], x[e0 + 64]);
-        pk[1] = pack_bf16x2(x[e0 + 128], x[e0 + 192]);
+        pk[0] = pack_bf16x2(y[0], y[1]);
+        pk[1] = pack_bf16x2(y[2], y[3]);
         *(u32x2*)(orow + db * 32 + gq * 8 + hf * 4) = pk;
       }
   }
