@@ -74,6 +74,8 @@ def _run(q, k, v, perm, W, ball, block, group, topk, mask, gate_const=None, qc=F
     (65536, 1, 32, 64, 32, 32, 8, True, None),        # 2,048 blocks: scores kept in LDS
     (8192, 2, 32, 256, 64, 128, 8, True, None),       # two 64-query waves per group
     (8192, 2, 32, 256, 128, 256, 4, False, None),     # four 64-query waves per group
+    (4096, 2, 32, 32, 32, 32, 4, True, None),         # 32-point balls: one 32-key block
+    (4096, 2, 64, 64, 32, 32, 3, True, None),         # d 64, 96 selected keys: a 32-key tail
 ])
 def test_parity(n, H, d, ball, block, group, topk, mask, gates):
     _, q, k, v, W, perm = _setup(n, H, d, seed=n + H + d + topk, leaf=block)

@@ -232,12 +232,14 @@ def test_ball_attn_kernel_tree_order_input(sim):
     assert np.abs(out - A.ball_attn(q, k, v, None, ball)).max() <= 2e-2
 
 
-@pytest.mark.parametrize("qc,group", [(0, 64), (1, 64), (0, 128)])
-def test_bsa_kernels(sim, qc, group):
+@pytest.mark.parametrize("qc,group,ball,block,topk", [(0, 64, 128, 64, 4), (1, 64, 128, 64, 4),
+                                                    (0, 128, 128, 64, 4), (0, 32, 32, 32, 5)])
+def test_bsa_kernels(sim, qc, group, ball, block, topk):
     """BSA, and BSA with group compression (qc = 1); group 128 runs two waves
-    of 64 queries per workgroup."""
+    of 64 queries per workgroup; 32-point balls and 5 selected 32-key blocks
+    leave 32-key tails in the ball and selection branches."""
     d_ = sim["dir"]
-    n, H, d, ball, block, topk = 2048, 2, 32, 128, 64, 4
+    n, H, d = 2048, 2, 32
     rng = np.random.default_rng(5)
     c = synth.deformed_sphere(rng, n)
     q, k, v = (synth.normal_features(rng, n, H, d, "bf16") for _ in range(3))
