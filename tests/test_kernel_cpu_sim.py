@@ -54,6 +54,74 @@ def sim(tmp_path_factory):
     return bins
 
 
+@pytest.fixture(scope="module")
+def sim_tsan(tmp_path_factory):
+    """The tree and pipeline drivers under ThreadSanitizer: the emulation runs
+    every lane as a host thread, so LDS or memory shared between the lanes or
+    waves of a workgroup without a barrier or an atomic is reported as a race."""
+    if not os.path.exists(CXX):
+        pytest.skip("clang++ not available")
+    d = tmp_path_factory.mktemp("cpu_sim_tsan")
+    flags = ["-std=c++20", "-O1", "-g", "-fsanitize=thread", "-fno-omit-frame-pointer",
+             "-I", SIM, "-I", os.path.join(ROOT, "include")]
+    bins, procs = {"dir": d}, []
+    for name, src in (("tree", "tree_driver.cpp"), ("pipeline", "pipeline_driver.cpp")):
+        out = str(d / name)
+        procs.append(subprocess.Popen([CXX, *flags, os.path.join(SIM, src),
+                                       os.path.join(SIM, "emu.cpp"), "-o", out, "-lpthread"],
+                                      stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                      text=True))
+        bins[name] = out
+    for p in procs:
+        o, _ = p.communicate()
+        assert p.returncode == 0, o[-4000:]
+    return bins
+
+
+def _tsan_env(shuffle):
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1 report_signal_unsafe=0")
+    env["EMU_SHUFFLE"] = str(shuffle)
+    return env
+
+
+def test_tree_kernels_no_races(sim_tsan):
+    """4,096 points, leaf 128 (two global levels and the finisher), plain and
+    rotated: no data race, and the permutations are the oracle's."""
+    d_ = sim_tsan["dir"]
+    w = synth.make("rotpair", n=4096, features=False)
+    w.coords.astype(np.float32).tofile(d_ / "coords.bin")
+    w.R.astype(np.float32).tofile(d_ / "R.bin")
+    for rot in (False, True):
+        args = [sim_tsan["tree"], "coords.bin", "4096", "128", "out.bin"] + (["R.bin"] if rot else [])
+        r = subprocess.run(args, cwd=d_, capture_output=True, text=True, timeout=900,
+                           env=_tsan_env(3))
+        assert r.returncode == 0 and "ThreadSanitizer" not in r.stderr, r.stderr[-4000:]
+        want = T.rotate_build(w.coords, 128, w.R) if rot else T.build(w.coords, 128)
+        assert np.array_equal(np.fromfile(d_ / "out.bin", np.int32), want)
+
+
+def test_rotated_pair_pipeline_no_races(sim_tsan):
+    """The rotated-pair pipeline (both trees, ball attention, gathers,
+    scatter, inverse) at 4,096 points and 2 heads: no data race."""
+    from oracle import permute as P
+    d_ = sim_tsan["dir"]
+    n, H = 4096, 2
+    w = synth.make("rotpair", n=n, features=False)
+    rng = np.random.default_rng(n)
+    q, k, v = (synth.normal_features(rng, n, H, 32, "bf16") for _ in range(3))
+    w.coords.astype(np.float32).tofile(d_ / "coords.bin")
+    w.R.astype(np.float32).tofile(d_ / "R.bin")
+    for t, nm in ((q, "q.bin"), (k, "k.bin"), (v, "v.bin")):
+        _dump(t, d_ / nm)
+    r = subprocess.run([sim_tsan["pipeline"], str(n), str(w.leaf), str(w.ball), str(H), "32"],
+                       cwd=d_, capture_output=True, text=True, timeout=1800, env=_tsan_env(9))
+    assert r.returncode == 0 and "done" in r.stdout and "ThreadSanitizer" not in r.stderr, \
+        r.stderr[-4000:]
+    pb = np.fromfile(d_ / "pb.bin", np.int32)
+    assert np.array_equal(pb, T.rotate_build(w.coords, w.leaf, w.R))
+    assert np.array_equal(np.fromfile(d_ / "inv.bin", np.int32), P.invert(pb))
+
+
 # Cases that take minutes of emulation run only with BT_SIM_SLOW=1 (their
 # results are recorded with the tree notes of the design document).
 SLOW = pytest.mark.skipif(os.environ.get("BT_SIM_SLOW") != "1",
