@@ -43,6 +43,13 @@
 //               -1.  Built by one workgroup in LDS (slots <= 1024).
 #include "common.h"
 
+// Test hook: the CPU emulation of these kernels under MemorySanitizer marks
+// a workgroup's LDS arrays uninitialised when the workgroup starts (so that a
+// read before any write is reported); here it is nothing.
+#ifndef BT_LDS_POISON
+#define BT_LDS_POISON(x)
+#endif
+
 namespace bt {
 
 constexpr int kThreads = 256;
@@ -155,6 +162,7 @@ __global__ __launch_bounds__(kThreads) void tree_hist(const float4* __restrict__
   constexpr int HI = PASS == 0 ? 32 : (PASS == 1 ? 21 : 10);
   constexpr uint32_t MASK = PASS == 2 ? 1023u : 2047u;
   __shared__ uint32_t lh[kBins];
+  BT_LDS_POISON(lh);
   const int tid = threadIdx.x;
   const int c = blockIdx.x;
   const int node = c / cpn;
@@ -188,7 +196,9 @@ __global__ __launch_bounds__(kThreads) void tree_select(int64_t nsize,
   constexpr int SHIFT = PASS == 0 ? 21 : (PASS == 1 ? 10 : 0);
   constexpr int PER = kBins / kThreads;   // 8 bins per thread
   __shared__ uint32_t red[kThreads / 64];
+  BT_LDS_POISON(red);
   __shared__ NodeState s_new;
+  BT_LDS_POISON(s_new);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int node = blockIdx.x;
   NodeState s;
@@ -236,6 +246,7 @@ __global__ __launch_bounds__(kThreads) void tree_count(const float4* __restrict_
                                                        int cpn, const NodeState* __restrict__ st,
                                                        uint2* __restrict__ counts) {
   __shared__ uint32_t red[kThreads / 64];
+  BT_LDS_POISON(red);
   const int c = blockIdx.x;
   const int node = c / cpn;
   const NodeState s = st[node];
@@ -257,8 +268,11 @@ __global__ __launch_bounds__(kThreads) void tree_scatter(
     const NodeState* __restrict__ st, const uint2* __restrict__ counts,
     uint32_t* __restrict__ partials) {
   __shared__ uint32_t red[kThreads / 64];
+  BT_LDS_POISON(red);
   __shared__ uint32_t wlt[kThreads / 64], weq[kThreads / 64];
+  BT_LDS_POISON(wlt); BT_LDS_POISON(weq);
   __shared__ uint32_t pred[12][kThreads / 64];
+  BT_LDS_POISON(pred);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = blockIdx.x;
   const int node = c / cpn;
@@ -346,6 +360,7 @@ __global__ __launch_bounds__(kThreads) void tree_scatter(
 __global__ __launch_bounds__(kThreads) void tree_extents(const uint32_t* __restrict__ partials,
                                                          int cpn, uint32_t* __restrict__ ext_next) {
   __shared__ uint32_t pred[12][kThreads / 64];
+  BT_LDS_POISON(pred);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int node = blockIdx.x;
   const int first = node * cpn;
@@ -474,7 +489,9 @@ __global__ __launch_bounds__(kFinishWaves * 64) void tree_finish(const float4* _
                                                                  int nf, int leaf, int nnodes,
                                                                  int32_t* __restrict__ perm) {
   __shared__ float4 srec[kFinishWaves][kFinish];
+  BT_LDS_POISON(srec);
   __shared__ uint32_t shist[kFinishWaves][256];
+  BT_LDS_POISON(shist);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int node = blockIdx.x * kFinishWaves + w;
   if (node >= nnodes) return;          // no workgroup barrier below
@@ -629,8 +646,11 @@ constexpr int kBlockSplitMin = 1024;
 __global__ __launch_bounds__(kFinishBlockWaves * 64) void tree_finish_block(
     const float4* __restrict__ rec, int nf, int leaf, int32_t* __restrict__ perm) {
   __shared__ float4 srec[kFinish];
+  BT_LDS_POISON(srec);
   __shared__ uint32_t shist[kFinishBlockWaves][256];
+  BT_LDS_POISON(shist);
   __shared__ BlockSplitLds bsl;
+  BT_LDS_POISON(bsl);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t base = (int64_t)blockIdx.x * nf;
   for (int i = tid; i < nf; i += kFinishBlockWaves * 64) srec[i] = rec[base + i];
@@ -673,8 +693,11 @@ BT_DEV void padded_segment(int n, int lev, int s, int* start, int* cnt) {
 __global__ __launch_bounds__(kFinishBlockWaves * 64) void tree_finish_padded(
     const float4* __restrict__ rec, int n, int ncap, int leaf, int32_t* __restrict__ perm) {
   __shared__ float4 srec[kFinish];
+  BT_LDS_POISON(srec);
   __shared__ uint32_t shist[kFinishBlockWaves][256];
+  BT_LDS_POISON(shist);
   __shared__ BlockSplitLds bsl;
+  BT_LDS_POISON(bsl);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int i = tid; i < n; i += kFinishBlockWaves * 64) srec[i] = rec[i];
   __syncthreads();

@@ -78,6 +78,48 @@ def sim_tsan(tmp_path_factory):
     return bins
 
 
+@pytest.fixture(scope="module")
+def sim_msan(tmp_path_factory):
+    """The tree driver under MemorySanitizer, with its workspace left
+    uninitialised and every LDS array marked uninitialised when a workgroup
+    starts (tests/cpu_sim/msan_lds.h): a read of either before any write that
+    steers a branch or an address is reported."""
+    if not os.path.exists(CXX):
+        pytest.skip("clang++ not available")
+    d = tmp_path_factory.mktemp("cpu_sim_msan")
+    out = str(d / "tree")
+    r = subprocess.run([CXX, "-std=c++20", "-O1", "-g", "-fsanitize=memory",
+                        "-fno-omit-frame-pointer", "-DBT_SIM_UNINIT_WS", "-include",
+                        os.path.join(SIM, "msan_lds.h"), "-I", SIM, "-I",
+                        os.path.join(ROOT, "include"), os.path.join(SIM, "tree_driver.cpp"),
+                        os.path.join(SIM, "emu.cpp"), "-o", out, "-lpthread"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout[-4000:] + r.stderr[-4000:]
+    return {"dir": d, "tree": out}
+
+
+@pytest.mark.parametrize("padded", [False, True])
+def test_tree_kernels_no_uninitialised_reads(sim_msan, padded):
+    """4,096 points, leaf 128 (global levels and the finisher), rotated, and a
+    972-point padded tree: nothing uninitialised is read, and the
+    permutations are the oracle's."""
+    d_ = sim_msan["dir"]
+    if padded:
+        c = synth.uniform_cube(np.random.default_rng(11), 972)
+        c.astype(np.float32).tofile(d_ / "coords.bin")
+        args, want = ["padded", "coords.bin", "972", "32", "out.bin"], T.build_padded(c, 32)
+    else:
+        w = synth.make("rotpair", n=4096, features=False)
+        w.coords.astype(np.float32).tofile(d_ / "coords.bin")
+        w.R.astype(np.float32).tofile(d_ / "R.bin")
+        args = ["coords.bin", "4096", "128", "out.bin", "R.bin"]
+        want = T.rotate_build(w.coords, 128, w.R)
+    r = subprocess.run([sim_msan["tree"], *args], cwd=d_, capture_output=True, text=True,
+                       timeout=900, env=dict(os.environ, EMU_SHUFFLE="4"))
+    assert r.returncode == 0 and "MemorySanitizer" not in r.stderr, r.stderr[-4000:]
+    assert np.array_equal(np.fromfile(d_ / "out.bin", np.int32), want)
+
+
 def _tsan_env(shuffle):
     env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1 report_signal_unsafe=0")
     env["EMU_SHUFFLE"] = str(shuffle)
