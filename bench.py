@@ -22,7 +22,8 @@ Prints ONE JSON line.  Besides the required fields it carries:
   roofline      for the ball-attention kernel: algorithmic bytes per launch
                 (q, k, v read once, out written once, perm read once) over the
                 mean launch time, against the 8 TB/s HBM peak (source in
-                peak_source); `traffic` is the HBM byte count of the kernel
+                peak_source, and gpu_rocminfo gives the clock and compute units
+                that rocminfo reports); `traffic` is the HBM byte count of the kernel
                 per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters
                 (profiles/), or null if the kernel source changed since they
                 were taken; `measured_copy_GBps` is a timed 128 MiB
@@ -58,6 +59,29 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_SOURCE = ("AMD Instinct MI355X public specification: HBM3E 8.0 TB/s; dense bf16 "
                "MFMA 2.5 PFLOP/s (without sparsity); 256 CUs at 2.4 GHz")
+
+
+def _rocminfo_gpu():
+    """The GPU agent's clock and compute units as rocminfo prints them (a
+    child process, run before this process touches the GPU), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    agent, found = {}, None
+    for line in r.stdout.splitlines():
+        t = line.strip()
+        if t.startswith("Name:") and "gfx" in t:
+            agent = {"name": t.split(":", 1)[1].strip()}
+        elif agent and t.startswith("Max Clock Freq. (MHz):"):
+            agent["max_clock_mhz"] = int(t.split(":", 1)[1].split()[0])
+        elif agent and t.startswith("Compute Unit:"):
+            agent["compute_units"] = int(t.split(":", 1)[1].split()[0])
+        if "max_clock_mhz" in agent and "compute_units" in agent:
+            found = agent
+            break
+    return found
 
 
 def _cpu_model():
@@ -523,10 +547,15 @@ def main():
                     help="time only the other rows (permute, coarsen/refine, BSA, padded "
                          "attention, backward, small trees); for kernel traces and counters")
     args = ap.parse_args()
+    # the CPU oracle's BLAS uses the host's cores (set before NumPy loads)
+    ncores = str(len(os.sched_getaffinity(0)))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
+        os.environ.setdefault(var, ncores)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    gpu_info = None if args.rows_only else _rocminfo_gpu()
     import torch
 
     from ball_tree_sparse_amd import ops, synth
@@ -547,6 +576,7 @@ def main():
     else:
         line = bench_ball(args, dev, torch, ops, synth)
     if line is not None:
+        line["gpu_rocminfo"] = gpu_info        # the clock and CU count the peaks assume
         print(json.dumps(line), flush=True)
 
 
