@@ -15,6 +15,8 @@
 // With MASK (the padded tree of an uneven point count) a negative permutation
 // entry marks an unused slot: its key takes no weight and no output row is
 // written for it; row indices are clamped to the nrows input rows.
+#include <type_traits>
+
 #include "common.h"
 
 namespace bt {
@@ -203,6 +205,9 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   __shared__ __attribute__((aligned(16))) uint16_t vt[HPW][D * VTS];
   // MASK: 1 where the key slot holds a point (read four keys at a time)
   __shared__ __attribute__((aligned(16))) uint8_t kok[MASK ? BALL : 4];
+  // unmasked 256-point balls: largest squared key norm per wave and head
+  constexpr bool kShift = BALL >= 256 && !MASK;
+  __shared__ __attribute__((aligned(16))) float knorm2[kShift ? HPW : 1][kShift ? NT / 64 : 1];
 
   const int64_t N = nrows;
   const int hgroups = H / HPW;
@@ -274,6 +279,7 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
   };
   auto stage = [&](const Rows& r) {
+    float kmax2 = 0.f;
 #pragma unroll
     for (int ii = 0; ii < IPT; ++ii) {
       const int it = tid + ii * NT;
@@ -288,6 +294,25 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       }
 #pragma unroll
       for (int u = 0; u < KPI; ++u) *(u32x4*)&ks[hh][(key0 + u) * KS + dc * 8] = kn[ii][u];
+      if constexpr (kShift) {
+        // squared norm of each key's head slice: this thread's 8 elements,
+        // then the D/8 adjacent lanes holding the rest of the slice
+        float nk = 0.f;
+#pragma unroll
+        for (int u = 0; u < KPI; ++u) {
+          float t = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t wd = kn[ii][u][e];
+            t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd),
+                                                __builtin_bit_cast(bf16x2, wd), t, false);
+          }
+#pragma unroll
+          for (int m = 1; m < D / 8; m <<= 1) t += __shfl_xor(t, m, 64);
+          nk = fmaxf(nk, t);
+        }
+        kmax2 = ii == 0 ? nk : fmaxf(kmax2, nk);
+      }
       const int pos0 = (key0 & ~15) + swap23(key0 & 15);   // keeps bits 0,1
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -301,13 +326,65 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
       }
     }
+    if constexpr (kShift) {
+      // lanes CPR apart hold the same head; lane hh * D/8 writes head hh
+#pragma unroll
+      for (int m = CPR; m < 64; m <<= 1) kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, m, 64));
+      if (lane < CPR && lane % (D / 8) == 0) knorm2[lane / (D / 8)][w] = kmax2;
+    }
   };
 
   const float c2 = 1.4426950408889634f / sqrtf((float)D);   // log2(e)/sqrt(d)
+  // Unmasked 256-point balls (their softmax binds with the gathers) take the
+  // scores from the MFMA in log2 units with a shift already subtracted
+  // (scale_query and shift_frag, common.h).  The shift is |q| * max_k |k|
+  // (log2 units, the queries scaled): no score exceeds it (Cauchy-Schwarz),
+  // so no maximum is taken.  When that bound is above kBound for a query of
+  // the wave, the largest weight could fall below 2^(-2 kBound) and the wave
+  // takes a running maximum instead, raised only when a chunk passes it by
+  // more than kLazy (the weights stay below 2^kLazy).
+  constexpr float kLazy = 8.f;
+  constexpr float kBound = 48.f;
   bf16x8 qc[HPW][DS];
+  float qnorm2[HPW];                 // kShift: squared norm of each head's scaled query
+  auto take_queries = [&]() {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      float nq = 0.f;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        qc[hh][s] = kShift ? scale_query(qn[hh][s], c2) : qn[hh][s];
+        if constexpr (kShift) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 pr = {qc[hh][s][2 * e], qc[hh][s][2 * e + 1]};
+            nq = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, nq, false);
+          }
+        }
+      }
+      if constexpr (kShift) nq += __shfl_xor(nq, 32, 64);
+      qnorm2[hh] = nq;
+    }
+  };
   // attention of the staged item for its HPW heads and this wave's queries
   auto attend = [&](const Rows& rc) {
     uint16_t* orow0 = out + row_of(rc.q) * rs + (int64_t)rc.h0 * D;
+    // kShift: the bound |q| max|k| of every head, up front
+    float bnd_q[HPW];
+    bool bnd_ok[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      bnd_q[hh] = 0.f;
+      bnd_ok[hh] = false;
+      if constexpr (kShift) {
+        const float nq = qnorm2[hh];
+        float nk = knorm2[hh][0];
+#pragma unroll
+        for (int i = 1; i < NT / 64; ++i) nk = fmaxf(nk, knorm2[hh][i]);
+        bnd_q[hh] = __builtin_sqrtf(nq * nk);
+        bnd_ok[hh] = __ballot(!(bnd_q[hh] <= kBound)) == 0;   // NaN or Inf: not bounded
+      }
+    }
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       // Keys go in chunks of CH 32-key blocks with an online softmax: one
@@ -319,82 +396,126 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
       float s4[4] = {0.f, 0.f, 0.f, 0.f};   // four chains of the normaliser
-      float mrun = -INFINITY;               // running maximum (raw scores)
+      float mrun = -INFINITY;               // running maximum (raw scores; kShift: log2 units)
+      bf16x8 shf = {};                      // kShift: shift_frag8(mrun)
+      const bool bounded = kShift && bnd_ok[hh];
+      if (bounded) {
+        mrun = bnd_q[hh];
+        shf = shift_frag8(mrun);
+      }
+      auto chunks = [&](auto bnd) {
+        constexpr bool BND = decltype(bnd)::value;
 #pragma unroll
-      for (int c0 = 0; c0 < KB; c0 += CH) {
-        // ---- S^T = K Q^T --------------------------------------------------
-        f32x16 sacc[CH];
+        for (int c0 = 0; c0 < KB; c0 += CH) {
+          // ---- S^T = K Q^T --------------------------------------------------
+          f32x16 sacc[CH];
 #pragma unroll
-        for (int kb = 0; kb < CH; ++kb) {
-          f32x16 a = {};
+          for (int kb = 0; kb < CH; ++kb) {
+            f32x16 a = {};
+            if constexpr (kShift) {
+              if (BND || c0 > 0)
+                a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_frag8(), shf, a, 0, 0, 0);
+            }
 #pragma unroll
-          for (int s = 0; s < DS; ++s) {
-            const bf16x8 kf =
-                *(const bf16x8*)&ks[hh][((c0 + kb) * 32 + c) * KS + s * 16 + hf * 8];
-            a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qc[hh][s], a, 0, 0, 0);
+            for (int s = 0; s < DS; ++s) {
+              const bf16x8 kf =
+                  *(const bf16x8*)&ks[hh][((c0 + kb) * 32 + c) * KS + s * 16 + hf * 8];
+              a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qc[hh][s], a, 0, 0, 0);
+            }
+            sacc[kb] = a;
           }
-          sacc[kb] = a;
-        }
-        if constexpr (MASK) {
-          // element e holds key kb*32 + 8*(e/4) + 4*hf + e%4
+          if constexpr (MASK) {
+            // element e holds key kb*32 + 8*(e/4) + 4*hf + e%4
+#pragma unroll
+            for (int kb = 0; kb < CH; ++kb)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const uint32_t ok4 = *(const uint32_t*)&kok[(c0 + kb) * 32 + 8 * g + 4 * hf];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (!((ok4 >> (8 * i)) & 0xffu)) sacc[kb][g * 4 + i] = -INFINITY;
+              }
+          }
+          // ---- softmax over the keys of query column c ----------------------
+          // Four independent chains for the maximum and the sum (BND: the
+          // maximum is not used).
+          float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
           for (int kb = 0; kb < CH; ++kb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const uint32_t ok4 = *(const uint32_t*)&kok[(c0 + kb) * 32 + 8 * g + 4 * hf];
+            for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
+          float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          float moff = -mx * c2;
+          if constexpr (BND) {
+            (void)mx;
+          } else if constexpr (kShift) {
+            // the scores are relative to mrun (on the first chunk, raw)
+            if (c0 == 0 || __ballot(mx > kLazy)) {
+              float delta;
+              if (c0 == 0) {
+                delta = mx;
+                mrun = mx;
+              } else {
+                const float mn = mrun + fmaxf(mx, 0.f);
+                delta = mn - mrun;
+                const float alpha = __builtin_amdgcn_exp2f(-delta);
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (!((ok4 >> (8 * i)) & 0xffu)) sacc[kb][g * 4 + i] = -INFINITY;
+                for (int i = 0; i < 4; ++i) s4[i] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                  for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+                mrun = mn;
+              }
+              shf = shift_frag8(mrun);
+#pragma unroll
+              for (int kb = 0; kb < CH; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sacc[kb][e] -= delta;
             }
-        }
-        // ---- softmax over the keys of query column c ----------------------
-        // Four independent chains for the maximum and the sum.
-        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+          } else if constexpr (CH < KB) {
+            const float mn = fmaxf(mrun, mx);
+            // nothing to rescale before the first chunk with a key; a chunk
+            // whose keys are all unused slots leaves the maximum at -inf
+            const float alpha =
+                mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mrun - mn) * c2);
 #pragma unroll
-        for (int kb = 0; kb < CH; ++kb)
+            for (int i = 0; i < 4; ++i) s4[i] *= alpha;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
-        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        float moff = -mx * c2;
-        if constexpr (CH < KB) {
-          const float mn = fmaxf(mrun, mx);
-          // nothing to rescale before the first chunk with a key; a chunk
-          // whose keys are all unused slots leaves the maximum at -inf
-          const float alpha =
-              mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mrun - mn) * c2);
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s4[i] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-          mrun = mn;
-          moff = mn == -INFINITY ? 0.f : -mn * c2;
-        }
-        bf16x8 pf[CH][2];                // P^T operands, rounded once
-#pragma unroll
-        for (int kb = 0; kb < CH; ++kb)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              pf[kb][s2][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][s2 * 8 + e], c2, moff));
-            s4[(kb * 2 + s2) & 3] = sum_bf16x8(pf[kb][s2], s4[(kb * 2 + s2) & 3]);
+              for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+            mrun = mn;
+            moff = mn == -INFINITY ? 0.f : -mn * c2;
           }
-        // ---- O^T += V^T P^T -------------------------------------------------
+          bf16x8 pf[CH][2];                // P^T operands, rounded once
 #pragma unroll
-        for (int kb = 0; kb < CH; ++kb)
+          for (int kb = 0; kb < CH; ++kb)
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
+            for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const bf16x8 vf = *(const bf16x8*)&vt[hh][(db * 32 + c) * VTS +
-                                                        ((c0 + kb) * 2 + s2) * 16 + hf * 8];
-              oacc[db] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][s2], oacc[db], 0, 0, 0);
+              for (int e = 0; e < 8; ++e)
+                pf[kb][s2][e] = (__bf16)__builtin_amdgcn_exp2f(
+                    kShift ? sacc[kb][s2 * 8 + e] : fmaf(sacc[kb][s2 * 8 + e], c2, moff));
+              s4[(kb * 2 + s2) & 3] = sum_bf16x8(pf[kb][s2], s4[(kb * 2 + s2) & 3]);
             }
-      }
+          // ---- O^T += V^T P^T -------------------------------------------------
+#pragma unroll
+          for (int kb = 0; kb < CH; ++kb)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+              for (int db = 0; db < DB; ++db) {
+                const bf16x8 vf = *(const bf16x8*)&vt[hh][(db * 32 + c) * VTS +
+                                                          ((c0 + kb) * 2 + s2) * 16 + hf * 8];
+                oacc[db] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][s2], oacc[db], 0, 0, 0);
+              }
+        }
+      };
+      if (kShift && bounded) chunks(std::true_type{});
+      else chunks(std::false_type{});
       float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
       sum += __shfl_xor(sum, 32, 64);
       // ---- normalise, regroup across the lane halves, store 16-byte runs ---
@@ -439,10 +560,7 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   Rows rc = load_rows(j);
   load_data(rc);
   stage(rc);
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh)
-#pragma unroll
-    for (int s = 0; s < DS; ++s) qc[hh][s] = qn[hh][s];
+  take_queries();
   if constexpr (!PIPE) {                     // one item per workgroup
     __syncthreads();
     attend(rc);
@@ -463,10 +581,7 @@ void ball_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     if (!has_next) break;
     __syncthreads();                         // everyone is done with LDS
     stage(rn);                               // waits for the next item's rows
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh)
-#pragma unroll
-      for (int s = 0; s < DS; ++s) qc[hh][s] = qn[hh][s];
+    take_queries();
     rc = rn;
     rn = rnn;
     jn = jnn;

@@ -91,35 +91,7 @@ struct Branch {
 // The scores reach the exponential without a pass over them on the VALU:
 // the queries are multiplied by log2(e)/sqrt(d) before their rounding to bf16
 // (scale_query), so S^T = K Q^T is already in log2 units, and the running
-// maximum m is subtracted inside the MFMAs.  A 32x32x8 MFMA of a fragment of
-// ones with shift_frag(m) puts -m in every row of a lane's column; the score
-// MFMAs accumulate onto it.  shift_frag splits -m into three bf16 pieces,
-// which between them hold all 24 bits of its significand, in the k rows of
-// the lanes of the lower half (the lanes of the upper half hold zeros), so
-// the sum over k is -m exactly.
-BT_DEV bf16x8 scale_query(bf16x8 x, float scale) {
-  bf16x8 y;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = (__bf16)((float)x[e] * scale);
-  return y;
-}
-BT_DEV float log2_score_scale(int d) { return 1.4426950408889634f / sqrtf((float)d); }
-
-BT_DEV s16x4 ones_frag() { return s16x4{0x3f80, 0x3f80, 0x3f80, 0x3f80}; }
-BT_DEV s16x4 shift_frag(float m) {
-  const float x = -m;
-  const float hi = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
-  const float r = x - hi;                                      // exact
-  const float mid = __uint_as_float(__float_as_uint(r) & 0xffff0000u);
-  const float lo = r - mid;                                    // exact, at most 8 bits
-  const bool lower = ((threadIdx.x >> 5) & 1) == 0;
-  s16x4 f;
-  f[0] = lower ? (short)(__float_as_uint(hi) >> 16) : (short)0;
-  f[1] = lower ? (short)(__float_as_uint(mid) >> 16) : (short)0;
-  f[2] = lower ? (short)(__float_as_uint(lo) >> 16) : (short)0;
-  f[3] = 0;
-  return f;
-}
+// maximum m is subtracted inside the MFMAs (shift_frag, common.h).
 
 // Fragments of NKB 32-key blocks: block kb's keys are rows row0(kb) ..
 // row0(kb)+31 of the head's row-major K (kh) and of its transposed V blocks

@@ -102,6 +102,49 @@ BT_DEV uint32_t wave_incl_scan_u32(uint32_t v) {
   return v;
 }
 
+// -------------------------------------------- softmax shift on the MFMA ----
+// Scores can leave the MFMA in log2 units with the running maximum m already
+// subtracted: the queries are multiplied by log2(e)/sqrt(d) before their
+// rounding to bf16 (scale_query), and a 32x32x8 MFMA of a fragment of ones
+// with shift_frag(m) puts -m in every row of a lane's column, for the score
+// MFMAs to accumulate onto.  shift_frag splits -m into three bf16 pieces,
+// which between them hold all 24 bits of its significand, in the k rows of
+// the lanes of the lower half (the lanes of the upper half hold zeros), so
+// the sum over k is -m exactly.
+BT_DEV bf16x8 scale_query(bf16x8 x, float scale) {
+  bf16x8 y;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = (__bf16)((float)x[e] * scale);
+  return y;
+}
+BT_DEV float log2_score_scale(int d) { return 1.4426950408889634f / sqrtf((float)d); }
+
+BT_DEV s16x4 ones_frag() { return s16x4{0x3f80, 0x3f80, 0x3f80, 0x3f80}; }
+BT_DEV s16x4 shift_frag(float m) {
+  const float x = -m;
+  const float hi = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
+  const float r = x - hi;                                      // exact
+  const float mid = __uint_as_float(__float_as_uint(r) & 0xffff0000u);
+  const float lo = r - mid;                                    // exact, at most 8 bits
+  const bool lower = ((threadIdx.x >> 5) & 1) == 0;
+  s16x4 f;
+  f[0] = lower ? (short)(__float_as_uint(hi) >> 16) : (short)0;
+  f[1] = lower ? (short)(__float_as_uint(mid) >> 16) : (short)0;
+  f[2] = lower ? (short)(__float_as_uint(lo) >> 16) : (short)0;
+  f[3] = 0;
+  return f;
+}
+
+// The same for a 32x32x16 MFMA: the three pieces in k rows 0-2, the rest 0.
+BT_DEV bf16x8 ones_frag8() {
+  return __builtin_bit_cast(bf16x8, s16x8{0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80,
+                                          0x3f80, 0x3f80});
+}
+BT_DEV bf16x8 shift_frag8(float m) {
+  const s16x4 f = shift_frag(m);
+  return __builtin_bit_cast(bf16x8, s16x8{f[0], f[1], f[2], 0, 0, 0, 0, 0});
+}
+
 }  // namespace bt
 
 // ------------------------------------------------------------ host side ----

@@ -22,3 +22,34 @@ def max_abs(a, b):
     a = a.detach().float().cpu().double().numpy() if hasattr(a, "detach") else np.asarray(a)
     b = b.detach().float().cpu().double().numpy() if hasattr(b, "detach") else np.asarray(b)
     return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def ramp_scores(q, k, perm, ball, seed, big_key=False):
+    """q and k altered so that scores move in steps along each ball.
+
+    Coordinate 0 of every key gets -8 * ((ball - 1 - t) // 64) added, t its
+    slot in the ball (perm[slot] is its row), and coordinate 0 of every query
+    gets +4 or -4 (random): against a head dimension of 32 or 64, a query of
+    the first kind sees its largest scores climb by 2^8 or more (in base-2
+    units) from one 64-key stretch to the next, one of the second kind sees
+    them fall.  A kernel that keeps a running maximum must raise it within a
+    ball for some queries while others in the same wave stay put.
+
+    big_key: coordinate 1 of every query is set to 0 and the key in slot 5
+    of every ball gets 256 there.  The scores do not change, but the product
+    of the norms |q| |k| (a bound on every score) becomes large.
+    """
+    dt = q.dtype
+    q, k = q.float().clone(), k.float().clone()
+    n, H, _ = q.shape
+    rng = np.random.default_rng(seed)
+    q[:, :, 0] += torch.from_numpy(rng.choice([-4.0, 4.0], size=(n, H)).astype(np.float32))
+    t = np.arange(len(perm)) % ball
+    off = np.zeros(n, np.float32)
+    off[np.asarray(perm)] = -8.0 * ((ball - 1 - t) // 64)
+    k[:, :, 0] += torch.from_numpy(off)[:, None]
+    if big_key:
+        q[:, :, 1] = 0.0
+        rows = np.asarray(perm)[t == 5]
+        k[torch.from_numpy(rows.astype(np.int64)), :, 1] = 256.0
+    return q.to(dt), k.to(dt)

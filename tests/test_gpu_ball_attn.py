@@ -6,7 +6,7 @@ import torch
 from ball_tree_sparse_amd import ops, synth
 from oracle import attention as A
 from oracle import tree as T
-from tests.helpers import gpu, max_abs, say
+from tests.helpers import gpu, max_abs, ramp_scores, say
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +54,23 @@ def test_parity_random_perm(n, H, d, ball, dtype):
     want = A.ball_attn(q, k, v, perm, ball)
     err = max_abs(got, want)
     assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("big", [False, True])
+@pytest.mark.parametrize("n,H,d,ball", [(4096, 4, 32, 256), (2048, 2, 64, 256),
+                                        (2048, 3, 32, 256), (4096, 4, 32, 128)])
+def test_parity_scores_stepping_along_the_ball(n, H, d, ball, big):
+    """Scores that climb (or fall) by 2^8 and more from one 64-key stretch of
+    a ball to the next.  big: one key per ball with a large component no
+    query has, so that the bound |q| max|k| on the scores is far above them
+    (a running maximum is then raised part way through)."""
+    dev = gpu()
+    q, k, v = _feats(n, H, d, "bf16", seed=n + d + 11)
+    perm = np.random.default_rng(8).permutation(n)
+    q, k = ramp_scores(q, k, perm, ball, seed=9, big_key=big)
+    say("ball_attn stepped scores", n, H, d, ball)
+    got = _run(q, k, v, perm, ball, dev)
+    assert max_abs(got, A.ball_attn(q, k, v, perm, ball)) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

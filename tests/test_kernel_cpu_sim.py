@@ -326,6 +326,31 @@ def test_ball_attn_kernels(sim, n, H, d, ball, dtype):
     assert err <= (2e-2 if dtype == "bf16" else 1e-5), err
 
 
+@pytest.mark.parametrize("n,H,d,big", [(512, 2, 32, False), (512, 1, 64, False),
+                                       (768, 3, 32, False), (512, 2, 32, True),
+                                       (512, 1, 64, True), (768, 3, 32, True)])
+def test_ball_attn_kernels_stepped_scores(sim, n, H, d, big):
+    """256-point balls whose scores climb or fall by 2^8 and more from one
+    64-key stretch to the next.  big: one key per ball with a large
+    component no query has, so that |q| max|k| is far above every score
+    (the kernel then keeps a running maximum, raised mid-ball)."""
+    from tests.helpers import ramp_scores
+    d_ = sim["dir"]
+    rng = np.random.default_rng(n + d + 5)
+    q, k, v = (synth.normal_features(rng, n, H, d, "bf16") for _ in range(3))
+    perm = rng.permutation(n).astype(np.int32)
+    q, k = ramp_scores(q, k, perm, 256, seed=n, big_key=big)
+    for t, nm in ((q, "q.bin"), (k, "k.bin"), (v, "v.bin")):
+        _dump(t, d_ / nm)
+    perm.tofile(d_ / "perm.bin")
+    r = subprocess.run([sim["attn"], "ball", str(n), str(H), str(d), "256", "1"], cwd=d_,
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
+    out = _read_out(d_ / "out.bin", n, H, d, "bf16")
+    err = np.abs(out - A.ball_attn(q, k, v, perm, 256)).max()
+    assert err <= 2e-2, err
+
+
 def test_ball_attn_kernel_tree_order_input(sim):
     """perm == NULL: inputs already in tree order."""
     d_ = sim["dir"]
