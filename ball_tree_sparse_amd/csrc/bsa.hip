@@ -7,7 +7,8 @@
 //           layout of the P V product), block means of K in fp32 ([h][d][j],
 //           for the scores) and bf16 ([h][j][d]) and of V in bf16 (transposed
 //           like V) over blocks of l tree positions; Q -> fp32 group means
-//           qbar (the pooled query).
+//           qbar (the pooled query); the largest squared key norm per block
+//           and head.
 //   select  s[g, j] = qbar_g . Kc_j / sqrt(d) in fp32; blocks inside the
 //           group's own ball are excluded; top-k per (group, head), ties to
 //           the smaller block index: a wave bitonic sort of the 64 lane
@@ -15,14 +16,17 @@
 //           score; the (score, block) pairs at least that good (k or a few
 //           more) are gathered through LDS and sorted the same way, best
 //           first.  Only when more than 64 pairs tie with the bound does the
-//           wave fall back to repeated arg-max.
+//           wave fall back to repeated arg-max.  One workgroup per head also
+//           reduces the block norm maxima to the head's.
 //   fused   one workgroup per (group, head), one wave per 32 queries: the
 //           ball, compression and selection branches run one after another
 //           as online-softmax attention over 64-key chunks (S^T = K Q^T and
 //           O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, both operands read
 //           straight from the pooled layouts, so waves never wait on each
 //           other), and are merged with G = sigmoid(W q + b) before one
-//           scatter of the bf16 result to original order.
+//           scatter of the bf16 result to original order.  The softmax shift
+//           is the bound |q| max|k| of every score when that bound is small
+//           enough (no maximum is taken), else a running maximum.
 #include "bsa_common.h"
 
 namespace bt {
@@ -47,8 +51,10 @@ __global__ __launch_bounds__(256) void bsa_pool_kv(const uint16_t* __restrict__ 
                                                    uint16_t* __restrict__ vtt,
                                                    float* __restrict__ kc32,
                                                    uint16_t* __restrict__ kcb,
-                                                   uint16_t* __restrict__ vct) {
+                                                   uint16_t* __restrict__ vct,
+                                                   float* __restrict__ kbmax) {
   HIP_DYNAMIC_SHARED(uint16_t, lds)
+  __shared__ float snorm[4][HP];      // largest squared key norm per wave and head
   constexpr int CPR = HP * D / 8;                 // 16-byte chunks per gathered row
   uint16_t* kl = lds;                             // [len][HP*D]
   uint16_t* vl = lds + (size_t)len * HP * D;      // [len][HP*D]
@@ -57,6 +63,12 @@ __global__ __launch_bounds__(256) void bsa_pool_kv(const uint16_t* __restrict__ 
   const int h0 = blockIdx.y * HP;
   const int64_t nc = N / len;
   const int64_t rs = (int64_t)H * D;
+  // Squared norms of the key head rows: a thread's 8 elements, summed over
+  // the D/8 adjacent lanes of the row; the largest per thread (256 is a
+  // multiple of CPR, so a thread keeps one head).  len * CPR is a multiple of
+  // 64 (len is a multiple of 32), so every lane of a wave runs the same
+  // iterations.
+  float n2max = 0.f;
   for (int it = tid; it < len * CPR; it += 256) {
     const int r = it / CPR, ch = it - r * CPR;
     const int64_t t = j * len + r;
@@ -68,7 +80,20 @@ __global__ __launch_bounds__(256) void bsa_pool_kv(const uint16_t* __restrict__ 
     *(u32x4*)(kt + ((int64_t)(h0 + hh) * N + t) * D + dc * 8) = xk;
     *(u32x4*)(kl + r * (HP * D) + ch * 8) = xk;
     *(u32x4*)(vl + r * (HP * D) + ch * 8) = xv;
+    float n2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      n2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bsa_bf16x2, xk[e]),
+                                           __builtin_bit_cast(bsa_bf16x2, xk[e]), n2, false);
+#pragma unroll
+    for (int m = 1; m < D / 8; m <<= 1) n2 += __shfl_xor(n2, m, 64);
+    n2max = fmaxf(n2max, n2);
   }
+  // lanes CPR apart hold the same head
+#pragma unroll
+  for (int m = CPR; m < 64; m <<= 1) n2max = fmaxf(n2max, __shfl_xor(n2max, m, 64));
+  if ((tid & 63) < CPR && (tid & 63) % (D / 8) == 0)
+    snorm[tid >> 6][(tid & 63) / (D / 8)] = n2max;
   __syncthreads();
   // V transposed: 16-byte runs of 8 positions of one (head, 32-key block, d)
   const int nkb = len / 32;
@@ -87,6 +112,9 @@ __global__ __launch_bounds__(256) void bsa_pool_kv(const uint16_t* __restrict__ 
     const int64_t blk = (j * len) / 32 + kb;
     *(u32x4*)(vtt + (((int64_t)(h0 + hh) * (N / 32) + blk) * D + dd) * 32 + q8 * 8) = o;
   }
+  if (tid < HP)
+    kbmax[(int64_t)(h0 + tid) * nc + j] =
+        fmaxf(fmaxf(snorm[0][tid], snorm[1][tid]), fmaxf(snorm[2][tid], snorm[3][tid]));
   // block means of K (fp32 and bf16) and V (bf16, transposed layout)
   for (int it = tid; it < 2 * HP * D; it += 256) {
     const int isv = it / (HP * D), hd = it - isv * (HP * D);
@@ -250,7 +278,9 @@ __global__ __launch_bounds__(kSelThreads) void bsa_select(const float* __restric
                                                   int32_t nc, int32_t ngroups,
                                                   int32_t tg, int32_t group, int32_t ball,
                                                   int32_t block, int32_t topk, int32_t mask,
-                                                  int32_t* __restrict__ sel) {
+                                                  int32_t* __restrict__ sel,
+                                                  const float* __restrict__ kbmax,
+                                                  float* __restrict__ kmax2) {
   HIP_DYNAMIC_SHARED(float, smem)
   constexpr int d = D;
   float* sc = smem + tg * d;           // [tg][nc] (after tg*d floats kept for the layout)
@@ -260,6 +290,21 @@ __global__ __launch_bounds__(kSelThreads) void bsa_select(const float* __restric
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ng = min(tg, ngroups - g0);
   const float scale = 1.0f / sqrtf((float)d);
+  if (blockIdx.x == 0) {
+    // the head's largest squared key norm, for the attention's softmax shift
+    // (smem[0 .. 7] lie in the tg*d floats that the scores leave unused)
+    float m = 0.f;
+    for (int jb = tid; jb < nc; jb += kSelThreads) m = fmaxf(m, kbmax[(int64_t)h * nc + jb]);
+    m = wave_max(m);
+    if (lane == 0) smem[w] = m;
+    __syncthreads();
+    if (tid == 0) {
+      float x = smem[0];
+      for (int i = 1; i < kSelThreads / 64; ++i) x = fmaxf(x, smem[i]);
+      kmax2[h] = x;
+    }
+    __syncthreads();
+  }
   const float* kh = kc32 + (int64_t)h * D * nc;   // [d][nc]: lanes read consecutive blocks
   // the pooled query of a group is the same for every lane: it is read with
   // scalar loads (SGPR operands of the FMAs), not from LDS once per lane
@@ -580,7 +625,7 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QC || D > 32 ? 2 : 3), 8
     const float* __restrict__ gate_b, float gc0, float gc1, float gc2, int32_t H, int64_t N,
     int32_t nc, int32_t ngroups, int32_t ball, int32_t block, int32_t topk, int32_t xcd_map,
     const float* __restrict__ ocmp, const float* __restrict__ oslc,
-    uint16_t* __restrict__ out) {
+    const float* __restrict__ kmax2, uint16_t* __restrict__ out) {
   constexpr int DS = D / 16, DB = D / 32;
   __shared__ int32_t ssel[64];
   // Without group compression the merged output and the gates of a wave's
@@ -648,6 +693,29 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QC || D > 32 ? 2 : 3), 8
   // from here on the queries are scaled: their scores come out in log2 units
 #pragma unroll
   for (int i = 0; i < QB * DS; ++i) qf[i] = scale_query(qf[i], log2_score_scale(D));
+  // The shift of every branch is the bound |q| max|k| when it is at most
+  // kBoundLog2 for every query of the wave (the largest weight is then at
+  // least 2^(-2 kBoundLog2), a normal float); otherwise the branches keep a
+  // running maximum.
+  float bound[QB];
+  bool bounded = true;
+  {
+    const float k2 = kmax2[h];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float n2 = 0.f;
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bsa_bf16x2 pr = {qf[qb * DS + s][2 * e], qf[qb * DS + s][2 * e + 1]};
+          n2 = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, n2, false);
+        }
+      n2 = xor32_sum(n2);
+      bound[qb] = __builtin_sqrtf(n2 * k2);
+      bounded = bounded && __ballot(!(bound[qb] <= kBoundLog2)) == 0;   // NaN: not bounded
+    }
+  }
 
   const uint16_t* kh = kt + (int64_t)h * N * D;
   const uint16_t* vh = vtt + (int64_t)h * N * D;
@@ -672,57 +740,66 @@ __global__ __launch_bounds__(NWV * 64) BT_WAVES_PER_EU((QC || D > 32 ? 2 : 3), 8
     }
   };
 
-  // ---- ball branch: the ball holding this group (group | ball) ----------
-  {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) branch_init<D>(br[qb]);
-    const int64_t b0 = ((int64_t)g * group / ball) * ball;
-    attend_range<D, QB>(kh, vh, [&](int key) -> int64_t { return b0 + key; }, ball, qf, br);
-    merge(0, true);
-  }
-  if constexpr (QC) {
-    // ---- group compression: the token's block and group results --------
-    const float* rsl = oslc + ((int64_t)h * ngroups + g) * D;
+  auto init = [&](auto bnd) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const int64_t t = t0 + qb * 32 + c;
-      const float* rc = ocmp + ((int64_t)h * nc + t / block) * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const float4 a = *(const float4*)(rc + db * 32 + gq * 8 + hf * 4);
-          const float4 b = *(const float4*)(rsl + db * 32 + gq * 8 + hf * 4);
-          const float g1 = G[qb][1], g2 = G[qb][2];
-          f32x16& x = accr[qb][db];
-          x[gq * 4 + 0] = fmaf(g2, b.x, fmaf(g1, a.x, x[gq * 4 + 0]));
-          x[gq * 4 + 1] = fmaf(g2, b.y, fmaf(g1, a.y, x[gq * 4 + 1]));
-          x[gq * 4 + 2] = fmaf(g2, b.z, fmaf(g1, a.z, x[gq * 4 + 2]));
-          x[gq * 4 + 3] = fmaf(g2, b.w, fmaf(g1, a.w, x[gq * 4 + 3]));
-        }
+      if constexpr (decltype(bnd)::value) branch_init_bound<D>(br[qb], bound[qb]);
+      else branch_init<D>(br[qb]);
     }
-  } else {
-    // ---- compression branch: every coarse token ---------------------------
+  };
+  auto branches = [&](auto bnd) {
+    constexpr bool BND = decltype(bnd)::value;
+    // ---- ball branch: the ball holding this group (group | ball) ----------
     {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) branch_init<D>(br[qb]);
-      const uint16_t* kch = kcb + (int64_t)h * nc * D;
-      const uint16_t* vch = vct + (int64_t)h * nc * D;
-      attend_range<D, QB>(kch, vch, [&](int key) -> int64_t { return key; }, nc, qf, br);
-      merge(1, false);
+      init(bnd);
+      const int64_t b0 = ((int64_t)g * group / ball) * ball;
+      attend_range<D, QB, BND>(kh, vh, [&](int key) -> int64_t { return b0 + key; }, ball, qf, br);
+      merge(0, true);
     }
-    // ---- selection branch: the union of the selected blocks ---------------
-    {
+    if constexpr (QC) {
+      // ---- group compression: the token's block and group results --------
+      const float* rsl = oslc + ((int64_t)h * ngroups + g) * D;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) branch_init<D>(br[qb]);
-      attend_range<D, QB>(kh, vh,
-                          [&](int key) -> int64_t {
-                            return (int64_t)ssel[key / block] * block + (key % block);
-                          },
-                          topk * block, qf, br);
-      merge(2, false);
+      for (int qb = 0; qb < QB; ++qb) {
+        const int64_t t = t0 + qb * 32 + c;
+        const float* rc = ocmp + ((int64_t)h * nc + t / block) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const float4 a = *(const float4*)(rc + db * 32 + gq * 8 + hf * 4);
+            const float4 b = *(const float4*)(rsl + db * 32 + gq * 8 + hf * 4);
+            const float g1 = G[qb][1], g2 = G[qb][2];
+            f32x16& x = accr[qb][db];
+            x[gq * 4 + 0] = fmaf(g2, b.x, fmaf(g1, a.x, x[gq * 4 + 0]));
+            x[gq * 4 + 1] = fmaf(g2, b.y, fmaf(g1, a.y, x[gq * 4 + 1]));
+            x[gq * 4 + 2] = fmaf(g2, b.z, fmaf(g1, a.z, x[gq * 4 + 2]));
+            x[gq * 4 + 3] = fmaf(g2, b.w, fmaf(g1, a.w, x[gq * 4 + 3]));
+          }
+      }
+    } else {
+      // ---- compression branch: every coarse token ---------------------------
+      {
+        init(bnd);
+        const uint16_t* kch = kcb + (int64_t)h * nc * D;
+        const uint16_t* vch = vct + (int64_t)h * nc * D;
+        attend_range<D, QB, BND>(kch, vch, [&](int key) -> int64_t { return key; }, nc, qf, br);
+        merge(1, false);
+      }
+      // ---- selection branch: the union of the selected blocks ---------------
+      {
+        init(bnd);
+        attend_range<D, QB, BND>(kh, vh,
+                                 [&](int key) -> int64_t {
+                                   return (int64_t)ssel[key / block] * block + (key % block);
+                                 },
+                                 topk * block, qf, br);
+        merge(2, false);
+      }
     }
-  }
+  };
+  if (bounded) branches(std::true_type{});
+  else branches(std::false_type{});
 
   // ---- store: lane owns d = db*32 + 8*gq + 4*hf + 0..3 of its query -------
 #pragma unroll
@@ -754,12 +831,13 @@ static void launch_fused(int group, dim3 grid, hipStream_t st, const uint16_t* q
                          const uint16_t* kcb, const uint16_t* vcb, const int32_t* sel,
                          const float* gw, const float* gb, const float* gc, int32_t H, int64_t N,
                          int32_t nc, int32_t ngroups, int32_t ball, int32_t block, int32_t topk,
-                         int32_t xmap, const float* ocmp, const float* oslc, uint16_t* out) {
+                         int32_t xmap, const float* ocmp, const float* oslc, const float* kmax2,
+                         uint16_t* out) {
   const float g0 = gc ? gc[0] : 0.f, g1 = gc ? gc[1] : 0.f, g2 = gc ? gc[2] : 0.f;
 #define BT_FUSED(NW, QBB)                                                                     \
   hipLaunchKernelGGL((bsa_fused<D, NW, QC, QBB>), grid, dim3(NW * 64), 0, st, q, perm, kt,    \
                      vt, kcb, vcb, sel, gw, gb, g0, g1, g2, H, N, nc, ngroups, ball, block,     \
-                     topk, xmap, ocmp, oslc, out)
+                     topk, xmap, ocmp, oslc, kmax2, out)
   // d = 32 and groups of 64 or more: each wave owns two 32-query blocks, so
   // every K and V fragment it loads serves 64 queries (at d = 64 the second
   // block's state would not fit the registers)
@@ -797,6 +875,8 @@ bt_status bsa_prepare(const void* q, const void* k, const void* v, const int32_t
   uint16_t* kcb = (uint16_t*)(b + L.kcb);
   uint16_t* vcb = (uint16_t*)(b + L.vcb);
   float* qbar = (float*)(b + L.qbar);
+  float* kbmax = (float*)(b + L.kbmax);
+  float* kmax2 = (float*)(b + L.kmax2);
   const int32_t nc = (int32_t)(N / p->block), ngroups = (int32_t)(N / p->group);
   const int cols = H * d / 8;
   const int slice = cols < 64 ? cols : 64;
@@ -809,13 +889,13 @@ bt_status bsa_prepare(const void* q, const void* k, const void* v, const int32_t
   const dim3 gk(nc, H / hp), gq(ngroups, (cols + slice - 1) / slice);
   if (d == 32 && hp == 2)
     hipLaunchKernelGGL((bsa_pool_kv<32, 2>), gk, pblk, pool_lds, st, (const uint16_t*)k,
-                       (const uint16_t*)v, perm, H, p->block, N, kt, vt, kc32, kcb, vcb);
+                       (const uint16_t*)v, perm, H, p->block, N, kt, vt, kc32, kcb, vcb, kbmax);
   else if (d == 32)
     hipLaunchKernelGGL((bsa_pool_kv<32, 1>), gk, pblk, pool_lds, st, (const uint16_t*)k,
-                       (const uint16_t*)v, perm, H, p->block, N, kt, vt, kc32, kcb, vcb);
+                       (const uint16_t*)v, perm, H, p->block, N, kt, vt, kc32, kcb, vcb, kbmax);
   else
     hipLaunchKernelGGL((bsa_pool_kv<64, 1>), gk, pblk, pool_lds, st, (const uint16_t*)k,
-                       (const uint16_t*)v, perm, H, p->block, N, kt, vt, kc32, kcb, vcb);
+                       (const uint16_t*)v, perm, H, p->block, N, kt, vt, kc32, kcb, vcb, kbmax);
   hipLaunchKernelGGL(bsa_pool_q, gq, pblk, 0, st, (const uint16_t*)q, perm, H, d, p->group, N,
                      qbar);
   bt_status s = launch_status("bsa_pool");
@@ -828,10 +908,10 @@ bt_status bsa_prepare(const void* q, const void* k, const void* v, const int32_t
   const dim3 gs((ngroups + tg - 1) / tg, H);
   if (d == 32)
     hipLaunchKernelGGL(bsa_select<32>, gs, dim3(kSelThreads), smem, st, qbar, kc32, H, nc, ngroups, tg,
-                       p->group, p->ball, p->block, p->topk, p->mask_own_ball, sel);
+                       p->group, p->ball, p->block, p->topk, p->mask_own_ball, sel, kbmax, kmax2);
   else
     hipLaunchKernelGGL(bsa_select<64>, gs, dim3(kSelThreads), smem, st, qbar, kc32, H, nc, ngroups, tg,
-                       p->group, p->ball, p->block, p->topk, p->mask_own_ball, sel);
+                       p->group, p->ball, p->block, p->topk, p->mask_own_ball, sel, kbmax, kmax2);
   return launch_status("bsa_select");
 }
 
@@ -846,6 +926,7 @@ bt_status bsa_launch(const void* q, const void* k, const void* v, const int32_t*
   uint16_t* kcb = (uint16_t*)(b + L.kcb);
   uint16_t* vcb = (uint16_t*)(b + L.vcb);
   float* qbar = (float*)(b + L.qbar);
+  const float* kmax2 = (const float*)(b + L.kmax2);
   int32_t* sel = sel_out ? sel_out : (int32_t*)(b + L.sel);
   const int32_t nc = (int32_t)(N / p->block), ngroups = (int32_t)(N / p->group);
   const int cols = H * d / 8;
@@ -883,7 +964,7 @@ bt_status bsa_launch(const void* q, const void* k, const void* v, const int32_t*
 #define BT_FUSED_CALL(DD, QCM)                                                                \
   launch_fused<DD, QCM>(p->group, dim3(total), st, (const uint16_t*)q, perm, kt, vt, kcb, vcb, sel, \
                         gate_w, gate_b, gate_const, H, N, nc, ngroups, p->ball, p->block,     \
-                        p->topk, xmap, ocmp, oslc, (uint16_t*)out)
+                        p->topk, xmap, ocmp, oslc, kmax2, (uint16_t*)out)
   if (d == 32) {
     if (qcm) BT_FUSED_CALL(32, true);
     else BT_FUSED_CALL(32, false);

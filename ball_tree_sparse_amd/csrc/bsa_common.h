@@ -13,10 +13,12 @@ constexpr int kChunk = 64;             // keys per online-softmax step
 constexpr int kSelRegs = 16;           // scores per lane held in registers by select
 constexpr int kSelThreads = 512;       // select: eight waves, one group of a tile each
 constexpr float kLazyLog2 = 8.0f;      // online softmax: rescale only past 2^8
+constexpr float kBoundLog2 = 48.0f;    // largest bound taken as the fixed softmax shift
 constexpr int kLChains = 2;            // chains of the softmax normaliser
 
 struct BsaLayout {
   size_t kt, vt, kc32, kcb, vcb, qbar, sel;   // vt, vcb: transposed blocks
+  size_t kbmax, kmax2;                        // largest squared key norm: per block, per head
   size_t qc, ocmp, oslc;                      // group compression only
   size_t total;
 };
@@ -34,6 +36,8 @@ static BsaLayout bsa_layout(int64_t N, int32_t H, int32_t d, const bsa_params* p
   L.vcb = o; o = a256(o + nc * H * d * 2);
   L.qbar = o; o = a256(o + G * H * d * 4);
   L.sel = o; o = a256(o + G * H * (size_t)p->topk * 4);
+  L.kbmax = o; o = a256(o + nc * H * 4);
+  L.kmax2 = o; o = a256(o + (size_t)H * 4);
   if (p->query_compression) {
     L.qc = o; o = a256(o + nc * H * d * 4);
     L.ocmp = o; o = a256(o + nc * H * d * 4);
@@ -92,6 +96,11 @@ struct Branch {
 // the queries are multiplied by log2(e)/sqrt(d) before their rounding to bf16
 // (scale_query), so S^T = K Q^T is already in log2 units, and the running
 // maximum m is subtracted inside the MFMAs (shift_frag, common.h).
+//
+// BND: m is fixed before the first chunk at a bound on every score of the
+// query, |q| * max_k |k| (Cauchy-Schwarz; the mean of keys is no longer than
+// the longest key, so the compressed tokens are covered too), and the chunks
+// take no maximum and never rescale.
 
 // Fragments of NKB 32-key blocks: block kb's keys are rows row0(kb) ..
 // row0(kb)+31 of the head's row-major K (kh) and of its transposed V blocks
@@ -124,14 +133,14 @@ BT_DEV void load_vfrags(const uint16_t* __restrict__ vh, RowFn row0,
 
 // S^T of NKB key blocks for one query block (qf: its D/16 B-operand
 // fragments of scaled queries), shifted by -m (not on the branch's first
-// chunk, FIRST).
-template <int D, int NKB, bool FIRST>
+// chunk, FIRST, unless m is a fixed bound, BND).
+template <int D, int NKB, bool FIRST, bool BND = false>
 BT_DEV void chunk_scores(const bf16x8 (&kf)[NKB][D / 16], const bf16x8* qf,
                          const Branch<D / 32>& b, f32x16 (&sacc)[NKB]) {
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     f32x16 a = {};
-    if constexpr (!FIRST)
+    if constexpr (!FIRST || BND)
       a = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ones_frag(), b.shf, a, 0, 0, 0);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
@@ -142,44 +151,47 @@ BT_DEV void chunk_scores(const bf16x8 (&kf)[NKB][D / 16], const bf16x8* qf,
 
 // The online-softmax update of one query block's branch state with the
 // chunk's scores, and O^T += V^T P^T.  FIRST: the branch's first chunk (its
-// maximum sets m; nothing is accumulated yet).
-template <int D, int NKB, bool FIRST>
+// maximum sets m; nothing is accumulated yet).  BND: m is a fixed bound and
+// the update is the weights alone.
+template <int D, int NKB, bool FIRST, bool BND = false>
 BT_DEV void chunk_softmax_pv(f32x16 (&sacc)[NKB], const bf16x8 (&vf)[NKB][2][D / 32],
                              Branch<D / 32>& b) {
   constexpr int DB = D / 32;
-  // chunk maximum of the shifted scores (of the scores on the first chunk)
-  float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
-  const float cm = xor32_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-  // The running maximum is raised (and the state rescaled) only when a
-  // chunk maximum exceeds it by more than kLazyLog2, for every lane of the
-  // wave at once; the weights then stay below 2^kLazyLog2, and the
-  // normalised result is the same up to rounding.
-  if (FIRST || __ballot(cm > kLazyLog2)) {
-    float delta;                                  // taken off this chunk's scores
-    if constexpr (FIRST) {
-      delta = cm;
-      b.m = cm;
-    } else {
-      const float mn = b.m + fmaxf(cm, 0.f);
-      delta = mn - b.m;
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
-#pragma unroll
-      for (int i = 0; i < kLChains; ++i) b.l[i] *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) b.o[db][e] *= alpha;
-      b.m = mn;
-    }
-    b.shf = shift_frag(b.m);
+  if constexpr (!BND) {
+    // chunk maximum of the shifted scores (of the scores on the first chunk)
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] -= delta;
+      for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], sacc[kb][e]);
+    const float cm = xor32_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+    // The running maximum is raised (and the state rescaled) only when a
+    // chunk maximum exceeds it by more than kLazyLog2, for every lane of the
+    // wave at once; the weights then stay below 2^kLazyLog2, and the
+    // normalised result is the same up to rounding.
+    if (FIRST || __ballot(cm > kLazyLog2)) {
+      float delta;                                  // taken off this chunk's scores
+      if constexpr (FIRST) {
+        delta = cm;
+        b.m = cm;
+      } else {
+        const float mn = b.m + fmaxf(cm, 0.f);
+        delta = mn - b.m;
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+        for (int i = 0; i < kLChains; ++i) b.l[i] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) b.o[db][e] *= alpha;
+        b.m = mn;
+      }
+      b.shf = shift_frag(b.m);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kb][e] -= delta;
+    }
   }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
@@ -199,7 +211,7 @@ BT_DEV void chunk_softmax_pv(f32x16 (&sacc)[NKB], const bf16x8 (&vf)[NKB][2][D /
 // (qf: QB x D/16 fragments, br: QB branch states), its fragments loaded here.
 // Every K and V fragment of the chunk serves all QB query blocks, so the
 // cache traffic per query falls by QB.
-template <int D, int NKB, int QB, bool FIRST, typename RowFn>
+template <int D, int NKB, int QB, bool FIRST, bool BND, typename RowFn>
 BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
                          RowFn row0, const bf16x8* qf, Branch<D / 32>* br) {
   bf16x8 kf[NKB][D / 16], vf[NKB][2][D / 32];
@@ -208,8 +220,8 @@ BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __rest
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     f32x16 sacc[NKB];
-    chunk_scores<D, NKB, FIRST>(kf, qf + qb * (D / 16), br[qb], sacc);
-    chunk_softmax_pv<D, NKB, FIRST>(sacc, vf, br[qb]);
+    chunk_scores<D, NKB, FIRST, BND>(kf, qf + qb * (D / 16), br[qb], sacc);
+    chunk_softmax_pv<D, NKB, FIRST, BND>(sacc, vf, br[qb]);
   }
 }
 
@@ -220,7 +232,7 @@ BT_DEV void attend_chunk(const uint16_t* __restrict__ kh, const uint16_t* __rest
 // taken theirs, and its V fragments once the last P V MFMAs have, so each
 // load is in flight while part of a chunk is computed.  A tail of 32-key
 // blocks follows unpipelined.
-template <int D, int QB, typename RowFn>
+template <int D, int QB, bool BND = false, typename RowFn>
 BT_DEV void attend_range(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
                          RowFn row0, int len, const bf16x8* qf, Branch<D / 32>* br) {
   constexpr int KB = kChunk / 32, DS = D / 16;
@@ -240,10 +252,11 @@ BT_DEV void attend_range(const uint16_t* __restrict__ kh, const uint16_t* __rest
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         f32x16 sacc[KB];
-        chunk_scores<D, KB, FIRST>(kf, qf + qb * DS, br[qb], sacc);
+        chunk_scores<D, KB, FIRST, BND>(kf, qf + qb * DS, br[qb], sacc);
         if (qb == QB - 1)                      // the last scores have taken kf
           load_kfrags<D, KB>(kh, [&](int kb) -> int64_t { return row0(kn + kb * 32); }, kf);
-        chunk_softmax_pv<D, KB, FIRST>(sacc, vf, br[qb]);
+        chunk_softmax_pv<D, KB, FIRST, BND>(sacc, vf, br[qb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       load_vfrags<D, KB>(vh, [&](int kb) -> int64_t { return row0(kn + kb * 32); }, vf);
     };
@@ -253,11 +266,14 @@ BT_DEV void attend_range(const uint16_t* __restrict__ kh, const uint16_t* __rest
   }
   if (k0 < len) {                            // a tail of 32-key blocks
     if (k0 == 0)
-      attend_chunk<D, 1, QB, true>(kh, vh, [&](int kb) -> int64_t { return row0(0); }, qf, br);
+      attend_chunk<D, 1, QB, true, BND>(kh, vh, [&](int kb) -> int64_t { return row0(0); }, qf,
+                                        br);
     else
-      attend_chunk<D, 1, QB, false>(kh, vh, [&](int kb) -> int64_t { return row0(k0); }, qf, br);
+      attend_chunk<D, 1, QB, false, BND>(kh, vh, [&](int kb) -> int64_t { return row0(k0); },
+                                         qf, br);
     for (k0 += 32; k0 < len; k0 += 32)
-      attend_chunk<D, 1, QB, false>(kh, vh, [&](int kb) -> int64_t { return row0(k0); }, qf, br);
+      attend_chunk<D, 1, QB, false, BND>(kh, vh, [&](int kb) -> int64_t { return row0(k0); },
+                                         qf, br);
   }
 }
 
@@ -278,6 +294,13 @@ BT_DEV void branch_init(Branch<D / 32>& br) {
 #pragma unroll
   for (int i = 0; i < kLChains; ++i) br.l[i] = 0.f;
   br.shf = s16x4{0, 0, 0, 0};
+}
+// A branch whose shift is fixed at the bound m (BND).
+template <int D>
+BT_DEV void branch_init_bound(Branch<D / 32>& br, float m) {
+  branch_init<D>(br);
+  br.m = m;
+  br.shf = shift_frag(m);
 }
 
 template <int D>

@@ -375,9 +375,11 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
     Wg = torch.from_numpy(w.gate_w).to(dev)
     q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
     out = torch.empty_like(q)
+    # 200 warm-up steps (about 55 ms): the GPU idles while the workload is
+    # generated on the host, and 20 steps do not bring its clocks back up
     us = _event_us(torch, lambda: ops.bsa_attn(q, k, v, p, w.ball, x["block"], x["group"],
                                                x["topk"], x["mask_own_ball"], gate_w=Wg,
-                                               out=out, workspace=bws), 100, warm=20)
+                                               out=out, workspace=bws), 300, warm=200)
     flops = 4 * N * H * d * (w.ball + N // x["block"] + x["topk"] * x["block"])
     if sel_check is not None:
         _, sel = ops.bsa_attn(q, k, v, p, w.ball, x["block"], x["group"], x["topk"],
@@ -396,7 +398,7 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
     us2 = _event_us(torch, lambda: ops.bsa_attn(q, k, v, p, w.ball, x["block"], x["group"],
                                                 x["topk"], x["mask_own_ball"], gate_w=Wg,
                                                 out=out, workspace=bws2, query_compression=True),
-                    100, warm=20)
+                    300, warm=100)
     flops2 = 4 * H * d * (N * w.ball + (N // x["block"]) ** 2 +
                           (N // x["group"]) * x["topk"] * x["block"])
     rows["f1_bsa_group_compression"] = {

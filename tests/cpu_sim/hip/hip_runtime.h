@@ -76,6 +76,8 @@ inline int emu_tid() { return threadIdx.x; }
 inline void __syncthreads() { g_blk->block_bar->arrive_and_wait(); }
 inline void emu_wave_sync() { g_blk->wave_bar[emu_tid() / 64]->arrive_and_wait(); }
 inline void __builtin_amdgcn_wave_barrier() { emu_wave_sync(); }
+// a compiler scheduling fence: nothing to do on the host
+inline void __builtin_amdgcn_sched_barrier(int) {}
 inline void __threadfence() { std::atomic_thread_fence(std::memory_order_seq_cst); }
 
 template <typename T>

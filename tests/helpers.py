@@ -53,3 +53,31 @@ def ramp_scores(q, k, perm, ball, seed, big_key=False):
         rows = np.asarray(perm)[t == 5]
         k[torch.from_numpy(rows.astype(np.int64)), :, 1] = 256.0
     return q.to(dt), k.to(dt)
+
+
+def step_ball_halves(q, k, perm, ball, big_key=False):
+    """q and k altered so that, within every ball, the keys of its second
+    64-key stretch score about 2^12 higher (base-2 units, head dimension 32)
+    than those of its first: coordinate 0 of every query is set to 4 plus its
+    draw, and coordinate 0 of the key in slot t gets +6 or -6 as t % ball is
+    past 64 or not.  A kernel with a running maximum must raise it part way
+    through each ball.
+
+    big_key: coordinate 1 of every query is set to 0 and the key in slot 3 of
+    every 64-slot block gets 256 there: no score changes, but |q| max|k| (a
+    bound on every score) becomes large.
+    """
+    dt = q.dtype
+    q, k = q.float().clone(), k.float().clone()
+    n = q.shape[0]
+    p = np.asarray(perm)
+    t = np.arange(len(p))
+    q[:, :, 0] += 4.0
+    off = np.zeros(n, np.float32)
+    off[p] = np.where(t % ball >= 64, 6.0, -6.0)
+    k[:, :, 0] += torch.from_numpy(off)[:, None]
+    if big_key:
+        q[:, :, 1] = 0.0
+        rows = p[t % 64 == 3]
+        k[torch.from_numpy(rows.astype(np.int64)), :, 1] = 256.0
+    return q.to(dt), k.to(dt)

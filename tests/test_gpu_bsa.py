@@ -14,7 +14,7 @@ from ball_tree_sparse_amd import ops, synth
 from oracle import attention as A
 from oracle import bsa as B
 from oracle import tree as T
-from tests.helpers import gpu, max_abs, say
+from tests.helpers import gpu, max_abs, say, step_ball_halves
 
 pytestmark = pytest.mark.gpu
 
@@ -87,6 +87,28 @@ def test_parity(n, H, d, ball, block, group, topk, mask, gates):
     if amb:
         ref = B.bsa(q, k, v, perm, ball, block, group, topk, mask,
                     W=None if gates else W, gate_const=gates, sel_override=use)
+    assert max_abs(out, ref) <= TOL
+
+
+@pytest.mark.parametrize("qc", [False, True])
+@pytest.mark.parametrize("big", [False, True])
+def test_parity_scores_stepping_within_balls(big, qc):
+    """Keys of the second 64-key stretch of every ball score about 2^12
+    higher than those of the first.  big: one key per block with a large
+    component no query has, so that the bound |q| max|k| is far above every
+    score and the branches keep a running maximum, raised part way through
+    each ball."""
+    n, H, d, ball, block, group, topk = 4096, 2, 32, 128, 64, 64, 4
+    _, q, k, v, W, perm = _setup(n, H, d, seed=17, leaf=block)
+    q, k = step_ball_halves(q, k, perm, ball, big_key=big)
+    say("bsa stepped scores", big, qc)
+    out, sel = _run(q, k, v, perm, W, ball, block, group, topk, True, qc=qc)
+    ref, parts = B.bsa(q, k, v, perm, ball, block, group, topk, True, W=W, return_parts=True,
+                       query_compression=qc)
+    use, amb = _check_sel(sel, parts, topk)
+    if amb:
+        ref = B.bsa(q, k, v, perm, ball, block, group, topk, True, W=W, sel_override=use,
+                    query_compression=qc)
     assert max_abs(out, ref) <= TOL
 
 

@@ -367,12 +367,19 @@ def test_ball_attn_kernel_tree_order_input(sim):
     assert np.abs(out - A.ball_attn(q, k, v, None, ball)).max() <= 2e-2
 
 
-@pytest.mark.parametrize("qc,group,ball,block,topk", [(0, 64, 128, 64, 4), (1, 64, 128, 64, 4),
-                                                    (0, 128, 128, 64, 4), (0, 32, 32, 32, 5)])
-def test_bsa_kernels(sim, qc, group, ball, block, topk):
+@pytest.mark.parametrize("qc,group,ball,block,topk,steps",
+                         [(0, 64, 128, 64, 4, None), (1, 64, 128, 64, 4, None),
+                          (0, 128, 128, 64, 4, None), (0, 32, 32, 32, 5, None),
+                          (0, 64, 128, 64, 4, "halves"), (0, 64, 128, 64, 4, "halves+big"),
+                          (1, 64, 128, 64, 4, "halves+big")])
+def test_bsa_kernels(sim, qc, group, ball, block, topk, steps):
     """BSA, and BSA with group compression (qc = 1); group 128 runs two waves
     of 64 queries per workgroup; 32-point balls and 5 selected 32-key blocks
-    leave 32-key tails in the ball and selection branches."""
+    leave 32-key tails in the ball and selection branches.  steps: scores
+    that step up by about 2^12 half way through every ball, with the bound
+    |q| max|k| small, or (big) far above every score, so that the kernel
+    keeps a running maximum and raises it."""
+    from tests.helpers import step_ball_halves
     d_ = sim["dir"]
     n, H, d = 2048, 2, 32
     rng = np.random.default_rng(5)
@@ -380,6 +387,8 @@ def test_bsa_kernels(sim, qc, group, ball, block, topk):
     q, k, v = (synth.normal_features(rng, n, H, d, "bf16") for _ in range(3))
     W = (0.02 * rng.standard_normal((3, d))).astype(np.float32)
     perm = T.build(c, block).astype(np.int32)
+    if steps:
+        q, k = step_ball_halves(q, k, perm, ball, big_key=steps.endswith("big"))
     for t, nm in ((q, "q.bin"), (k, "k.bin"), (v, "v.bin")):
         _dump(t, d_ / nm)
     perm.tofile(d_ / "perm.bin")
