@@ -37,30 +37,25 @@ size_t bsa_ws_size(int64_t N, int32_t H, int32_t d, const bsa_params* p) {
 
 // ------------------------------------------------------------------ pool ----
 
-// Grid (block j of `len` tree positions, head group of HP heads), 256
-// threads.  Rows of K and V are gathered through perm (HP*D*2 bytes each, a
-// whole 128-byte line for two heads at d = 32) into LDS; K is written back
-// row-major to kt[h][t][:], V transposed to vt[h][t/32][:][tpos(t%32)]; the
-// block means are summed from LDS in a fixed order (deterministic).
+// Workgroup (block j of `len` tree positions, head group hg of HP heads),
+// 256 threads.  Rows of K and V are gathered through perm (HP*D*2 bytes
+// each, a whole 128-byte line for two heads at d = 32) into LDS (lds: 2 len
+// HP D bf16); K is written back row-major to kt[h][t][:], V transposed to
+// vt[h][t/32][:][tpos(t%32)]; the block means are summed from LDS in a fixed
+// order (deterministic).
 template <int D, int HP>
-__global__ __launch_bounds__(256) void bsa_pool_kv(const uint16_t* __restrict__ k,
-                                                   const uint16_t* __restrict__ v,
-                                                   const int32_t* __restrict__ perm, int32_t H,
-                                                   int32_t len, int64_t N,
-                                                   uint16_t* __restrict__ kt,
-                                                   uint16_t* __restrict__ vtt,
-                                                   float* __restrict__ kc32,
-                                                   uint16_t* __restrict__ kcb,
-                                                   uint16_t* __restrict__ vct,
-                                                   float* __restrict__ kbmax) {
-  HIP_DYNAMIC_SHARED(uint16_t, lds)
+BT_DEV void pool_kv_block(int64_t j, int hg, uint16_t* lds, const uint16_t* __restrict__ k,
+                          const uint16_t* __restrict__ v, const int32_t* __restrict__ perm,
+                          int32_t H, int32_t len, int64_t N, uint16_t* __restrict__ kt,
+                          uint16_t* __restrict__ vtt, float* __restrict__ kc32,
+                          uint16_t* __restrict__ kcb, uint16_t* __restrict__ vct,
+                          float* __restrict__ kbmax) {
   __shared__ float snorm[4][HP];      // largest squared key norm per wave and head
   constexpr int CPR = HP * D / 8;                 // 16-byte chunks per gathered row
   uint16_t* kl = lds;                             // [len][HP*D]
   uint16_t* vl = lds + (size_t)len * HP * D;      // [len][HP*D]
   const int tid = threadIdx.x;
-  const int64_t j = blockIdx.x;
-  const int h0 = blockIdx.y * HP;
+  const int h0 = hg * HP;
   const int64_t nc = N / len;
   const int64_t rs = (int64_t)H * D;
   // Squared norms of the key head rows: a thread's 8 elements, summed over
@@ -134,21 +129,19 @@ __global__ __launch_bounds__(256) void bsa_pool_kv(const uint16_t* __restrict__ 
   }
 }
 
-// Grid (groups, column slices): fp32 means of Q over groups of `len` tree
-// positions.  A column is 8 consecutive bf16 of one head; thread (col, rg)
-// sums rows rg, rg+RG, ...; the RG partial sums are added in a fixed order.
-__global__ __launch_bounds__(256) void bsa_pool_q(const uint16_t* __restrict__ src,
-                                                  const int32_t* __restrict__ perm, int32_t H,
-                                                  int32_t d, int32_t len, int64_t N,
-                                                  float* __restrict__ mean32) {
-  __shared__ float part[256][9];
+// Workgroup (group j, column slice sy), 256 threads: fp32 means of Q over
+// groups of `len` tree positions.  A column is 8 consecutive bf16 of one
+// head; thread (col, rg) sums rows rg, rg+RG, ...; the RG partial sums
+// (part: 256 x 9 floats of LDS) are added in a fixed order.
+BT_DEV void pool_q_group(int64_t j, int sy, float (*part)[9], const uint16_t* __restrict__ src,
+                         const int32_t* __restrict__ perm, int32_t H, int32_t d, int32_t len,
+                         int64_t N, float* __restrict__ mean32) {
   const int cols = H * d / 8;
   const int slice = cols < 64 ? cols : 64;
   const int RG = 256 / slice;
   const int tid = threadIdx.x;
   const int colw = tid % slice, rg = tid / slice;
-  const int col = blockIdx.y * slice + colw;
-  const int64_t j = blockIdx.x;
+  const int col = sy * slice + colw;
   const int h = (col * 8) / d, dd = (col * 8) % d;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (rg < RG && col < cols) {
@@ -178,6 +171,47 @@ __global__ __launch_bounds__(256) void bsa_pool_q(const uint16_t* __restrict__ s
     float* m32 = mean32 + ((int64_t)h * nb + j) * d + dd;
 #pragma unroll
     for (int e = 0; e < 8; ++e) m32[e] = s[e] * inv;
+  }
+}
+
+// Grid (groups, column slices): the query means alone.
+__global__ __launch_bounds__(256) void bsa_pool_q(const uint16_t* __restrict__ src,
+                                                  const int32_t* __restrict__ perm, int32_t H,
+                                                  int32_t d, int32_t len, int64_t N,
+                                                  float* __restrict__ mean32) {
+  __shared__ float part[256][9];
+  pool_q_group(blockIdx.x, blockIdx.y, part, src, perm, H, d, len, N, mean32);
+}
+
+// One launch for the pooling of a BSA step: workgroups 0 .. nc*H/HP - 1
+// pool K and V (block j = id % nc, head group id / nc), the rest the group
+// means of Q (group id' % ngroups, column slice id' / ngroups), so that the
+// lighter query pooling fills the tail of the K and V gathers.  Dynamic LDS:
+// the larger of 2 len HP D bf16 and 256 x 9 floats.
+template <int D, int HP>
+__global__ __launch_bounds__(256) void bsa_pool(const uint16_t* __restrict__ q,
+                                                const uint16_t* __restrict__ k,
+                                                const uint16_t* __restrict__ v,
+                                                const int32_t* __restrict__ perm, int32_t H,
+                                                int32_t block, int32_t group, int64_t N,
+                                                uint16_t* __restrict__ kt,
+                                                uint16_t* __restrict__ vtt,
+                                                float* __restrict__ kc32,
+                                                uint16_t* __restrict__ kcb,
+                                                uint16_t* __restrict__ vct,
+                                                float* __restrict__ kbmax,
+                                                float* __restrict__ qbar) {
+  HIP_DYNAMIC_SHARED(uint16_t, lds)
+  const int64_t nc = N / block, ngroups = N / group;
+  const int64_t nkv = nc * (H / HP);
+  const int64_t id = blockIdx.x;          // uniform over the workgroup
+  if (id < nkv) {
+    pool_kv_block<D, HP>(id % nc, (int)(id / nc), lds, k, v, perm, H, block, N, kt, vtt, kc32,
+                         kcb, vct, kbmax);
+  } else {
+    const int64_t iq = id - nkv;
+    pool_q_group(iq % ngroups, (int)(iq / ngroups), (float (*)[9])lds, q, perm, H, D, group, N,
+                 qbar);
   }
 }
 
@@ -883,21 +917,20 @@ bt_status bsa_prepare(const void* q, const void* k, const void* v, const int32_t
   const dim3 pblk(256);
 
   // K, V: tree-ordered copies (V transposed) and block means; Q: fp32 group
-  // means (the pooled queries that score the blocks)
+  // means (the pooled queries that score the blocks); one launch
   const int hp = (H % 2 == 0 && d == 32) ? 2 : 1;
-  const size_t pool_lds = (size_t)2 * p->block * hp * d * sizeof(uint16_t);
-  const dim3 gk(nc, H / hp), gq(ngroups, (cols + slice - 1) / slice);
-  if (d == 32 && hp == 2)
-    hipLaunchKernelGGL((bsa_pool_kv<32, 2>), gk, pblk, pool_lds, st, (const uint16_t*)k,
-                       (const uint16_t*)v, perm, H, p->block, N, kt, vt, kc32, kcb, vcb, kbmax);
-  else if (d == 32)
-    hipLaunchKernelGGL((bsa_pool_kv<32, 1>), gk, pblk, pool_lds, st, (const uint16_t*)k,
-                       (const uint16_t*)v, perm, H, p->block, N, kt, vt, kc32, kcb, vcb, kbmax);
-  else
-    hipLaunchKernelGGL((bsa_pool_kv<64, 1>), gk, pblk, pool_lds, st, (const uint16_t*)k,
-                       (const uint16_t*)v, perm, H, p->block, N, kt, vt, kc32, kcb, vcb, kbmax);
-  hipLaunchKernelGGL(bsa_pool_q, gq, pblk, 0, st, (const uint16_t*)q, perm, H, d, p->group, N,
-                     qbar);
+  size_t pool_lds = (size_t)2 * p->block * hp * d * sizeof(uint16_t);
+  if (pool_lds < 256 * 9 * sizeof(float)) pool_lds = 256 * 9 * sizeof(float);
+  const int64_t npool = (int64_t)nc * (H / hp) + (int64_t)ngroups * ((cols + slice - 1) / slice);
+  const dim3 gp((unsigned)npool);
+#define BT_POOL(DD, HH)                                                                       \
+  hipLaunchKernelGGL((bsa_pool<DD, HH>), gp, pblk, pool_lds, st, (const uint16_t*)q,          \
+                     (const uint16_t*)k, (const uint16_t*)v, perm, H, p->block, p->group, N, kt, \
+                     vt, kc32, kcb, vcb, kbmax, qbar)
+  if (d == 32 && hp == 2) BT_POOL(32, 2);
+  else if (d == 32) BT_POOL(32, 1);
+  else BT_POOL(64, 1);
+#undef BT_POOL
   bt_status s = launch_status("bsa_pool");
   if (s != BT_OK) return s;
 
