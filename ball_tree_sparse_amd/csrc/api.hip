@@ -70,8 +70,9 @@ bt_status bsa_bwd_launch(const void* q, const void* k, const void* v, const int3
 
 static bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
-// Largest N that bt_build / bt_rotate_build accept (see build_common).
-constexpr int64_t kTreeMaxGpuNode = 1024;
+// Largest tree (points, or slots of a padded tree) that the builders accept:
+// trees that one workgroup builds in LDS (see build_common).
+constexpr int64_t kTreeMaxGpu = 8192;
 
 static bool valid_tree_shape(int64_t N, int32_t leaf) {
   return N >= 1 && leaf >= 1 && N < ((int64_t)1 << 31) && N % leaf == 0 && is_pow2(N / leaf);
@@ -116,13 +117,13 @@ static bt_status build_common(const float* coords, int64_t N, int32_t leaf, cons
   BT_REQUIRE(N < ((int64_t)1 << 31), "N must be below 2^31");
   BT_REQUIRE(N % leaf == 0 && is_pow2(N / leaf), "N must be leaf * 2^L (N=%lld, leaf=%d)",
              (long long)N, leaf);
-  // The passes that split nodes above 1,024 points faulted the GPU in
-  // testing and the cause has not been found, so they are switched off:
-  // only trees whose root fits the one-wave LDS finisher are built.
-  BT_REQUIRE(N <= kTreeMaxGpuNode || N == leaf,
-             "bt_build: trees with nodes above %lld points are switched off in this version "
-             "(their global passes faulted the GPU; cause not found); N=%lld",
-             (long long)kTreeMaxGpuNode, (long long)N);
+  // The multi-workgroup passes that split nodes above 1,024 points faulted
+  // the GPU in testing and the cause has not been found, so they are
+  // switched off: only trees that one workgroup builds in LDS are accepted.
+  BT_REQUIRE(N <= kTreeMaxGpu || N == leaf,
+             "bt_build: trees above %lld points are switched off in this version "
+             "(the multi-workgroup passes faulted the GPU; cause not found); N=%lld",
+             (long long)kTreeMaxGpu, (long long)N);
   BT_REQUIRE(ws != nullptr, "workspace must be non-null");
   BT_REQUIRE(((uintptr_t)ws & 255) == 0, "workspace must be 256-byte aligned");
   const size_t need = tree_workspace_size(N, leaf);
@@ -279,10 +280,10 @@ bt_status bt_build_padded(const float* coords, int64_t N, int32_t leaf, const fl
   const int64_t S = bt_padded_size(N, leaf);
   BT_REQUIRE(S > 0, "need N >= 1, leaf >= 1 and fewer than 2^31 slots (N=%lld, leaf=%d)",
              (long long)N, leaf);
-  BT_REQUIRE(S <= kTreeMaxGpuNode || S == leaf,
+  BT_REQUIRE(S <= kTreeMaxGpu || S == leaf,
              "bt_build_padded: trees above %lld slots are switched off in this version "
-             "(their global passes faulted the GPU; cause not found); slots=%lld",
-             (long long)kTreeMaxGpuNode, (long long)S);
+             "(the multi-workgroup passes faulted the GPU; cause not found); slots=%lld",
+             (long long)kTreeMaxGpu, (long long)S);
   if (R_host) {
     for (int i = 0; i < 9; ++i)
       BT_REQUIRE(R_host[i] == R_host[i] && R_host[i] - R_host[i] == 0.0f,

@@ -726,6 +726,205 @@ __global__ __launch_bounds__(kFinishBlockWaves * 64) void tree_finish_padded(
   }
 }
 
+// ------------------------------------------------ one-workgroup tree -------
+// Trees of up to kLdsTree slots are built by one workgroup with every point
+// in LDS (128 KB of records on a CU's 160 KB): the coordinates are read (and
+// rotated) straight into LDS, every level is split there, and the
+// permutation is written out.  Segments above 1,024 points are split by all
+// threads, each holding up to kLdsPer points; the lower levels reuse the
+// block and wave splits of the finisher.  The points of a segment of m
+// points sit at R[0..m) in ascending original index, and position p of the
+// segment belongs to thread p % 1024 in round p / 1024.
+constexpr int kLdsTree = 8192;
+constexpr int kLdsThreads = kFinishBlockWaves * 64;
+constexpr int kLdsPer = kLdsTree / kLdsThreads;   // 8 points per thread
+
+// The split of block_split (same axis, pivot and stable order) on a segment
+// of kFinish < m <= kLdsTree points.
+BT_DEV void big_split(float4* R, int m, BlockSplitLds& L, uint32_t (*whist)[256]) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float4 x[kLdsPer];
+  uint32_t mn[3] = {~0u, ~0u, ~0u}, mx[3] = {0u, 0u, 0u};
+#pragma unroll
+  for (int r = 0; r < kLdsPer; ++r) {
+    const int p = r * kLdsThreads + tid;
+    x[r] = p < m ? R[p] : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p < m) {
+      const uint32_t k3[3] = {float_key(x[r].x), float_key(x[r].y), float_key(x[r].z)};
+#pragma unroll
+      for (int a = 0; a < 3; ++a) { mn[a] = min(mn[a], k3[a]); mx[a] = max(mx[a], k3[a]); }
+    }
+  }
+  // extents of the segment
+  uint32_t e[6];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) { e[a] = wave_min_u32(mn[a]); e[3 + a] = wave_max_u32(mx[a]); }
+  if (lane == 0) {
+#pragma unroll
+    for (int a = 0; a < 6; ++a) L.ext[w][a] = e[a];
+  }
+  __syncthreads();
+  if (tid < 6) {
+    uint32_t v = L.ext[0][tid];
+    for (int i = 1; i < kFinishBlockWaves; ++i)
+      v = tid < 3 ? min(v, L.ext[i][tid]) : max(v, L.ext[i][tid]);
+    L.e6[tid] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < 6; ++a) e[a] = L.e6[a];
+  const int axis = axis_of(e);
+  // the keys are taken again from the records where needed (fewer live
+  // registers than keeping them)
+  auto key = [&](int r) -> uint32_t { return float_key(comp(x[r], axis)); };
+  const uint32_t kmin = e[axis], kmax = e[3 + axis];
+
+  // radix select of rank ceil(m/2)-1 on 8-bit digits from the highest byte
+  // in which kmin and kmax differ (as block_split)
+  uint32_t prefix = kmin;
+  uint32_t rank = (uint32_t)((m + 1) / 2 - 1);
+  const uint32_t diff = kmin ^ kmax;
+  if (diff) {
+    const int top = 31 - __clz((int)diff);
+    prefix = kmin & ~((2u << top) - 1u);
+    for (int shift = (top / 8) * 8; shift >= 0; shift -= 8) {
+      const int hi = shift + 8;
+      const uint32_t hmask = hi >= 32 ? 0u : (0xffffffffu << hi);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) whist[w][lane * 4 + j] = 0u;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int r = 0; r < kLdsPer; ++r) {
+        const int p = r * kLdsThreads + tid;
+        if (p < m && (key(r) & hmask) == (prefix & hmask))
+          atomicAdd(&whist[w][(key(r) >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 256) {
+        uint32_t t = 0;
+        for (int i = 0; i < kFinishBlockWaves; ++i) t += whist[i][tid];
+        L.hist[tid] = t;
+      }
+      __syncthreads();
+      if (w == 0) {
+        uint32_t h[4], tot = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { h[j] = L.hist[lane * 4 + j]; tot += h[j]; }
+        const uint32_t incl = wave_incl_scan_u32(tot);
+        uint32_t cum = incl - tot;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (h[j] && cum <= rank && rank < cum + h[j]) {
+            L.pick[0] = (uint32_t)(lane * 4 + j);
+            L.pick[1] = rank - cum;
+          }
+          cum += h[j];
+        }
+      }
+      __syncthreads();
+      prefix = (prefix & ~(255u << shift)) | (L.pick[0] << shift);
+      rank = L.pick[1];
+      __syncthreads();                       // pick is rewritten next pass
+    }
+  }
+  const uint32_t pivot = prefix;
+  const uint32_t need_eq = rank + 1u;
+
+  // stable partition, round by round in position order: left = keys below
+  // the pivot and the first need_eq keys equal to it; a right point's rank
+  // is its position minus the left points before it
+  const uint32_t half = (uint32_t)((m + 1) / 2);
+  uint32_t dest[kLdsPer];
+  uint32_t E = 0, Lrun = 0;
+#pragma unroll
+  for (int r = 0; r < kLdsPer; ++r) {
+    dest[r] = ~0u;
+    if (r * kLdsThreads >= m) continue;      // uniform over the workgroup
+    const int p = r * kLdsThreads + tid;
+    const bool valid = p < m;
+    const bool is_lt = valid && key(r) < pivot, is_eq = valid && key(r) == pivot;
+    uint32_t eq_tot = 0, left_tot = 0;
+    const uint32_t eq_before = E + block_excl_count(is_eq, L.cnt, &eq_tot);
+    const bool left = is_lt || (is_eq && eq_before < need_eq);
+    const uint32_t left_before = Lrun + block_excl_count(valid && left, L.cnt, &left_tot);
+    if (valid) dest[r] = left ? left_before : half + ((uint32_t)p - left_before);
+    E += eq_tot;
+    Lrun += left_tot;
+  }
+  // every thread read its points before the barriers above
+#pragma unroll
+  for (int r = 0; r < kLdsPer; ++r)
+    if (dest[r] < (uint32_t)m) R[dest[r]] = x[r];
+  __syncthreads();
+}
+
+// One workgroup builds the tree of n points in ncap = leaf * 2^L slots
+// (kFinish < ncap <= kLdsTree; ncap == n for a full tree): a segment of c
+// points gives its left child the ceil(c/2) smallest (c/2 in a full tree,
+// where c is always even), and the slots of a leaf past its points get -1.
+__global__ __launch_bounds__(kLdsThreads) void tree_lds_build(
+    const float* __restrict__ coords, int n, int ncap, int leaf, int rotate, float r00, float r01,
+    float r02, float r10, float r11, float r12, float r20, float r21, float r22,
+    int32_t* __restrict__ perm) {
+  __shared__ float4 srec[kLdsTree];
+  BT_LDS_POISON(srec);
+  __shared__ uint32_t shist[kFinishBlockWaves][256];
+  BT_LDS_POISON(shist);
+  __shared__ BlockSplitLds bsl;
+  BT_LDS_POISON(bsl);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < n; i += kLdsThreads) {
+    float x = coords[3 * (int64_t)i], y = coords[3 * (int64_t)i + 1], z = coords[3 * (int64_t)i + 2];
+    if (rotate) {
+      const float a0 = rot_row(r00, r01, r02, x, y, z);
+      const float a1 = rot_row(r10, r11, r12, x, y, z);
+      const float a2 = rot_row(r20, r21, r22, x, y, z);
+      x = a0; y = a1; z = a2;
+    }
+    srec[i] = make_float4(canon_zero(x), canon_zero(y), canon_zero(z), __int_as_float(i));
+  }
+  __syncthreads();
+  int lev = 0;
+  for (int slots = ncap; slots > leaf; slots >>= 1, ++lev) {
+    if (slots >= kBlockSplitMin) {           // uniform: every thread walks the segments
+      for (int sgi = 0; sgi < (1 << lev); ++sgi) {
+        int st, cnt;
+        padded_segment(n, lev, sgi, &st, &cnt);
+        if (cnt > kFinish) big_split(srec + st, cnt, bsl, shist);
+        else if (cnt >= 2) block_split(srec + st, cnt, bsl, shist);
+      }
+    } else {
+      for (int sgi = w; sgi < (1 << lev); sgi += kFinishBlockWaves) {
+        int st, cnt;
+        padded_segment(n, lev, sgi, &st, &cnt);
+        if (cnt >= 2) wave_split(srec + st, cnt, shist[w], lane);
+      }
+      __syncthreads();
+    }
+  }
+  for (int t = tid; t < ncap; t += kLdsThreads) {
+    const int j = t / leaf, i = t - j * leaf;
+    int st, cnt;
+    padded_segment(n, lev, j, &st, &cnt);
+    perm[t] = i < cnt ? __float_as_int(srec[st + i].w) : -1;
+  }
+}
+
+static bt_status tree_lds_launch(const float* coords, int64_t n, int64_t ncap, int leaf,
+                                 const float* R, int32_t* perm, hipStream_t st) {
+  if (ncap <= kFinish || ncap > kLdsTree || n > ncap || n < 1 || leaf < 1 || ncap % leaf != 0) {
+    set_error("tree: %lld points in %lld slots do not fit the one-workgroup builder",
+              (long long)n, (long long)ncap);
+    return BT_EINVAL;
+  }
+  float rr[9] = {1, 0, 0, 0, 1, 0, 0, 0, 1};
+  if (R) for (int i = 0; i < 9; ++i) rr[i] = R[i];
+  hipLaunchKernelGGL(tree_lds_build, dim3(1), dim3(kLdsThreads), 0, st, coords, (int)n,
+                     (int)ncap, leaf, R ? 1 : 0, rr[0], rr[1], rr[2], rr[3], rr[4], rr[5], rr[6],
+                     rr[7], rr[8], perm);
+  return launch_status("tree_lds_build");
+}
+
 // A padded tree that is a single leaf: the points in index order, then -1.
 __global__ __launch_bounds__(kThreads) void tree_single_leaf_padded(int64_t n, int64_t ncap,
                                                                     int32_t* __restrict__ perm) {
@@ -809,7 +1008,13 @@ static TreePlan plan_tree(int64_t n, int leaf) {
   return p;
 }
 
-size_t tree_workspace_size(int64_t n, int leaf) { return plan_tree(n, leaf).total; }
+// Trees of kFinish < n <= kLdsTree points are built in LDS and need no
+// workspace (the library still asks for its 256-byte minimum).
+static bool lds_tree(int64_t n, int leaf) { return n > kFinish && n <= kLdsTree && n > leaf; }
+
+size_t tree_workspace_size(int64_t n, int leaf) {
+  return lds_tree(n, leaf) ? 256 : plan_tree(n, leaf).total;
+}
 
 static TreeBufs carve_tree(const TreePlan& p, void* ws) {
   char* b = (char*)ws;
@@ -938,6 +1143,7 @@ bt_status tree_build_bufs(const TreePlan& p, const TreeBufs& b, const float* coo
 
 bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const float* R,
                             int32_t* perm, void* ws, hipStream_t st) {
+  if (lds_tree(n, leaf)) return tree_lds_launch(coords, n, n, leaf, R, perm, st);
   const TreePlan p = plan_tree(n, leaf);
   return tree_build_bufs(p, carve_tree(p, ws), coords, R, perm, st);
 }
@@ -949,10 +1155,12 @@ int64_t tree_padded_slots(int64_t n, int leaf) {
 }
 
 size_t tree_padded_workspace_size(int64_t n, int leaf) {
-  return tree_padded_slots(n, leaf) == leaf ? 256 : align256((size_t)n * 16);
+  const int64_t ncap = tree_padded_slots(n, leaf);
+  return (ncap == leaf || ncap > kFinish) ? 256 : align256((size_t)n * 16);
 }
 
-// Padded tree of n points: one leaf of any size, or up to kFinish slots.
+// Padded tree of n points: one leaf of any size, up to kFinish slots from a
+// record copy in the workspace, or up to kLdsTree slots in LDS.
 bt_status tree_build_padded_launch(const float* coords, int64_t n, int leaf, const float* R,
                                    int32_t* perm, void* ws, hipStream_t st) {
   const int64_t ncap = tree_padded_slots(n, leaf);
@@ -963,7 +1171,7 @@ bt_status tree_build_padded_launch(const float* coords, int64_t n, int leaf, con
                        perm);
     return launch_status("tree_single_leaf_padded");
   }
-  if (ncap > kFinish) return BT_EINVAL;
+  if (ncap > kFinish) return tree_lds_launch(coords, n, ncap, leaf, R, perm, st);
   float4* rec = (float4*)ws;
   const float* r = R;
   float rr[9] = {1, 0, 0, 0, 1, 0, 0, 0, 1};

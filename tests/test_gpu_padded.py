@@ -16,7 +16,10 @@ import torch  # noqa: E402
 
 
 @pytest.mark.parametrize("n,leaf", [(972, 32), (1000, 16), (513, 64), (5, 2), (3, 1), (1, 1),
-                                    (700, 700), (1024, 32), (129, 1), (4000, 4096)])
+                                    (700, 700), (1024, 32), (129, 1), (4000, 4096),
+                                    # one-workgroup LDS builder (1,025-8,192 slots)
+                                    (3586, 32), (5000, 64), (1025, 1), (6001, 3), (8192, 64),
+                                    (2049, 2048)])
 def test_padded_tree_bit_exact(n, leaf):
     dev = gpu()
     rng = np.random.default_rng(n * 7 + leaf)
@@ -134,3 +137,27 @@ def test_padded_pipeline_972():
     assert max_abs(out.cpu(), ref) <= 2e-2
     assert torch.equal(ot.cpu()[torch.from_numpy(pr < 0)],
                        torch.zeros(int((pr < 0).sum()), 4, 32, dtype=torch.bfloat16))
+
+
+@pytest.mark.parametrize("name,n,leaf,ball,H,d", [
+    ("shapenet_car", 3586, 32, 128, 8, 32),   # ShapeNet-Car's point count
+    ("cosmology", 5000, 64, 64, 4, 64),       # a cosmology-sized cloud
+])
+def test_padded_pipeline_pages_sizes(name, n, leaf, ball, H, d):
+    """The pages' uneven clouds end to end on the GPU: padded tree (bit for
+    bit), padded ball attention through the GPU permutation, gather into
+    tree order."""
+    dev = gpu()
+    rng = np.random.default_rng(n)
+    c = synth.deformed_sphere(rng, n)
+    q, k, v = (synth.normal_features(rng, n, H, d, "bf16") for _ in range(3))
+    say("padded pipeline", name, n, leaf, ball)
+    p = ops.bt_build_padded(torch.from_numpy(c).to(dev), leaf)
+    out = ops.ball_attn_padded(q.to(dev), k.to(dev), v.to(dev), p, ball)
+    ot = ops.bt_permute_padded(out, p, n, ops.BT_GATHER)
+    torch.cuda.synchronize()
+    pr = T.build_padded(c, leaf)
+    assert np.array_equal(p.cpu().numpy(), pr)
+    assert max_abs(out.cpu(), A.ball_attn_padded(q, k, v, pr, ball)) <= 2e-2
+    as_i16 = lambda t: t.cpu().view(torch.int16).numpy()
+    assert np.array_equal(as_i16(ot), P.gather_padded(as_i16(out), pr))

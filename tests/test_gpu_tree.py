@@ -10,13 +10,14 @@ from tests.helpers import gpu, say
 
 pytestmark = pytest.mark.gpu
 
-# The GPU builder's passes for nodes above 1,024 points faulted the GPU in
-# two runs (first failing case: tests/test_gpu_permute.py::
+# The GPU builder's multi-workgroup passes for nodes above 1,024 points
+# faulted the GPU in two runs (first failing case: tests/test_gpu_permute.py::
 # test_rotated_pair_pipeline_small) and the cause has not been found; the
-# library refuses such trees, and these cases stay skipped until it is.
+# library refuses trees above 8,192 points (the largest that one workgroup
+# builds in LDS), and these cases stay skipped until it is found.
 GLOBAL_PASSES_OFF = pytest.mark.skip(
-    reason="GPU tree passes above 1,024 points are switched off: they faulted the GPU twice "
-           "and the cause is not found (the same kernels are checked on the CPU by "
+    reason="GPU tree passes for trees above 8,192 points are switched off: they faulted the "
+           "GPU twice and the cause is not found (the same kernels are checked on the CPU by "
            "tests/test_kernel_cpu_sim.py)")
 
 
@@ -48,13 +49,26 @@ def _clouds():
     yield "golden8", tiny, 2
 
 
-def _big_clouds():
+def _lds_clouds():
+    """Trees of 2,048-8,192 points: one workgroup builds them in LDS."""
     rng = np.random.default_rng(22)
     yield "cube4k_leaf8", synth.uniform_cube(rng, 4096), 8
-    yield "sphere16k", synth.deformed_sphere(rng, 16384), 64
-    yield "mixture32k", synth.gaussian_mixture(rng, 32768, k=32), 128
     yield "lattice8k", rng.integers(0, 5, size=(8192, 3)).astype(np.float32), 16
     yield "leaf2048", synth.uniform_cube(rng, 8192), 2048
+    yield "sphere8k_leaf64", synth.deformed_sphere(rng, 8192), 64
+    yield "mixture8k_leaf1", synth.gaussian_mixture(rng, 8192, k=16), 1
+    yield "cube2k_leaf1024", synth.uniform_cube(rng, 2048), 1024
+    yield "identical4k", np.full((4096, 3), 0.25, np.float32), 4
+    z = rng.integers(-1, 2, size=(4096, 3)).astype(np.float32)
+    z[rng.random(z.shape) < 0.5] *= 0.0
+    z[rng.random(z.shape) < 0.5] *= -1.0
+    yield "signed_zeros4k", z, 2
+
+
+def _big_clouds():
+    rng = np.random.default_rng(22)
+    yield "sphere16k", synth.deformed_sphere(rng, 16384), 64
+    yield "mixture32k", synth.gaussian_mixture(rng, 32768, k=32), 128
 
 
 @pytest.mark.parametrize("name,coords,leaf", list(_clouds()), ids=[c[0] for c in _clouds()])
@@ -64,6 +78,29 @@ def test_bit_exact(name, coords, leaf):
     want = T.build(coords, leaf)
     assert np.array_equal(got, want), np.flatnonzero(got != want)[:10]
     assert checks.check_tree(coords, got, leaf)[0]
+
+
+@pytest.mark.parametrize("name,coords,leaf", list(_lds_clouds()),
+                         ids=[c[0] for c in _lds_clouds()])
+def test_bit_exact_lds_builder(name, coords, leaf):
+    say("bt_build (one-workgroup LDS builder)", name, coords.shape, leaf)
+    got = _gpu_tree(coords, leaf)
+    assert np.array_equal(got, T.build(coords, leaf)), name
+    assert checks.check_tree(coords, got, leaf)[0]
+
+
+def test_rotate_build_lds_builder():
+    """The rotated-pair recipe at 8,192 points, leaf 128, and a random
+    rotation of Gaussian points at leaf 4: the rotation's fp32 roundings
+    and the tree, bit for bit."""
+    w = synth.make("rotpair", n=8192, features=False)
+    say("bt_rotate_build rotpair recipe at 8192")
+    assert np.array_equal(_gpu_tree(w.coords, w.leaf, R=w.R), T.rotate_build(w.coords, w.leaf, w.R))
+    rng = np.random.default_rng(6)
+    c = rng.standard_normal((4096, 3)).astype(np.float32)
+    R = synth.random_rotation(rng)
+    say("bt_rotate_build random 4096")
+    assert np.array_equal(_gpu_tree(c, 4, R=R), T.rotate_build(c, 4, R))
 
 
 @GLOBAL_PASSES_OFF
@@ -82,9 +119,11 @@ def test_tiny_workload_bit_exact():
 
 def test_rejects_above_limit():
     dev = gpu()
-    c = torch.zeros((2048, 3), device=dev)
+    c = torch.zeros((16384, 3), device=dev)
     with pytest.raises(ops.BtError):
         ops.bt_build(c, 2)
+    with pytest.raises(ops.BtError):
+        ops.bt_build_padded(c[:8193], 2)
 
 
 @GLOBAL_PASSES_OFF

@@ -3,9 +3,10 @@
 tests/cpu_sim/ holds a host SIMT emulation of the HIP constructs the kernels
 use (see its header); the kernel .hip files are included unchanged, built
 with clang++ and AddressSanitizer, and run on small inputs.  The results are
-compared with the oracle: tree permutations bit for bit (including the
-global passes above 1,024 points, which the library switches off on the
-GPU), attention within the GPU tolerances.  An out-of-bounds access in a
+compared with the oracle: tree permutations bit for bit (the one-workgroup
+LDS builder of trees up to 8,192 points, and the multi-workgroup passes,
+which the library switches off on the GPU; BT_SIM_GLOBAL=1 makes the tree
+driver take those at any size), attention within the GPU tolerances.  An out-of-bounds access in a
 kernel aborts the run under AddressSanitizer.
 """
 import os
@@ -98,16 +99,21 @@ def sim_msan(tmp_path_factory):
     return {"dir": d, "tree": out}
 
 
-@pytest.mark.parametrize("padded", [False, True])
-def test_tree_kernels_no_uninitialised_reads(sim_msan, padded):
-    """4,096 points, leaf 128 (global levels and the finisher), rotated, and a
-    972-point padded tree: nothing uninitialised is read, and the
-    permutations are the oracle's."""
+@pytest.mark.parametrize("case", ["global_passes", "lds_builder", "padded", "padded_lds"])
+def test_tree_kernels_no_uninitialised_reads(sim_msan, case):
+    """4,096 points, leaf 128, rotated (by the multi-workgroup passes and the
+    finisher, or in LDS by one workgroup), and padded trees of 972 and 5,000
+    points: nothing uninitialised is read, and the permutations are the
+    oracle's."""
     d_ = sim_msan["dir"]
-    if padded:
-        c = synth.uniform_cube(np.random.default_rng(11), 972)
+    env = dict(os.environ, EMU_SHUFFLE="4")
+    if case == "global_passes":
+        env["BT_SIM_GLOBAL"] = "1"
+    if case.startswith("padded"):
+        n, leaf = (972, 32) if case == "padded" else (5000, 64)
+        c = synth.uniform_cube(np.random.default_rng(11), n)
         c.astype(np.float32).tofile(d_ / "coords.bin")
-        args, want = ["padded", "coords.bin", "972", "32", "out.bin"], T.build_padded(c, 32)
+        args, want = ["padded", "coords.bin", str(n), str(leaf), "out.bin"], T.build_padded(c, leaf)
     else:
         w = synth.make("rotpair", n=4096, features=False)
         w.coords.astype(np.float32).tofile(d_ / "coords.bin")
@@ -115,20 +121,24 @@ def test_tree_kernels_no_uninitialised_reads(sim_msan, padded):
         args = ["coords.bin", "4096", "128", "out.bin", "R.bin"]
         want = T.rotate_build(w.coords, 128, w.R)
     r = subprocess.run([sim_msan["tree"], *args], cwd=d_, capture_output=True, text=True,
-                       timeout=900, env=dict(os.environ, EMU_SHUFFLE="4"))
+                       timeout=900, env=env)
     assert r.returncode == 0 and "MemorySanitizer" not in r.stderr, r.stderr[-4000:]
     assert np.array_equal(np.fromfile(d_ / "out.bin", np.int32), want)
 
 
-def _tsan_env(shuffle):
+def _tsan_env(shuffle, glob=False):
     env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1 report_signal_unsafe=0")
     env["EMU_SHUFFLE"] = str(shuffle)
+    if glob:
+        env["BT_SIM_GLOBAL"] = "1"
     return env
 
 
-def test_tree_kernels_no_races(sim_tsan):
-    """4,096 points, leaf 128 (two global levels and the finisher), plain and
-    rotated: no data race, and the permutations are the oracle's."""
+@pytest.mark.parametrize("glob", [False, True], ids=["lds_builder", "global_passes"])
+def test_tree_kernels_no_races(sim_tsan, glob):
+    """4,096 points, leaf 128, plain and rotated, built in LDS by one
+    workgroup or by the multi-workgroup passes (two global levels, then the
+    finisher): no data race, and the permutations are the oracle's."""
     d_ = sim_tsan["dir"]
     w = synth.make("rotpair", n=4096, features=False)
     w.coords.astype(np.float32).tofile(d_ / "coords.bin")
@@ -136,7 +146,7 @@ def test_tree_kernels_no_races(sim_tsan):
     for rot in (False, True):
         args = [sim_tsan["tree"], "coords.bin", "4096", "128", "out.bin"] + (["R.bin"] if rot else [])
         r = subprocess.run(args, cwd=d_, capture_output=True, text=True, timeout=900,
-                           env=_tsan_env(3))
+                           env=_tsan_env(3, glob))
         assert r.returncode == 0 and "ThreadSanitizer" not in r.stderr, r.stderr[-4000:]
         want = T.rotate_build(w.coords, 128, w.R) if rot else T.build(w.coords, 128)
         assert np.array_equal(np.fromfile(d_ / "out.bin", np.int32), want)
@@ -170,14 +180,16 @@ SLOW = pytest.mark.skipif(os.environ.get("BT_SIM_SLOW") != "1",
                           reason="long emulation: set BT_SIM_SLOW=1")
 
 
-def _env(shuffle):
+def _env(shuffle, glob=False):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0")
     if shuffle is not None:
         env["EMU_SHUFFLE"] = str(shuffle)
+    if glob:
+        env["BT_SIM_GLOBAL"] = "1"
     return env
 
 
-def _tree(sim, coords, leaf, R=None, shuffle=None, timeout=600):
+def _tree(sim, coords, leaf, R=None, shuffle=None, timeout=600, glob=False):
     d = sim["dir"]
     c = d / "c.bin"
     np.ascontiguousarray(coords, np.float32).tofile(c)
@@ -185,15 +197,25 @@ def _tree(sim, coords, leaf, R=None, shuffle=None, timeout=600):
     if R is not None:
         np.asarray(R, np.float32).tofile(d / "R.bin")
         args.append(str(d / "R.bin"))
-    r = subprocess.run(args, capture_output=True, text=True, timeout=timeout, env=_env(shuffle))
+    r = subprocess.run(args, capture_output=True, text=True, timeout=timeout,
+                       env=_env(shuffle, glob))
     assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
     return np.fromfile(d / "p.bin", np.int32)
 
 
-@pytest.mark.parametrize("case", ["cube4k_leaf32", "lattice2k_leaf8", "signed_zeros2k_leaf2",
-                                  "mixture4k_leaf16", "leaf2048", "cube1536_leaf3",
-                                  "cube2000_leaf1000"])
-def test_tree_kernels_bit_exact(sim, case):
+_TREE_CASES = ["cube4k_leaf32", "lattice2k_leaf8", "signed_zeros2k_leaf2", "mixture4k_leaf16",
+               "leaf2048", "cube1536_leaf3", "cube2000_leaf1000", "lattice8k_leaf16"]
+# every case in LDS; the multi-workgroup passes on the cases that shape
+# their chunks (ragged nodes, chunks off the workgroup size, ties)
+_GLOBAL_CASES = ["cube4k_leaf32", "signed_zeros2k_leaf2", "leaf2048", "cube1536_leaf3",
+                 "cube2000_leaf1000"]
+
+
+@pytest.mark.parametrize("case,glob", [(c, False) for c in _TREE_CASES] +
+                         [(c, True) for c in _GLOBAL_CASES],
+                         ids=[c + "-lds_builder" for c in _TREE_CASES] +
+                             [c + "-global_passes" for c in _GLOBAL_CASES])
+def test_tree_kernels_bit_exact(sim, case, glob):
     rng = np.random.default_rng(31)
     if case == "cube4k_leaf32":
         c, leaf = synth.uniform_cube(rng, 4096), 32
@@ -210,14 +232,17 @@ def test_tree_kernels_bit_exact(sim, case):
         c, leaf = synth.uniform_cube(rng, 4096), 2048
     elif case == "cube1536_leaf3":        # a 1,536-point node: not a multiple of 1,024
         c, leaf = synth.uniform_cube(rng, 3 << 9), 3
-    else:                                 # chunks that are not a multiple of 256
+    elif case == "cube2000_leaf1000":     # chunks that are not a multiple of 256
         c, leaf = synth.uniform_cube(rng, 2000), 1000
-    assert np.array_equal(_tree(sim, c, leaf), T.build(c, leaf))
+    else:                                 # the largest tree built in LDS
+        c, leaf = rng.integers(0, 5, size=(8192, 3)).astype(np.float32), 16
+    assert np.array_equal(_tree(sim, c, leaf, glob=glob), T.build(c, leaf))
 
 
-def test_rotated_tree_kernels_bit_exact(sim):
+@pytest.mark.parametrize("glob", [False, True], ids=["lds_builder", "global_passes"])
+def test_rotated_tree_kernels_bit_exact(sim, glob):
     w = synth.make("rotpair", n=4096, features=False)
-    assert np.array_equal(_tree(sim, w.coords, 64, R=w.R),
+    assert np.array_equal(_tree(sim, w.coords, 64, R=w.R, glob=glob),
                           T.rotate_build(w.coords, 64, w.R))
 
 
@@ -227,7 +252,7 @@ def test_tree_kernels_shuffled_workgroups(sim, shuffle):
     not depend on the order (no workgroup reads what another one of the same
     launch writes; the histogram atomics commute)."""
     w = synth.make("rotpair", n=4096, features=False)
-    assert np.array_equal(_tree(sim, w.coords, 128, R=w.R, shuffle=shuffle),
+    assert np.array_equal(_tree(sim, w.coords, 128, R=w.R, shuffle=shuffle, glob=True),
                           T.rotate_build(w.coords, 128, w.R))
 
 
@@ -484,9 +509,11 @@ def _tree_padded(sim, coords, leaf, R=None):
 
 
 @pytest.mark.parametrize("n,leaf", [(972, 32), (1000, 16), (513, 64), (5, 2), (3, 1), (1, 1),
-                                    (2, 1), (700, 700), (1024, 32), (129, 1)])
+                                    (2, 1), (700, 700), (1024, 32), (129, 1),
+                                    (3586, 32), (5000, 64), (1025, 1), (6001, 3), (2049, 2048)])
 def test_padded_tree_kernels_bit_exact(sim, n, leaf):
-    """Uneven N: the padded tree (one workgroup in LDS), bit for bit."""
+    """Uneven N: the padded tree (one workgroup in LDS; above 1,024 slots the
+    coordinates are read straight into LDS), bit for bit."""
     rng = np.random.default_rng(n * 7 + leaf)
     c = synth.uniform_cube(rng, n)
     assert np.array_equal(_tree_padded(sim, c, leaf), T.build_padded(c, leaf))
