@@ -40,7 +40,15 @@
 //   padded      an uneven point count n: the tree has leaf * 2^L slots (the
 //               smallest that holds n); a node of m points gives its left
 //               child the ceil(m/2) smallest, and a leaf's unused slots hold
-//               -1.  Built by one workgroup in LDS (slots <= 1024).
+//               -1.  Built by one workgroup in LDS (slots <= 8192).
+//   one-workgroup tree (1,024 < points or slots <= 8,192): the coordinates
+//               go straight into LDS (128 KB of records) and one 16-wave
+//               workgroup splits every level there: segments above 1,024
+//               points with all threads (up to eight points each), smaller
+//               ones as in the finisher.  No workspace, no global passes.
+//               The library builds trees above 1,024 points only this way:
+//               the multi-workgroup passes above are switched off at its
+//               boundary (they stay in this file, exercised on the CPU).
 #include "common.h"
 
 // Test hook: the CPU emulation of these kernels under MemorySanitizer marks

@@ -4,7 +4,7 @@
 One step = one ball-attention pass (ball_attn) over one synthetic point cloud
 of the measured shape, gathering q/k/v through a permutation into ball order
 and scattering the result back to original order.  The GPU tree builder
-refuses trees above 1,024 points in this version, so the step's permutation
+refuses trees above 8,192 points in this version, so the step's permutation
 is a seeded random one (the config says so): the synthetic clouds are in
 random original order, so a tree order is a random gather pattern too, and
 the kernel's work does not depend on which permutation it is.  Inputs are
@@ -37,7 +37,8 @@ Prints ONE JSON line.  Besides the required fields it carries:
                 group compression) with the count of top-k rows whose
                 selection differs from the oracle's (near ties), padded
                 attention, the backward passes, and tree build + fp32 ball
-                attention at 1,024 points.
+                attention at 1,024 points, and trees of 8,192 points and of
+                the pages' 3,586- and 5,000-point clouds (padded).
 
 Other workloads (--workload bsa | cosmo | rotpair) print their own line and
 are not the default measurement.
@@ -315,8 +316,10 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
     """The other rows of the path, timed in the same run on their own
     workloads: permute (gather and scatter of 512-byte rows at the rotated-
     pair size), coarsen / refine, the BSA steps, padded ball attention of an
-    uneven N, the backward of ball attention, and tree build + fp32 ball
-    attention at the size the GPU tree builder takes (1,024 points)."""
+    uneven N, the backward of ball attention, tree build + fp32 ball
+    attention at 1,024 points, and the largest trees the GPU builder takes
+    (8,192 points or padded slots, built by one workgroup in LDS)."""
+    import numpy as np
     rows = {}
     # permute: N = 262,144 rows of H*d bf16 = 512 bytes; three source and
     # destination pairs (805 MB) rotate so that no call finds its rows in the
@@ -481,6 +484,33 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
     us_p = _event_us(torch, lambda: ops.bt_build_padded(c9, 32, perm=pt9, workspace=tws9), 200)
     rows["f3_tree_padded"] = {"workload": "N=972 uniform cube in 1,024 slots, leaf 32",
                               "build_us": us_p, "bound": "latency (one workgroup)"}
+    # the largest trees one workgroup builds in LDS: 8,192 sphere points
+    # (leaf 64), the rotated tree of the rotated-pair recipe at 8,192 points
+    # (leaf 128), and the pages' uneven clouds as padded trees
+    w8 = synth.make("sphere", n=8192, features=False)
+    c8 = torch.from_numpy(w8.coords).to(dev)
+    wr = synth.make("rotpair", n=8192, features=False)
+    cr = torch.from_numpy(wr.coords).to(dev)
+    ws8 = torch.empty(256, dtype=torch.uint8, device=dev)
+    p8 = torch.empty(8192, dtype=torch.int32, device=dev)
+    us_8 = _event_us(torch, lambda: ops.bt_build(c8, 64, perm=p8, workspace=ws8), 100)
+    us_r = _event_us(torch, lambda: ops.bt_rotate_build(cr, wr.leaf, wr.R, perm=p8, workspace=ws8),
+                     100)
+    rows["a1_a4_tree_lds_8192"] = {
+        "workload": "N=8192: deformed sphere, leaf 64; rotated-pair recipe rotated, leaf 128",
+        "build_us": us_8, "rotate_build_us": us_r, "points_per_s": 8192 / (us_8 * 1e-6),
+        "bound": "latency (one 16-wave workgroup, all points in LDS; 12 B/point read, "
+                 "4 B/point written)"}
+    padded = {}
+    for name, n_, leaf_ in (("shapenet_car_3586", 3586, 32), ("cosmology_5000", 5000, 64)):
+        cp = torch.from_numpy(synth.deformed_sphere(np.random.default_rng(n_), n_)).to(dev)
+        pp = torch.empty(ops.bt_padded_size(n_, leaf_), dtype=torch.int32, device=dev)
+        padded[name] = {"slots": pp.numel(), "leaf": leaf_,
+                        "build_us": _event_us(torch, lambda: ops.bt_build_padded(
+                            cp, leaf_, perm=pp, workspace=ws8), 100)}
+    rows["f3_tree_padded_pages_sizes"] = {"workload": "deformed-sphere clouds of the pages' "
+                                          "uneven point counts", **padded,
+                                          "bound": "latency (one workgroup)"}
     return rows
 
 
