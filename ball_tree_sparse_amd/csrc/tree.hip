@@ -747,9 +747,33 @@ constexpr int kLdsTree = 8192;
 constexpr int kLdsThreads = kFinishBlockWaves * 64;
 constexpr int kLdsPer = kLdsTree / kLdsThreads;   // 8 points per thread
 
+// Counts of a big split, one per (round, wave) in position order, and the
+// pivot decision of its radix passes.
+struct BigSplitLds {
+  uint32_t rc[kLdsPer * kFinishBlockWaves];
+  uint32_t pick[3];
+};
+
+// Turns the counts rc[r * waves + w] (written, then a barrier) into their
+// exclusive prefix sums in position order.  Wave 0 scans; every thread
+// calls it (one workgroup barrier at the end).
+BT_DEV void round_wave_prefix(uint32_t* rc) {
+  constexpr int kE = kLdsPer * kFinishBlockWaves;   // 128 entries, two per lane
+  static_assert(kE == 128, "two entries per lane of wave 0");
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const uint32_t a = rc[2 * lane], b = rc[2 * lane + 1];
+    const uint32_t ex = wave_incl_scan_u32(a + b) - (a + b);
+    rc[2 * lane] = ex;
+    rc[2 * lane + 1] = ex + a;
+  }
+  __syncthreads();
+}
+
 // The split of block_split (same axis, pivot and stable order) on a segment
 // of kFinish < m <= kLdsTree points.
-BT_DEV void big_split(float4* R, int m, BlockSplitLds& L, uint32_t (*whist)[256]) {
+BT_DEV void big_split(float4* R, int m, BlockSplitLds& L, BigSplitLds& B,
+                      uint32_t (*whist)[256]) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float4 x[kLdsPer];
   uint32_t mn[3] = {~0u, ~0u, ~0u}, mx[3] = {0u, 0u, 0u};
@@ -788,7 +812,9 @@ BT_DEV void big_split(float4* R, int m, BlockSplitLds& L, uint32_t (*whist)[256]
   const uint32_t kmin = e[axis], kmax = e[3 + axis];
 
   // radix select of rank ceil(m/2)-1 on 8-bit digits from the highest byte
-  // in which kmin and kmax differ (as block_split)
+  // in which kmin and kmax differ (as block_split).  When the bin holding
+  // that rank has a single key, that key is the pivot (it is the only key
+  // equal to itself, so rank 0 among equal keys) and the passes stop.
   uint32_t prefix = kmin;
   uint32_t rank = (uint32_t)((m + 1) / 2 - 1);
   const uint32_t diff = kmin ^ kmax;
@@ -823,41 +849,78 @@ BT_DEV void big_split(float4* R, int m, BlockSplitLds& L, uint32_t (*whist)[256]
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if (h[j] && cum <= rank && rank < cum + h[j]) {
-            L.pick[0] = (uint32_t)(lane * 4 + j);
-            L.pick[1] = rank - cum;
+            B.pick[0] = (uint32_t)(lane * 4 + j);
+            B.pick[1] = rank - cum;
+            B.pick[2] = h[j];
           }
           cum += h[j];
         }
       }
       __syncthreads();
-      prefix = (prefix & ~(255u << shift)) | (L.pick[0] << shift);
-      rank = L.pick[1];
-      __syncthreads();                       // pick is rewritten next pass
+      prefix = (prefix & ~(255u << shift)) | (B.pick[0] << shift);
+      rank = B.pick[1];
+      const bool single = B.pick[2] == 1u && shift > 0;
+      __syncthreads();                       // pick is rewritten below or next pass
+      if (single) {                          // uniform: one key matches prefix above shift
+        const uint32_t pmask = 0xffffffffu << shift;
+#pragma unroll
+        for (int r = 0; r < kLdsPer; ++r) {
+          const int p = r * kLdsThreads + tid;
+          if (p < m && (key(r) & pmask) == prefix) B.pick[0] = key(r);
+        }
+        __syncthreads();
+        prefix = B.pick[0];
+        rank = 0u;
+        __syncthreads();
+        break;
+      }
     }
   }
   const uint32_t pivot = prefix;
   const uint32_t need_eq = rank + 1u;
 
-  // stable partition, round by round in position order: left = keys below
-  // the pivot and the first need_eq keys equal to it; a right point's rank
-  // is its position minus the left points before it
-  const uint32_t half = (uint32_t)((m + 1) / 2);
-  uint32_t dest[kLdsPer];
-  uint32_t E = 0, Lrun = 0;
+  // stable partition in position order: left = keys below the pivot and the
+  // first need_eq keys equal to it; a right point's rank is its position
+  // minus the left points before it.  The ranks come from one exclusive scan
+  // of per-(round, wave) counts for the pivot-equal keys, then one for the
+  // left points (rounds at or past m count zero).
+  uint32_t in_w[kLdsPer];
 #pragma unroll
   for (int r = 0; r < kLdsPer; ++r) {
-    dest[r] = ~0u;
-    if (r * kLdsThreads >= m) continue;      // uniform over the workgroup
     const int p = r * kLdsThreads + tid;
-    const bool valid = p < m;
-    const bool is_lt = valid && key(r) < pivot, is_eq = valid && key(r) == pivot;
-    uint32_t eq_tot = 0, left_tot = 0;
-    const uint32_t eq_before = E + block_excl_count(is_eq, L.cnt, &eq_tot);
-    const bool left = is_lt || (is_eq && eq_before < need_eq);
-    const uint32_t left_before = Lrun + block_excl_count(valid && left, L.cnt, &left_tot);
-    if (valid) dest[r] = left ? left_before : half + ((uint32_t)p - left_before);
-    E += eq_tot;
-    Lrun += left_tot;
+    const uint64_t b = __ballot(p < m && key(r) == pivot);
+    in_w[r] = mbcnt64(b);
+    if (lane == 0) B.rc[r * kFinishBlockWaves + w] = (uint32_t)__popcll(b);
+  }
+  __syncthreads();
+  round_wave_prefix(B.rc);
+  uint32_t left_bits = 0;
+#pragma unroll
+  for (int r = 0; r < kLdsPer; ++r) {
+    const int p = r * kLdsThreads + tid;
+    const uint32_t kr = key(r);
+    const bool left = p < m && (kr < pivot ||
+                                (kr == pivot && B.rc[r * kFinishBlockWaves + w] + in_w[r] < need_eq));
+    left_bits |= (uint32_t)left << r;
+  }
+  __syncthreads();                           // every thread read the pivot-equal ranks
+#pragma unroll
+  for (int r = 0; r < kLdsPer; ++r) {
+    const uint64_t b = __ballot((left_bits >> r) & 1u);
+    in_w[r] = mbcnt64(b);
+    if (lane == 0) B.rc[r * kFinishBlockWaves + w] = (uint32_t)__popcll(b);
+  }
+  __syncthreads();
+  round_wave_prefix(B.rc);
+  const uint32_t half = (uint32_t)((m + 1) / 2);
+  uint32_t dest[kLdsPer];
+#pragma unroll
+  for (int r = 0; r < kLdsPer; ++r) {
+    const int p = r * kLdsThreads + tid;
+    const uint32_t left_before = B.rc[r * kFinishBlockWaves + w] + in_w[r];
+    dest[r] = p >= m ? ~0u
+                     : ((left_bits >> r) & 1u) ? left_before
+                                               : half + ((uint32_t)p - left_before);
   }
   // every thread read its points before the barriers above
 #pragma unroll
@@ -880,6 +943,8 @@ __global__ __launch_bounds__(kLdsThreads) void tree_lds_build(
   BT_LDS_POISON(shist);
   __shared__ BlockSplitLds bsl;
   BT_LDS_POISON(bsl);
+  __shared__ BigSplitLds bgl;
+  BT_LDS_POISON(bgl);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int i = tid; i < n; i += kLdsThreads) {
     float x = coords[3 * (int64_t)i], y = coords[3 * (int64_t)i + 1], z = coords[3 * (int64_t)i + 2];
@@ -894,11 +959,15 @@ __global__ __launch_bounds__(kLdsThreads) void tree_lds_build(
   __syncthreads();
   int lev = 0;
   for (int slots = ncap; slots > leaf; slots >>= 1, ++lev) {
-    if (slots >= kBlockSplitMin) {           // uniform: every thread walks the segments
+    // segments above 1,024 points, and up to three of 1,024, are split by
+    // the whole workgroup one after another; otherwise the waves take the
+    // segments in turn (four or more 1,024-point segments finish sooner as
+    // parallel wave splits than as block splits in sequence)
+    if (slots > kFinish || (slots == kFinish && (1 << lev) < 4)) {   // uniform
       for (int sgi = 0; sgi < (1 << lev); ++sgi) {
         int st, cnt;
         padded_segment(n, lev, sgi, &st, &cnt);
-        if (cnt > kFinish) big_split(srec + st, cnt, bsl, shist);
+        if (cnt > kFinish) big_split(srec + st, cnt, bsl, bgl, shist);
         else if (cnt >= 2) block_split(srec + st, cnt, bsl, shist);
       }
     } else {
