@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 
 import torch  # noqa: E402
 
-TOL = {"bf16": 2e-2, "f32": 2e-5}
+TOL = {"bf16": 2e-2, "f32": 1e-5}   # fp32: measured max abs errors 0.4-1.2e-6
 
 
 @pytest.mark.parametrize("n,H,d,ball,dtype", [
