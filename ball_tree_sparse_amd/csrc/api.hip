@@ -70,9 +70,9 @@ bt_status bsa_bwd_launch(const void* q, const void* k, const void* v, const int3
 
 static bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
-// Largest tree (points, or slots of a padded tree) that the builders accept:
-// trees that one workgroup builds in LDS (see build_common).
-constexpr int64_t kTreeMaxGpu = 8192;
+// Largest padded tree (slots) that bt_build_padded accepts: one workgroup
+// builds it in LDS.
+constexpr int64_t kTreeMaxPadded = 8192;
 
 static bool valid_tree_shape(int64_t N, int32_t leaf) {
   return N >= 1 && leaf >= 1 && N < ((int64_t)1 << 31) && N % leaf == 0 && is_pow2(N / leaf);
@@ -117,13 +117,6 @@ static bt_status build_common(const float* coords, int64_t N, int32_t leaf, cons
   BT_REQUIRE(N < ((int64_t)1 << 31), "N must be below 2^31");
   BT_REQUIRE(N % leaf == 0 && is_pow2(N / leaf), "N must be leaf * 2^L (N=%lld, leaf=%d)",
              (long long)N, leaf);
-  // The multi-workgroup passes that split nodes above 1,024 points faulted
-  // the GPU in testing and the cause has not been found, so they are
-  // switched off: only trees that one workgroup builds in LDS are accepted.
-  BT_REQUIRE(N <= kTreeMaxGpu || N == leaf,
-             "bt_build: trees above %lld points are switched off in this version "
-             "(the multi-workgroup passes faulted the GPU; cause not found); N=%lld",
-             (long long)kTreeMaxGpu, (long long)N);
   BT_REQUIRE(ws != nullptr, "workspace must be non-null");
   BT_REQUIRE(((uintptr_t)ws & 255) == 0, "workspace must be 256-byte aligned");
   const size_t need = tree_workspace_size(N, leaf);
@@ -280,10 +273,10 @@ bt_status bt_build_padded(const float* coords, int64_t N, int32_t leaf, const fl
   const int64_t S = bt_padded_size(N, leaf);
   BT_REQUIRE(S > 0, "need N >= 1, leaf >= 1 and fewer than 2^31 slots (N=%lld, leaf=%d)",
              (long long)N, leaf);
-  BT_REQUIRE(S <= kTreeMaxGpu || S == leaf,
-             "bt_build_padded: trees above %lld slots are switched off in this version "
-             "(the multi-workgroup passes faulted the GPU; cause not found); slots=%lld",
-             (long long)kTreeMaxGpu, (long long)S);
+  BT_REQUIRE(S <= kTreeMaxPadded || S == leaf,
+             "bt_build_padded: padded trees above %lld slots are not supported in this "
+             "version (one workgroup builds them in LDS); slots=%lld",
+             (long long)kTreeMaxPadded, (long long)S);
   if (R_host) {
     for (int i = 0; i < 9; ++i)
       BT_REQUIRE(R_host[i] == R_host[i] && R_host[i] - R_host[i] == 0.0f,

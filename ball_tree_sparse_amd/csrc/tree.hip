@@ -752,20 +752,23 @@ constexpr int kLdsPer = kLdsTree / kLdsThreads;   // 8 points per thread
 struct BigSplitLds {
   uint32_t rc[kLdsPer * kFinishBlockWaves];
   uint32_t pick[3];
+  uint32_t total;                  // sum of rc, written by round_wave_prefix
 };
 
 // Turns the counts rc[r * waves + w] (written, then a barrier) into their
 // exclusive prefix sums in position order.  Wave 0 scans; every thread
 // calls it (one workgroup barrier at the end).
-BT_DEV void round_wave_prefix(uint32_t* rc) {
+BT_DEV void round_wave_prefix(uint32_t* rc, uint32_t* total) {
   constexpr int kE = kLdsPer * kFinishBlockWaves;   // 128 entries, two per lane
   static_assert(kE == 128, "two entries per lane of wave 0");
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const uint32_t a = rc[2 * lane], b = rc[2 * lane + 1];
-    const uint32_t ex = wave_incl_scan_u32(a + b) - (a + b);
+    const uint32_t incl = wave_incl_scan_u32(a + b);
+    const uint32_t ex = incl - (a + b);
     rc[2 * lane] = ex;
     rc[2 * lane + 1] = ex + a;
+    if (lane == 63) *total = incl;
   }
   __syncthreads();
 }
@@ -893,7 +896,7 @@ BT_DEV void big_split(float4* R, int m, BlockSplitLds& L, BigSplitLds& B,
     if (lane == 0) B.rc[r * kFinishBlockWaves + w] = (uint32_t)__popcll(b);
   }
   __syncthreads();
-  round_wave_prefix(B.rc);
+  round_wave_prefix(B.rc, &B.total);
   uint32_t left_bits = 0;
 #pragma unroll
   for (int r = 0; r < kLdsPer; ++r) {
@@ -911,7 +914,7 @@ BT_DEV void big_split(float4* R, int m, BlockSplitLds& L, BigSplitLds& B,
     if (lane == 0) B.rc[r * kFinishBlockWaves + w] = (uint32_t)__popcll(b);
   }
   __syncthreads();
-  round_wave_prefix(B.rc);
+  round_wave_prefix(B.rc, &B.total);
   const uint32_t half = (uint32_t)((m + 1) / 2);
   uint32_t dest[kLdsPer];
 #pragma unroll
@@ -933,30 +936,12 @@ BT_DEV void big_split(float4* R, int m, BlockSplitLds& L, BigSplitLds& B,
 // (kFinish < ncap <= kLdsTree; ncap == n for a full tree): a segment of c
 // points gives its left child the ceil(c/2) smallest (c/2 in a full tree,
 // where c is always even), and the slots of a leaf past its points get -1.
-__global__ __launch_bounds__(kLdsThreads) void tree_lds_build(
-    const float* __restrict__ coords, int n, int ncap, int leaf, int rotate, float r00, float r01,
-    float r02, float r10, float r11, float r12, float r20, float r21, float r22,
-    int32_t* __restrict__ perm) {
-  __shared__ float4 srec[kLdsTree];
-  BT_LDS_POISON(srec);
-  __shared__ uint32_t shist[kFinishBlockWaves][256];
-  BT_LDS_POISON(shist);
-  __shared__ BlockSplitLds bsl;
-  BT_LDS_POISON(bsl);
-  __shared__ BigSplitLds bgl;
-  BT_LDS_POISON(bgl);
+// Splits every level of the n points at srec[0..n) (a tree of ncap slots,
+// kFinish < ncap <= kLdsTree) in LDS and writes the ncap permutation entries
+// to perm.  Every thread of the workgroup calls it.
+BT_DEV void lds_levels(float4* srec, int n, int ncap, int leaf, BlockSplitLds& bsl,
+                       BigSplitLds& bgl, uint32_t (*shist)[256], int32_t* __restrict__ perm) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int i = tid; i < n; i += kLdsThreads) {
-    float x = coords[3 * (int64_t)i], y = coords[3 * (int64_t)i + 1], z = coords[3 * (int64_t)i + 2];
-    if (rotate) {
-      const float a0 = rot_row(r00, r01, r02, x, y, z);
-      const float a1 = rot_row(r10, r11, r12, x, y, z);
-      const float a2 = rot_row(r20, r21, r22, x, y, z);
-      x = a0; y = a1; z = a2;
-    }
-    srec[i] = make_float4(canon_zero(x), canon_zero(y), canon_zero(z), __int_as_float(i));
-  }
-  __syncthreads();
   int lev = 0;
   for (int slots = ncap; slots > leaf; slots >>= 1, ++lev) {
     // segments above 1,024 points, and up to three of 1,024, are split by
@@ -984,6 +969,234 @@ __global__ __launch_bounds__(kLdsThreads) void tree_lds_build(
     int st, cnt;
     padded_segment(n, lev, j, &st, &cnt);
     perm[t] = i < cnt ? __float_as_int(srec[st + i].w) : -1;
+  }
+}
+
+__global__ __launch_bounds__(kLdsThreads) void tree_lds_build(
+    const float* __restrict__ coords, int n, int ncap, int leaf, int rotate, float r00, float r01,
+    float r02, float r10, float r11, float r12, float r20, float r21, float r22,
+    int32_t* __restrict__ perm) {
+  __shared__ float4 srec[kLdsTree];
+  BT_LDS_POISON(srec);
+  __shared__ uint32_t shist[kFinishBlockWaves][256];
+  BT_LDS_POISON(shist);
+  __shared__ BlockSplitLds bsl;
+  BT_LDS_POISON(bsl);
+  __shared__ BigSplitLds bgl;
+  BT_LDS_POISON(bgl);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < n; i += kLdsThreads) {
+    float x = coords[3 * (int64_t)i], y = coords[3 * (int64_t)i + 1], z = coords[3 * (int64_t)i + 2];
+    if (rotate) {
+      const float a0 = rot_row(r00, r01, r02, x, y, z);
+      const float a1 = rot_row(r10, r11, r12, x, y, z);
+      const float a2 = rot_row(r20, r21, r22, x, y, z);
+      x = a0; y = a1; z = a2;
+    }
+    srec[i] = make_float4(canon_zero(x), canon_zero(y), canon_zero(z), __int_as_float(i));
+  }
+  __syncthreads();
+  lds_levels(srec, n, ncap, leaf, bsl, bgl, shist, perm);
+}
+
+// One workgroup per node of nf points (leaf < nf <= kLdsTree) of a full tree
+// whose records rec are in node order: the node is loaded into LDS, split
+// down to its leaves there, and its permutation entries written.
+__global__ __launch_bounds__(kLdsThreads) void tree_lds_nodes(const float4* __restrict__ rec,
+                                                              int nf, int leaf,
+                                                              int32_t* __restrict__ perm) {
+  __shared__ float4 srec[kLdsTree];
+  BT_LDS_POISON(srec);
+  __shared__ uint32_t shist[kFinishBlockWaves][256];
+  BT_LDS_POISON(shist);
+  __shared__ BlockSplitLds bsl;
+  BT_LDS_POISON(bsl);
+  __shared__ BigSplitLds bgl;
+  BT_LDS_POISON(bgl);
+  const int64_t base = (int64_t)blockIdx.x * nf;
+  for (int i = threadIdx.x; i < nf; i += kLdsThreads) srec[i] = rec[base + i];
+  __syncthreads();
+  lds_levels(srec, nf, nf, leaf, bsl, bgl, shist, perm + base);
+}
+
+// One workgroup per node of m > kLdsTree points (m even): the split of
+// big_split with the node streamed from global memory in chunks of
+// kLdsThreads * kLdsPer positions (position p of a chunk belongs to thread
+// p % kLdsThreads in round p / kLdsThreads), the children written to out at
+// the node's place.  No workgroup reads what another one writes.
+__global__ __launch_bounds__(kLdsThreads) void tree_stream_split(const float4* __restrict__ in,
+                                                                 float4* __restrict__ out,
+                                                                 int64_t m) {
+  __shared__ uint32_t shist[kFinishBlockWaves][256];
+  BT_LDS_POISON(shist);
+  __shared__ BlockSplitLds L;
+  BT_LDS_POISON(L);
+  __shared__ BigSplitLds B;
+  BT_LDS_POISON(B);
+  constexpr int64_t CH = (int64_t)kLdsThreads * kLdsPer;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t base = (int64_t)blockIdx.x * m;
+  const float4* R = in + base;
+  float4* O = out + base;
+  const int64_t nch = (m + CH - 1) / CH;
+
+  // extents of the node
+  uint32_t mn[3] = {~0u, ~0u, ~0u}, mx[3] = {0u, 0u, 0u};
+  for (int64_t c = 0; c < nch; ++c) {
+#pragma unroll
+    for (int r = 0; r < kLdsPer; ++r) {
+      const int64_t p = c * CH + r * kLdsThreads + tid;
+      if (p < m) {
+        const float4 x = R[p];
+        const uint32_t k3[3] = {float_key(x.x), float_key(x.y), float_key(x.z)};
+#pragma unroll
+        for (int a = 0; a < 3; ++a) { mn[a] = min(mn[a], k3[a]); mx[a] = max(mx[a], k3[a]); }
+      }
+    }
+  }
+  uint32_t e[6];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) { e[a] = wave_min_u32(mn[a]); e[3 + a] = wave_max_u32(mx[a]); }
+  if (lane == 0) {
+#pragma unroll
+    for (int a = 0; a < 6; ++a) L.ext[w][a] = e[a];
+  }
+  __syncthreads();
+  if (tid < 6) {
+    uint32_t v = L.ext[0][tid];
+    for (int i = 1; i < kFinishBlockWaves; ++i)
+      v = tid < 3 ? min(v, L.ext[i][tid]) : max(v, L.ext[i][tid]);
+    L.e6[tid] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < 6; ++a) e[a] = L.e6[a];
+  const int axis = axis_of(e);
+  const uint32_t kmin = e[axis], kmax = e[3 + axis];
+
+  // radix select of rank m/2-1 (as big_split, the keys read again per pass)
+  uint32_t prefix = kmin;
+  uint32_t rank = (uint32_t)(m / 2 - 1);
+  const uint32_t diff = kmin ^ kmax;
+  if (diff) {
+    const int top = 31 - __clz((int)diff);
+    prefix = kmin & ~((2u << top) - 1u);
+    for (int shift = (top / 8) * 8; shift >= 0; shift -= 8) {
+      const int hi = shift + 8;
+      const uint32_t hmask = hi >= 32 ? 0u : (0xffffffffu << hi);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) shist[w][lane * 4 + j] = 0u;
+      __builtin_amdgcn_wave_barrier();
+      for (int64_t c = 0; c < nch; ++c) {
+#pragma unroll
+        for (int r = 0; r < kLdsPer; ++r) {
+          const int64_t p = c * CH + r * kLdsThreads + tid;
+          if (p < m) {
+            const uint32_t key = float_key(comp(R[p], axis));
+            if ((key & hmask) == (prefix & hmask)) atomicAdd(&shist[w][(key >> shift) & 255u], 1u);
+          }
+        }
+      }
+      __syncthreads();
+      if (tid < 256) {
+        uint32_t t = 0;
+        for (int i = 0; i < kFinishBlockWaves; ++i) t += shist[i][tid];
+        L.hist[tid] = t;
+      }
+      __syncthreads();
+      if (w == 0) {
+        uint32_t h[4], tot = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { h[j] = L.hist[lane * 4 + j]; tot += h[j]; }
+        const uint32_t incl = wave_incl_scan_u32(tot);
+        uint32_t cum = incl - tot;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (h[j] && cum <= rank && rank < cum + h[j]) {
+            B.pick[0] = (uint32_t)(lane * 4 + j);
+            B.pick[1] = rank - cum;
+            B.pick[2] = h[j];
+          }
+          cum += h[j];
+        }
+      }
+      __syncthreads();
+      prefix = (prefix & ~(255u << shift)) | (B.pick[0] << shift);
+      rank = B.pick[1];
+      const bool single = B.pick[2] == 1u && shift > 0;
+      __syncthreads();
+      if (single) {                          // uniform: one key matches prefix above shift
+        const uint32_t pmask = 0xffffffffu << shift;
+        for (int64_t c = 0; c < nch; ++c) {
+#pragma unroll
+          for (int r = 0; r < kLdsPer; ++r) {
+            const int64_t p = c * CH + r * kLdsThreads + tid;
+            if (p < m) {
+              const uint32_t key = float_key(comp(R[p], axis));
+              if ((key & pmask) == prefix) B.pick[0] = key;
+            }
+          }
+        }
+        __syncthreads();
+        prefix = B.pick[0];
+        rank = 0u;
+        __syncthreads();
+        break;
+      }
+    }
+  }
+  const uint32_t pivot = prefix;
+  const uint32_t need_eq = rank + 1u;
+
+  // stable partition, chunk by chunk in position order (as big_split, with
+  // the pivot-equal and left counts of the earlier chunks carried along)
+  const uint64_t half = (uint64_t)(m / 2);
+  uint32_t E = 0, Lrun = 0;
+  for (int64_t c = 0; c < nch; ++c) {
+    float4 x[kLdsPer];
+    uint32_t in_w[kLdsPer];
+#pragma unroll
+    for (int r = 0; r < kLdsPer; ++r) {
+      const int64_t p = c * CH + r * kLdsThreads + tid;
+      x[r] = p < m ? R[p] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const uint64_t b = __ballot(p < m && float_key(comp(x[r], axis)) == pivot);
+      in_w[r] = mbcnt64(b);
+      if (lane == 0) B.rc[r * kFinishBlockWaves + w] = (uint32_t)__popcll(b);
+    }
+    __syncthreads();
+    round_wave_prefix(B.rc, &B.total);
+    uint32_t left_bits = 0;
+#pragma unroll
+    for (int r = 0; r < kLdsPer; ++r) {
+      const int64_t p = c * CH + r * kLdsThreads + tid;
+      const uint32_t kr = float_key(comp(x[r], axis));
+      const bool left =
+          p < m && (kr < pivot ||
+                    (kr == pivot && E + B.rc[r * kFinishBlockWaves + w] + in_w[r] < need_eq));
+      left_bits |= (uint32_t)left << r;
+    }
+    E += B.total;
+    __syncthreads();                         // every thread read the counts and the total
+#pragma unroll
+    for (int r = 0; r < kLdsPer; ++r) {
+      const uint64_t b = __ballot((left_bits >> r) & 1u);
+      in_w[r] = mbcnt64(b);
+      if (lane == 0) B.rc[r * kFinishBlockWaves + w] = (uint32_t)__popcll(b);
+    }
+    __syncthreads();
+    round_wave_prefix(B.rc, &B.total);
+#pragma unroll
+    for (int r = 0; r < kLdsPer; ++r) {
+      const int64_t p = c * CH + r * kLdsThreads + tid;
+      if (p < m) {
+        const uint64_t left_before = (uint64_t)Lrun + B.rc[r * kFinishBlockWaves + w] + in_w[r];
+        const uint64_t dest = ((left_bits >> r) & 1u) ? left_before
+                                                      : half + ((uint64_t)p - left_before);
+        if (dest < (uint64_t)m) O[dest] = x[r];
+      }
+    }
+    Lrun += B.total;
+    __syncthreads();                         // the counts are rewritten by the next chunk
   }
 }
 
@@ -1089,8 +1302,63 @@ static TreePlan plan_tree(int64_t n, int leaf) {
 // workspace (the library still asks for its 256-byte minimum).
 static bool lds_tree(int64_t n, int leaf) { return n > kFinish && n <= kLdsTree && n > leaf; }
 
+// Trees above kLdsTree points: nodes are split by one workgroup each,
+// streamed through two record arrays, down to nodes of <= kLdsTree points,
+// which one workgroup each finishes in LDS.
+static bool stream_tree(int64_t n, int leaf) { return n > kLdsTree && n > leaf; }
+
 size_t tree_workspace_size(int64_t n, int leaf) {
-  return lds_tree(n, leaf) ? 256 : plan_tree(n, leaf).total;
+  if (lds_tree(n, leaf)) return 256;
+  if (stream_tree(n, leaf)) return 2 * align256((size_t)n * 16);
+  return plan_tree(n, leaf).total;
+}
+
+// The streamed build of n = leaf * 2^L > kLdsTree points (n > leaf) with the
+// records in ws (two arrays of n records).  Every launch is checked on the
+// host against the arrays it indexes: nodes * nsize == n.
+static bt_status tree_stream_launch(const float* coords, int64_t n, int leaf, const float* R,
+                                    int32_t* perm, void* ws, hipStream_t st) {
+  float4* rec[2] = {(float4*)ws, (float4*)((char*)ws + align256((size_t)n * 16))};
+  float rr[9] = {1, 0, 0, 0, 1, 0, 0, 0, 1};
+  if (R) for (int i = 0; i < 9; ++i) rr[i] = R[i];
+  {
+    int64_t g = (n + kThreads - 1) / kThreads;
+    if (g > 4096) g = 4096;
+    hipLaunchKernelGGL(tree_ingest, dim3((int)g), dim3(kThreads), 0, st, coords, n, R ? 1 : 0,
+                       rr[0], rr[1], rr[2], rr[3], rr[4], rr[5], rr[6], rr[7], rr[8], rec[0],
+                       (uint32_t*)nullptr, 0);
+    bt_status s = launch_status("tree_ingest");
+    if (s != BT_OK) return s;
+  }
+  int64_t nsize = n;
+  int cur = 0;
+  while (nsize > leaf && nsize > kLdsTree) {
+    const int64_t nodes = n / nsize;
+    if (nodes * nsize != n || (nsize & 1) || nodes > INT32_MAX) {
+      set_error("tree: nodes of %lld points do not tile %lld", (long long)nsize, (long long)n);
+      return BT_EINVAL;
+    }
+    hipLaunchKernelGGL(tree_stream_split, dim3((unsigned)nodes), dim3(kLdsThreads), 0, st,
+                       rec[cur], rec[cur ^ 1], nsize);
+    bt_status s = launch_status("tree_stream_split");
+    if (s != BT_OK) return s;
+    cur ^= 1;
+    nsize >>= 1;
+  }
+  const int64_t nodes = n / nsize;
+  if (nodes * nsize != n || nodes > INT32_MAX) {
+    set_error("tree: nodes of %lld points do not tile %lld", (long long)nsize, (long long)n);
+    return BT_EINVAL;
+  }
+  if (nsize == leaf) {
+    int64_t g = (n + kThreads - 1) / kThreads;
+    if (g > 4096) g = 4096;
+    hipLaunchKernelGGL(tree_write_perm, dim3((int)g), dim3(kThreads), 0, st, rec[cur], n, perm);
+    return launch_status("tree_write_perm");
+  }
+  hipLaunchKernelGGL(tree_lds_nodes, dim3((unsigned)nodes), dim3(kLdsThreads), 0, st, rec[cur],
+                     (int)nsize, leaf, perm);
+  return launch_status("tree_lds_nodes");
 }
 
 static TreeBufs carve_tree(const TreePlan& p, void* ws) {
@@ -1221,6 +1489,7 @@ bt_status tree_build_bufs(const TreePlan& p, const TreeBufs& b, const float* coo
 bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const float* R,
                             int32_t* perm, void* ws, hipStream_t st) {
   if (lds_tree(n, leaf)) return tree_lds_launch(coords, n, n, leaf, R, perm, st);
+  if (stream_tree(n, leaf)) return tree_stream_launch(coords, n, leaf, R, perm, ws, st);
   const TreePlan p = plan_tree(n, leaf);
   return tree_build_bufs(p, carve_tree(p, ws), coords, R, perm, st);
 }

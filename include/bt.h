@@ -80,13 +80,13 @@ const char* bt_version(void);
  *   N < 2^31; writes perm [N] int32 (device).  ws: device workspace of at
  *   least bt_build_workspace_size(N, leaf) bytes, 256-byte aligned.
  *   Coordinates must be finite (not checked).
- *   In this version N is limited to 8192 (or N == leaf): such trees are
- *   built by one workgroup in LDS (up to 1,024 points from a workspace copy
- *   of the records, above that straight from coords, so the workspace size
- *   is then the 256-byte minimum); the multi-workgroup passes that split
- *   larger nodes are switched off after they faulted the GPU in testing.
- *   Errors: BT_EINVAL for null pointers, N not leaf*2^L, N >= 2^31, N above
- *   the limit; BT_ENOMEM for a short workspace.
+ *   Up to 8,192 points one workgroup builds the tree in LDS (from 1,025
+ *   points straight from coords: the workspace size is then the 256-byte
+ *   minimum); above that each node is split by one workgroup, streamed
+ *   through two record arrays in ws, until the nodes have at most 8,192
+ *   points, which one workgroup each finishes in LDS.
+ *   Errors: BT_EINVAL for null pointers, N not leaf*2^L, N >= 2^31;
+ *   BT_ENOMEM for a short workspace.
  * ---------------------------------------------------------------------- */
 size_t bt_build_workspace_size(int64_t N, int32_t leaf);
 bt_status bt_build(const float* coords, int64_t N, int32_t leaf, int32_t* perm,
@@ -198,8 +198,8 @@ bt_status ball_attn(const void* q, const void* k, const void* v,
  *   a finite 3x3 row-major fp32 rotation in host memory, applied as in
  *   bt_rotate_build; writes perm [S] int32 (device).  ws: device workspace of
  *   bt_build_padded_workspace_size(N, leaf) bytes, 256-byte aligned.  In this
- *   build S <= 8192 (or S == leaf, a single leaf), for the reason given at
- *   bt_build.  Errors: BT_EINVAL for null pointers or a violated limit,
+ *   build S <= 8192 (or S == leaf, a single leaf): one workgroup builds the
+ *   padded tree in LDS.  Errors: BT_EINVAL for null pointers or a violated limit,
  *   BT_ENOMEM for a short workspace.
  * bt_permute_padded: perm has n_slots entries, negative for an unused slot,
  *   the others row indices below n_rows (not checked beyond clamping).

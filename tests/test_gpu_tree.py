@@ -10,16 +10,6 @@ from tests.helpers import gpu, say
 
 pytestmark = pytest.mark.gpu
 
-# The GPU builder's multi-workgroup passes for nodes above 1,024 points
-# faulted the GPU in two runs (first failing case: tests/test_gpu_permute.py::
-# test_rotated_pair_pipeline_small) and the cause has not been found; the
-# library refuses trees above 8,192 points (the largest that one workgroup
-# builds in LDS), and these cases stay skipped until it is found.
-GLOBAL_PASSES_OFF = pytest.mark.skip(
-    reason="GPU tree passes for trees above 8,192 points are switched off: they faulted the "
-           "GPU twice and the cause is not found (the same kernels are checked on the CPU by "
-           "tests/test_kernel_cpu_sim.py)")
-
 
 def _gpu_tree(coords, leaf, R=None):
     dev = gpu()
@@ -63,12 +53,19 @@ def _lds_clouds():
     z[rng.random(z.shape) < 0.5] *= 0.0
     z[rng.random(z.shape) < 0.5] *= -1.0
     yield "signed_zeros4k", z, 2
+    yield "big_range8k", (rng.standard_normal((8192, 3)) * 1e30).astype(np.float32), 32
+    yield "dups8k", np.repeat(rng.random((512, 3)).astype(np.float32), 16, axis=0), 8
+    yield "collinear8k", np.stack([rng.random(8192), np.zeros(8192), np.zeros(8192)],
+                                  1).astype(np.float32), 64
 
 
 def _big_clouds():
     rng = np.random.default_rng(22)
     yield "sphere16k", synth.deformed_sphere(rng, 16384), 64
     yield "mixture32k", synth.gaussian_mixture(rng, 32768, k=32), 128
+    yield "cube12288_leaf3", synth.uniform_cube(rng, 12288), 3      # a chunk and a half
+    yield "lattice16k_leaf8", rng.integers(0, 4, size=(16384, 3)).astype(np.float32), 8
+    yield "leaf16384", synth.uniform_cube(rng, 32768), 16384
 
 
 @pytest.mark.parametrize("name,coords,leaf", list(_clouds()), ids=[c[0] for c in _clouds()])
@@ -103,11 +100,12 @@ def test_rotate_build_lds_builder():
     assert np.array_equal(_gpu_tree(c, 4, R=R), T.rotate_build(c, 4, R))
 
 
-@GLOBAL_PASSES_OFF
 @pytest.mark.parametrize("name,coords,leaf", list(_big_clouds()),
                          ids=[c[0] for c in _big_clouds()])
-def test_bit_exact_above_1024(name, coords, leaf):
-    say("bt_build", name, coords.shape, leaf)
+def test_bit_exact_streamed(name, coords, leaf):
+    """Trees above 8,192 points: one workgroup per node streamed through
+    global memory, then one workgroup per node of <= 8,192 points in LDS."""
+    say("bt_build (streamed)", name, coords.shape, leaf)
     assert np.array_equal(_gpu_tree(coords, leaf), T.build(coords, leaf))
 
 
@@ -119,14 +117,11 @@ def test_tiny_workload_bit_exact():
 
 def test_rejects_above_limit():
     dev = gpu()
-    c = torch.zeros((16384, 3), device=dev)
+    c = torch.zeros((8193, 3), device=dev)
     with pytest.raises(ops.BtError):
-        ops.bt_build(c, 2)
-    with pytest.raises(ops.BtError):
-        ops.bt_build_padded(c[:8193], 2)
+        ops.bt_build_padded(c, 2)                    # 16,384 slots
 
 
-@GLOBAL_PASSES_OFF
 @pytest.mark.parametrize("name", ["sphere", "rotpair", "cosmo"])
 def test_workloads_bit_exact(name):
     w = synth.make(name, features=False)
@@ -135,7 +130,6 @@ def test_workloads_bit_exact(name):
     assert np.array_equal(got, T.build(w.coords, w.leaf))
 
 
-@GLOBAL_PASSES_OFF
 def test_sphere_leaf64_nests_leaf128():
     w = synth.make("sphere", features=False)
     say("bt_build sphere leaf 64")
@@ -148,7 +142,6 @@ def test_sphere_leaf64_nests_leaf128():
     assert np.array_equal(a, b)
 
 
-@GLOBAL_PASSES_OFF
 def test_rotate_build_rotpair():
     w = synth.make("rotpair", features=False)
     say("bt_rotate_build rotpair")

@@ -239,6 +239,18 @@ def test_tree_kernels_bit_exact(sim, case, glob):
     assert np.array_equal(_tree(sim, c, leaf, glob=glob), T.build(c, leaf))
 
 
+@pytest.mark.parametrize("n,leaf,rot", [(16384, 128, True), (32768, 16384, False)],
+                         ids=["rotpair16k_rotated", "leaf16384"])
+def test_streamed_tree_kernels_bit_exact(sim, n, leaf, rot):
+    """Trees above 8,192 points: one workgroup per node streamed through the
+    workspace's two record arrays (AddressSanitizer on the exact-size
+    workspace), then one workgroup per node in LDS, or the leaves directly."""
+    w = synth.make("rotpair", n=n, features=False)
+    R = w.R if rot else None
+    want = T.rotate_build(w.coords, leaf, R) if rot else T.build(w.coords, leaf)
+    assert np.array_equal(_tree(sim, w.coords, leaf, R=R, shuffle=6), want)
+
+
 @pytest.mark.parametrize("glob", [False, True], ids=["lds_builder", "global_passes"])
 def test_rotated_tree_kernels_bit_exact(sim, glob):
     w = synth.make("rotpair", n=4096, features=False)
