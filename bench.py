@@ -3,12 +3,9 @@
 
 One step = one ball-attention pass (ball_attn) over one synthetic point cloud
 of the measured shape, gathering q/k/v through a permutation into ball order
-and scattering the result back to original order.  The GPU tree builder
-refuses trees above 8,192 points in this version, so the step's permutation
-is a seeded random one (the config says so): the synthetic clouds are in
-random original order, so a tree order is a random gather pattern too, and
-the kernel's work does not depend on which permutation it is.  Inputs are
-resident in HBM before the timed region starts.  The q/k/v/out tensors rotate
+and scattering the result back to original order.  The permutation is the
+cloud's ball tree, built on the GPU (bt_build) before the timed region.
+Inputs are resident in HBM before the timed region starts.  The q/k/v/out tensors rotate
 over several copies (default 4, 540 MB in all) so that no step finds its
 inputs in the 256 MB Infinity Cache left behind by the previous one.
 
@@ -126,8 +123,9 @@ def _cpu_baseline(w, budget_s, sel_check=None):
     from threadpoolctl import threadpool_info
 
     from oracle import attention as A
+    from oracle import tree as T
     n = w.coords.shape[0]
-    p = np.random.default_rng(1234).permutation(n)
+    p = T.build(w.coords, w.leaf)              # the oracle's tree, outside the timed steps
     steps, t0 = 0, time.perf_counter()
     while True:
         A.ball_attn(w.q, w.k, w.v, p, w.ball)
@@ -138,8 +136,9 @@ def _cpu_baseline(w, budget_s, sel_check=None):
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     out = {"value": steps * n / el, "unit": "points/s", "cores": threads, "kind": "oracle",
            "cpu_model": _cpu_model(), "host_cores_visible": len(os.sched_getaffinity(0)),
-           "sample": f"{steps} whole steps (fp64 ball attention over all balls) of the "
-                     f"{n}-point workload in {el:.1f} s, through {threads}-thread BLAS"}
+           "sample": f"{steps} whole steps (fp64 ball attention over all balls of the "
+                     f"oracle's tree) of the {n}-point workload in {el:.1f} s, through "
+                     f"{threads}-thread BLAS"}
     if sel_check is not None:
         out["bsa_topk_rows_differing"] = _sel_differences(**sel_check)
     return out
@@ -176,8 +175,9 @@ def _sel_differences(wb, perm, sel_gpu, tau_rel=1e-4):
 def bench_ball(args, dev, torch, ops, synth):
     w = synth.make(args.workload)
     N, H, d, ball, leaf = w.coords.shape[0], w.H, w.d, w.ball, w.leaf
-    g = torch.Generator().manual_seed(1234)
-    perm = torch.randperm(N, generator=g).to(torch.int32).to(dev)
+    # the step's permutation: the GPU tree of the cloud, built before the
+    # timed region
+    perm = ops.bt_build(torch.from_numpy(w.coords).to(dev), leaf)
     sets = []
     for _ in range(args.sets):
         q, k, v = (t.to(dev).clone() for t in (w.q, w.k, w.v))
@@ -266,10 +266,10 @@ def bench_ball(args, dev, torch, ops, synth):
         "steps": nsteps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"{args.workload}: ball attention over a seeded random "
-                               f"permutation (gather through it, scatter back; the GPU tree "
-                               f"builder refuses {N} points in this version), N={N}, "
-                               f"ball {ball}, H={H}, d={d}, {w.dtype}",
+        "config": {"workload": f"{args.workload}: ball attention over the cloud's ball tree "
+                               f"(built on the GPU before the timed region; gather through "
+                               f"it, scatter back), N={N}, ball {ball}, leaf {leaf}, H={H}, "
+                               f"d={d}, {w.dtype}",
                    "N": N, "ball": ball, "leaf": leaf, "H": H, "d": d,
                    "input_sets_rotated": len(sets), "settle_launches": settle,
                    "timing": "exactly `steps` back-to-back launches on one stream between "
@@ -329,7 +329,8 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
     srcs = [torch.randint(-32768, 32767, (n, row), dtype=torch.int16, device=dev, generator=gen)
             for _ in range(3)]
     dsts = [torch.empty_like(srcs[0]) for _ in range(3)]
-    perm = torch.randperm(n, generator=torch.Generator().manual_seed(4)).to(torch.int32).to(dev)
+    wr = synth.make("rotpair", features=False)               # the rotated tree B
+    perm = ops.bt_rotate_build(torch.from_numpy(wr.coords).to(dev), wr.leaf, wr.R)
     nbytes = 2 * n * row * 2 + 4 * n
     for name, mode in (("gather", ops.BT_GATHER), ("scatter", ops.BT_SCATTER)):
         it = [0]
@@ -339,7 +340,8 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
             it[0] += 1
             ops.bt_permute(srcs[i], perm, mode, dst=dsts[i])
         us = _event_us(torch, call, 60, warm=6)
-        rows["a5_permute_" + name] = {"workload": "N=262144 rows of 512 B (rotated-pair size)",
+        rows["a5_permute_" + name] = {"workload": "N=262144 rows of 512 B through the rotated "
+                                                  "tree of the rotated-pair cloud",
                                       "us": us, "GBps": nbytes / us / 1e3,
                                       "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS}
     del srcs, dsts
@@ -349,7 +351,7 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
     xs = [torch.randint(-32768, 32767, (n, H, d), dtype=torch.int16, device=dev,
                         generator=gen).view(torch.bfloat16) for _ in range(3)]
     xs = [x.masked_fill(~torch.isfinite(x), 0) for x in xs]
-    pc = torch.randperm(n, generator=torch.Generator().manual_seed(5)).to(torch.int32).to(dev)
+    pc = ops.bt_build(torch.from_numpy(synth.make("sphere", features=False).coords).to(dev), 128)
     cs = [torch.empty((n // s, H, d), dtype=torch.bfloat16, device=dev) for _ in range(3)]
     fs = [torch.empty_like(xs[0]) for _ in range(3)]
     row = H * d * 2
@@ -364,7 +366,8 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
             fn(it[0])
             it[0] += 1
         us = _event_us(torch, call, 60, warm=6)
-        rows["f2_" + name] = {"workload": "N=65536, H=8, d=32 bf16, s=8, perm",
+        rows["f2_" + name] = {"workload": "N=65536, H=8, d=32 bf16, s=8, through the sphere's "
+                                          "GPU tree (leaf 128)",
                               "us": us, "GBps": nbytes / us / 1e3,
                               "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS}
     del xs, cs, fs
@@ -372,7 +375,7 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
     w = synth.make("bsa")
     x = w.extra
     N, H, d = w.coords.shape[0], w.H, w.d
-    p = torch.randperm(N, generator=torch.Generator().manual_seed(1234)).to(torch.int32).to(dev)
+    p = ops.bt_build(torch.from_numpy(w.coords).to(dev), w.leaf)     # leaf 64: blocks are nodes
     bws = torch.empty(ops.bsa_workspace_size(N, H, d, w.ball, x["block"], x["group"], x["topk"]),
                       dtype=torch.uint8, device=dev)
     Wg = torch.from_numpy(w.gate_w).to(dev)
@@ -449,8 +452,7 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
     w = synth.make("sphere")
     gq, gk, gv = (t.to(dev) for t in (w.q, w.k, w.v))
     gdo = gq.clone()
-    pb = torch.randperm(w.coords.shape[0], generator=torch.Generator().manual_seed(7)) \
-        .to(torch.int32).to(dev)
+    pb = ops.bt_build(torch.from_numpy(w.coords).to(dev), w.leaf)
     grads = [torch.empty_like(gq) for _ in range(3)]
     us_b = _event_us(torch, lambda: ops.ball_attn_bwd(gq, gk, gv, gdo, pb, w.ball, *grads), 300,
                      warm=100)
@@ -511,6 +513,35 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
     rows["f3_tree_padded_pages_sizes"] = {"workload": "deformed-sphere clouds of the pages' "
                                           "uneven point counts", **padded,
                                           "bound": "latency (one workgroup)"}
+    # tree builds at the configured sizes (nodes above 8,192 points split by
+    # one workgroup each, streamed through the workspace; then one workgroup
+    # per node in LDS).  Algorithmic bytes: the coordinates read once
+    # (12 B/point), a 16-byte record read and written per point and level,
+    # the permutation written (4 B/point).
+    builds = {}
+    for name, wl, leaf_, rot in (("sphere_leaf128", "sphere", 128, False),
+                                 ("sphere_leaf64", "sphere", 64, False),
+                                 ("rotpair", "rotpair", 128, False),
+                                 ("rotpair_rotated", "rotpair", 128, True),
+                                 ("cosmology", "cosmo", 256, False)):
+        wt = synth.make(wl, features=False)
+        n_ = wt.coords.shape[0]
+        ct = torch.from_numpy(wt.coords).to(dev)
+        wst = torch.empty(ops.bt_build_workspace_size(n_, leaf_), dtype=torch.uint8, device=dev)
+        ptt = torch.empty(n_, dtype=torch.int32, device=dev)
+        fn = (lambda: ops.bt_rotate_build(ct, leaf_, wt.R, perm=ptt, workspace=wst)) if rot else \
+             (lambda: ops.bt_build(ct, leaf_, perm=ptt, workspace=wst))
+        us_t = _event_us(torch, fn, 20, warm=3)
+        levels = int(round(np.log2(n_ // leaf_)))
+        alg = n_ * (12 + 32 * levels + 4)
+        builds[name] = {"N": n_, "leaf": leaf_, "levels": levels, "build_us": us_t,
+                        "points_per_s": n_ / (us_t * 1e-6), "algorithmic_bytes": alg,
+                        "GBps": alg / us_t / 1e3, "hbm_frac": alg / us_t / 1e3 / HBM_PEAK_GBS}
+        del ct, wst, ptt
+    rows["a1_a4_tree_build"] = {"workload": "GPU ball trees of the sphere (65,536), rotated-pair "
+                                            "(262,144) and cosmology (1,048,576) clouds",
+                                **builds,
+                                "bound": "latency of one workgroup per node at the top levels"}
     return rows
 
 
@@ -518,8 +549,7 @@ def bench_bsa(args, dev, torch, ops, synth):
     w = synth.make("bsa")
     x = w.extra
     N, H, d = w.coords.shape[0], w.H, w.d
-    g = torch.Generator().manual_seed(1234)
-    perm = torch.randperm(N, generator=g).to(torch.int32).to(dev)
+    perm = ops.bt_build(torch.from_numpy(w.coords).to(dev), w.leaf)  # leaf 64: blocks are nodes
     bws = torch.empty(ops.bsa_workspace_size(N, H, d, w.ball, x["block"], x["group"], x["topk"]),
                       dtype=torch.uint8, device=dev)
     Wg = torch.from_numpy(w.gate_w).to(dev)
@@ -548,8 +578,8 @@ def bench_bsa(args, dev, torch, ops, synth):
             "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": ms,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic",
-            "config": {"workload": "bsa: BSA over a seeded random permutation (ball 128, "
-                                   "block 64, group 64, top-16), N=65536, H=8, d=32",
+            "config": {"workload": "bsa: BSA over the cloud's GPU ball tree (leaf 64, ball "
+                                   "128, block 64, group 64, top-16), N=65536, H=8, d=32",
                        "timing": "back-to-back steps between two HIP events on the launching "
                                  "stream", "host_wall_ms_per_step": el / steps * 1e3},
             "attention_tflops": flops / (ms * 1e-3) / 1e12}
