@@ -9,46 +9,28 @@
 // keeps its points in ascending original index.  This makes the permutation
 // unique, so it is reproduced bit for bit.
 //
-// Structure (all nodes of a level are handled by the same launches):
-//   ingest      coords (optionally rotated, every product and sum rounded to
-//               fp32) -> 16-byte records {x, y, z, idx}; root extents.
-//   per level while the node size n is above kFinish (= 1024 points):
-//     hist<p>     radix-select of the median key on the split axis, 11/11/10
-//                 bit digits of the order-preserving uint32 key (p = 0,1,2).
-//                 Workgroups own equal chunks of one node (the node halved
-//                 down to at most 1-4K points while its size is even), build
-//                 an LDS histogram and add it to the node's global histogram.
-//     select<p>   one workgroup per node scans that histogram, fixes the next
-//                 digit of the pivot (and, at p = 0, the split axis) and
-//                 clears the histogram.
-//     count       per chunk: keys below / equal to the pivot.
-//     scatter     stable partition: per 256-point round a ballot/mbcnt scan
-//                 gives each point its rank among left or right points; the
-//                 pivot-equal points with the smallest indices fill the left
-//                 half.  Child extents are reduced per chunk.
-//     extents     one workgroup per node merges the chunk extents into the
-//                 two children.
-//   Workgroups never wait on each other inside a launch: every hand-over is
-//   a launch boundary.
-//   finish      every node of <= 1024 points is loaded into LDS and every
-//               remaining level is split there by single waves (8-bit radix
-//               select with an LDS histogram, ballot-scan partition), then
-//               perm[t] = idx.  With few nodes a 16-wave workgroup owns a
-//               node: all its threads split a 1,024-point top segment
-//               together, and below that its waves split a level's
-//               segments in parallel; otherwise each wave owns a node.
+// Structure:
+//   up to kLdsTree (8,192) points or slots: one 16-wave workgroup reads the
+//               coordinates (rotated if asked, every product and sum rounded
+//               to fp32) into 16-byte LDS records {x, y, z, idx} and splits
+//               every level there: segments above 1,024 points with all
+//               threads (up to eight points each), 1,024-point segments by the
+//               whole workgroup or, four or more at a time, by single waves,
+//               smaller ones by single waves (8-bit radix select of the
+//               median key from the highest byte in which the segment's
+//               extreme keys differ, ballot/mbcnt partition), then
+//               perm[t] = idx.
+//   above that  the records go to the workspace; each level whose nodes
+//               hold more than 8,192 points is one launch with a workgroup
+//               per node, which streams its node from one record array to
+//               the other (extents, radix select, stable partition chunk by
+//               chunk); then one workgroup per node of <= 8,192 points
+//               finishes its subtree in LDS.  No workgroup ever reads what
+//               another one of the same launch writes.
 //   padded      an uneven point count n: the tree has leaf * 2^L slots (the
 //               smallest that holds n); a node of m points gives its left
 //               child the ceil(m/2) smallest, and a leaf's unused slots hold
-//               -1.  Built by one workgroup in LDS (slots <= 8192).
-//   one-workgroup tree (1,024 < points or slots <= 8,192): the coordinates
-//               go straight into LDS (128 KB of records) and one 16-wave
-//               workgroup splits every level there: segments above 1,024
-//               points with all threads (up to eight points each), smaller
-//               ones as in the finisher.  No workspace, no global passes.
-//               The library builds trees above 1,024 points only this way:
-//               the multi-workgroup passes above are switched off at its
-//               boundary (they stay in this file, exercised on the CPU).
+//               -1 (up to 8,192 slots, in LDS as above).
 #include "common.h"
 
 // Test hook: the CPU emulation of these kernels under MemorySanitizer marks
@@ -61,16 +43,7 @@
 namespace bt {
 
 constexpr int kThreads = 256;
-constexpr int kFinish = 1024;   // largest node finished in LDS by one wave
-constexpr int kFinishWaves = 2;   // 2 x 16 KB of records per workgroup
-constexpr int kBins = 2048;
-
-struct NodeState {
-  uint32_t prefix;   // pivot bits fixed so far
-  uint32_t rank;     // rank of the median inside the bits not yet fixed
-  uint32_t need_eq;  // pivot-equal points that go left (after the last pass)
-  uint32_t axis;
-};
+constexpr int kFinish = 1024;   // largest segment split by one wave
 
 BT_DEV int axis_of(const uint32_t* e) {
   // e = {min x, min y, min z, max x, max y, max z} as order-preserving keys
@@ -91,25 +64,6 @@ BT_DEV uint32_t mbcnt64(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-BT_DEV uint32_t block_sum_u32(uint32_t v, uint32_t* red) {
-  v = wave_sum_u32(v);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  uint32_t t = 0;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += red[i];
-  return t;
-}
-
-// ------------------------------------------------------------------ init ----
-__global__ void tree_init(uint32_t* zero_region, int64_t nwords, uint32_t* ext_root) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords;
-       i += (int64_t)gridDim.x * blockDim.x)
-    zero_region[i] = 0u;
-  if (blockIdx.x == 0 && threadIdx.x < 6) ext_root[threadIdx.x] = threadIdx.x < 3 ? 0xffffffffu : 0u;
-}
-
 // ---------------------------------------------------------------- ingest ----
 // ((r0*x + r1*y) + r2*z) with every product and sum rounded to fp32: the
 // operations are written out here, inside a scope that forbids contraction
@@ -128,10 +82,7 @@ __global__ __launch_bounds__(kThreads) void tree_ingest(const float* __restrict_
                                                         float r01, float r02, float r10,
                                                         float r11, float r12, float r20,
                                                         float r21, float r22,
-                                                        float4* __restrict__ rec,
-                                                        uint32_t* __restrict__ ext_root,
-                                                        int want_ext) {
-  uint32_t mn[3] = {0xffffffffu, 0xffffffffu, 0xffffffffu}, mx[3] = {0u, 0u, 0u};
+                                                        float4* __restrict__ rec) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     float x = coords[3 * i], y = coords[3 * i + 1], z = coords[3 * i + 2];
@@ -141,259 +92,7 @@ __global__ __launch_bounds__(kThreads) void tree_ingest(const float* __restrict_
       const float a2 = rot_row(r20, r21, r22, x, y, z);
       x = a0; y = a1; z = a2;
     }
-    x = canon_zero(x); y = canon_zero(y); z = canon_zero(z);
-    rec[i] = make_float4(x, y, z, __int_as_float((int)i));
-    const uint32_t k[3] = {float_key(x), float_key(y), float_key(z)};
-#pragma unroll
-    for (int a = 0; a < 3; ++a) { mn[a] = min(mn[a], k[a]); mx[a] = max(mx[a], k[a]); }
-  }
-  if (!want_ext) return;
-#pragma unroll
-  for (int a = 0; a < 3; ++a) { mn[a] = wave_min_u32(mn[a]); mx[a] = wave_max_u32(mx[a]); }
-  if ((threadIdx.x & 63) == 0) {
-#pragma unroll
-    for (int a = 0; a < 3; ++a) { atomicMin(&ext_root[a], mn[a]); atomicMax(&ext_root[3 + a], mx[a]); }
-  }
-}
-
-// ---------------------------------------------------------- radix passes ----
-// Pass 0: bits 31..21, pass 1: bits 20..10, pass 2: bits 9..0.  Workgroups
-// own one chunk of one node; they only add their LDS histogram into the
-// node's global histogram.  Nothing is handed between workgroups inside a
-// launch: the select of each pass is its own launch.
-template <int PASS>
-__global__ __launch_bounds__(kThreads) void tree_hist(const float4* __restrict__ rec, int chunk,
-                                                      int cpn, const uint32_t* __restrict__ ext,
-                                                      const NodeState* __restrict__ st,
-                                                      uint32_t* __restrict__ hist) {
-  constexpr int SHIFT = PASS == 0 ? 21 : (PASS == 1 ? 10 : 0);
-  constexpr int HI = PASS == 0 ? 32 : (PASS == 1 ? 21 : 10);
-  constexpr uint32_t MASK = PASS == 2 ? 1023u : 2047u;
-  __shared__ uint32_t lh[kBins];
-  BT_LDS_POISON(lh);
-  const int tid = threadIdx.x;
-  const int c = blockIdx.x;
-  const int node = c / cpn;
-  // pass 0 takes the axis from the node's extents; later passes from the
-  // state written by the previous select
-  const int axis = PASS == 0 ? axis_of(ext + 6 * node) : (int)st[node].axis;
-  const uint32_t prefix = PASS == 0 ? 0u : st[node].prefix;
-  for (int i = tid; i < kBins; i += kThreads) lh[i] = 0u;
-  __syncthreads();
-  const float4* r = rec + (int64_t)c * chunk;
-  for (int i = tid; i < chunk; i += kThreads) {
-    const uint32_t key = float_key(comp(r[i], axis));
-    bool match = true;
-    if constexpr (PASS > 0) match = (key >> HI) == (prefix >> HI);
-    if (match) atomicAdd(&lh[(key >> SHIFT) & MASK], 1u);
-  }
-  __syncthreads();
-  uint32_t* gh = hist + (int64_t)node * kBins;
-  for (int i = tid; i < kBins; i += kThreads)
-    if (lh[i]) atomicAdd(&gh[i], lh[i]);
-}
-
-// One workgroup per node: find the bin holding the median's rank, fix that
-// digit of the pivot, and clear the histogram for the next pass.  Pass 0
-// also chooses the split axis from the node's extents.
-template <int PASS>
-__global__ __launch_bounds__(kThreads) void tree_select(int64_t nsize,
-                                                        const uint32_t* __restrict__ ext,
-                                                        NodeState* __restrict__ st,
-                                                        uint32_t* __restrict__ hist) {
-  constexpr int SHIFT = PASS == 0 ? 21 : (PASS == 1 ? 10 : 0);
-  constexpr int PER = kBins / kThreads;   // 8 bins per thread
-  __shared__ uint32_t red[kThreads / 64];
-  BT_LDS_POISON(red);
-  __shared__ NodeState s_new;
-  BT_LDS_POISON(s_new);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int node = blockIdx.x;
-  NodeState s;
-  if (PASS == 0) {
-    s.prefix = 0u;
-    s.rank = (uint32_t)(nsize / 2 - 1);
-    s.need_eq = 0u;
-    s.axis = (uint32_t)axis_of(ext + 6 * node);
-  } else {
-    s = st[node];
-  }
-  uint32_t* gh = hist + (int64_t)node * kBins;
-  uint32_t h[PER];
-  uint32_t tot = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) { h[j] = gh[tid * PER + j]; tot += h[j]; }
-  const uint32_t incl = wave_incl_scan_u32(tot);
-  if (lane == 63) red[w] = incl;
-  if (tid == 0) {                     // written if no bin matches (never,
-    s_new = s;                        // for a consistent histogram)
-    s_new.need_eq = 1u;
-  }
-  __syncthreads();
-  uint32_t cum = incl - tot;
-  for (int i = 0; i < w; ++i) cum += red[i];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    if (h[j] && cum <= s.rank && s.rank < cum + h[j]) {
-      NodeState t = s;
-      t.prefix = s.prefix | ((uint32_t)(tid * PER + j) << SHIFT);
-      t.rank = s.rank - cum;
-      t.need_eq = t.rank + 1u;        // meaningful after the last pass
-      s_new = t;
-    }
-    cum += h[j];
-  }
-#pragma unroll
-  for (int j = 0; j < PER; ++j) gh[tid * PER + j] = 0u;
-  __syncthreads();
-  if (tid == 0) st[node] = s_new;
-}
-
-// ----------------------------------------------------------------- count ----
-__global__ __launch_bounds__(kThreads) void tree_count(const float4* __restrict__ rec, int chunk,
-                                                       int cpn, const NodeState* __restrict__ st,
-                                                       uint2* __restrict__ counts) {
-  __shared__ uint32_t red[kThreads / 64];
-  BT_LDS_POISON(red);
-  const int c = blockIdx.x;
-  const int node = c / cpn;
-  const NodeState s = st[node];
-  const float4* r = rec + (int64_t)c * chunk;
-  uint32_t lt = 0, eq = 0;
-  for (int i = threadIdx.x; i < chunk; i += kThreads) {
-    const uint32_t key = float_key(comp(r[i], (int)s.axis));
-    lt += key < s.prefix;
-    eq += key == s.prefix;
-  }
-  lt = block_sum_u32(lt, red);
-  eq = block_sum_u32(eq, red);
-  if (threadIdx.x == 0) counts[c] = make_uint2(lt, eq);
-}
-
-// --------------------------------------------------------------- scatter ----
-__global__ __launch_bounds__(kThreads) void tree_scatter(
-    const float4* __restrict__ rec, float4* __restrict__ out, int64_t nsize, int chunk, int cpn,
-    const NodeState* __restrict__ st, const uint2* __restrict__ counts,
-    uint32_t* __restrict__ partials) {
-  __shared__ uint32_t red[kThreads / 64];
-  BT_LDS_POISON(red);
-  __shared__ uint32_t wlt[kThreads / 64], weq[kThreads / 64];
-  BT_LDS_POISON(wlt); BT_LDS_POISON(weq);
-  __shared__ uint32_t pred[12][kThreads / 64];
-  BT_LDS_POISON(pred);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int c = blockIdx.x;
-  const int node = c / cpn;
-  const int first = node * cpn;
-  const NodeState s = st[node];
-  const uint32_t pivot = s.prefix, need_eq = s.need_eq;
-  const int axis = (int)s.axis;
-
-  // points of this node in earlier chunks
-  uint32_t ltb = 0, eqb = 0;
-  for (int i = first + tid; i < c; i += kThreads) { ltb += counts[i].x; eqb += counts[i].y; }
-  ltb = block_sum_u32(ltb, red);
-  eqb = block_sum_u32(eqb, red);
-  const uint32_t left_before = ltb + min(eqb, need_eq);
-  const uint32_t right_before = (uint32_t)(c - first) * (uint32_t)chunk - left_before;
-  const int64_t nstart = (int64_t)node * nsize;
-  const int64_t half = nsize / 2;
-
-  uint32_t E = eqb, Lrun = left_before, Rrun = right_before;
-  uint32_t lmin[3] = {~0u, ~0u, ~0u}, lmax[3] = {0u, 0u, 0u};
-  uint32_t rmin[3] = {~0u, ~0u, ~0u}, rmax[3] = {0u, 0u, 0u};
-  const float4* r = rec + (int64_t)c * chunk;
-  for (int base = 0; base < chunk; base += kThreads) {
-    // a chunk need not be a multiple of the workgroup: the valid lanes of
-    // the last round are its first chunk - base threads
-    const bool valid = base + tid < chunk;
-    const int nvalid = min(kThreads, chunk - base);
-    const float4 x = valid ? r[base + tid] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const uint32_t key = float_key(comp(x, axis));
-    const bool is_lt = valid && key < pivot, is_eq = valid && key == pivot;
-    const uint64_t blt = __ballot(is_lt), beq = __ballot(is_eq);
-    const uint32_t lt_ex = mbcnt64(blt);
-    const uint32_t eq_ex = mbcnt64(beq);
-    if (lane == 0) { wlt[w] = __popcll(blt); weq[w] = __popcll(beq); }
-    __syncthreads();
-    uint32_t ltw = 0, eqw = 0, ltt = 0, eqt = 0;
-#pragma unroll
-    for (int i = 0; i < kThreads / 64; ++i) {
-      if (i < w) { ltw += wlt[i]; eqw += weq[i]; }
-      ltt += wlt[i]; eqt += weq[i];
-    }
-    const uint32_t lt_p = ltw + lt_ex, eq_p = eqw + eq_ex;       // exclusive in round
-    const uint32_t cap0 = min(E, need_eq);
-    const bool left = is_lt || (is_eq && (E + eq_p) < need_eq);
-    const uint32_t left_p = lt_p + (min(E + eq_p, need_eq) - cap0);
-    const uint32_t left_tot = ltt + (min(E + eqt, need_eq) - cap0);
-    const int64_t dest = left ? nstart + Lrun + left_p
-                              : nstart + half + Rrun + ((uint32_t)tid - left_p);
-    // ranks are consistent by construction; the guard keeps a broken
-    // invariant from ever writing outside the node
-    if (valid && dest >= nstart && dest < nstart + nsize) out[dest] = x;
-    const uint32_t k3[3] = {float_key(x.x), float_key(x.y), float_key(x.z)};
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      if (!valid) continue;
-      if (left) { lmin[a] = min(lmin[a], k3[a]); lmax[a] = max(lmax[a], k3[a]); }
-      else { rmin[a] = min(rmin[a], k3[a]); rmax[a] = max(rmax[a], k3[a]); }
-    }
-    Lrun += left_tot;
-    Rrun += (uint32_t)nvalid - left_tot;
-    E += eqt;
-    __syncthreads();
-  }
-  // ---- child extents of this chunk ----
-  uint32_t v12[12];
-#pragma unroll
-  for (int a = 0; a < 3; ++a) {
-    v12[a] = wave_min_u32(lmin[a]); v12[3 + a] = wave_max_u32(lmax[a]);
-    v12[6 + a] = wave_min_u32(rmin[a]); v12[9 + a] = wave_max_u32(rmax[a]);
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < 12; ++j) pred[j][w] = v12[j];
-  }
-  __syncthreads();
-  if (tid < 12) {
-    uint32_t v = pred[tid][0];
-    for (int i = 1; i < kThreads / 64; ++i)
-      v = ((tid % 6) < 3) ? min(v, pred[tid][i]) : max(v, pred[tid][i]);
-    partials[(int64_t)c * 12 + tid] = v;
-  }
-}
-
-// One workgroup per node: merge the chunk extents into both children.
-__global__ __launch_bounds__(kThreads) void tree_extents(const uint32_t* __restrict__ partials,
-                                                         int cpn, uint32_t* __restrict__ ext_next) {
-  __shared__ uint32_t pred[12][kThreads / 64];
-  BT_LDS_POISON(pred);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int node = blockIdx.x;
-  const int first = node * cpn;
-  uint32_t acc[12];
-#pragma unroll
-  for (int j = 0; j < 12; ++j) acc[j] = ((j % 6) < 3) ? ~0u : 0u;
-  for (int i = first + tid; i < first + cpn; i += kThreads) {
-#pragma unroll
-    for (int j = 0; j < 12; ++j) {
-      const uint32_t v = partials[(int64_t)i * 12 + j];
-      acc[j] = ((j % 6) < 3) ? min(acc[j], v) : max(acc[j], v);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 12; ++j) acc[j] = ((j % 6) < 3) ? wave_min_u32(acc[j]) : wave_max_u32(acc[j]);
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < 12; ++j) pred[j][w] = acc[j];
-  }
-  __syncthreads();
-  if (tid < 12) {
-    uint32_t v = pred[tid][0];
-    for (int i = 1; i < kThreads / 64; ++i)
-      v = ((tid % 6) < 3) ? min(v, pred[tid][i]) : max(v, pred[tid][i]);
-    ext_next[(int64_t)(2 * node) * 6 + tid] = v;   // 12 words: left child then right
+    rec[i] = make_float4(canon_zero(x), canon_zero(y), canon_zero(z), __int_as_float((int)i));
   }
 }
 
@@ -493,30 +192,9 @@ BT_DEV void wave_split(float4* R, int m, uint32_t* hist, int lane) {
   __builtin_amdgcn_wave_barrier();
 }
 
-__global__ __launch_bounds__(kFinishWaves * 64) void tree_finish(const float4* __restrict__ rec,
-                                                                 int nf, int leaf, int nnodes,
-                                                                 int32_t* __restrict__ perm) {
-  __shared__ float4 srec[kFinishWaves][kFinish];
-  BT_LDS_POISON(srec);
-  __shared__ uint32_t shist[kFinishWaves][256];
-  BT_LDS_POISON(shist);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int node = blockIdx.x * kFinishWaves + w;
-  if (node >= nnodes) return;          // no workgroup barrier below
-  float4* R = srec[w];
-  uint32_t* hist = shist[w];
-  const int64_t base = (int64_t)node * nf;
-  for (int i = lane; i < nf; i += 64) R[i] = rec[base + i];
-  __builtin_amdgcn_wave_barrier();
-  for (int m = nf; m > leaf; m >>= 1)
-    for (int o = 0; o < nf; o += m) wave_split(R + o, m, hist, lane);
-  for (int i = lane; i < nf; i += 64) perm[base + i] = __float_as_int(R[i].w);
-}
-
-// One workgroup of kFinishBlockWaves waves per node of <= kFinish points:
-// the segments of a level are independent, so the waves take them in turn
-// (wave w splits segments w, w + waves, ...), with a workgroup barrier
-// between levels.  Used when there are few nodes (a small tree has one).
+// Waves of a tree workgroup.  The segments of a level are independent, so
+// the waves take the small ones in turn (wave w splits segments w, w +
+// waves, ...), with a workgroup barrier between levels.
 constexpr int kFinishBlockWaves = 16;
 
 // Scratch of a block-wide split (LDS).
@@ -644,38 +322,6 @@ BT_DEV void block_split(float4* R, int m, BlockSplitLds& L,
   __syncthreads();
 }
 
-// Segments of at least this many points are split by the whole workgroup;
-// smaller ones by one wave each, the waves taking the segments in turn.  At
-// 1,024 points the block-wide top split took the build from 47 to 39 us;
-// block-wide splits of 256- and 512-point segments (one after another) lost
-// more to barriers than they gained.
-constexpr int kBlockSplitMin = 1024;
-
-__global__ __launch_bounds__(kFinishBlockWaves * 64) void tree_finish_block(
-    const float4* __restrict__ rec, int nf, int leaf, int32_t* __restrict__ perm) {
-  __shared__ float4 srec[kFinish];
-  BT_LDS_POISON(srec);
-  __shared__ uint32_t shist[kFinishBlockWaves][256];
-  BT_LDS_POISON(shist);
-  __shared__ BlockSplitLds bsl;
-  BT_LDS_POISON(bsl);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t base = (int64_t)blockIdx.x * nf;
-  for (int i = tid; i < nf; i += kFinishBlockWaves * 64) srec[i] = rec[base + i];
-  __syncthreads();
-  for (int m = nf; m > leaf; m >>= 1) {
-    const int nseg = nf / m;
-    if (m >= kBlockSplitMin) {
-      for (int sgi = 0; sgi < nseg; ++sgi) block_split(srec + sgi * m, m, bsl, shist);
-    } else {
-      for (int sgi = w; sgi < nseg; sgi += kFinishBlockWaves)
-        wave_split(srec + sgi * m, m, shist[w], lane);
-      __syncthreads();
-    }
-  }
-  for (int i = tid; i < nf; i += kFinishBlockWaves * 64) perm[base + i] = __float_as_int(srec[i].w);
-}
-
 // Padded tree: start and point count of segment s at level lev, found by
 // walking down from the root (n points), the left child taking ceil(cnt/2).
 BT_DEV void padded_segment(int n, int lev, int s, int* start, int* cnt) {
@@ -691,47 +337,6 @@ BT_DEV void padded_segment(int n, int lev, int s, int* start, int* cnt) {
   }
   *start = st;
   *cnt = c;
-}
-
-// One workgroup builds a padded tree of n <= ncap <= kFinish points: the
-// points stay compacted in LDS (every segment of a level is a contiguous run),
-// each level splits its segments of two or more points in place (the waves
-// take them in turn), then leaf j's points go to slots j*leaf ... in order
-// and the leaf's remaining slots get -1.
-__global__ __launch_bounds__(kFinishBlockWaves * 64) void tree_finish_padded(
-    const float4* __restrict__ rec, int n, int ncap, int leaf, int32_t* __restrict__ perm) {
-  __shared__ float4 srec[kFinish];
-  BT_LDS_POISON(srec);
-  __shared__ uint32_t shist[kFinishBlockWaves][256];
-  BT_LDS_POISON(shist);
-  __shared__ BlockSplitLds bsl;
-  BT_LDS_POISON(bsl);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int i = tid; i < n; i += kFinishBlockWaves * 64) srec[i] = rec[i];
-  __syncthreads();
-  int lev = 0;
-  for (int slots = ncap; slots > leaf; slots >>= 1, ++lev) {
-    if (slots >= kBlockSplitMin) {           // uniform: every thread walks the segments
-      for (int sgi = 0; sgi < (1 << lev); ++sgi) {
-        int st, cnt;
-        padded_segment(n, lev, sgi, &st, &cnt);
-        if (cnt >= 2) block_split(srec + st, cnt, bsl, shist);
-      }
-    } else {
-      for (int sgi = w; sgi < (1 << lev); sgi += kFinishBlockWaves) {
-        int st, cnt;
-        padded_segment(n, lev, sgi, &st, &cnt);
-        if (cnt >= 2) wave_split(srec + st, cnt, shist[w], lane);
-      }
-      __syncthreads();
-    }
-  }
-  for (int t = tid; t < ncap; t += kFinishBlockWaves * 64) {
-    const int j = t / leaf, i = t - j * leaf;
-    int st, cnt;
-    padded_segment(n, lev, j, &st, &cnt);
-    perm[t] = i < cnt ? __float_as_int(srec[st + i].w) : -1;
-  }
 }
 
 // ------------------------------------------------ one-workgroup tree -------
@@ -1202,7 +807,7 @@ __global__ __launch_bounds__(kLdsThreads) void tree_stream_split(const float4* _
 
 static bt_status tree_lds_launch(const float* coords, int64_t n, int64_t ncap, int leaf,
                                  const float* R, int32_t* perm, hipStream_t st) {
-  if (ncap <= kFinish || ncap > kLdsTree || n > ncap || n < 1 || leaf < 1 || ncap % leaf != 0) {
+  if (ncap < 2 || ncap > kLdsTree || n > ncap || n < 1 || leaf < 1 || ncap % leaf != 0) {
     set_error("tree: %lld points in %lld slots do not fit the one-workgroup builder",
               (long long)n, (long long)ncap);
     return BT_EINVAL;
@@ -1215,12 +820,20 @@ static bt_status tree_lds_launch(const float* coords, int64_t n, int64_t ncap, i
   return launch_status("tree_lds_build");
 }
 
-// A padded tree that is a single leaf: the points in index order, then -1.
-__global__ __launch_bounds__(kThreads) void tree_single_leaf_padded(int64_t n, int64_t ncap,
-                                                                    int32_t* __restrict__ perm) {
+// A tree that is a single leaf of ncap >= n slots: the points in index
+// order, then -1.
+__global__ __launch_bounds__(kThreads) void tree_single_leaf(int64_t n, int64_t ncap,
+                                                             int32_t* __restrict__ perm) {
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < ncap;
        t += (int64_t)gridDim.x * blockDim.x)
     perm[t] = t < n ? (int32_t)t : -1;
+}
+
+static bt_status single_leaf_launch(int64_t n, int64_t ncap, int32_t* perm, hipStream_t st) {
+  int64_t g = (ncap + kThreads - 1) / kThreads;
+  if (g > 4096) g = 4096;
+  hipLaunchKernelGGL(tree_single_leaf, dim3((int)g), dim3(kThreads), 0, st, n, ncap, perm);
+  return launch_status("tree_single_leaf");
 }
 
 __global__ __launch_bounds__(kThreads) void tree_write_perm(const float4* __restrict__ rec,
@@ -1231,86 +844,15 @@ __global__ __launch_bounds__(kThreads) void tree_write_perm(const float4* __rest
 }
 
 // ------------------------------------------------------------------ host ----
-struct TreePlan {
-  int64_t n;
-  int leaf;
-  int L;         // total levels
-  int G;         // levels split by the global passes
-  int64_t nf;    // node size handed to the finisher
-  size_t nodes_next, nodes_max, max_chunks;
-  size_t off_rec0, off_rec1, off_ext0, off_ext1, off_hist, off_state, off_counts,
-      off_part, total;
-};
-
-// The workspace arrays of one build, with their capacities in elements.
-struct TreeBufs {
-  float4* rec[2];
-  uint32_t* ext[2];
-  uint32_t* hist;
-  NodeState* state;
-  uint2* counts;
-  uint32_t* part;
-  size_t n_rec, n_ext, n_hist, n_state, n_counts, n_part;
-};
-
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Points per chunk of a node of nsize = leaf * 2^k points: nsize halved while
-// it is even and above the target, so that the chunks tile every node
-// exactly.  A chunk is above half the target, or odd and above it.
-static int chunk_for(int64_t n_total, int64_t nsize) {
-  int64_t target = 1024;
-  if (n_total >= (int64_t)1 << 19) target = 4096;
-  else if (n_total >= (int64_t)1 << 18) target = 2048;
-  int64_t c = nsize;
-  while (c > target && (c & 1) == 0) c >>= 1;
-  return (int)c;
-}
-
-static TreePlan plan_tree(int64_t n, int leaf) {
-  TreePlan p{};
-  p.n = n;
-  p.leaf = leaf;
-  int L = 0;
-  while (((int64_t)leaf << L) < n) ++L;
-  p.L = L;
-  int G = 0;
-  while (G < L && (n >> G) > kFinish) ++G;
-  p.G = G;
-  p.nf = n >> G;
-  p.nodes_next = (size_t)1 << G;                       // children of the last global level
-  p.nodes_max = G ? ((size_t)1 << (G - 1)) : 1;        // nodes of the last global level
-  p.max_chunks = 1;
-  for (int lev = 0; lev < G; ++lev) {
-    const size_t nc = (size_t)(n / chunk_for(n, n >> lev));
-    if (nc > p.max_chunks) p.max_chunks = nc;
-  }
-  size_t o = 0;
-  p.off_rec0 = o; o = align256(o + (size_t)n * 16);
-  p.off_rec1 = o; o = align256(o + (size_t)n * 16);
-  p.off_ext0 = o; o = align256(o + p.nodes_next * 6 * 4);
-  p.off_ext1 = o; o = align256(o + p.nodes_next * 6 * 4);
-  p.off_hist = o; o = align256(o + p.nodes_max * kBins * 4);
-  p.off_state = o; o = align256(o + p.nodes_max * sizeof(NodeState));
-  p.off_counts = o; o = align256(o + p.max_chunks * 8);
-  p.off_part = o; o = align256(o + p.max_chunks * 12 * 4);
-  p.total = o;
-  return p;
-}
-
-// Trees of kFinish < n <= kLdsTree points are built in LDS and need no
-// workspace (the library still asks for its 256-byte minimum).
-static bool lds_tree(int64_t n, int leaf) { return n > kFinish && n <= kLdsTree && n > leaf; }
-
-// Trees above kLdsTree points: nodes are split by one workgroup each,
-// streamed through two record arrays, down to nodes of <= kLdsTree points,
-// which one workgroup each finishes in LDS.
+// Trees above kLdsTree points (and above one leaf) are streamed through two
+// record arrays in the workspace; smaller ones need none (the library still
+// asks for its 256-byte minimum).
 static bool stream_tree(int64_t n, int leaf) { return n > kLdsTree && n > leaf; }
 
 size_t tree_workspace_size(int64_t n, int leaf) {
-  if (lds_tree(n, leaf)) return 256;
-  if (stream_tree(n, leaf)) return 2 * align256((size_t)n * 16);
-  return plan_tree(n, leaf).total;
+  return stream_tree(n, leaf) ? 2 * align256((size_t)n * 16) : 256;
 }
 
 // The streamed build of n = leaf * 2^L > kLdsTree points (n > leaf) with the
@@ -1325,8 +867,7 @@ static bt_status tree_stream_launch(const float* coords, int64_t n, int leaf, co
     int64_t g = (n + kThreads - 1) / kThreads;
     if (g > 4096) g = 4096;
     hipLaunchKernelGGL(tree_ingest, dim3((int)g), dim3(kThreads), 0, st, coords, n, R ? 1 : 0,
-                       rr[0], rr[1], rr[2], rr[3], rr[4], rr[5], rr[6], rr[7], rr[8], rec[0],
-                       (uint32_t*)nullptr, 0);
+                       rr[0], rr[1], rr[2], rr[3], rr[4], rr[5], rr[6], rr[7], rr[8], rec[0]);
     bt_status s = launch_status("tree_ingest");
     if (s != BT_OK) return s;
   }
@@ -1361,137 +902,11 @@ static bt_status tree_stream_launch(const float* coords, int64_t n, int leaf, co
   return launch_status("tree_lds_nodes");
 }
 
-static TreeBufs carve_tree(const TreePlan& p, void* ws) {
-  char* b = (char*)ws;
-  TreeBufs t{};
-  t.rec[0] = (float4*)(b + p.off_rec0);
-  t.rec[1] = (float4*)(b + p.off_rec1);
-  t.ext[0] = (uint32_t*)(b + p.off_ext0);
-  t.ext[1] = (uint32_t*)(b + p.off_ext1);
-  t.hist = (uint32_t*)(b + p.off_hist);
-  t.state = (NodeState*)(b + p.off_state);
-  t.counts = (uint2*)(b + p.off_counts);
-  t.part = (uint32_t*)(b + p.off_part);
-  t.n_rec = (size_t)p.n;
-  t.n_ext = p.nodes_next * 6;
-  t.n_hist = p.nodes_max * kBins;
-  t.n_state = p.nodes_max;
-  t.n_counts = p.max_chunks;
-  t.n_part = p.max_chunks * 12;
-  return t;
-}
-
-// Host check, before any launch of a level, that every index the level's
-// kernels derive from their grid fits the array it addresses: chunk c of
-// node c / cpn reads rec[c * chunk + i] (i < chunk) and writes counts[c] and
-// part[12 c + j] (j < 12); node k uses hist[k * kBins + b] (b < kBins),
-// state[k] and ext[6 k + a] (a < 6), and its scatter writes rec[k * nsize +
-// i] (i < nsize); tree_extents writes ext[12 k + j] of the next level.  The
-// plan makes these hold by construction; a violation is reported, never
-// launched.
-static bool level_fits(const TreePlan& p, const TreeBufs& b, int lev, int64_t nsize, int chunk,
-                       int cpn, int nchunks, int nodes) {
-  const bool tiles = chunk > 0 && (int64_t)chunk * cpn == nsize && (int64_t)nodes * nsize == p.n &&
-                     nchunks == nodes * cpn;
-  return tiles && (size_t)nchunks * chunk <= b.n_rec && (size_t)nodes * nsize <= b.n_rec &&
-         (size_t)nchunks <= b.n_counts && (size_t)nchunks * 12 <= b.n_part &&
-         (size_t)nodes * kBins <= b.n_hist && (size_t)nodes <= b.n_state &&
-         (size_t)nodes * 6 <= b.n_ext && (size_t)nodes * 12 <= b.n_ext && lev < p.G;
-}
-
-// Runs the build on the arrays of b (carved from one workspace by
-// tree_build_launch; given separately by tests).
-bt_status tree_build_bufs(const TreePlan& p, const TreeBufs& b, const float* coords,
-                          const float* R, int32_t* perm, hipStream_t st) {
-  const int64_t n = p.n;
-  const int leaf = p.leaf;
-  if (b.n_rec < (size_t)n) {
-    set_error("tree: record arrays hold %zu points, the build needs %lld", b.n_rec,
-              (long long)n);
-    return BT_EINVAL;
-  }
-  if (p.G > 0) {
-    // zero the histogram region once and set the root extents; afterwards
-    // each tree_select<p> clears its node's histogram after reading it, so
-    // the histograms are zero at the start of every radix pass
-    hipLaunchKernelGGL(tree_init, dim3(64), dim3(256), 0, st, b.hist, (int64_t)b.n_hist, b.ext[0]);
-    bt_status s = launch_status("tree_init");
-    if (s != BT_OK) return s;
-  }
-  {
-    int64_t g = (n + kThreads - 1) / kThreads;
-    if (g > 256) g = 256;
-    const float* r = R;
-    float rr[9] = {1, 0, 0, 0, 1, 0, 0, 0, 1};
-    if (r) for (int i = 0; i < 9; ++i) rr[i] = r[i];
-    hipLaunchKernelGGL(tree_ingest, dim3((int)g), dim3(kThreads), 0, st, coords, n, r ? 1 : 0,
-                       rr[0], rr[1], rr[2], rr[3], rr[4], rr[5], rr[6], rr[7], rr[8], b.rec[0],
-                       b.ext[0], p.G > 0 ? 1 : 0);
-    bt_status s = launch_status("tree_ingest");
-    if (s != BT_OK) return s;
-  }
-  for (int lev = 0; lev < p.G; ++lev) {
-    const int64_t nsize = n >> lev;
-    const int chunk = chunk_for(n, nsize);
-    const int cpn = (int)(nsize / chunk);
-    const int nchunks = (int)(n / chunk);
-    const int nodes = 1 << lev;
-    if (!level_fits(p, b, lev, nsize, chunk, cpn, nchunks, nodes)) {
-      set_error("tree: level %d geometry does not fit the workspace (nsize %lld, chunk %d)", lev,
-                (long long)nsize, chunk);
-      return BT_EINVAL;
-    }
-    float4* cur = b.rec[lev & 1];
-    float4* nxt = b.rec[(lev + 1) & 1];
-    uint32_t* ec = b.ext[lev & 1];
-    uint32_t* en = b.ext[(lev + 1) & 1];
-    uint32_t* hist = b.hist;
-    NodeState* state = b.state;
-    uint2* counts = b.counts;
-    uint32_t* part = b.part;
-    const dim3 gc(nchunks), gn(nodes), blk(kThreads);
-    hipLaunchKernelGGL(tree_hist<0>, gc, blk, 0, st, cur, chunk, cpn, ec, state, hist);
-    hipLaunchKernelGGL(tree_select<0>, gn, blk, 0, st, nsize, ec, state, hist);
-    hipLaunchKernelGGL(tree_hist<1>, gc, blk, 0, st, cur, chunk, cpn, ec, state, hist);
-    hipLaunchKernelGGL(tree_select<1>, gn, blk, 0, st, nsize, ec, state, hist);
-    hipLaunchKernelGGL(tree_hist<2>, gc, blk, 0, st, cur, chunk, cpn, ec, state, hist);
-    hipLaunchKernelGGL(tree_select<2>, gn, blk, 0, st, nsize, ec, state, hist);
-    hipLaunchKernelGGL(tree_count, gc, blk, 0, st, cur, chunk, cpn, state, counts);
-    hipLaunchKernelGGL(tree_scatter, gc, blk, 0, st, cur, nxt, nsize, chunk, cpn, state, counts,
-                       part);
-    hipLaunchKernelGGL(tree_extents, gn, blk, 0, st, part, cpn, en);
-    bt_status s = launch_status("tree level");
-    if (s != BT_OK) return s;
-  }
-  const float4* fin = b.rec[p.G & 1];
-  if (p.nf == leaf) {
-    int64_t g = (n + kThreads - 1) / kThreads;
-    if (g > 4096) g = 4096;
-    hipLaunchKernelGGL(tree_write_perm, dim3((int)g), dim3(kThreads), 0, st, fin, n, perm);
-    return launch_status("tree_write_perm");
-  }
-  const int nnodes = (int)(n / p.nf);
-  if (p.nf > kFinish || (int64_t)nnodes * p.nf != n) {
-    set_error("tree: finisher nodes of %lld points do not tile %lld", (long long)p.nf,
-              (long long)n);
-    return BT_EINVAL;
-  }
-  if (nnodes <= 256) {                       // few nodes: a workgroup per node
-    hipLaunchKernelGGL(tree_finish_block, dim3(nnodes), dim3(kFinishBlockWaves * 64), 0, st,
-                       fin, (int)p.nf, leaf, perm);
-    return launch_status("tree_finish_block");
-  }
-  hipLaunchKernelGGL(tree_finish, dim3((nnodes + kFinishWaves - 1) / kFinishWaves),
-                     dim3(kFinishWaves * 64), 0, st, fin, (int)p.nf, leaf, nnodes, perm);
-  return launch_status("tree_finish");
-}
-
 bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const float* R,
                             int32_t* perm, void* ws, hipStream_t st) {
-  if (lds_tree(n, leaf)) return tree_lds_launch(coords, n, n, leaf, R, perm, st);
+  if (n == leaf) return single_leaf_launch(n, n, perm, st);
   if (stream_tree(n, leaf)) return tree_stream_launch(coords, n, leaf, R, perm, ws, st);
-  const TreePlan p = plan_tree(n, leaf);
-  return tree_build_bufs(p, carve_tree(p, ws), coords, R, perm, st);
+  return tree_lds_launch(coords, n, n, leaf, R, perm, st);
 }
 
 int64_t tree_padded_slots(int64_t n, int leaf) {
@@ -1500,37 +915,14 @@ int64_t tree_padded_slots(int64_t n, int leaf) {
   return cap;
 }
 
-size_t tree_padded_workspace_size(int64_t n, int leaf) {
-  const int64_t ncap = tree_padded_slots(n, leaf);
-  return (ncap == leaf || ncap > kFinish) ? 256 : align256((size_t)n * 16);
-}
+size_t tree_padded_workspace_size(int64_t, int) { return 256; }
 
-// Padded tree of n points: one leaf of any size, up to kFinish slots from a
-// record copy in the workspace, or up to kLdsTree slots in LDS.
+// Padded tree of n points: one leaf of any size, or up to kLdsTree slots.
 bt_status tree_build_padded_launch(const float* coords, int64_t n, int leaf, const float* R,
-                                   int32_t* perm, void* ws, hipStream_t st) {
+                                   int32_t* perm, void*, hipStream_t st) {
   const int64_t ncap = tree_padded_slots(n, leaf);
-  if (ncap == leaf) {
-    int64_t g = (ncap + kThreads - 1) / kThreads;
-    if (g > 4096) g = 4096;
-    hipLaunchKernelGGL(tree_single_leaf_padded, dim3((int)g), dim3(kThreads), 0, st, n, ncap,
-                       perm);
-    return launch_status("tree_single_leaf_padded");
-  }
-  if (ncap > kFinish) return tree_lds_launch(coords, n, ncap, leaf, R, perm, st);
-  float4* rec = (float4*)ws;
-  const float* r = R;
-  float rr[9] = {1, 0, 0, 0, 1, 0, 0, 0, 1};
-  if (r) for (int i = 0; i < 9; ++i) rr[i] = r[i];
-  int64_t g = (n + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(tree_ingest, dim3((int)g), dim3(kThreads), 0, st, coords, n, r ? 1 : 0,
-                     rr[0], rr[1], rr[2], rr[3], rr[4], rr[5], rr[6], rr[7], rr[8], rec,
-                     (uint32_t*)nullptr, 0);
-  bt_status s = launch_status("tree_ingest");
-  if (s != BT_OK) return s;
-  hipLaunchKernelGGL(tree_finish_padded, dim3(1), dim3(kFinishBlockWaves * 64), 0, st, rec,
-                     (int)n, (int)ncap, leaf, perm);
-  return launch_status("tree_finish_padded");
+  if (ncap == leaf) return single_leaf_launch(n, ncap, perm, st);
+  return tree_lds_launch(coords, n, ncap, leaf, R, perm, st);
 }
 
 }  // namespace bt

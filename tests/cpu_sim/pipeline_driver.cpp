@@ -44,31 +44,6 @@ static void save(const char* path, const void* p, size_t n) {
   fclose(f);
 }
 
-// The tree's workspace arrays, each in its own allocation.
-static bt::TreeBufs tree_bufs(const bt::TreePlan& p) {
-  bt::TreeBufs b{};
-  b.n_rec = (size_t)p.n;
-  b.n_ext = p.nodes_next * 6;
-  b.n_hist = p.nodes_max * bt::kBins;
-  b.n_state = p.nodes_max;
-  b.n_counts = p.max_chunks;
-  b.n_part = p.max_chunks * 12;
-  b.rec[0] = (float4*)exact(b.n_rec * sizeof(float4));
-  b.rec[1] = (float4*)exact(b.n_rec * sizeof(float4));
-  b.ext[0] = (uint32_t*)exact(b.n_ext * 4);
-  b.ext[1] = (uint32_t*)exact(b.n_ext * 4);
-  b.hist = (uint32_t*)exact(b.n_hist * 4);
-  b.state = (bt::NodeState*)exact(b.n_state * sizeof(bt::NodeState));
-  b.counts = (uint2*)exact(b.n_counts * sizeof(uint2));
-  b.part = (uint32_t*)exact(b.n_part * 4);
-  return b;
-}
-
-static void free_bufs(bt::TreeBufs& b) {
-  free(b.rec[0]); free(b.rec[1]); free(b.ext[0]); free(b.ext[1]);
-  free(b.hist); free(b.state); free(b.counts); free(b.part);
-}
-
 int main(int argc, char** argv) {
   if (argc < 6) { fprintf(stderr, "usage: pipeline_sim N leaf ball H d\n"); return 2; }
   const long long n = atoll(argv[1]);
@@ -86,11 +61,13 @@ int main(int argc, char** argv) {
   void *o1 = exact(featb), *qb = exact(featb), *kb = exact(featb), *vb = exact(featb),
        *o2b = exact(featb), *o2 = exact(featb);
 
-  const bt::TreePlan plan = bt::plan_tree(n, leaf);
-  bt::TreeBufs ba = tree_bufs(plan), bb = tree_bufs(plan);
+  // each tree its own workspace of exactly the size the library asks for
+  const size_t wsb = bt::tree_workspace_size(n, leaf);
+  void* wa = exact(wsb);
+  void* wb = exact(wsb);
   int st = 0;
-  st |= bt::tree_build_bufs(plan, ba, coords, nullptr, pa, nullptr);
-  st |= bt::tree_build_bufs(plan, bb, coords, R, pb, nullptr);
+  st |= bt::tree_build_launch(coords, n, leaf, nullptr, pa, wa, nullptr);
+  st |= bt::tree_build_launch(coords, n, leaf, R, pb, wb, nullptr);
   st |= bt::ball_attn_launch(q, k, v, pa, n, ball, H, d, BT_BF16, o1, nullptr);
   st |= bt::permute_launch(q, pb, n, (int64_t)rowb, BT_GATHER, qb, nullptr);
   st |= bt::permute_launch(k, pb, n, (int64_t)rowb, BT_GATHER, kb, nullptr);
@@ -104,10 +81,9 @@ int main(int argc, char** argv) {
   save("inv.bin", inv, (size_t)n * 4);
   save("o1.bin", o1, featb);
   save("o2.bin", o2, featb);
-  free_bufs(ba);
-  free_bufs(bb);
-  for (void* x : {(void*)coords, q, k, v, (void*)pa, (void*)pb, (void*)inv, o1, qb, kb, vb, o2b, o2})
+  for (void* x : {(void*)coords, q, k, v, (void*)pa, (void*)pb, (void*)inv, o1, qb, kb, vb, o2b, o2,
+                  wa, wb})
     free(x);
-  printf("done pipeline n=%lld leaf=%d G=%d nf=%lld\n", n, leaf, plan.G, (long long)plan.nf);
+  printf("done pipeline n=%lld leaf=%d ws=%zu\n", n, leaf, wsb);
   return 0;
 }

@@ -1,6 +1,5 @@
 // Runs the tree.hip kernels on the host under the SIMT emulation.
 // usage: tree_sim [padded] coords.bin N leaf out.bin [R.bin]
-// BT_SIM_GLOBAL=1: run the multi-workgroup passes whatever the size
 #include <cstdarg>
 #include <string>
 #include "hip/hip_runtime.h"
@@ -48,18 +47,9 @@ int main(int argc, char** argv) {
   for (size_t i = 0; i < ws; ++i) ((unsigned char*)w)[i] = (unsigned char)(i * 131 + 7);
 #endif
   std::vector<int32_t> perm(n, -1);
-  if (getenv("BT_SIM_GLOBAL")) {
-    // the multi-workgroup passes, also for trees the library builds in LDS
-    const bt::TreePlan p = bt::plan_tree(n, leaf);
-    if (ws < p.total) { free(w); ws = p.total; if (posix_memalign(&w, 256, ws) != 0) return 2; }
-#ifndef BT_SIM_UNINIT_WS
-    for (size_t i = 0; i < ws; ++i) ((unsigned char*)w)[i] = (unsigned char)(i * 131 + 7);
-#endif
-    bt::tree_build_bufs(p, bt::carve_tree(p, w), coords.data(), rot ? R : nullptr, perm.data(),
-                        nullptr);
-  } else {
-    bt::tree_build_launch(coords.data(), n, leaf, rot ? R : nullptr, perm.data(), w, nullptr);
-  }
+  const bt_status st = bt::tree_build_launch(coords.data(), n, leaf, rot ? R : nullptr,
+                                             perm.data(), w, nullptr);
+  if (st != BT_OK) { free(w); fprintf(stderr, "status %d\n", (int)st); return 3; }
   free(w);
   f = fopen(argv[4], "wb"); fwrite(perm.data(), 4, n, f); fclose(f);
   printf("done n=%lld leaf=%d ws=%zu\n", n, leaf, ws);

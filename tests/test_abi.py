@@ -55,8 +55,8 @@ def test_build_rejects(L):
     assert L.bt_build(f, 1 << 31, 1, f, f, 1 << 20, None) == ops.BT_EINVAL
     assert L.bt_build(f, 8, 2, f, None, 1 << 20, None) == ops.BT_EINVAL
     assert L.bt_build_workspace_size(12, 4) == 0
-    assert L.bt_build_workspace_size(1024, 32) > 1024 * 32
-    assert L.bt_build_workspace_size(8192, 32) == 256    # built in LDS from coords
+    assert L.bt_build_workspace_size(1024, 32) == 256    # built in LDS from coords
+    assert L.bt_build_workspace_size(8192, 32) == 256
     assert L.bt_build_workspace_size(16384, 32) == 2 * 16384 * 16   # two record arrays
 
 
@@ -64,8 +64,8 @@ def test_build_rejects_short_workspace(L):
     buf = C.create_string_buffer(4096 + 512)
     addr = (C.addressof(buf) + 255) & ~255
     f = _fake()
-    assert L.bt_build(f, 1024, 32, f, C.c_void_p(addr), 4096, None) == ops.BT_ENOMEM
-    assert L.bt_build(f, 1024, 32, f, C.c_void_p(addr + 8), 1 << 30, None) == ops.BT_EINVAL
+    assert L.bt_build(f, 16384, 32, f, C.c_void_p(addr), 4096, None) == ops.BT_ENOMEM
+    assert L.bt_build(f, 16384, 32, f, C.c_void_p(addr + 8), 1 << 30, None) == ops.BT_EINVAL
 
 
 def test_rotate_rejects_nonfinite(L):
@@ -194,7 +194,7 @@ def test_padded_size_and_workspace(L):
     assert L.bt_padded_size(5, 0) == -1
     assert L.bt_padded_size((1 << 31) - 1, 3) == -1          # slots would reach 2^31
     assert L.bt_build_padded_workspace_size(0, 4) == 0
-    assert L.bt_build_padded_workspace_size(972, 32) >= 972 * 16
+    assert L.bt_build_padded_workspace_size(972, 32) == 256
 
 
 def test_build_padded_rejects(L):

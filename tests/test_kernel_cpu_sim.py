@@ -4,9 +4,8 @@ tests/cpu_sim/ holds a host SIMT emulation of the HIP constructs the kernels
 use (see its header); the kernel .hip files are included unchanged, built
 with clang++ and AddressSanitizer, and run on small inputs.  The results are
 compared with the oracle: tree permutations bit for bit (the one-workgroup
-LDS builder of trees up to 8,192 points, and the multi-workgroup passes,
-which the library switches off on the GPU; BT_SIM_GLOBAL=1 makes the tree
-driver take those at any size), attention within the GPU tolerances.  An out-of-bounds access in a
+LDS builder of trees up to 8,192 points and the streamed one-workgroup-per-
+node splits above that), attention within the GPU tolerances.  An out-of-bounds access in a
 kernel aborts the run under AddressSanitizer.
 """
 import os
@@ -99,26 +98,25 @@ def sim_msan(tmp_path_factory):
     return {"dir": d, "tree": out}
 
 
-@pytest.mark.parametrize("case", ["global_passes", "lds_builder", "padded", "padded_lds"])
+@pytest.mark.parametrize("case", ["lds_builder", "streamed", "padded", "padded_lds"])
 def test_tree_kernels_no_uninitialised_reads(sim_msan, case):
-    """4,096 points, leaf 128, rotated (by the multi-workgroup passes and the
-    finisher, or in LDS by one workgroup), and padded trees of 972 and 5,000
-    points: nothing uninitialised is read, and the permutations are the
-    oracle's."""
+    """The rotated-pair recipe rotated, leaf 128, at 4,096 points (in LDS by
+    one workgroup) and 16,384 points (streamed splits, then LDS), and padded
+    trees of 972 and 5,000 points: nothing uninitialised is read, and the
+    permutations are the oracle's."""
     d_ = sim_msan["dir"]
     env = dict(os.environ, EMU_SHUFFLE="4")
-    if case == "global_passes":
-        env["BT_SIM_GLOBAL"] = "1"
     if case.startswith("padded"):
         n, leaf = (972, 32) if case == "padded" else (5000, 64)
         c = synth.uniform_cube(np.random.default_rng(11), n)
         c.astype(np.float32).tofile(d_ / "coords.bin")
         args, want = ["padded", "coords.bin", str(n), str(leaf), "out.bin"], T.build_padded(c, leaf)
     else:
-        w = synth.make("rotpair", n=4096, features=False)
+        n = 4096 if case == "lds_builder" else 16384
+        w = synth.make("rotpair", n=n, features=False)
         w.coords.astype(np.float32).tofile(d_ / "coords.bin")
         w.R.astype(np.float32).tofile(d_ / "R.bin")
-        args = ["coords.bin", "4096", "128", "out.bin", "R.bin"]
+        args = ["coords.bin", str(n), "128", "out.bin", "R.bin"]
         want = T.rotate_build(w.coords, 128, w.R)
     r = subprocess.run([sim_msan["tree"], *args], cwd=d_, capture_output=True, text=True,
                        timeout=900, env=env)
@@ -126,27 +124,26 @@ def test_tree_kernels_no_uninitialised_reads(sim_msan, case):
     assert np.array_equal(np.fromfile(d_ / "out.bin", np.int32), want)
 
 
-def _tsan_env(shuffle, glob=False):
+def _tsan_env(shuffle):
     env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1 report_signal_unsafe=0")
     env["EMU_SHUFFLE"] = str(shuffle)
-    if glob:
-        env["BT_SIM_GLOBAL"] = "1"
     return env
 
 
-@pytest.mark.parametrize("glob", [False, True], ids=["lds_builder", "global_passes"])
-def test_tree_kernels_no_races(sim_tsan, glob):
-    """4,096 points, leaf 128, plain and rotated, built in LDS by one
-    workgroup or by the multi-workgroup passes (two global levels, then the
-    finisher): no data race, and the permutations are the oracle's."""
+@pytest.mark.parametrize("n", [4096, 16384], ids=["lds_builder", "streamed"])
+def test_tree_kernels_no_races(sim_tsan, n):
+    """The rotated-pair recipe at 4,096 points (built in LDS by one
+    workgroup) and 16,384 points (streamed splits, then one workgroup per
+    node in LDS), leaf 128, plain and rotated: no data race, and the
+    permutations are the oracle's."""
     d_ = sim_tsan["dir"]
-    w = synth.make("rotpair", n=4096, features=False)
+    w = synth.make("rotpair", n=n, features=False)
     w.coords.astype(np.float32).tofile(d_ / "coords.bin")
     w.R.astype(np.float32).tofile(d_ / "R.bin")
     for rot in (False, True):
-        args = [sim_tsan["tree"], "coords.bin", "4096", "128", "out.bin"] + (["R.bin"] if rot else [])
+        args = [sim_tsan["tree"], "coords.bin", str(n), "128", "out.bin"] + (["R.bin"] if rot else [])
         r = subprocess.run(args, cwd=d_, capture_output=True, text=True, timeout=900,
-                           env=_tsan_env(3, glob))
+                           env=_tsan_env(3))
         assert r.returncode == 0 and "ThreadSanitizer" not in r.stderr, r.stderr[-4000:]
         want = T.rotate_build(w.coords, 128, w.R) if rot else T.build(w.coords, 128)
         assert np.array_equal(np.fromfile(d_ / "out.bin", np.int32), want)
@@ -180,16 +177,14 @@ SLOW = pytest.mark.skipif(os.environ.get("BT_SIM_SLOW") != "1",
                           reason="long emulation: set BT_SIM_SLOW=1")
 
 
-def _env(shuffle, glob=False):
+def _env(shuffle):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0")
     if shuffle is not None:
         env["EMU_SHUFFLE"] = str(shuffle)
-    if glob:
-        env["BT_SIM_GLOBAL"] = "1"
     return env
 
 
-def _tree(sim, coords, leaf, R=None, shuffle=None, timeout=600, glob=False):
+def _tree(sim, coords, leaf, R=None, shuffle=None, timeout=600):
     d = sim["dir"]
     c = d / "c.bin"
     np.ascontiguousarray(coords, np.float32).tofile(c)
@@ -198,24 +193,15 @@ def _tree(sim, coords, leaf, R=None, shuffle=None, timeout=600, glob=False):
         np.asarray(R, np.float32).tofile(d / "R.bin")
         args.append(str(d / "R.bin"))
     r = subprocess.run(args, capture_output=True, text=True, timeout=timeout,
-                       env=_env(shuffle, glob))
+                       env=_env(shuffle))
     assert r.returncode == 0 and "done" in r.stdout, r.stderr[-4000:]
     return np.fromfile(d / "p.bin", np.int32)
 
 
-_TREE_CASES = ["cube4k_leaf32", "lattice2k_leaf8", "signed_zeros2k_leaf2", "mixture4k_leaf16",
-               "leaf2048", "cube1536_leaf3", "cube2000_leaf1000", "lattice8k_leaf16"]
-# every case in LDS; the multi-workgroup passes on the cases that shape
-# their chunks (ragged nodes, chunks off the workgroup size, ties)
-_GLOBAL_CASES = ["cube4k_leaf32", "signed_zeros2k_leaf2", "leaf2048", "cube1536_leaf3",
-                 "cube2000_leaf1000"]
-
-
-@pytest.mark.parametrize("case,glob", [(c, False) for c in _TREE_CASES] +
-                         [(c, True) for c in _GLOBAL_CASES],
-                         ids=[c + "-lds_builder" for c in _TREE_CASES] +
-                             [c + "-global_passes" for c in _GLOBAL_CASES])
-def test_tree_kernels_bit_exact(sim, case, glob):
+@pytest.mark.parametrize("case", ["cube4k_leaf32", "lattice2k_leaf8", "signed_zeros2k_leaf2",
+                                  "mixture4k_leaf16", "leaf2048", "cube1536_leaf3",
+                                  "cube2000_leaf1000", "lattice8k_leaf16"])
+def test_tree_kernels_bit_exact(sim, case):
     rng = np.random.default_rng(31)
     if case == "cube4k_leaf32":
         c, leaf = synth.uniform_cube(rng, 4096), 32
@@ -236,7 +222,7 @@ def test_tree_kernels_bit_exact(sim, case, glob):
         c, leaf = synth.uniform_cube(rng, 2000), 1000
     else:                                 # the largest tree built in LDS
         c, leaf = rng.integers(0, 5, size=(8192, 3)).astype(np.float32), 16
-    assert np.array_equal(_tree(sim, c, leaf, glob=glob), T.build(c, leaf))
+    assert np.array_equal(_tree(sim, c, leaf), T.build(c, leaf))
 
 
 @pytest.mark.parametrize("n,leaf,rot", [(16384, 128, True), (32768, 16384, False)],
@@ -251,21 +237,20 @@ def test_streamed_tree_kernels_bit_exact(sim, n, leaf, rot):
     assert np.array_equal(_tree(sim, w.coords, leaf, R=R, shuffle=6), want)
 
 
-@pytest.mark.parametrize("glob", [False, True], ids=["lds_builder", "global_passes"])
-def test_rotated_tree_kernels_bit_exact(sim, glob):
+def test_rotated_tree_kernels_bit_exact(sim):
     w = synth.make("rotpair", n=4096, features=False)
-    assert np.array_equal(_tree(sim, w.coords, 64, R=w.R, glob=glob),
-                          T.rotate_build(w.coords, 64, w.R))
+    assert np.array_equal(_tree(sim, w.coords, 64, R=w.R), T.rotate_build(w.coords, 64, w.R))
 
 
 @pytest.mark.parametrize("shuffle", [1, 2])
 def test_tree_kernels_shuffled_workgroups(sim, shuffle):
-    """Workgroups of every launch in a seeded random order: the result does
-    not depend on the order (no workgroup reads what another one of the same
-    launch writes; the histogram atomics commute)."""
-    w = synth.make("rotpair", n=4096, features=False)
-    assert np.array_equal(_tree(sim, w.coords, 128, R=w.R, shuffle=shuffle, glob=True),
-                          T.rotate_build(w.coords, 128, w.R))
+    """Workgroups of every launch in a seeded random order (32,768 points,
+    leaf 16: streamed levels of two and four workgroups, then four
+    workgroups in LDS): the result does not depend on the order (no
+    workgroup reads what another one of the same launch writes)."""
+    w = synth.make("rotpair", n=32768, features=False)
+    assert np.array_equal(_tree(sim, w.coords, 16, R=w.R, shuffle=shuffle),
+                          T.rotate_build(w.coords, 16, w.R))
 
 
 def _pipeline(sim, n, H, shuffle):
@@ -295,8 +280,8 @@ def _pipeline(sim, n, H, shuffle):
 
 
 def test_rotated_pair_pipeline(sim):
-    """4,096 points, leaf = ball 128: two global levels, then the finisher;
-    ball attention in tree A, gather into tree B, attention, scatter back."""
+    """4,096 points, leaf = ball 128: both trees in LDS; ball attention in
+    tree A, gather into tree B, attention, scatter back."""
     _pipeline(sim, 4096, 2, shuffle=5)
 
 
@@ -316,10 +301,9 @@ def test_sphere_65536_tree(sim, leaf):
 
 
 @SLOW
-def test_tree_finish_many_nodes(sim):
-    """524,288 points, leaf 128: 512 finisher nodes of 1,024 points, so the
-    one-wave-per-node finisher (tree_finish) runs, after nine global levels
-    with 4,096-point chunks."""
+def test_tree_many_nodes(sim):
+    """524,288 points, leaf 128: six streamed levels (up to 32 workgroups),
+    then 64 workgroups of 8,192 points in LDS."""
     w = synth.make("rotpair", n=524288, features=False)
     assert np.array_equal(_tree(sim, w.coords, 128, shuffle=11, timeout=7200),
                           T.build(w.coords, 128))
