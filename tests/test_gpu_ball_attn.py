@@ -163,6 +163,30 @@ def test_cosmo_workload_sampled():
     assert g.abs().max() <= w.v.float().abs().max() + 1e-2
 
 
+@pytest.mark.parametrize("name", ["sphere", "cosmo"])
+def test_workload_gpu_tree_then_attention(name):
+    """The workload's build and pass on the GPU: bt_build (bit for bit
+    against the oracle's tree), then ball_attn through that device
+    permutation; every output (sphere) or 3,002 sampled rows (cosmology)
+    against the oracle."""
+    dev = gpu()
+    w = synth.make(name)
+    say(name, ": GPU tree then ball_attn")
+    perm = ops.bt_build(torch.from_numpy(w.coords).to(dev), w.leaf)
+    out = ops.ball_attn(w.q.to(dev), w.k.to(dev), w.v.to(dev), perm, w.ball)
+    torch.cuda.synchronize()
+    p_ref = T.build(w.coords, w.leaf)
+    assert np.array_equal(perm.cpu().numpy(), p_ref)
+    got = out.cpu()
+    if name == "sphere":
+        assert max_abs(got, A.ball_attn(w.q, w.k, w.v, p_ref, w.ball)) <= 2e-2
+    else:
+        rows = np.random.default_rng(2).choice(w.coords.shape[0], 3000, replace=False)
+        rows = np.concatenate([rows, [0, w.coords.shape[0] - 1]])
+        want = A.ball_attn_rows(w.q, w.k, w.v, p_ref, w.ball, rows)
+        assert max_abs(got[torch.from_numpy(p_ref[rows])], want) <= 2e-2
+
+
 def test_deterministic():
     dev = gpu()
     q, k, v = _feats(8192, 8, 32, "bf16", seed=9)

@@ -90,8 +90,17 @@ def test_rotated_pair_pipeline_8192():
     _rotated_pair(8192, 128)
 
 
-@pytest.mark.skip(reason="faulted the GPU in two runs: the GPU tree passes for trees above "
-                         "8,192 points are switched off and the cause is not found")
+def test_rotated_pair_pipeline_full_size():
+    """The rotated-pair workload end to end at its full size (262,144 points,
+    leaf = ball 128, 8 heads of 32): both GPU trees bit for bit, then the
+    attention passes and permutes against the oracle on the GPU trees."""
+    say("rotated pair 262144")
+    _rotated_pair(262144, 128)
+
+
+@pytest.mark.skip(reason="faulted the GPU in two runs with the multi-workgroup tree passes "
+                         "(since removed); the cause was not found, so this case stays off "
+                         "the GPU")
 def test_rotated_pair_pipeline_small():
     """Tree A and rotated tree B; attention in A, scatter back to original
     order, gather into B order, attention in B (tree order, perm=None), and
