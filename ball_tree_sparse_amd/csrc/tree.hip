@@ -624,88 +624,125 @@ __global__ __launch_bounds__(kLdsThreads) void tree_lds_nodes(const float4* __re
   lds_levels(srec, nf, nf, leaf, bsl, bgl, shist, perm + base);
 }
 
+// LDS of a streamed split beyond the histograms: the children's extents per
+// wave.
+struct StreamLds {
+  uint32_t cext[kFinishBlockWaves][12];
+};
+
+// Histogram copies per wave of a streamed split: lane l counts into copy
+// l % kSubHist, so that keys of one bin collide in at most 64 / kSubHist
+// lanes of an atomic (the top levels' keys crowd into few bins).
+constexpr int kSubHist = 4;
+
 // One workgroup per node of m > kLdsTree points (m even): the split of
 // big_split with the node streamed from global memory in chunks of
 // kLdsThreads * kLdsPer positions (position p of a chunk belongs to thread
 // p % kLdsThreads in round p / kLdsThreads), the children written to out at
-// the node's place.  No workgroup reads what another one writes.
-__global__ __launch_bounds__(kLdsThreads) void tree_stream_split(const float4* __restrict__ in,
-                                                                 float4* __restrict__ out,
-                                                                 int64_t m) {
-  __shared__ uint32_t shist[kFinishBlockWaves][256];
+// the node's place and their extents to ext_out[12 node ...] (left child,
+// then right).  The node's own extents come from ext_in[6 node ...] (the
+// previous level's ext_out) or, with ext_in null, from a pass over the node.
+// The radix digits are the 8 bits below the highest bit not yet fixed (the
+// last one shorter), so that every pass resolves 8 bits that vary.  No
+// workgroup reads what another one of the same launch writes.
+__global__ __launch_bounds__(kLdsThreads) void tree_stream_split(
+    const float4* __restrict__ in, float4* __restrict__ out, int64_t m,
+    const uint32_t* __restrict__ ext_in, uint32_t* __restrict__ ext_out) {
+  __shared__ uint32_t shist[kFinishBlockWaves][kSubHist][256];
   BT_LDS_POISON(shist);
   __shared__ BlockSplitLds L;
   BT_LDS_POISON(L);
   __shared__ BigSplitLds B;
   BT_LDS_POISON(B);
+  __shared__ StreamLds S;
+  BT_LDS_POISON(S);
   constexpr int64_t CH = (int64_t)kLdsThreads * kLdsPer;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t base = (int64_t)blockIdx.x * m;
+  const int sub = lane % kSubHist;
+  const int64_t node = blockIdx.x;
+  const int64_t base = node * m;
   const float4* R = in + base;
   float4* O = out + base;
   const int64_t nch = (m + CH - 1) / CH;
 
-  // extents of the node
-  uint32_t mn[3] = {~0u, ~0u, ~0u}, mx[3] = {0u, 0u, 0u};
-  for (int64_t c = 0; c < nch; ++c) {
+  uint32_t e[6];
+  if (ext_in) {
 #pragma unroll
-    for (int r = 0; r < kLdsPer; ++r) {
-      const int64_t p = c * CH + r * kLdsThreads + tid;
-      if (p < m) {
-        const float4 x = R[p];
-        const uint32_t k3[3] = {float_key(x.x), float_key(x.y), float_key(x.z)};
+    for (int a = 0; a < 6; ++a) e[a] = ext_in[node * 6 + a];
+  } else {                                   // extents of the node: a pass over it
+    uint32_t mn[3] = {~0u, ~0u, ~0u}, mx[3] = {0u, 0u, 0u};
+    for (int64_t c = 0; c < nch; ++c) {
 #pragma unroll
-        for (int a = 0; a < 3; ++a) { mn[a] = min(mn[a], k3[a]); mx[a] = max(mx[a], k3[a]); }
+      for (int r = 0; r < kLdsPer; ++r) {
+        const int64_t p = c * CH + r * kLdsThreads + tid;
+        if (p < m) {
+          const float4 x = R[p];
+          const uint32_t k3[3] = {float_key(x.x), float_key(x.y), float_key(x.z)};
+#pragma unroll
+          for (int a = 0; a < 3; ++a) { mn[a] = min(mn[a], k3[a]); mx[a] = max(mx[a], k3[a]); }
+        }
       }
     }
-  }
-  uint32_t e[6];
 #pragma unroll
-  for (int a = 0; a < 3; ++a) { e[a] = wave_min_u32(mn[a]); e[3 + a] = wave_max_u32(mx[a]); }
-  if (lane == 0) {
+    for (int a = 0; a < 3; ++a) { e[a] = wave_min_u32(mn[a]); e[3 + a] = wave_max_u32(mx[a]); }
+    if (lane == 0) {
 #pragma unroll
-    for (int a = 0; a < 6; ++a) L.ext[w][a] = e[a];
-  }
-  __syncthreads();
-  if (tid < 6) {
-    uint32_t v = L.ext[0][tid];
-    for (int i = 1; i < kFinishBlockWaves; ++i)
-      v = tid < 3 ? min(v, L.ext[i][tid]) : max(v, L.ext[i][tid]);
-    L.e6[tid] = v;
-  }
-  __syncthreads();
+      for (int a = 0; a < 6; ++a) L.ext[w][a] = e[a];
+    }
+    __syncthreads();
+    if (tid < 6) {
+      uint32_t v = L.ext[0][tid];
+      for (int i = 1; i < kFinishBlockWaves; ++i)
+        v = tid < 3 ? min(v, L.ext[i][tid]) : max(v, L.ext[i][tid]);
+      L.e6[tid] = v;
+    }
+    __syncthreads();
 #pragma unroll
-  for (int a = 0; a < 6; ++a) e[a] = L.e6[a];
+    for (int a = 0; a < 6; ++a) e[a] = L.e6[a];
+  }
   const int axis = axis_of(e);
   const uint32_t kmin = e[axis], kmax = e[3 + axis];
+  // the split coordinate of position p, one 4-byte load
+  const float* RC = (const float*)R + axis;
+  auto key_at = [&](int64_t p) -> uint32_t { return float_key(RC[4 * p]); };
 
-  // radix select of rank m/2-1 (as big_split, the keys read again per pass)
+  // radix select of rank m/2-1: bits at and above hi are fixed in prefix;
+  // each pass takes the (up to) 8 bits below hi
   uint32_t prefix = kmin;
   uint32_t rank = (uint32_t)(m / 2 - 1);
   const uint32_t diff = kmin ^ kmax;
   if (diff) {
-    const int top = 31 - __clz((int)diff);
-    prefix = kmin & ~((2u << top) - 1u);
-    for (int shift = (top / 8) * 8; shift >= 0; shift -= 8) {
-      const int hi = shift + 8;
+    int hi = 32 - __clz((int)diff);          // the keys agree above bit hi - 1
+    prefix = hi >= 32 ? 0u : (kmin & (0xffffffffu << hi));
+    while (hi > 0) {
+      const int shift = hi > 8 ? hi - 8 : 0;
+      const uint32_t dmask = (1u << (hi - shift)) - 1u;
       const uint32_t hmask = hi >= 32 ? 0u : (0xffffffffu << hi);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) shist[w][lane * 4 + j] = 0u;
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int u = 0; u < kSubHist; ++u) shist[w][u][lane * 4 + j] = 0u;
       __builtin_amdgcn_wave_barrier();
       for (int64_t c = 0; c < nch; ++c) {
+        uint32_t kk[kLdsPer];
 #pragma unroll
         for (int r = 0; r < kLdsPer; ++r) {
           const int64_t p = c * CH + r * kLdsThreads + tid;
-          if (p < m) {
-            const uint32_t key = float_key(comp(R[p], axis));
-            if ((key & hmask) == (prefix & hmask)) atomicAdd(&shist[w][(key >> shift) & 255u], 1u);
-          }
+          kk[r] = p < m ? key_at(p) : 0u;
+        }
+#pragma unroll
+        for (int r = 0; r < kLdsPer; ++r) {
+          const int64_t p = c * CH + r * kLdsThreads + tid;
+          if (p < m && (kk[r] & hmask) == (prefix & hmask))
+            atomicAdd(&shist[w][sub][(kk[r] >> shift) & dmask], 1u);
         }
       }
       __syncthreads();
       if (tid < 256) {
         uint32_t t = 0;
-        for (int i = 0; i < kFinishBlockWaves; ++i) t += shist[i][tid];
+        for (int i = 0; i < kFinishBlockWaves; ++i)
+#pragma unroll
+          for (int u = 0; u < kSubHist; ++u) t += shist[i][u][tid];
         L.hist[tid] = t;
       }
       __syncthreads();
@@ -726,10 +763,11 @@ __global__ __launch_bounds__(kLdsThreads) void tree_stream_split(const float4* _
         }
       }
       __syncthreads();
-      prefix = (prefix & ~(255u << shift)) | (B.pick[0] << shift);
+      prefix |= B.pick[0] << shift;
       rank = B.pick[1];
       const bool single = B.pick[2] == 1u && shift > 0;
-      __syncthreads();
+      __syncthreads();                       // pick and hist are rewritten next pass
+      hi = shift;
       if (single) {                          // uniform: one key matches prefix above shift
         const uint32_t pmask = 0xffffffffu << shift;
         for (int64_t c = 0; c < nch; ++c) {
@@ -737,7 +775,7 @@ __global__ __launch_bounds__(kLdsThreads) void tree_stream_split(const float4* _
           for (int r = 0; r < kLdsPer; ++r) {
             const int64_t p = c * CH + r * kLdsThreads + tid;
             if (p < m) {
-              const uint32_t key = float_key(comp(R[p], axis));
+              const uint32_t key = key_at(p);
               if ((key & pmask) == prefix) B.pick[0] = key;
             }
           }
@@ -754,9 +792,11 @@ __global__ __launch_bounds__(kLdsThreads) void tree_stream_split(const float4* _
   const uint32_t need_eq = rank + 1u;
 
   // stable partition, chunk by chunk in position order (as big_split, with
-  // the pivot-equal and left counts of the earlier chunks carried along)
+  // the pivot-equal and left counts of the earlier chunks carried along);
+  // the children's extents are gathered on the way
   const uint64_t half = (uint64_t)(m / 2);
   uint32_t E = 0, Lrun = 0;
+  uint32_t cmn[2][3] = {{~0u, ~0u, ~0u}, {~0u, ~0u, ~0u}}, cmx[2][3] = {{0u, 0u, 0u}, {0u, 0u, 0u}};
   for (int64_t c = 0; c < nch; ++c) {
     float4 x[kLdsPer];
     uint32_t in_w[kLdsPer];
@@ -764,6 +804,10 @@ __global__ __launch_bounds__(kLdsThreads) void tree_stream_split(const float4* _
     for (int r = 0; r < kLdsPer; ++r) {
       const int64_t p = c * CH + r * kLdsThreads + tid;
       x[r] = p < m ? R[p] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int r = 0; r < kLdsPer; ++r) {
+      const int64_t p = c * CH + r * kLdsThreads + tid;
       const uint64_t b = __ballot(p < m && float_key(comp(x[r], axis)) == pivot);
       in_w[r] = mbcnt64(b);
       if (lane == 0) B.rc[r * kFinishBlockWaves + w] = (uint32_t)__popcll(b);
@@ -779,6 +823,15 @@ __global__ __launch_bounds__(kLdsThreads) void tree_stream_split(const float4* _
           p < m && (kr < pivot ||
                     (kr == pivot && E + B.rc[r * kFinishBlockWaves + w] + in_w[r] < need_eq));
       left_bits |= (uint32_t)left << r;
+      if (p < m) {
+        const int side = left ? 0 : 1;
+        const uint32_t k3[3] = {float_key(x[r].x), float_key(x[r].y), float_key(x[r].z)};
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+          cmn[side][a] = min(cmn[side][a], k3[a]);
+          cmx[side][a] = max(cmx[side][a], k3[a]);
+        }
+      }
     }
     E += B.total;
     __syncthreads();                         // every thread read the counts and the total
@@ -802,6 +855,26 @@ __global__ __launch_bounds__(kLdsThreads) void tree_stream_split(const float4* _
     }
     Lrun += B.total;
     __syncthreads();                         // the counts are rewritten by the next chunk
+  }
+  // the children's extents: {min x, min y, min z, max x, max y, max z} each
+  uint32_t v12[12];
+#pragma unroll
+  for (int sd = 0; sd < 2; ++sd)
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      v12[6 * sd + a] = wave_min_u32(cmn[sd][a]);
+      v12[6 * sd + 3 + a] = wave_max_u32(cmx[sd][a]);
+    }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < 12; ++j) S.cext[w][j] = v12[j];
+  }
+  __syncthreads();
+  if (tid < 12) {
+    uint32_t v = S.cext[0][tid];
+    for (int i = 1; i < kFinishBlockWaves; ++i)
+      v = (tid % 6) < 3 ? min(v, S.cext[i][tid]) : max(v, S.cext[i][tid]);
+    ext_out[node * 12 + tid] = v;
   }
 }
 
@@ -847,20 +920,39 @@ __global__ __launch_bounds__(kThreads) void tree_write_perm(const float4* __rest
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Trees above kLdsTree points (and above one leaf) are streamed through two
-// record arrays in the workspace; smaller ones need none (the library still
-// asks for its 256-byte minimum).
+// record arrays in the workspace, with two arrays of node extents (six
+// words per child of the last streamed level); smaller ones need none (the
+// library still asks for its 256-byte minimum).
 static bool stream_tree(int64_t n, int leaf) { return n > kLdsTree && n > leaf; }
 
+// Children of the last streamed level: twice its nodes.
+static int64_t stream_children(int64_t n, int leaf) {
+  int64_t nsize = n, kids = 0;
+  while (nsize > leaf && nsize > kLdsTree) {
+    kids = 2 * (n / nsize);
+    nsize >>= 1;
+  }
+  return kids;
+}
+
+static size_t stream_ext_bytes(int64_t n, int leaf) {
+  return align256((size_t)stream_children(n, leaf) * 6 * 4);
+}
+
 size_t tree_workspace_size(int64_t n, int leaf) {
-  return stream_tree(n, leaf) ? 2 * align256((size_t)n * 16) : 256;
+  return stream_tree(n, leaf) ? 2 * align256((size_t)n * 16) + 2 * stream_ext_bytes(n, leaf)
+                              : 256;
 }
 
 // The streamed build of n = leaf * 2^L > kLdsTree points (n > leaf) with the
-// records in ws (two arrays of n records).  Every launch is checked on the
-// host against the arrays it indexes: nodes * nsize == n.
+// records in ws (two arrays of n records, then two extent arrays).  Every
+// launch is checked on the host against the arrays it indexes: nodes * nsize
+// == n, and the 12 extent words per node of a level fit the extent array.
 static bt_status tree_stream_launch(const float* coords, int64_t n, int leaf, const float* R,
                                     int32_t* perm, void* ws, hipStream_t st) {
-  float4* rec[2] = {(float4*)ws, (float4*)((char*)ws + align256((size_t)n * 16))};
+  const size_t rb = align256((size_t)n * 16), eb = stream_ext_bytes(n, leaf);
+  float4* rec[2] = {(float4*)ws, (float4*)((char*)ws + rb)};
+  uint32_t* ext[2] = {(uint32_t*)((char*)ws + 2 * rb), (uint32_t*)((char*)ws + 2 * rb + eb)};
   float rr[9] = {1, 0, 0, 0, 1, 0, 0, 0, 1};
   if (R) for (int i = 0; i < 9; ++i) rr[i] = R[i];
   {
@@ -875,12 +967,17 @@ static bt_status tree_stream_launch(const float* coords, int64_t n, int leaf, co
   int cur = 0;
   while (nsize > leaf && nsize > kLdsTree) {
     const int64_t nodes = n / nsize;
-    if (nodes * nsize != n || (nsize & 1) || nodes > INT32_MAX) {
+    if (nodes * nsize != n || (nsize & 1) || nodes > INT32_MAX ||
+        (size_t)nodes * 12 * 4 > eb) {
       set_error("tree: nodes of %lld points do not tile %lld", (long long)nsize, (long long)n);
       return BT_EINVAL;
     }
+    // level 0 takes its extents from a pass over the records; later levels
+    // from the children's extents the level above wrote
     hipLaunchKernelGGL(tree_stream_split, dim3((unsigned)nodes), dim3(kLdsThreads), 0, st,
-                       rec[cur], rec[cur ^ 1], nsize);
+                       rec[cur], rec[cur ^ 1], nsize, nsize == n ? (const uint32_t*)nullptr
+                                                                 : (const uint32_t*)ext[cur],
+                       ext[cur ^ 1]);
     bt_status s = launch_status("tree_stream_split");
     if (s != BT_OK) return s;
     cur ^= 1;
