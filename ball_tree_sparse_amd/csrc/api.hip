@@ -70,9 +70,6 @@ bt_status bsa_bwd_launch(const void* q, const void* k, const void* v, const int3
 
 static bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
-// Largest padded tree (slots) that bt_build_padded accepts: one workgroup
-// builds it in LDS.
-constexpr int64_t kTreeMaxPadded = 8192;
 
 static bool valid_tree_shape(int64_t N, int32_t leaf) {
   return N >= 1 && leaf >= 1 && N < ((int64_t)1 << 31) && N % leaf == 0 && is_pow2(N / leaf);
@@ -273,10 +270,6 @@ bt_status bt_build_padded(const float* coords, int64_t N, int32_t leaf, const fl
   const int64_t S = bt_padded_size(N, leaf);
   BT_REQUIRE(S > 0, "need N >= 1, leaf >= 1 and fewer than 2^31 slots (N=%lld, leaf=%d)",
              (long long)N, leaf);
-  BT_REQUIRE(S <= kTreeMaxPadded || S == leaf,
-             "bt_build_padded: padded trees above %lld slots are not supported in this "
-             "version (one workgroup builds them in LDS); slots=%lld",
-             (long long)kTreeMaxPadded, (long long)S);
   if (R_host) {
     for (int i = 0; i < 9; ++i)
       BT_REQUIRE(R_host[i] == R_host[i] && R_host[i] - R_host[i] == 0.0f,

@@ -30,7 +30,8 @@
 //   padded      an uneven point count n: the tree has leaf * 2^L slots (the
 //               smallest that holds n); a node of m points gives its left
 //               child the ceil(m/2) smallest, and a leaf's unused slots hold
-//               -1 (up to 8,192 slots, in LDS as above).
+//               -1 (built as above: in LDS up to 8,192 slots, streamed
+//               above that).
 #include "common.h"
 
 // Test hook: the CPU emulation of these kernels under MemorySanitizer marks
@@ -327,7 +328,7 @@ BT_DEV void block_split(float4* R, int m, BlockSplitLds& L,
 BT_DEV void padded_segment(int n, int lev, int s, int* start, int* cnt) {
   int st = 0, c = n;
   for (int i = lev - 1; i >= 0; --i) {
-    const int nl = (c + 1) >> 1;
+    const int nl = c - (c >> 1);   // ceil(c/2) without overflow
     if ((s >> i) & 1) {
       st += nl;
       c -= nl;
@@ -604,11 +605,13 @@ __global__ __launch_bounds__(kLdsThreads) void tree_lds_build(
   lds_levels(srec, n, ncap, leaf, bsl, bgl, shist, perm);
 }
 
-// One workgroup per node of nf points (leaf < nf <= kLdsTree) of a full tree
-// whose records rec are in node order: the node is loaded into LDS, split
-// down to its leaves there, and its permutation entries written.
+// One workgroup per node of level lev (nodes of `slots` slots, leaf < slots
+// <= kLdsTree) of the tree of n points whose records rec are in node order
+// (node k holds the points padded_segment(n, lev, k) gives): the node is
+// loaded into LDS, split down to its leaves there, and the permutation
+// entries of its slots written.
 __global__ __launch_bounds__(kLdsThreads) void tree_lds_nodes(const float4* __restrict__ rec,
-                                                              int nf, int leaf,
+                                                              int n, int lev, int slots, int leaf,
                                                               int32_t* __restrict__ perm) {
   __shared__ float4 srec[kLdsTree];
   BT_LDS_POISON(srec);
@@ -618,10 +621,11 @@ __global__ __launch_bounds__(kLdsThreads) void tree_lds_nodes(const float4* __re
   BT_LDS_POISON(bsl);
   __shared__ BigSplitLds bgl;
   BT_LDS_POISON(bgl);
-  const int64_t base = (int64_t)blockIdx.x * nf;
-  for (int i = threadIdx.x; i < nf; i += kLdsThreads) srec[i] = rec[base + i];
+  int st, cnt;
+  padded_segment(n, lev, (int)blockIdx.x, &st, &cnt);
+  for (int i = threadIdx.x; i < cnt; i += kLdsThreads) srec[i] = rec[st + i];
   __syncthreads();
-  lds_levels(srec, nf, nf, leaf, bsl, bgl, shist, perm + base);
+  lds_levels(srec, cnt, slots, leaf, bsl, bgl, shist, perm + (int64_t)blockIdx.x * slots);
 }
 
 // LDS of a streamed split beyond the histograms: the children's extents per
@@ -635,8 +639,10 @@ struct StreamLds {
 // lanes of an atomic (the top levels' keys crowd into few bins).
 constexpr int kSubHist = 4;
 
-// One workgroup per node of m > kLdsTree points (m even): the split of
-// big_split with the node streamed from global memory in chunks of
+// One workgroup per node of level lev of the tree of n points (node k holds
+// the m points padded_segment(n, lev, k) gives, more than half of its
+// slots, which are above kLdsTree): the split of big_split (left child:
+// the ceil(m/2) smallest) with the node streamed from global memory in chunks of
 // kLdsThreads * kLdsPer positions (position p of a chunk belongs to thread
 // p % kLdsThreads in round p / kLdsThreads), the children written to out at
 // the node's place and their extents to ext_out[12 node ...] (left child,
@@ -646,7 +652,7 @@ constexpr int kSubHist = 4;
 // last one shorter), so that every pass resolves 8 bits that vary.  No
 // workgroup reads what another one of the same launch writes.
 __global__ __launch_bounds__(kLdsThreads) void tree_stream_split(
-    const float4* __restrict__ in, float4* __restrict__ out, int64_t m,
+    const float4* __restrict__ in, float4* __restrict__ out, int n, int lev,
     const uint32_t* __restrict__ ext_in, uint32_t* __restrict__ ext_out) {
   __shared__ uint32_t shist[kFinishBlockWaves][kSubHist][256];
   BT_LDS_POISON(shist);
@@ -660,7 +666,9 @@ __global__ __launch_bounds__(kLdsThreads) void tree_stream_split(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int sub = lane % kSubHist;
   const int64_t node = blockIdx.x;
-  const int64_t base = node * m;
+  int st, cnt;
+  padded_segment(n, lev, (int)node, &st, &cnt);
+  const int64_t base = st, m = cnt;
   const float4* R = in + base;
   float4* O = out + base;
   const int64_t nch = (m + CH - 1) / CH;
@@ -706,10 +714,10 @@ __global__ __launch_bounds__(kLdsThreads) void tree_stream_split(
   const float* RC = (const float*)R + axis;
   auto key_at = [&](int64_t p) -> uint32_t { return float_key(RC[4 * p]); };
 
-  // radix select of rank m/2-1: bits at and above hi are fixed in prefix;
-  // each pass takes the (up to) 8 bits below hi
+  // radix select of rank ceil(m/2)-1: bits at and above hi are fixed in
+  // prefix; each pass takes the (up to) 8 bits below hi
   uint32_t prefix = kmin;
-  uint32_t rank = (uint32_t)(m / 2 - 1);
+  uint32_t rank = (uint32_t)((m + 1) / 2 - 1);
   const uint32_t diff = kmin ^ kmax;
   if (diff) {
     int hi = 32 - __clz((int)diff);          // the keys agree above bit hi - 1
@@ -794,7 +802,7 @@ __global__ __launch_bounds__(kLdsThreads) void tree_stream_split(
   // stable partition, chunk by chunk in position order (as big_split, with
   // the pivot-equal and left counts of the earlier chunks carried along);
   // the children's extents are gathered on the way
-  const uint64_t half = (uint64_t)(m / 2);
+  const uint64_t half = (uint64_t)((m + 1) / 2);
   uint32_t E = 0, Lrun = 0;
   uint32_t cmn[2][3] = {{~0u, ~0u, ~0u}, {~0u, ~0u, ~0u}}, cmx[2][3] = {{0u, 0u, 0u}, {0u, 0u, 0u}};
   for (int64_t c = 0; c < nch; ++c) {
@@ -909,48 +917,59 @@ static bt_status single_leaf_launch(int64_t n, int64_t ncap, int32_t* perm, hipS
   return launch_status("tree_single_leaf");
 }
 
+// The leaves of level lev (leaf slots each) of the tree of n points in
+// ncap slots, records in node order: slot t of leaf j holds the index of
+// its t-th point, -1 past them.
 __global__ __launch_bounds__(kThreads) void tree_write_perm(const float4* __restrict__ rec,
-                                                            int64_t n, int32_t* __restrict__ perm) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    perm[i] = __float_as_int(rec[i].w);
+                                                            int n, int lev, int64_t ncap,
+                                                            int leaf, int32_t* __restrict__ perm) {
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < ncap;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(t / leaf), i = (int)(t - (int64_t)j * leaf);
+    int st, cnt;
+    padded_segment(n, lev, j, &st, &cnt);
+    perm[t] = i < cnt ? __float_as_int(rec[st + i].w) : -1;
+  }
 }
 
 // ------------------------------------------------------------------ host ----
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Trees above kLdsTree points (and above one leaf) are streamed through two
+// Trees above kLdsTree slots (and above one leaf) are streamed through two
 // record arrays in the workspace, with two arrays of node extents (six
 // words per child of the last streamed level); smaller ones need none (the
 // library still asks for its 256-byte minimum).
-static bool stream_tree(int64_t n, int leaf) { return n > kLdsTree && n > leaf; }
+static bool stream_tree(int64_t ncap, int leaf) { return ncap > kLdsTree && ncap > leaf; }
 
 // Children of the last streamed level: twice its nodes.
-static int64_t stream_children(int64_t n, int leaf) {
-  int64_t nsize = n, kids = 0;
-  while (nsize > leaf && nsize > kLdsTree) {
-    kids = 2 * (n / nsize);
-    nsize >>= 1;
+static int64_t stream_children(int64_t ncap, int leaf) {
+  int64_t slots = ncap, kids = 0;
+  while (slots > leaf && slots > kLdsTree) {
+    kids = 2 * (ncap / slots);
+    slots >>= 1;
   }
   return kids;
 }
 
-static size_t stream_ext_bytes(int64_t n, int leaf) {
-  return align256((size_t)stream_children(n, leaf) * 6 * 4);
+static size_t stream_ext_bytes(int64_t ncap, int leaf) {
+  return align256((size_t)stream_children(ncap, leaf) * 6 * 4);
 }
 
-size_t tree_workspace_size(int64_t n, int leaf) {
-  return stream_tree(n, leaf) ? 2 * align256((size_t)n * 16) + 2 * stream_ext_bytes(n, leaf)
-                              : 256;
+static size_t stream_ws_bytes(int64_t n, int64_t ncap, int leaf) {
+  return stream_tree(ncap, leaf) ? 2 * align256((size_t)n * 16) + 2 * stream_ext_bytes(ncap, leaf)
+                                 : 256;
 }
 
-// The streamed build of n = leaf * 2^L > kLdsTree points (n > leaf) with the
-// records in ws (two arrays of n records, then two extent arrays).  Every
-// launch is checked on the host against the arrays it indexes: nodes * nsize
-// == n, and the 12 extent words per node of a level fit the extent array.
-static bt_status tree_stream_launch(const float* coords, int64_t n, int leaf, const float* R,
-                                    int32_t* perm, void* ws, hipStream_t st) {
-  const size_t rb = align256((size_t)n * 16), eb = stream_ext_bytes(n, leaf);
+size_t tree_workspace_size(int64_t n, int leaf) { return stream_ws_bytes(n, n, leaf); }
+
+// The streamed build of n points in ncap = leaf * 2^L > kLdsTree slots (ncap
+// > leaf) with the records in ws (two arrays of n records, then two extent
+// arrays).  Every launch is checked on the host against the arrays it
+// indexes: the nodes of a level tile the slots, and the 12 extent words per
+// node fit the extent array.
+static bt_status tree_stream_launch(const float* coords, int64_t n, int64_t ncap, int leaf,
+                                    const float* R, int32_t* perm, void* ws, hipStream_t st) {
+  const size_t rb = align256((size_t)n * 16), eb = stream_ext_bytes(ncap, leaf);
   float4* rec[2] = {(float4*)ws, (float4*)((char*)ws + rb)};
   uint32_t* ext[2] = {(uint32_t*)((char*)ws + 2 * rb), (uint32_t*)((char*)ws + 2 * rb + eb)};
   float rr[9] = {1, 0, 0, 0, 1, 0, 0, 0, 1};
@@ -963,46 +982,47 @@ static bt_status tree_stream_launch(const float* coords, int64_t n, int leaf, co
     bt_status s = launch_status("tree_ingest");
     if (s != BT_OK) return s;
   }
-  int64_t nsize = n;
-  int cur = 0;
-  while (nsize > leaf && nsize > kLdsTree) {
-    const int64_t nodes = n / nsize;
-    if (nodes * nsize != n || (nsize & 1) || nodes > INT32_MAX ||
-        (size_t)nodes * 12 * 4 > eb) {
-      set_error("tree: nodes of %lld points do not tile %lld", (long long)nsize, (long long)n);
+  int64_t slots = ncap;
+  int lev = 0, cur = 0;
+  while (slots > leaf && slots > kLdsTree) {
+    const int64_t nodes = ncap / slots;
+    if (nodes * slots != ncap || nodes > INT32_MAX || (size_t)nodes * 12 * 4 > eb) {
+      set_error("tree: level %d geometry does not fit the workspace", lev);
       return BT_EINVAL;
     }
     // level 0 takes its extents from a pass over the records; later levels
     // from the children's extents the level above wrote
     hipLaunchKernelGGL(tree_stream_split, dim3((unsigned)nodes), dim3(kLdsThreads), 0, st,
-                       rec[cur], rec[cur ^ 1], nsize, nsize == n ? (const uint32_t*)nullptr
-                                                                 : (const uint32_t*)ext[cur],
+                       rec[cur], rec[cur ^ 1], (int)n, lev,
+                       lev == 0 ? (const uint32_t*)nullptr : (const uint32_t*)ext[cur],
                        ext[cur ^ 1]);
     bt_status s = launch_status("tree_stream_split");
     if (s != BT_OK) return s;
     cur ^= 1;
-    nsize >>= 1;
+    slots >>= 1;
+    ++lev;
   }
-  const int64_t nodes = n / nsize;
-  if (nodes * nsize != n || nodes > INT32_MAX) {
-    set_error("tree: nodes of %lld points do not tile %lld", (long long)nsize, (long long)n);
+  const int64_t nodes = ncap / slots;
+  if (nodes * slots != ncap || nodes > INT32_MAX) {
+    set_error("tree: level %d geometry does not fit the workspace", lev);
     return BT_EINVAL;
   }
-  if (nsize == leaf) {
-    int64_t g = (n + kThreads - 1) / kThreads;
+  if (slots == leaf) {
+    int64_t g = (ncap + kThreads - 1) / kThreads;
     if (g > 4096) g = 4096;
-    hipLaunchKernelGGL(tree_write_perm, dim3((int)g), dim3(kThreads), 0, st, rec[cur], n, perm);
+    hipLaunchKernelGGL(tree_write_perm, dim3((int)g), dim3(kThreads), 0, st, rec[cur], (int)n,
+                       lev, ncap, leaf, perm);
     return launch_status("tree_write_perm");
   }
   hipLaunchKernelGGL(tree_lds_nodes, dim3((unsigned)nodes), dim3(kLdsThreads), 0, st, rec[cur],
-                     (int)nsize, leaf, perm);
+                     (int)n, lev, (int)slots, leaf, perm);
   return launch_status("tree_lds_nodes");
 }
 
 bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const float* R,
                             int32_t* perm, void* ws, hipStream_t st) {
   if (n == leaf) return single_leaf_launch(n, n, perm, st);
-  if (stream_tree(n, leaf)) return tree_stream_launch(coords, n, leaf, R, perm, ws, st);
+  if (stream_tree(n, leaf)) return tree_stream_launch(coords, n, n, leaf, R, perm, ws, st);
   return tree_lds_launch(coords, n, n, leaf, R, perm, st);
 }
 
@@ -1012,13 +1032,17 @@ int64_t tree_padded_slots(int64_t n, int leaf) {
   return cap;
 }
 
-size_t tree_padded_workspace_size(int64_t, int) { return 256; }
+size_t tree_padded_workspace_size(int64_t n, int leaf) {
+  return stream_ws_bytes(n, tree_padded_slots(n, leaf), leaf);
+}
 
-// Padded tree of n points: one leaf of any size, or up to kLdsTree slots.
+// Padded tree of n points: one leaf of any size, up to kLdsTree slots in
+// LDS, or streamed above that.
 bt_status tree_build_padded_launch(const float* coords, int64_t n, int leaf, const float* R,
-                                   int32_t* perm, void*, hipStream_t st) {
+                                   int32_t* perm, void* ws, hipStream_t st) {
   const int64_t ncap = tree_padded_slots(n, leaf);
   if (ncap == leaf) return single_leaf_launch(n, ncap, perm, st);
+  if (stream_tree(ncap, leaf)) return tree_stream_launch(coords, n, ncap, leaf, R, perm, ws, st);
   return tree_lds_launch(coords, n, ncap, leaf, R, perm, st);
 }
 

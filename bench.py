@@ -426,14 +426,15 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
                           "mfma_frac": 2.5 * flops / (us4 * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
                           "vs_forward": us4 / us}
     del q, k, v, out, bws, bws2, bws3, bdo, bgr
-    # uneven N: 65,000 sphere points in 65,536 slots (535 unused slots spread
-    # over the balls), masked ball attention; three input sets rotate
+    # uneven N: 65,000 sphere points in the 65,536 slots of their padded GPU
+    # tree (leaf 128; the 536 unused slots end up spread over the leaves),
+    # masked ball attention; three input sets rotate
     n3, slots = 65000, 65536
     w = synth.make("sphere", n=n3)
-    g3 = torch.Generator().manual_seed(11)
-    pp = torch.full((slots,), -1, dtype=torch.int32)
-    pp[torch.randperm(slots, generator=g3)[:n3]] = torch.randperm(n3, generator=g3).to(torch.int32)
-    pp = pp.to(dev)
+    c3 = torch.from_numpy(w.coords).to(dev)
+    us_pt = _event_us(torch, lambda: ops.bt_build_padded(c3, w.leaf), 20, warm=3)
+    pp = ops.bt_build_padded(c3, w.leaf)
+    assert pp.numel() == slots
     sets = [tuple(t.to(dev).clone() for t in (w.q, w.k, w.v)) for _ in range(3)]
     o3 = [torch.empty_like(sets[0][0]) for _ in range(3)]
     it = [0]
@@ -444,7 +445,9 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
         ops.ball_attn_padded(*sets[i], pp, w.ball, out=o3[i])
     us3 = _event_us(torch, call3, 300, warm=100)
     nb3 = 4 * n3 * w.H * w.d * 2 + 4 * slots
-    rows["f3_ball_attn_padded"] = {"workload": "N=65,000 in 65,536 slots, ball 128, H=8, d=32 bf16",
+    rows["f3_ball_attn_padded"] = {"workload": "N=65,000 in the 65,536 slots of the padded GPU "
+                                                "tree, ball 128, H=8, d=32 bf16",
+                                   "padded_tree_build_us": us_pt,
                                    "us": us3, "GBps": nb3 / us3 / 1e3,
                                    "hbm_frac": nb3 / us3 / 1e3 / HBM_PEAK_GBS}
     del sets, o3

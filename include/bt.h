@@ -197,10 +197,11 @@ bt_status ball_attn(const void* q, const void* k, const void* v,
  * bt_build_padded: coords [N,3] fp32 (device); R_host NULL (no rotation) or
  *   a finite 3x3 row-major fp32 rotation in host memory, applied as in
  *   bt_rotate_build; writes perm [S] int32 (device).  ws: device workspace of
- *   bt_build_padded_workspace_size(N, leaf) bytes, 256-byte aligned.  In this
- *   build S <= 8192 (or S == leaf, a single leaf): one workgroup builds the
- *   padded tree in LDS.  Errors: BT_EINVAL for null pointers or a violated limit,
- *   BT_ENOMEM for a short workspace.
+ *   bt_build_padded_workspace_size(N, leaf) bytes, 256-byte aligned (the
+ *   256-byte minimum up to 8,192 slots, which one workgroup builds in LDS;
+ *   two record arrays of N points above that, built as bt_build does).
+ *   Errors: BT_EINVAL for null pointers or a violated limit, BT_ENOMEM for a
+ *   short workspace.
  * bt_permute_padded: perm has n_slots entries, negative for an unused slot,
  *   the others row indices below n_rows (not checked beyond clamping).
  *   GATHER:  dst[t] = src[perm[t]] (dst [n_slots] rows, src [n_rows] rows),

@@ -19,7 +19,10 @@ import torch  # noqa: E402
                                     (700, 700), (1024, 32), (129, 1), (4000, 4096),
                                     # one-workgroup LDS builder (1,025-8,192 slots)
                                     (3586, 32), (5000, 64), (1025, 1), (6001, 3), (8192, 64),
-                                    (2049, 2048)])
+                                    (2049, 2048),
+                                    # streamed splits above 8,192 slots
+                                    (9000, 64), (12289, 3), (16385, 128), (20000, 8192),
+                                    (65000, 128)])
 def test_padded_tree_bit_exact(n, leaf):
     dev = gpu()
     rng = np.random.default_rng(n * 7 + leaf)
@@ -106,15 +109,17 @@ def test_ball_attn_padded(n, leaf, H, d, ball, dtype):
 
 def test_ball_attn_padded_full_size():
     """65,000 points of the sphere workload in 65,536 slots (ball 128, 8 heads,
-    d 32): every output row against the oracle."""
+    d 32): the padded GPU tree bit for bit, then every output row of padded
+    attention through it against the oracle."""
     dev = gpu()
     w = synth.make("sphere", n=65000)
+    say("bt_build_padded + ball_attn_padded sphere 65000")
+    p = ops.bt_build_padded(torch.from_numpy(w.coords).to(dev), w.leaf)
+    out = ops.ball_attn_padded(w.q.to(dev), w.k.to(dev), w.v.to(dev), p, w.ball)
+    torch.cuda.synchronize()
     perm = T.build_padded(w.coords, w.leaf).astype(np.int32)
     assert len(perm) == 65536
-    say("ball_attn_padded sphere 65000")
-    out = ops.ball_attn_padded(w.q.to(dev), w.k.to(dev), w.v.to(dev),
-                               torch.from_numpy(perm).to(dev), w.ball)
-    torch.cuda.synchronize()
+    assert np.array_equal(p.cpu().numpy(), perm)
     assert max_abs(out.cpu(), A.ball_attn_padded(w.q, w.k, w.v, perm, w.ball)) <= 2e-2
 
 

@@ -115,11 +115,11 @@ def test_tiny_workload_bit_exact():
     assert np.array_equal(_gpu_tree(w.coords, w.leaf), T.build(w.coords, w.leaf))
 
 
-def test_rejects_above_limit():
+def test_rejects_bad_shapes():
     dev = gpu()
-    c = torch.zeros((8193, 3), device=dev)
+    c = torch.zeros((12, 3), device=dev)
     with pytest.raises(ops.BtError):
-        ops.bt_build_padded(c, 2)                    # 16,384 slots
+        ops.bt_build(c, 5)                           # 12 is not 5 * 2^L
 
 
 @pytest.mark.parametrize("name", ["sphere", "rotpair", "cosmo"])
