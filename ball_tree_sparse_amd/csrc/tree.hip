@@ -23,10 +23,12 @@
 //   above that  the records go to the workspace; each level whose nodes
 //               hold more than 8,192 points is one launch with a workgroup
 //               per node, which streams its node from one record array to
-//               the other (extents, radix select, stable partition chunk by
-//               chunk); then one workgroup per node of <= 8,192 points
-//               finishes its subtree in LDS.  No workgroup ever reads what
-//               another one of the same launch writes.
+//               the other (radix select on the 8 bits below the highest bit
+//               not yet fixed, stable partition chunk by chunk, the
+//               children's extents gathered on the way); then one workgroup
+//               per node of <= 8,192 points finishes its subtree in LDS.  No
+//               workgroup ever reads what another one of the same launch
+//               writes.
 //   padded      an uneven point count n: the tree has leaf * 2^L slots (the
 //               smallest that holds n); a node of m points gives its left
 //               child the ceil(m/2) smallest, and a leaf's unused slots hold
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void tree_ingest(const float* __restrict_
   }
 }
 
-// ---------------------------------------------------------------- finish ----
+// ------------------------------------------------------------ LDS splits ----
 
 // Split the m-point segment R[0..m) of a wave's LDS node in place: the left
 // part takes the ceil(m/2) smallest points (m/2 for the even m of a full tree).
