@@ -83,8 +83,9 @@ const char* bt_version(void);
  *   Up to 8,192 points one workgroup builds the tree in LDS (from 1,025
  *   points straight from coords: the workspace size is then the 256-byte
  *   minimum); above that each node is split by one workgroup, streamed
- *   through two record arrays in ws, until the nodes have at most 8,192
- *   points, which one workgroup each finishes in LDS.
+ *   through two record arrays in ws (with two small arrays of node
+ *   extents), until the nodes have at most 8,192 points, which one
+ *   workgroup each finishes in LDS.
  *   Errors: BT_EINVAL for null pointers, N not leaf*2^L, N >= 2^31;
  *   BT_ENOMEM for a short workspace.
  * ---------------------------------------------------------------------- */

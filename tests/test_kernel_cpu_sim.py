@@ -508,10 +508,12 @@ def _tree_padded(sim, coords, leaf, R=None):
 
 @pytest.mark.parametrize("n,leaf", [(972, 32), (1000, 16), (513, 64), (5, 2), (3, 1), (1, 1),
                                     (2, 1), (700, 700), (1024, 32), (129, 1),
-                                    (3586, 32), (5000, 64), (1025, 1), (6001, 3), (2049, 2048)])
+                                    (3586, 32), (5000, 64), (1025, 1), (6001, 3), (2049, 2048),
+                                    (9000, 64), (20000, 8192)])
 def test_padded_tree_kernels_bit_exact(sim, n, leaf):
-    """Uneven N: the padded tree (one workgroup in LDS; above 1,024 slots the
-    coordinates are read straight into LDS), bit for bit."""
+    """Uneven N: the padded tree (one workgroup in LDS up to 8,192 slots;
+    above that streamed splits of the padded segments, then LDS or the
+    leaves directly), bit for bit."""
     rng = np.random.default_rng(n * 7 + leaf)
     c = synth.uniform_cube(rng, n)
     assert np.array_equal(_tree_padded(sim, c, leaf), T.build_padded(c, leaf))
