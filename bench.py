@@ -539,7 +539,10 @@ def side_rows(dev, torch, ops, synth, sel_check=None):
         alg = n_ * (12 + 32 * levels + 4)
         builds[name] = {"N": n_, "leaf": leaf_, "levels": levels, "build_us": us_t,
                         "points_per_s": n_ / (us_t * 1e-6), "algorithmic_bytes": alg,
-                        "GBps": alg / us_t / 1e3, "hbm_frac": alg / us_t / 1e3 / HBM_PEAK_GBS}
+                        "GBps": alg / us_t / 1e3, "hbm_frac": alg / us_t / 1e3 / HBM_PEAK_GBS,
+                        # HBM bytes per build from FETCH_SIZE / WRITE_SIZE counters of
+                        # its kernels (profiles/), null once tree.hip has changed
+                        "traffic": _traffic(f"tree/{name}", ["tree.hip", "common.h"])}
         del ct, wst, ptt
     rows["a1_a4_tree_build"] = {"workload": "GPU ball trees of the sphere (65,536), rotated-pair "
                                             "(262,144) and cosmology (1,048,576) clouds",
