@@ -33,6 +33,7 @@ bt_status tree_build_launch(const float* coords, int64_t n, int leaf, const floa
 bt_status permute_launch(const void* src, const int32_t* perm, int64_t n, int64_t row_bytes,
                          bt_perm_mode mode, void* dst, hipStream_t st);
 bt_status invert_perm_launch(const int32_t* perm, int64_t n, int32_t* inv, hipStream_t st);
+bt_status count_nonfinite_launch(const float* x, int64_t n, uint32_t* count, hipStream_t st);
 bt_status ball_attn_launch(const void* q, const void* k, const void* v, const int32_t* perm,
                            int64_t N, int32_t ball, int32_t H, int32_t d, bt_dtype dt,
                            void* out, hipStream_t st);
@@ -149,6 +150,13 @@ bt_status bt_permute(const void* src, const int32_t* perm, int64_t N, int64_t ro
   BT_REQUIRE(!overlaps(src, (size_t)(N * row_bytes), dst, (size_t)(N * row_bytes)),
              "src and dst must not overlap");
   return permute_launch(src, perm, N, row_bytes, mode, dst, (hipStream_t)stream);
+}
+
+bt_status bt_count_nonfinite(const float* x, int64_t n, uint32_t* count, void* stream) {
+  BT_REQUIRE(n >= 0, "need n >= 0");
+  BT_REQUIRE(count != nullptr && (x != nullptr || n == 0), "x and count must be non-null");
+  BT_REQUIRE(((uintptr_t)count & 3) == 0, "count must be 4-byte aligned");
+  return count_nonfinite_launch(x, n, count, (hipStream_t)stream);
 }
 
 bt_status bt_invert_perm(const int32_t* perm, int64_t N, int32_t* inv, void* stream) {

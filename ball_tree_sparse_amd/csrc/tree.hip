@@ -934,6 +934,37 @@ __global__ __launch_bounds__(kThreads) void tree_write_perm(const float4* __rest
   }
 }
 
+// -------------------------------------------------------- coordinate check ----
+// Finite coordinates are a precondition of the builders; this debug check
+// counts the values of x[0..n) that are NaN or infinite into *count (which
+// tree_zero_count clears first, on the same stream).
+__global__ void tree_zero_count(uint32_t* __restrict__ count) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *count = 0u;
+}
+
+__global__ __launch_bounds__(kThreads) void tree_count_nonfinite(const float* __restrict__ x,
+                                                                 int64_t n,
+                                                                 uint32_t* __restrict__ count) {
+  uint32_t c = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t u = __float_as_uint(x[i]);
+    c += (u & 0x7f800000u) == 0x7f800000u;         // exponent all ones: NaN or infinity
+  }
+  c = wave_sum_u32(c);
+  if ((threadIdx.x & 63) == 0 && c) atomicAdd(count, c);
+}
+
+bt_status count_nonfinite_launch(const float* x, int64_t n, uint32_t* count, hipStream_t st) {
+  hipLaunchKernelGGL(tree_zero_count, dim3(1), dim3(64), 0, st, count);
+  bt_status s = launch_status("tree_zero_count");
+  if (s != BT_OK || n == 0) return s;
+  int64_t g = (n + kThreads - 1) / kThreads;
+  if (g > 1024) g = 1024;
+  hipLaunchKernelGGL(tree_count_nonfinite, dim3((int)g), dim3(kThreads), 0, st, x, n, count);
+  return launch_status("tree_count_nonfinite");
+}
+
 // ------------------------------------------------------------------ host ----
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

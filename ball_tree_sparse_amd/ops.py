@@ -52,6 +52,7 @@ _SIGS = [
                                   C.c_size_t, _P]),
     ("bt_permute", C.c_int, [_P, _P, C.c_int64, C.c_int64, C.c_int, _P, _P]),
     ("bt_invert_perm", C.c_int, [_P, C.c_int64, _P, _P]),
+    ("bt_count_nonfinite", C.c_int, [_P, C.c_int64, _P, _P]),
     ("ball_attn", C.c_int, [_P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32,
                             C.c_int, _P, _P]),
     ("bsa_workspace_size", C.c_size_t, [C.c_int64, C.c_int32, C.c_int32,
@@ -273,6 +274,19 @@ def bt_permute_padded(src, perm, n_rows: int, mode: int, dst=None):
     _check(lib().bt_permute_padded(_ptr(src), _ptr(perm), n_rows, S, row_bytes, mode, _ptr(dst),
                                    _stream(src.device)))
     return dst
+
+
+def bt_count_nonfinite(x, count=None):
+    """Number of NaN or infinite values in the fp32 tensor x (device int32
+    [1] holding the count; the debug check of the builders' precondition)."""
+    _dev(x, "x", torch.float32)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    _dev(count, "count", torch.int32)
+    if count.numel() != 1:
+        raise ValueError("count must hold one int32")
+    _check(lib().bt_count_nonfinite(_ptr(x), x.numel(), _ptr(count), _stream(x.device)))
+    return count
 
 
 def bt_invert_perm(perm, inv=None):

@@ -79,7 +79,8 @@ const char* bt_version(void);
  * bt_build: coords [N,3] fp32 (device), N = leaf * 2^L with 1 <= leaf,
  *   N < 2^31; writes perm [N] int32 (device).  ws: device workspace of at
  *   least bt_build_workspace_size(N, leaf) bytes, 256-byte aligned.
- *   Coordinates must be finite (not checked).
+ *   Coordinates must be finite (not checked here; bt_count_nonfinite is the
+ *   debug check).
  *   Up to 8,192 points one workgroup builds the tree in LDS (from 1,025
  *   points straight from coords: the workspace size is then the 256-byte
  *   minimum); above that each node is split by one workgroup, streamed
@@ -92,6 +93,15 @@ const char* bt_version(void);
 size_t bt_build_workspace_size(int64_t N, int32_t leaf);
 bt_status bt_build(const float* coords, int64_t N, int32_t leaf, int32_t* perm,
                    void* ws, size_t ws_bytes, void* stream);
+
+/* bt_count_nonfinite: the debug check of the builders' precondition.  Writes
+ * to *count (a device uint32) the number of the n fp32 values x[0..n) (pass
+ * coords and n = 3 N) that are NaN or infinite; 0 means the coordinates may
+ * be passed to bt_build.  Asynchronous on stream: *count is cleared and then
+ * accumulated by kernels on that stream, so read it after the stream.
+ * Errors: BT_EINVAL for n < 0, a null count (or a null x with n > 0), or a
+ * count that is not 4-byte aligned. */
+bt_status bt_count_nonfinite(const float* x, int64_t n, uint32_t* count, void* stream);
 
 /* bt_rotate_build: the second tree of a rotated pair (Erwin thread: trees are
  * rotated instead of shifting windows, so that alternate layers exchange

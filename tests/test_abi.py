@@ -87,6 +87,14 @@ def test_permute_rejects(L):
     assert L.bt_invert_perm(a, 4, a, None) == ops.BT_EINVAL               # overlap
 
 
+def test_count_nonfinite_rejects(L):
+    a = _fake(64)
+    assert L.bt_count_nonfinite(a, -1, a, None) == ops.BT_EINVAL
+    assert L.bt_count_nonfinite(a, 4, None, None) == ops.BT_EINVAL
+    assert L.bt_count_nonfinite(None, 4, a, None) == ops.BT_EINVAL
+    assert L.bt_count_nonfinite(a, 4, C.c_void_p(a.value + 2), None) == ops.BT_EINVAL
+
+
 def test_ball_attn_rejects(L):
     q, k, v, o = (_fake(1 << 16) for _ in range(4))
     args = lambda **kw: dict(dict(q=q, k=k, v=v, perm=None, N=1024, ball=32, H=4, d=16,

@@ -178,3 +178,25 @@ def test_deterministic_and_workspace_reuse():
     b = ops.bt_build(c, 32, workspace=ws).clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_count_nonfinite():
+    """The debug check of the builders' precondition: NaN and both
+    infinities are counted, -0.0, denormals and the largest finite values
+    are not; a second call on a clean array reads 0."""
+    dev = gpu()
+    rng = np.random.default_rng(8)
+    c = rng.standard_normal((10001, 3)).astype(np.float32)
+    c[5, 1] = np.nan
+    c[77, 0] = np.inf
+    c[9000, 2] = -np.inf
+    c[10, 0] = -0.0
+    c[11, 1] = np.float32(1e-42)                      # a denormal
+    c[12, 2] = np.finfo(np.float32).max
+    say("bt_count_nonfinite")
+    n_bad = ops.bt_count_nonfinite(torch.from_numpy(c).to(dev))
+    torch.cuda.synchronize()
+    assert int(n_bad.item()) == 3
+    clean = torch.from_numpy(np.nan_to_num(c, nan=0.0, posinf=1.0, neginf=-1.0)).to(dev)
+    assert int(ops.bt_count_nonfinite(clean, count=n_bad).item()) == 0
+    assert int(ops.bt_count_nonfinite(clean[:0]).item()) == 0
