@@ -25,8 +25,9 @@
 //               per node, which streams its node from one record array to
 //               the other (radix select on the 8 bits below the highest bit
 //               not yet fixed, stable partition chunk by chunk, the
-//               children's extents gathered on the way); then one workgroup
-//               per node of <= 8,192 points finishes its subtree in LDS.  No
+//               children's extents gathered on the way), down to nodes of
+//               2,048 slots; then one workgroup per node finishes its
+//               subtree in LDS.  No
 //               workgroup ever reads what another one of the same launch
 //               writes.
 //   padded      an uneven point count n: the tree has leaf * 2^L slots (the
@@ -974,10 +975,21 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // library still asks for its 256-byte minimum).
 static bool stream_tree(int64_t ncap, int leaf) { return ncap > kLdsTree && ncap > leaf; }
 
+// A streamed build splits nodes down to this many slots before one
+// workgroup per node finishes them in LDS: more, smaller nodes keep more
+// CUs busy in the LDS finish (65,536 points: 395 us stopping at 8,192 slots,
+// 345 us at 2,048; 262,144 points: 1.25 / 1.20 ms; 1,048,576 points about
+// 5.2 ms either way).
+#ifndef BT_STREAM_STOP
+#define BT_STREAM_STOP 2048
+#endif
+constexpr int64_t kStreamStop = BT_STREAM_STOP;
+static_assert(kStreamStop <= kLdsTree, "nodes finished in LDS fit it");
+
 // Children of the last streamed level: twice its nodes.
 static int64_t stream_children(int64_t ncap, int leaf) {
   int64_t slots = ncap, kids = 0;
-  while (slots > leaf && slots > kLdsTree) {
+  while (slots > leaf && slots > kStreamStop) {
     kids = 2 * (ncap / slots);
     slots >>= 1;
   }
@@ -1017,7 +1029,7 @@ static bt_status tree_stream_launch(const float* coords, int64_t n, int64_t ncap
   }
   int64_t slots = ncap;
   int lev = 0, cur = 0;
-  while (slots > leaf && slots > kLdsTree) {
+  while (slots > leaf && slots > kStreamStop) {
     const int64_t nodes = ncap / slots;
     if (nodes * slots != ncap || nodes > INT32_MAX || (size_t)nodes * 12 * 4 > eb) {
       set_error("tree: level %d geometry does not fit the workspace", lev);
