@@ -245,7 +245,7 @@ def test_rotated_tree_kernels_bit_exact(sim):
 @pytest.mark.parametrize("shuffle", [1, 2])
 def test_tree_kernels_shuffled_workgroups(sim, shuffle):
     """Workgroups of every launch in a seeded random order (32,768 points,
-    leaf 16: streamed levels of two and four workgroups, then four
+    leaf 16: streamed levels of up to eight workgroups, then sixteen
     workgroups in LDS): the result does not depend on the order (no
     workgroup reads what another one of the same launch writes)."""
     w = synth.make("rotpair", n=32768, features=False)
@@ -302,8 +302,8 @@ def test_sphere_65536_tree(sim, leaf):
 
 @SLOW
 def test_tree_many_nodes(sim):
-    """524,288 points, leaf 128: six streamed levels (up to 32 workgroups),
-    then 64 workgroups of 8,192 points in LDS."""
+    """524,288 points, leaf 128: eight streamed levels (up to 128
+    workgroups), then 256 workgroups of 2,048 points in LDS."""
     w = synth.make("rotpair", n=524288, features=False)
     assert np.array_equal(_tree(sim, w.coords, 128, shuffle=11, timeout=7200),
                           T.build(w.coords, 128))
