@@ -180,6 +180,27 @@ def test_deterministic_and_workspace_reuse():
     assert torch.equal(a, b)
 
 
+def test_streamed_build_deterministic_with_garbage_workspace():
+    """The streamed build (65,536 points, leaf 64) twice on one workspace
+    filled with garbage, and once more with the rotation on the same
+    workspace: equal to the oracle every time (nothing reads workspace bytes
+    it has not written)."""
+    dev = gpu()
+    w = synth.make("rotpair", n=65536, features=False)
+    c = torch.from_numpy(w.coords).to(dev)
+    ws = torch.empty(ops.bt_build_workspace_size(c.shape[0], 64), dtype=torch.uint8, device=dev)
+    ws.fill_(0xA5)
+    say("bt_build streamed, garbage workspace")
+    a = ops.bt_build(c, 64, workspace=ws).clone()
+    b = ops.bt_build(c, 64, workspace=ws).clone()
+    r = ops.bt_rotate_build(c, 64, w.R, workspace=ws).clone()
+    torch.cuda.synchronize()
+    want = T.build(w.coords, 64)
+    assert np.array_equal(a.cpu().numpy(), want)
+    assert torch.equal(a, b)
+    assert np.array_equal(r.cpu().numpy(), T.rotate_build(w.coords, 64, w.R))
+
+
 def test_count_nonfinite():
     """The debug check of the builders' precondition: NaN and both
     infinities are counted, -0.0, denormals and the largest finite values
